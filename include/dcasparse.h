@@ -1,0 +1,139 @@
+/*
+ * dcasparse.h — C ABI of the MI355X (gfx950) library for long-context prefill
+ * attention with Dual Chunk Attention (DCA), YaRN logit scaling and
+ * vertical-slash sparsity chosen per prefill chunk.
+ *
+ * What is computed (sources: "Qwen2.5-1M Technical Report" as summarised on
+ * the xllm-io paper-review page, section 4 "Inference & deployment":
+ * Dual Chunk Attention (Figure 2), the YaRN attention-scaling equation, and
+ * the sparse attention of Figure 4; chunk size from the agentlenshq release
+ * blog, section "Sparse Attention"):
+ *
+ *   For query head h (KV head g = h / (h_q / h_kv)), query row i at absolute
+ *   position p_i and key j of the prefix, with S = dca_chunk, W = dca_local,
+ *   r = position mod S and m = position div S:
+ *     key position      pi_k = r_j
+ *     query position    pi_q = r_i                    if m_j == m_i   (intra-chunk)
+ *                             = min(S + r_i, S+W-1)    if m_j == m_i-1 (successive chunk)
+ *                             = S + W - 1              if m_j <= m_i-2 (inter-chunk)
+ *     logit l_ij = (0.1 ln s + 1)^2 / sqrt(d) * < RoPE(q_i, pi_q), RoPE(k_j, pi_k) >
+ *   RoPE pairs component c with c + d/2 and turns it by position * base^(-2c/d).
+ *   out_i = sum_{j in A(i)} softmax_j(l_ij) v_j, lse_i = ln sum_{j in A(i)} e^{l_ij}.
+ *   Dense: A(i) = { j <= p_i }.  Sparse (block cover, 64-row granule): for the
+ *   query block whose first row sits at i0 (a multiple of 64), every selected
+ *   slash offset delta (delta = 0 is always included) covers keys
+ *   [i0-delta, i0-delta+63]; the selected vertical columns are added; row i
+ *   attends the covered keys j <= p_i.
+ *
+ * Conventions shared by every entry point:
+ *   - Tensors are row-major, contiguous, device memory, raw bfloat16 bits:
+ *       q, out : [n_q][h_q][head_dim]      k, v : [n_k][h_kv][head_dim]
+ *     q and k are BEFORE any rotary embedding: the library applies every
+ *     rotation itself.
+ *   - positions is a HOST int32 array of n_q entries that must be the
+ *     contiguous run p0, p0+1, ..., n_k-1 (a chunk of a chunked prefill whose
+ *     KV prefix ends with the chunk), with p0 a multiple of 64.  It is read
+ *     before anything is enqueued so that malformed calls fail synchronously.
+ *   - Every buffer belongs to the caller.  No entry point allocates device
+ *     memory: scratch comes from cfg->workspace, sized by dca_workspace_size.
+ *   - Work is enqueued on cfg->stream and the call returns without waiting.
+ *     Outputs are bitwise deterministic for identical inputs.
+ *   - Calls sharing one workspace must not overlap in time (same stream, or
+ *     the caller orders them).
+ *   - Errors: validation happens before any launch; on error nothing is
+ *     enqueued and no output is written.  No exception crosses the ABI.
+ */
+#ifndef DCASPARSE_H
+#define DCASPARSE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__) || defined(__clang__)
+#define DCA_API __attribute__((visibility("default")))
+#else
+#define DCA_API
+#endif
+
+#define DCA_OK            0
+#define DCA_EINVAL       (-1)  /* null pointer, inconsistent sizes, bad positions */
+#define DCA_EUNSUPPORTED (-2)  /* head_dim != 128, dca_chunk % 64, p0 % 64, W > S, ... */
+#define DCA_EWORKSPACE   (-3)  /* workspace missing or smaller than dca_workspace_size */
+#define DCA_EHIP         (-4)  /* a HIP launch or runtime call failed */
+
+typedef uint16_t dca_bf16;     /* raw bfloat16 bits */
+
+/* Number of optional timing events dca_sparse_prefill records (see stage_events). */
+#define DCA_STAGE_COUNT 4      /* 0: key rotation, 1: sparse plan, 2: attention, 3: LSE merge */
+
+typedef struct dca_cfg {
+  int32_t n_q;            /* query rows in this call (>= 1) */
+  int32_t n_k;            /* keys in the prefix; must equal positions[n_q-1] + 1 */
+  int32_t h_q, h_kv;      /* query / KV heads; h_q % h_kv == 0 (GQA: consecutive grouping) */
+  int32_t head_dim;       /* must be 128 */
+  int32_t dca_chunk;      /* S: multiple of 64, >= 64 */
+  int32_t dca_local;      /* W: 0 < W <= S */
+  double  rope_base;      /* RoPE base, > 1 (e.g. 1e6, 1e7) */
+  double  yarn_s;         /* s: logit factor (0.1 ln s + 1)^2 when s > 1, else 1 */
+  int32_t vs_last_q;      /* index builder: scoring rows = the last min(vs_last_q, n_q) rows; 1..64 */
+  int32_t vs_k_vertical;  /* k_v: vertical columns per query head (>= 0) */
+  int32_t vs_k_slash;     /* k_s: slash offsets per query head (>= 0) */
+  /* Sparse pattern for dca_sparse_prefill (device int32).  Both NULL: dense
+   * causal DCA attention.  Otherwise v_idx is [h_q][vs_k_vertical] absolute
+   * key ids and s_off is [h_q][vs_k_slash] offsets, each row ascending, with
+   * -1 entries as padding (vs_index_build's output format).  Entries out of
+   * range are ignored; a row that is not ascending gives an unspecified cover
+   * but never an out-of-bounds access. */
+  const int32_t *v_idx;
+  const int32_t *s_off;
+  float   *lse_out;       /* optional device [h_q][n_q] natural-log LSE of each row; NULL: not written */
+  float   precise_norm;   /* keys whose L2 norm exceeds this get split-bf16 (hi+lo) logits;
+                             0: default 2*sqrt(head_dim); < 0: never */
+  int32_t split_k;        /* key-range splits per query block, merged by LSE: 0 = library's choice */
+  void   *workspace;      /* device scratch, >= dca_workspace_size bytes, 256-byte aligned */
+  size_t  workspace_bytes;
+  void   *stream;         /* hipStream_t; NULL = the null stream */
+  /* Optional: array of 2*DCA_STAGE_COUNT hipEvent_t (start, stop per stage)
+   * that dca_sparse_prefill records on cfg->stream around each stage; NULL =
+   * no timing.  Stages that do not run still get both events recorded. */
+  void  **stage_events;
+} dca_cfg;
+
+/* Bytes of workspace both entry points need for this configuration (the
+ * largest of the two).  Pure host computation.  Returns DCA_OK and writes
+ * *bytes, or a validation error. */
+DCA_API int dca_workspace_size(const dca_cfg *cfg, size_t *bytes);
+
+/* Vertical-slash index of one prefill chunk (paper-review page, section 4,
+ * Figure 4: key tokens chosen per chunk, with continuous relative positions
+ * restored while choosing).  Scores the last n_s = min(vs_last_q, n_q) rows
+ * against every key j <= p_i in float64, with query position r_i for keys of
+ * its own DCA chunk and S + r_i for keys of any earlier chunk (key position
+ * r_j), the same YaRN-scaled logits, and a row softmax.  vertical[j] = sum of
+ * the rows' probabilities in column j; slash[delta] = sum over rows of the
+ * probability at key p_i - delta.  Offset 0 is always selected.  The k best
+ * of each list by (score desc, index asc) are written ascending:
+ *   v_idx [h_q][vs_k_vertical] key ids, s_off [h_q][vs_k_slash] offsets,
+ * padded with -1 when there are fewer candidates (n_k keys, p_last+1 offsets).
+ * Inputs q (only its last n_s rows are read) and k as in the conventions. */
+DCA_API int vs_index_build(const dca_bf16 *q, const dca_bf16 *k, const int32_t *positions,
+                   const dca_cfg *cfg, int32_t *v_idx, int32_t *s_off);
+
+/* DCA prefill attention of one chunk over its KV prefix, dense or
+ * block-sparse (see the definition at the top).  Writes out [n_q][h_q][128]
+ * bf16 (round to nearest even from fp32) and, when cfg->lse_out is set, the
+ * natural-log LSE of every row.  bf16 inputs, fp32 accumulation. */
+DCA_API int dca_sparse_prefill(const dca_bf16 *q, const dca_bf16 *k, const dca_bf16 *v,
+                       const int32_t *positions, const dca_cfg *cfg, dca_bf16 *out);
+
+/* Static message for an error code; never NULL. */
+DCA_API const char *dca_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DCASPARSE_H */

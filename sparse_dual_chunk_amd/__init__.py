@@ -1,0 +1,185 @@
+"""Python binding of libdcasparse.so: DCA + vertical-slash sparse prefill attention on MI355X.
+
+Argument marshalling only.  Every step of the computation runs in the HIP
+kernels of the library; torch provides device memory and the stream.  If the
+library has not been built the import of :func:`lib` fails loudly; there is no
+CPU fallback.
+
+Names follow the C ABI in ``include/dcasparse.h``:
+
+* :func:`dca_workspace_size`
+* :func:`vs_index_build`
+* :func:`dca_sparse_prefill`
+* :func:`dca_strerror`
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libdcasparse.so")
+
+DCA_OK = 0
+DCA_EINVAL = -1
+DCA_EUNSUPPORTED = -2
+DCA_EWORKSPACE = -3
+DCA_EHIP = -4
+DCA_STAGE_COUNT = 4
+STAGES = ("rotate_keys", "plan", "attention", "lse_merge")
+
+
+class dca_cfg(ctypes.Structure):
+    """Mirror of ``struct dca_cfg`` (field order and types as in the header)."""
+    _fields_ = [
+        ("n_q", ctypes.c_int32),
+        ("n_k", ctypes.c_int32),
+        ("h_q", ctypes.c_int32),
+        ("h_kv", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("dca_chunk", ctypes.c_int32),
+        ("dca_local", ctypes.c_int32),
+        ("rope_base", ctypes.c_double),
+        ("yarn_s", ctypes.c_double),
+        ("vs_last_q", ctypes.c_int32),
+        ("vs_k_vertical", ctypes.c_int32),
+        ("vs_k_slash", ctypes.c_int32),
+        ("v_idx", ctypes.c_void_p),
+        ("s_off", ctypes.c_void_p),
+        ("lse_out", ctypes.c_void_p),
+        ("precise_norm", ctypes.c_float),
+        ("split_k", ctypes.c_int32),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
+        ("stream", ctypes.c_void_p),
+        ("stage_events", ctypes.c_void_p),
+    ]
+
+
+class DcaError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        super().__init__(f"{where}: error {code} ({dca_strerror(code)})")
+        self.code = code
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with `python -m sparse_dual_chunk_amd.build` "
+                              "(there is no fallback path)")
+        L = ctypes.CDLL(LIB_PATH)
+        L.dca_workspace_size.argtypes = [ctypes.POINTER(dca_cfg), ctypes.POINTER(ctypes.c_size_t)]
+        L.dca_workspace_size.restype = ctypes.c_int
+        L.vs_index_build.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(dca_cfg),
+                                     ctypes.c_void_p, ctypes.c_void_p]
+        L.vs_index_build.restype = ctypes.c_int
+        L.dca_sparse_prefill.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                         ctypes.POINTER(dca_cfg), ctypes.c_void_p]
+        L.dca_sparse_prefill.restype = ctypes.c_int
+        L.dca_strerror.argtypes = [ctypes.c_int]
+        L.dca_strerror.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+@dataclasses.dataclass
+class Config:
+    """Python view of ``dca_cfg``; pointers are filled in by the calls."""
+    n_q: int
+    n_k: int
+    h_q: int
+    h_kv: int
+    dca_chunk: int
+    dca_local: int
+    rope_base: float
+    yarn_s: float
+    head_dim: int = 128
+    vs_last_q: int = 64
+    vs_k_vertical: int = 0
+    vs_k_slash: int = 0
+    precise_norm: float = 0.0
+    split_k: int = 0
+
+    def to_c(self, **ptrs) -> dca_cfg:
+        c = dca_cfg()
+        for f in dataclasses.fields(self):
+            setattr(c, f.name, getattr(self, f.name))
+        for k, v in ptrs.items():
+            setattr(c, k, v)
+        return c
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    return int(t.data_ptr())
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return int(torch.cuda.current_stream().cuda_stream)
+    return int(stream)
+
+
+def _positions(positions):
+    a = np.ascontiguousarray(np.asarray(positions, dtype=np.int32))
+    return a, a.ctypes.data_as(ctypes.c_void_p)
+
+
+def dca_strerror(code: int) -> str:
+    return lib().dca_strerror(int(code)).decode()
+
+
+def dca_workspace_size(cfg: Config) -> int:
+    c = cfg.to_c()
+    n = ctypes.c_size_t(0)
+    rc = lib().dca_workspace_size(ctypes.byref(c), ctypes.byref(n))
+    if rc != DCA_OK:
+        raise DcaError(rc, "dca_workspace_size")
+    return int(n.value)
+
+
+def vs_index_build(q, k, positions, cfg: Config, v_idx, s_off, workspace, stream=None) -> None:
+    """Vertical-slash index of one chunk; writes v_idx [h_q][k_v] and s_off [h_q][k_s] (int32, device)."""
+    pos, pos_p = _positions(positions)
+    c = cfg.to_c(workspace=_ptr(workspace), workspace_bytes=workspace.numel() * workspace.element_size(),
+                 stream=_stream(stream))
+    rc = lib().vs_index_build(_ptr(q), _ptr(k), pos_p, ctypes.byref(c), _ptr(v_idx), _ptr(s_off))
+    if rc != DCA_OK:
+        raise DcaError(rc, "vs_index_build")
+
+
+def dca_sparse_prefill(q, k, v, positions, cfg: Config, out, workspace, v_idx=None, s_off=None, lse_out=None,
+                       stream=None, stage_events: Optional[Sequence[int]] = None) -> None:
+    """DCA prefill attention of one chunk (dense when v_idx and s_off are None)."""
+    pos, pos_p = _positions(positions)
+    ev_arr = None
+    if stage_events is not None:
+        ev_arr = (ctypes.c_void_p * (2 * DCA_STAGE_COUNT))(*[int(e) for e in stage_events])
+    c = cfg.to_c(workspace=_ptr(workspace), workspace_bytes=workspace.numel() * workspace.element_size(),
+                 stream=_stream(stream), v_idx=_ptr(v_idx), s_off=_ptr(s_off), lse_out=_ptr(lse_out),
+                 stage_events=ctypes.cast(ev_arr, ctypes.c_void_p) if ev_arr is not None else None)
+    rc = lib().dca_sparse_prefill(_ptr(q), _ptr(k), _ptr(v), pos_p, ctypes.byref(c), _ptr(out))
+    if rc != DCA_OK:
+        raise DcaError(rc, "dca_sparse_prefill")
+
+
+def config_for(w, chunk: int = 0, **overrides) -> Config:
+    """Config of one prefill call of a workload description (see ``workloads``)."""
+    p0, n_q = w.chunks[chunk]
+    cfg = Config(n_q=n_q, n_k=p0 + n_q, h_q=w.h_q, h_kv=w.h_kv, dca_chunk=w.dca_chunk, dca_local=w.dca_local,
+                 rope_base=w.rope_base, yarn_s=w.yarn_s, head_dim=w.head_dim, vs_last_q=w.vs_last_q,
+                 vs_k_vertical=w.k_vertical, vs_k_slash=w.k_slash)
+    for k2, v2 in overrides.items():
+        setattr(cfg, k2, v2)
+    return cfg

@@ -1,0 +1,295 @@
+// C ABI of the DCA sparse prefill library: validation, workspace layout and
+// launch sequences.  Declared in include/dcasparse.h.
+#include <cmath>
+#include <cstring>
+
+#include "../../include/dcasparse.h"
+#include "args.h"
+#include "common.h"
+
+namespace dca {
+
+hipError_t launch_rotate_keys(const uint16_t* k, uint16_t* khi, uint16_t* klo, uint8_t* kflag,
+                              const double* inv_freq, int n_k, int h_kv, int S, float thr2, hipStream_t stream);
+hipError_t launch_attn(const AttnArgs& A, hipStream_t stream);
+hipError_t launch_lse_merge(const float* part_o, const float* part_lse, uint16_t* out, float* lse_out,
+                            int P, int n_q, int h_q, hipStream_t stream);
+hipError_t launch_vs_score(const VsArgs& A, const uint16_t* q, int n_q, hipStream_t stream);
+hipError_t launch_select(const SelArgs& A, hipStream_t stream);
+hipError_t launch_plan(const PlanArgs& A, hipStream_t stream);
+
+}  // namespace dca
+
+namespace {
+
+using namespace dca;
+
+struct Freqs { double v[HALF]; };
+
+__global__ void write_freqs_kernel(Freqs f, double* dst) { dst[threadIdx.x] = f.v[threadIdx.x]; }
+
+constexpr size_t ALIGN = 256;
+inline size_t up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
+
+struct Region { size_t off = 0, bytes = 0; };
+
+// Workspace layouts of the two entry points (regions are 256-byte aligned).
+struct Layout {
+  // shared
+  Region freqs;
+  // prefill
+  Region khi, klo, kflag, iv, n_iv, cov, ext, n_ext, part_o, part_lse;
+  // index
+  Region qs, part_ms, lse, vert, slash, edge, hist, prefix, krem, bcount;
+  size_t prefill_bytes = 0, index_bytes = 0;
+  int split = 1, nb = 0, n_ranges = 0, range_keys = 0, cov_words = 0, max_blocks = 0;
+};
+
+inline void place(Region& r, size_t& cur, size_t bytes) { r.off = cur; r.bytes = bytes; cur += up(bytes); }
+
+int validate(const dca_cfg* c, const int32_t* positions) {
+  if (!c) return DCA_EINVAL;
+  if (c->n_q < 1 || c->n_k < 1 || c->h_q < 1 || c->h_kv < 1) return DCA_EINVAL;
+  if (c->h_q % c->h_kv != 0) return DCA_EINVAL;
+  if (c->n_k < c->n_q) return DCA_EINVAL;
+  if (c->head_dim != 128) return DCA_EUNSUPPORTED;
+  if (c->dca_chunk < 64 || c->dca_chunk % 64 != 0) return DCA_EUNSUPPORTED;
+  if (c->dca_local < 1 || c->dca_local > c->dca_chunk) return DCA_EUNSUPPORTED;
+  if (!(c->rope_base > 1.0) || !std::isfinite(c->rope_base)) return DCA_EINVAL;
+  if (!(c->yarn_s > 0.0) || !std::isfinite(c->yarn_s)) return DCA_EINVAL;
+  if (c->vs_k_vertical < 0 || c->vs_k_slash < 0) return DCA_EINVAL;
+  if (c->vs_last_q < 1 || c->vs_last_q > 64) return DCA_EUNSUPPORTED;
+  if (c->split_k < 0 || c->split_k > 64) return DCA_EINVAL;
+  if (!std::isfinite(c->precise_norm)) return DCA_EINVAL;
+  // the chunk of rows must be the tail of the prefix, starting on a 64 boundary
+  const long long p0 = (long long)c->n_k - c->n_q;
+  if (p0 % 64 != 0) return DCA_EUNSUPPORTED;
+  // int32 key and offset arithmetic inside the kernels
+  if ((long long)c->n_k + 2LL * c->dca_chunk + 128 > (1LL << 30)) return DCA_EUNSUPPORTED;
+  if (positions) {
+    for (int i = 0; i < c->n_q; ++i)
+      if ((long long)positions[i] != p0 + i) return DCA_EINVAL;
+  }
+  return DCA_OK;
+}
+
+Layout make_layout(const dca_cfg* c) {
+  Layout L;
+  const int n_q = c->n_q, n_k = c->n_k, h_q = c->h_q, h_kv = c->h_kv;
+  const int p_last = n_k - 1;
+  L.nb = (n_q + 63) / 64;
+  const int units = h_q * L.nb;
+  if (c->split_k > 0) {
+    L.split = c->split_k;
+  } else {
+    // enough independent work items to fill 256 compute units several times over
+    L.split = 1;
+    while (units * L.split < 2048 && L.split < 16) L.split *= 2;
+    const int tiles = (n_k + 63) / 64;
+    while (L.split > 1 && L.split > tiles) L.split /= 2;
+  }
+  size_t cur = 0;
+  place(L.freqs, cur, HALF * sizeof(double));
+  const size_t base = cur;
+  // --- prefill
+  place(L.khi, cur, (size_t)n_k * h_kv * D * 2);
+  place(L.klo, cur, (size_t)n_k * h_kv * D * 2);
+  place(L.kflag, cur, (size_t)n_k * h_kv);
+  place(L.iv, cur, (size_t)h_q * (c->vs_k_slash + 1) * 2 * 4);
+  place(L.n_iv, cur, (size_t)h_q * 4);
+  L.cov_words = (p_last + 64 + 31) / 32;
+  place(L.cov, cur, (size_t)h_q * L.cov_words * 4);
+  place(L.ext, cur, (size_t)h_q * L.nb * (size_t)(c->vs_k_vertical > 0 ? c->vs_k_vertical : 1) * 4);
+  place(L.n_ext, cur, (size_t)h_q * L.nb * 4);
+  if (L.split > 1) {
+    place(L.part_o, cur, (size_t)L.split * n_q * h_q * D * 4);
+    place(L.part_lse, cur, (size_t)L.split * h_q * n_q * 4);
+  }
+  L.prefill_bytes = cur;
+  // --- index (reuses the space after the frequencies)
+  cur = base;
+  long long target = 2048;
+  long long rk = ((long long)n_k * h_q) / target;
+  rk = (rk + 31) / 32 * 32;
+  if (rk < 64) rk = 64;
+  if (rk > 2048) rk = 2048;
+  L.range_keys = (int)rk;
+  L.n_ranges = (int)((n_k + rk - 1) / rk);
+  place(L.qs, cur, (size_t)2 * h_q * 64 * D * 8);
+  place(L.part_ms, cur, (size_t)h_q * L.n_ranges * 64 * 2 * 8);
+  place(L.lse, cur, (size_t)h_q * 64 * 8);
+  place(L.vert, cur, (size_t)h_q * n_k * 8);
+  place(L.slash, cur, (size_t)h_q * (p_last + 1) * 8);
+  place(L.edge, cur, (size_t)h_q * L.n_ranges * 2 * 64 * 2 * 8);
+  place(L.hist, cur, (size_t)2 * h_q * 256 * 4);
+  place(L.prefix, cur, (size_t)2 * h_q * 8);
+  place(L.krem, cur, (size_t)2 * h_q * 4);
+  L.max_blocks = (n_k + 8191) / 8192;
+  place(L.bcount, cur, (size_t)2 * h_q * L.max_blocks * 2 * 4);
+  L.index_bytes = cur;
+  return L;
+}
+
+template <class T>
+T* at(const dca_cfg* c, const Region& r) { return (T*)((char*)c->workspace + r.off); }
+
+int check_workspace(const dca_cfg* c, size_t need) {
+  if (!c->workspace) return DCA_EWORKSPACE;
+  if (c->workspace_bytes < need) return DCA_EWORKSPACE;
+  if (((uintptr_t)c->workspace) % ALIGN != 0) return DCA_EWORKSPACE;
+  return DCA_OK;
+}
+
+Freqs make_freqs(double base) {
+  Freqs f;
+  for (int k = 0; k < HALF; ++k) f.v[k] = std::pow(base, -(2.0 * k) / (double)D);
+  return f;
+}
+
+double yarn_factor(double s) {
+  if (s <= 1.0) return 1.0;
+  const double r = 0.1 * std::log(s) + 1.0;
+  return r * r;
+}
+
+void record(const dca_cfg* c, int stage, int which) {
+  if (!c->stage_events) return;
+  hipEvent_t ev = (hipEvent_t)c->stage_events[2 * stage + which];
+  if (ev) (void)hipEventRecord(ev, (hipStream_t)c->stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+int dca_workspace_size(const dca_cfg* cfg, size_t* bytes) {
+  if (!bytes) return DCA_EINVAL;
+  const int rc = validate(cfg, nullptr);
+  if (rc != DCA_OK) return rc;
+  const Layout L = make_layout(cfg);
+  *bytes = L.prefill_bytes > L.index_bytes ? L.prefill_bytes : L.index_bytes;
+  return DCA_OK;
+}
+
+int vs_index_build(const dca_bf16* q, const dca_bf16* k, const int32_t* positions, const dca_cfg* cfg,
+                   int32_t* v_idx, int32_t* s_off) {
+  int rc = validate(cfg, positions);
+  if (rc != DCA_OK) return rc;
+  if (!q || !k || !positions) return DCA_EINVAL;
+  if ((cfg->vs_k_vertical > 0 && !v_idx) || (cfg->vs_k_slash > 0 && !s_off)) return DCA_EINVAL;
+  const Layout L = make_layout(cfg);
+  rc = check_workspace(cfg, L.index_bytes);
+  if (rc != DCA_OK) return rc;
+  hipStream_t st = (hipStream_t)cfg->stream;
+  const int n_q = cfg->n_q, n_k = cfg->n_k, h_q = cfg->h_q;
+  const int p_last = n_k - 1;
+  const int n_s = cfg->vs_last_q < n_q ? cfg->vs_last_q : n_q;
+
+  hipLaunchKernelGGL(write_freqs_kernel, dim3(1), dim3(HALF), 0, st, make_freqs(cfg->rope_base),
+                     at<double>(cfg, L.freqs));
+  VsArgs V;
+  V.k = k;
+  V.qs = at<double>(cfg, L.qs);
+  V.inv_freq = at<double>(cfg, L.freqs);
+  V.part_ms = at<double>(cfg, L.part_ms);
+  V.lse = at<double>(cfg, L.lse);
+  V.vert = at<double>(cfg, L.vert);
+  V.slash = at<double>(cfg, L.slash);
+  V.edge = at<double>(cfg, L.edge);
+  V.n_k = n_k; V.h_q = h_q; V.h_kv = cfg->h_kv; V.S = cfg->dca_chunk; V.n_s = n_s;
+  V.p_first = p_last - n_s + 1; V.range_keys = L.range_keys; V.n_ranges = L.n_ranges; V.n_off = p_last + 1;
+  V.scale = yarn_factor(cfg->yarn_s) / std::sqrt((double)D);
+  if (launch_vs_score(V, q, n_q, st) != hipSuccess) return DCA_EHIP;
+
+  SelArgs S;
+  S.vert = V.vert; S.slash = V.slash;
+  S.v_out = v_idx; S.s_out = s_off;
+  S.h_q = h_q; S.n_v = n_k; S.n_sl = p_last + 1; S.k_v = cfg->vs_k_vertical; S.k_s = cfg->vs_k_slash;
+  S.hist = at<uint32_t>(cfg, L.hist);
+  S.prefix = at<uint64_t>(cfg, L.prefix);
+  S.krem = at<int32_t>(cfg, L.krem);
+  S.bcount = at<uint32_t>(cfg, L.bcount);
+  S.max_blocks = L.max_blocks;
+  if (launch_select(S, st) != hipSuccess) return DCA_EHIP;
+  return DCA_OK;
+}
+
+int dca_sparse_prefill(const dca_bf16* q, const dca_bf16* k, const dca_bf16* v, const int32_t* positions,
+                       const dca_cfg* cfg, dca_bf16* out) {
+  int rc = validate(cfg, positions);
+  if (rc != DCA_OK) return rc;
+  if (!q || !k || !v || !out || !positions) return DCA_EINVAL;
+  const bool sparse = cfg->v_idx || cfg->s_off;
+  if (sparse && ((cfg->vs_k_vertical > 0 && !cfg->v_idx) || (cfg->vs_k_slash > 0 && !cfg->s_off)))
+    return DCA_EINVAL;
+  const Layout L = make_layout(cfg);
+  rc = check_workspace(cfg, L.prefill_bytes);
+  if (rc != DCA_OK) return rc;
+  hipStream_t st = (hipStream_t)cfg->stream;
+  const int n_q = cfg->n_q, n_k = cfg->n_k, h_q = cfg->h_q, h_kv = cfg->h_kv;
+  const int p0 = n_k - n_q;
+  const int p_last = n_k - 1;
+
+  hipLaunchKernelGGL(write_freqs_kernel, dim3(1), dim3(HALF), 0, st, make_freqs(cfg->rope_base),
+                     at<double>(cfg, L.freqs));
+  // stage 0: chunk-local key rotation
+  record(cfg, 0, 0);
+  float thr = cfg->precise_norm == 0.f ? 2.f * std::sqrt((float)D) : cfg->precise_norm;
+  const float thr2 = thr < 0.f ? -1.f : thr * thr;
+  if (launch_rotate_keys(k, at<uint16_t>(cfg, L.khi), at<uint16_t>(cfg, L.klo), at<uint8_t>(cfg, L.kflag),
+                         at<double>(cfg, L.freqs), n_k, h_kv, cfg->dca_chunk, thr2, st) != hipSuccess)
+    return DCA_EHIP;
+  record(cfg, 0, 1);
+  // stage 1: sparse plan
+  record(cfg, 1, 0);
+  if (sparse) {
+    PlanArgs P;
+    P.v_idx = cfg->v_idx; P.s_off = cfg->s_off;
+    P.iv = at<int32_t>(cfg, L.iv); P.n_iv = at<int32_t>(cfg, L.n_iv);
+    P.cov = at<uint32_t>(cfg, L.cov);
+    P.ext = at<int32_t>(cfg, L.ext); P.n_ext = at<int32_t>(cfg, L.n_ext);
+    P.h_q = h_q; P.k_v = cfg->vs_k_vertical; P.k_s = cfg->vs_k_slash; P.p_last = p_last; P.p0 = p0;
+    P.n_q = n_q; P.nb = L.nb; P.iv_stride = cfg->vs_k_slash + 1;
+    P.ext_stride = cfg->vs_k_vertical > 0 ? cfg->vs_k_vertical : 1; P.cov_words = L.cov_words;
+    if (launch_plan(P, st) != hipSuccess) return DCA_EHIP;
+  }
+  record(cfg, 1, 1);
+  // stage 2: attention
+  record(cfg, 2, 0);
+  AttnArgs A;
+  A.q = q; A.khi = at<uint16_t>(cfg, L.khi); A.klo = at<uint16_t>(cfg, L.klo); A.v = v;
+  A.kflag = at<uint8_t>(cfg, L.kflag); A.inv_freq = at<double>(cfg, L.freqs);
+  A.out = out; A.lse_out = cfg->lse_out;
+  A.part_o = L.split > 1 ? at<float>(cfg, L.part_o) : nullptr;
+  A.part_lse = L.split > 1 ? at<float>(cfg, L.part_lse) : nullptr;
+  A.iv = at<int32_t>(cfg, L.iv); A.n_iv = at<int32_t>(cfg, L.n_iv);
+  A.ext = at<int32_t>(cfg, L.ext); A.n_ext = at<int32_t>(cfg, L.n_ext);
+  A.n_q = n_q; A.n_k = n_k; A.h_q = h_q; A.h_kv = h_kv; A.p0 = p0; A.S = cfg->dca_chunk; A.W = cfg->dca_local;
+  A.nb = L.nb; A.iv_stride = cfg->vs_k_slash + 1;
+  A.ext_stride = cfg->vs_k_vertical > 0 ? cfg->vs_k_vertical : 1;
+  A.split = L.split; A.dense = sparse ? 0 : 1;
+  A.qscale = (float)(yarn_factor(cfg->yarn_s) / std::sqrt((double)D) * 1.4426950408889634);
+  if (launch_attn(A, st) != hipSuccess) return DCA_EHIP;
+  record(cfg, 2, 1);
+  // stage 3: LSE merge of the split partials
+  record(cfg, 3, 0);
+  if (L.split > 1) {
+    if (launch_lse_merge(A.part_o, A.part_lse, out, cfg->lse_out, L.split, n_q, h_q, st) != hipSuccess)
+      return DCA_EHIP;
+  }
+  record(cfg, 3, 1);
+  return DCA_OK;
+}
+
+const char* dca_strerror(int code) {
+  switch (code) {
+    case DCA_OK: return "ok";
+    case DCA_EINVAL: return "invalid argument (null pointer, inconsistent sizes or positions)";
+    case DCA_EUNSUPPORTED: return "unsupported configuration (head_dim, chunk, window, alignment or size)";
+    case DCA_EWORKSPACE: return "workspace missing, misaligned or smaller than dca_workspace_size";
+    case DCA_EHIP: return "HIP launch or runtime error";
+    default: return "unknown error code";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,63 @@
+// Argument blocks of the kernels, shared by the kernels and the host entry points.
+#pragma once
+#include <stdint.h>
+
+namespace dca {
+
+struct AttnArgs {
+  const uint16_t* q;        // [n_q][h_q][128] raw
+  const uint16_t* khi;      // [n_k][h_kv][128] rotated, bf16 hi
+  const uint16_t* klo;      // same, lo residual
+  const uint16_t* v;        // [n_k][h_kv][128]
+  const uint8_t* kflag;     // [h_kv][n_k]
+  const double* inv_freq;   // [64]
+  uint16_t* out;            // [n_q][h_q][128]
+  float* lse_out;           // [h_q][n_q] or null
+  float* part_o;            // [P][n_q][h_q][128] (P > 1)
+  float* part_lse;          // [P][h_q][n_q]      (P > 1)
+  const int32_t* iv;        // [h_q][iv_stride][2] merged slash intervals (offset space)
+  const int32_t* n_iv;      // [h_q]
+  const int32_t* ext;       // [h_q][nb][ext_stride] vertical keys outside the ranges
+  const int32_t* n_ext;     // [h_q][nb]
+  int n_q, n_k, h_q, h_kv, p0, S, W, nb, iv_stride, ext_stride, split, dense;
+  float qscale;             // softmax scale * log2(e), folded into the query rotation
+};
+
+struct VsArgs {
+  const uint16_t* k;         // raw keys [n_k][h_kv][128]
+  const double* qs;          // [2][h_q][64][128] scoring rows rotated at r_i ([0]) and S + r_i ([1])
+  const double* inv_freq;    // [64]
+  double* part_ms;           // [h_q][n_ranges][64][2] pass-1 (max, sum) per row and range
+  const double* lse;         // [h_q][64]
+  double* vert;              // [h_q][n_k]
+  double* slash;             // [h_q][n_off], n_off = p_last + 1
+  double* edge;              // [h_q][n_ranges][2][64][2] double-double partial diagonals at range edges
+  int n_k, h_q, h_kv, S, n_s, p_first, range_keys, n_ranges, n_off;
+  double scale;
+};
+
+struct SelArgs {
+  const double* vert;      // [h_q][n_v]
+  const double* slash;     // [h_q][n_s]
+  int32_t* v_out;          // [h_q][k_v]
+  int32_t* s_out;          // [h_q][k_s]
+  int h_q, n_v, n_sl, k_v, k_s;
+  uint32_t* hist;          // [2*h_q][256]
+  uint64_t* prefix;        // [2*h_q]
+  int32_t* krem;           // [2*h_q]
+  uint32_t* bcount;        // [2*h_q][max_blocks][2] (gt, eq)
+  int max_blocks;
+};
+
+struct PlanArgs {
+  const int32_t* v_idx;    // [h_q][k_v]
+  const int32_t* s_off;    // [h_q][k_s]
+  int32_t* iv;             // [h_q][iv_stride][2]
+  int32_t* n_iv;           // [h_q]
+  uint32_t* cov;           // [h_q][cov_words] bitmap over offsets o in [-p_last, 64)
+  int32_t* ext;            // [h_q][nb][ext_stride]
+  int32_t* n_ext;          // [h_q][nb]
+  int h_q, k_v, k_s, p_last, p0, n_q, nb, iv_stride, ext_stride, cov_words;
+};
+
+}  // namespace dca

@@ -1,0 +1,78 @@
+// Chunk-local key rotation (DCA key positions r_j = j mod S) for the attention kernel.
+//
+// Dual Chunk Attention (paper-review page, section 4, Figure 2) gives every key
+// the position of its offset inside its own chunk, so a key is rotated once and
+// the three query rotations carry the mode.  The rotated key is stored as a
+// bf16 pair (hi, lo) with hi + lo within 2^-16 relative of the fp32 rotation;
+// the attention kernel adds the lo half only for keys flagged as high-norm,
+// whose logits would otherwise carry bf16 rounding errors large enough to move
+// the output (sink keys, periodic high-norm keys).
+#include "common.h"
+
+namespace dca {
+
+// One 16-lane group per (key, kv head) row; lane c16 owns pairs 4*c16 .. 4*c16+3.
+__global__ void __launch_bounds__(256) rotate_keys_kernel(
+    const uint16_t* __restrict__ k, uint16_t* __restrict__ khi, uint16_t* __restrict__ klo,
+    uint8_t* __restrict__ kflag, const double* __restrict__ inv_freq,
+    int n_k, int h_kv, int S, float thr2) {
+  const int lane16 = threadIdx.x & 15;
+  const long long row = (long long)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const long long n_rows = (long long)n_k * h_kv;
+  const bool active = row < n_rows;
+  const long long rrow = active ? row : 0;
+  const int j = (int)(rrow / h_kv);
+  const int g = (int)(rrow % h_kv);
+  const double pos = (double)(j % S);
+  const uint16_t* src = k + rrow * D;
+  // two 8-byte loads: dims 4c..4c+3 and 64+4c..64+4c+3
+  uint2 a = *(const uint2*)(src + 4 * lane16);
+  uint2 b = *(const uint2*)(src + HALF + 4 * lane16);
+  uint16_t xa[4] = {(uint16_t)(a.x & 0xFFFF), (uint16_t)(a.x >> 16), (uint16_t)(a.y & 0xFFFF), (uint16_t)(a.y >> 16)};
+  uint16_t xb[4] = {(uint16_t)(b.x & 0xFFFF), (uint16_t)(b.x >> 16), (uint16_t)(b.y & 0xFFFF), (uint16_t)(b.y >> 16)};
+  uint16_t ha[4], hb[4], la[4], lb[4];
+  float ss = 0.f;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int c = 4 * lane16 + t;
+    float sn, cs;
+    sincosf(reduce_angle(pos, inv_freq[c]), &sn, &cs);
+    const float x = bf16_bits_to_f32(xa[t]);
+    const float y = bf16_bits_to_f32(xb[t]);
+    ss += x * x + y * y;
+    const float xr = x * cs - y * sn;
+    const float yr = x * sn + y * cs;
+    ha[t] = f32_to_bf16_bits(xr);
+    hb[t] = f32_to_bf16_bits(yr);
+    la[t] = f32_to_bf16_bits(xr - bf16_bits_to_f32(ha[t]));
+    lb[t] = f32_to_bf16_bits(yr - bf16_bits_to_f32(hb[t]));
+  }
+  // squared norm of the raw key row over its 16 lanes
+  ss += __shfl_xor(ss, 8, 16);
+  ss += __shfl_xor(ss, 4, 16);
+  ss += __shfl_xor(ss, 2, 16);
+  ss += __shfl_xor(ss, 1, 16);
+  if (!active) return;
+  uint2 oa, ob, pa, pb;
+  oa.x = ha[0] | ((uint32_t)ha[1] << 16); oa.y = ha[2] | ((uint32_t)ha[3] << 16);
+  ob.x = hb[0] | ((uint32_t)hb[1] << 16); ob.y = hb[2] | ((uint32_t)hb[3] << 16);
+  pa.x = la[0] | ((uint32_t)la[1] << 16); pa.y = la[2] | ((uint32_t)la[3] << 16);
+  pb.x = lb[0] | ((uint32_t)lb[1] << 16); pb.y = lb[2] | ((uint32_t)lb[3] << 16);
+  *(uint2*)(khi + rrow * D + 4 * lane16) = oa;
+  *(uint2*)(khi + rrow * D + HALF + 4 * lane16) = ob;
+  *(uint2*)(klo + rrow * D + 4 * lane16) = pa;
+  *(uint2*)(klo + rrow * D + HALF + 4 * lane16) = pb;
+  if (lane16 == 0) kflag[(long long)g * n_k + j] = (thr2 >= 0.f && ss > thr2) ? 1 : 0;
+}
+
+hipError_t launch_rotate_keys(const uint16_t* k, uint16_t* khi, uint16_t* klo, uint8_t* kflag,
+                              const double* inv_freq, int n_k, int h_kv, int S, float thr2,
+                              hipStream_t stream) {
+  const long long rows = (long long)n_k * h_kv;
+  const int blocks = (int)((rows + 15) / 16);
+  hipLaunchKernelGGL(rotate_keys_kernel, dim3(blocks), dim3(256), 0, stream,
+                     k, khi, klo, kflag, inv_freq, n_k, h_kv, S, thr2);
+  return hipGetLastError();
+}
+
+}  // namespace dca

@@ -1,0 +1,339 @@
+// Top-k selection of vertical columns and slash offsets, and the sparse plan.
+//
+// Selection: the k best scores of each list by (score desc, index asc),
+// emitted in ascending index order and padded with -1.  Scores are
+// non-negative doubles, so their bit patterns order like the values; the k-th
+// largest bit pattern T is found by an 8-pass radix select (8 bits per pass,
+// integer histograms: deterministic), then every score above T and the
+// lowest-index scores equal to T are compacted in index order.  Slash offset 0
+// is forced in by ranking it as +inf.
+//
+// Plan: per query head, the selected offsets (plus 0) become disjoint key
+// ranges in offset space, [-delta, -delta+64) merged when they touch; per
+// query block, the vertical columns those ranges do not already cover are
+// listed for the attention kernel.
+#include "common.h"
+#include "args.h"
+
+namespace dca {
+
+constexpr int SEL_CHUNK = 8192;           // list elements per histogram / compaction block
+constexpr uint64_t FORCED_KEY = 0x7FF0000000000000ull;   // +inf
+
+
+__device__ __forceinline__ void sel_list(const SelArgs& A, int list, const double*& s, int32_t*& out, int& n,
+                                         int& k, int& forced0) {
+  const int h = list >> 1;
+  if ((list & 1) == 0) {
+    s = A.vert + (long long)h * A.n_v; out = A.v_out + (long long)h * A.k_v; n = A.n_v; k = A.k_v; forced0 = 0;
+  } else {
+    s = A.slash + (long long)h * A.n_sl; out = A.s_out + (long long)h * A.k_s; n = A.n_sl; k = A.k_s; forced0 = 1;
+  }
+}
+
+__device__ __forceinline__ uint64_t sel_key(const double* s, int i, int forced0) {
+  if (forced0 && i == 0) return FORCED_KEY;
+  return (uint64_t)__double_as_longlong(s[i]);
+}
+
+__global__ void sel_init_kernel(SelArgs A) {
+  const int list = blockIdx.x;
+  const double* s; int32_t* out; int n, k, f;
+  sel_list(A, list, s, out, n, k, f);
+  A.hist[list * 256 + threadIdx.x] = 0;
+  if (threadIdx.x == 0) { A.prefix[list] = 0; A.krem[list] = k; }
+}
+
+// Histogram of the byte at `shift` among elements whose higher bytes equal the prefix.
+__global__ void __launch_bounds__(256) sel_hist_kernel(SelArgs A, int shift) {
+  __shared__ uint32_t lh[256];
+  const int list = blockIdx.y;
+  const double* s; int32_t* out; int n, k, f;
+  sel_list(A, list, s, out, n, k, f);
+  lh[threadIdx.x] = 0;
+  __syncthreads();
+  const int beg = blockIdx.x * SEL_CHUNK;
+  if (k > 0 && k < n && beg < n) {
+    const uint64_t pre = A.prefix[list];
+    const uint64_t mask = (shift >= 56) ? 0ull : (~0ull << (shift + 8));
+    const int end = min(n, beg + SEL_CHUNK);
+    for (int i = beg + threadIdx.x; i < end; i += 256) {
+      const uint64_t key = sel_key(s, i, f);
+      if ((key & mask) == pre) atomicAdd(&lh[(key >> shift) & 0xFF], 1u);
+    }
+  }
+  __syncthreads();
+  const uint32_t c = lh[threadIdx.x];
+  if (c) atomicAdd(&A.hist[list * 256 + threadIdx.x], c);
+}
+
+// Pick the byte holding the k_rem-th largest key; clear the histogram for the next pass.
+__global__ void sel_pick_kernel(SelArgs A, int shift) {
+  __shared__ uint32_t hs[256];
+  const int list = blockIdx.x;
+  hs[threadIdx.x] = A.hist[list * 256 + threadIdx.x];
+  A.hist[list * 256 + threadIdx.x] = 0;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const double* s; int32_t* out; int n, k, f;
+    sel_list(A, list, s, out, n, k, f);
+    if (k > 0 && k < n) {
+      int rem = A.krem[list];
+      uint32_t above = 0;
+      int d = 255;
+      for (; d > 0; --d) {
+        if (above + hs[d] >= (uint32_t)rem) break;
+        above += hs[d];
+      }
+      A.prefix[list] |= ((uint64_t)d) << shift;
+      A.krem[list] = rem - (int)above;
+    }
+  }
+}
+
+// Per-block counts of keys above T and equal to T.
+__global__ void __launch_bounds__(256) sel_count_kernel(SelArgs A) {
+  __shared__ uint32_t cg[256], ce[256];
+  const int list = blockIdx.y;
+  const double* s; int32_t* out; int n, k, f;
+  sel_list(A, list, s, out, n, k, f);
+  const int beg = blockIdx.x * SEL_CHUNK;
+  uint32_t ng = 0, ne = 0;
+  if (beg < n) {
+    const int end = min(n, beg + SEL_CHUNK);
+    const uint64_t T = A.prefix[list];
+    const bool all = (k >= n);
+    for (int i = beg + threadIdx.x; i < end; i += 256) {
+      const uint64_t key = sel_key(s, i, f);
+      if (all || key > T) ++ng; else if (key == T) ++ne;
+    }
+  }
+  cg[threadIdx.x] = ng; ce[threadIdx.x] = ne;
+  __syncthreads();
+  for (int off = 128; off > 0; off >>= 1) {
+    if (threadIdx.x < off) { cg[threadIdx.x] += cg[threadIdx.x + off]; ce[threadIdx.x] += ce[threadIdx.x + off]; }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    uint32_t* dst = A.bcount + ((long long)list * A.max_blocks + blockIdx.x) * 2;
+    dst[0] = cg[0]; dst[1] = ce[0];
+  }
+}
+
+// Exclusive scan of the block counts (one thread per list; block counts are few).
+__global__ void sel_scan_kernel(SelArgs A) {
+  const int list = blockIdx.x * blockDim.x + threadIdx.x;
+  if (list >= 2 * A.h_q) return;
+  const double* s; int32_t* out; int n, k, f;
+  sel_list(A, list, s, out, n, k, f);
+  const int nb = (n + SEL_CHUNK - 1) / SEL_CHUNK;
+  uint32_t g = 0, e = 0;
+  for (int b = 0; b < nb; ++b) {
+    uint32_t* p = A.bcount + ((long long)list * A.max_blocks + b) * 2;
+    const uint32_t tg = p[0], te = p[1];
+    p[0] = g; p[1] = e;
+    g += tg; e += te;
+  }
+}
+
+// Write selected indices in ascending order; the first block of each list pads with -1.
+__global__ void __launch_bounds__(256) sel_write_kernel(SelArgs A) {
+  __shared__ uint32_t sg[256], se[256];
+  const int list = blockIdx.y;
+  const double* s; int32_t* out; int n, k, f;
+  sel_list(A, list, s, out, n, k, f);
+  if (k <= 0) return;
+  const int beg = blockIdx.x * SEL_CHUNK;
+  const bool all = (k >= n);
+  const uint64_t T = A.prefix[list];
+  const int need_eq = all ? 0 : A.krem[list];
+  if (blockIdx.x == 0) {
+    for (int i = min(k, n) + threadIdx.x; i < k; i += 256) out[i] = -1;
+  }
+  if (beg >= n) return;
+  const int end = min(n, beg + SEL_CHUNK);
+  const uint32_t* bc = A.bcount + ((long long)list * A.max_blocks + blockIdx.x) * 2;
+  uint32_t run_g = bc[0], run_e = bc[1];
+  // each thread owns a contiguous run of 32 elements so that index order is kept
+  const int per = SEL_CHUNK / 256;
+  const int my0 = beg + threadIdx.x * per;
+  uint32_t tg = 0, te = 0;
+  for (int i = my0; i < min(end, my0 + per); ++i) {
+    const uint64_t key = sel_key(s, i, f);
+    if (all || key > T) ++tg; else if (key == T) ++te;
+  }
+  sg[threadIdx.x] = tg; se[threadIdx.x] = te;
+  __syncthreads();
+  // exclusive scan over threads (Hillis-Steele on 256 entries)
+  for (int off = 1; off < 256; off <<= 1) {
+    uint32_t a = 0, b2 = 0;
+    if (threadIdx.x >= off) { a = sg[threadIdx.x - off]; b2 = se[threadIdx.x - off]; }
+    __syncthreads();
+    sg[threadIdx.x] += a; se[threadIdx.x] += b2;
+    __syncthreads();
+  }
+  uint32_t gb = run_g + sg[threadIdx.x] - tg;
+  uint32_t eb = run_e + se[threadIdx.x] - te;
+  for (int i = my0; i < min(end, my0 + per); ++i) {
+    const uint64_t key = sel_key(s, i, f);
+    if (all || key > T) {
+      out[gb + min(eb, (uint32_t)need_eq)] = i;
+      ++gb;
+    } else if (key == T) {
+      if (eb < (uint32_t)need_eq) out[gb + eb] = i;
+      ++eb;
+    }
+  }
+}
+
+hipError_t launch_select(const SelArgs& A, hipStream_t stream) {
+  const int lists = 2 * A.h_q;
+  const int nblk = (max(A.n_v, A.n_sl) + SEL_CHUNK - 1) / SEL_CHUNK;
+  hipLaunchKernelGGL(sel_init_kernel, dim3(lists), dim3(256), 0, stream, A);
+  for (int shift = 56; shift >= 0; shift -= 8) {
+    hipLaunchKernelGGL(sel_hist_kernel, dim3(nblk, lists), dim3(256), 0, stream, A, shift);
+    hipLaunchKernelGGL(sel_pick_kernel, dim3(lists), dim3(256), 0, stream, A, shift);
+  }
+  hipLaunchKernelGGL(sel_count_kernel, dim3(nblk, lists), dim3(256), 0, stream, A);
+  hipLaunchKernelGGL(sel_scan_kernel, dim3((lists + 63) / 64), dim3(64), 0, stream, A);
+  hipLaunchKernelGGL(sel_write_kernel, dim3(nblk, lists), dim3(256), 0, stream, A);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Sparse plan
+// ---------------------------------------------------------------------------
+
+// One workgroup per head: valid offsets in descending order (ascending key
+// offset -delta), 0 forced, duplicates dropped, runs merged when consecutive
+// offsets differ by at most 64.
+__global__ void __launch_bounds__(1024) plan_intervals_kernel(PlanArgs A) {
+  __shared__ int32_t sd[1024];
+  __shared__ int32_t sflag[1024];
+  __shared__ int32_t carry_last;    // last kept delta of the previous chunk (or -1)
+  __shared__ int32_t carry_count;   // intervals emitted so far
+  __shared__ int32_t open_lo;       // lo of the interval being built
+  const int h = blockIdx.x;
+  const int32_t* so = A.s_off + (long long)h * A.k_s;
+  int32_t* ivh = A.iv + (long long)h * A.iv_stride * 2;
+  const int total = A.k_s + 1;      // descending list: s_off reversed, then the forced 0
+  if (threadIdx.x == 0) { carry_last = -1; carry_count = 0; open_lo = 0; }
+  __syncthreads();
+  for (int base = 0; base < total; base += 1024) {
+    const int t = base + threadIdx.x;
+    int d = -1;
+    if (t < A.k_s) d = so[A.k_s - 1 - t];
+    else if (t == A.k_s) d = 0;
+    if (d < 0 || d > A.p_last) d = -1;
+    sd[threadIdx.x] = d;
+    __syncthreads();
+    // keep d if valid and strictly below every earlier kept value (drops duplicates,
+    // and a forced 0 that the list already held)
+    // previous valid element: scan back within the chunk, else the carry
+    int prev = -1;
+    if (d >= 0) {
+      for (int u = (int)threadIdx.x - 1; u >= 0; --u) { if (sd[u] >= 0) { prev = sd[u]; break; } }
+      if (prev < 0) prev = carry_last;
+    }
+    const bool keep = (d >= 0) && (prev < 0 || d < prev);
+    // a kept value starts a new interval when the gap to the previous kept value exceeds 64
+    sflag[threadIdx.x] = keep ? ((prev < 0 || prev - d > 64) ? 2 : 1) : 0;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      int cnt = carry_count;
+      int last = carry_last;
+      int lo = open_lo;
+      for (int u = 0; u < 1024 && base + u < total; ++u) {
+        const int fl = sflag[u];
+        if (!fl) continue;
+        const int dv = sd[u];
+        if (fl == 2) {
+          if (last >= 0) { ivh[2 * (cnt - 1) + 1] = -last + 64; }
+          lo = -dv;
+          ivh[2 * cnt] = lo;
+          ++cnt;
+        }
+        last = dv;
+      }
+      carry_count = cnt; carry_last = last; open_lo = lo;
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    if (carry_count > 0) ivh[2 * (carry_count - 1) + 1] = -carry_last + 64;
+    A.n_iv[h] = carry_count;
+  }
+}
+
+__global__ void plan_cov_clear_kernel(PlanArgs A) {
+  const long long n = (long long)A.h_q * A.cov_words;
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (long long)gridDim.x * blockDim.x)
+    A.cov[i] = 0u;
+}
+
+// Set the coverage bits of every merged interval (offset o -> bit o + p_last).
+__global__ void plan_cov_kernel(PlanArgs A) {
+  const int h = blockIdx.y;
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= A.n_iv[h]) return;
+  const int32_t* ivh = A.iv + (long long)h * A.iv_stride * 2;
+  uint32_t* cv = A.cov + (long long)h * A.cov_words;
+  const int b0 = max(ivh[2 * t], -A.p_last) + A.p_last;
+  const int b1 = min(ivh[2 * t + 1], 64) + A.p_last;   // exclusive
+  for (int bit = b0; bit < b1;) {
+    const int w = bit >> 5;
+    const int lo = bit & 31;
+    const int hi = min(32, lo + (b1 - bit));
+    const uint32_t m = (hi == 32 ? 0xFFFFFFFFu : ((1u << hi) - 1u)) & ~((1u << lo) - 1u);
+    atomicOr(&cv[w], m);
+    bit += hi - lo;
+  }
+}
+
+// One wave per (head, query block): vertical columns inside the block's causal
+// extent that the block's ranges miss, ascending, duplicates dropped.
+__global__ void __launch_bounds__(256) plan_ext_kernel(PlanArgs A) {
+  const int unit = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (unit >= A.h_q * A.nb) return;
+  const int h = unit / A.nb;
+  const int b = unit % A.nb;
+  const int i0 = A.p0 + 64 * b;
+  const int hi_key = i0 + min(64, A.n_q - 64 * b);
+  const int32_t* vi = A.v_idx + (long long)h * A.k_v;
+  const uint32_t* cv = A.cov + (long long)h * A.cov_words;
+  int32_t* dst = A.ext + ((long long)h * A.nb + b) * A.ext_stride;
+  int cnt = 0;
+  for (int base = 0; base < A.k_v; base += 64) {
+    const int t = base + lane;
+    bool keep = false;
+    int j = -1;
+    if (t < A.k_v) {
+      j = vi[t];
+      const int prev = (t > 0) ? vi[t - 1] : -1;
+      if (j >= 0 && j < hi_key && j != prev) {
+        const int bit = j - i0 + A.p_last;
+        keep = !((cv[bit >> 5] >> (bit & 31)) & 1u);
+      }
+    }
+    const unsigned long long bal = __ballot(keep);
+    if (keep) {
+      const int pos = __popcll(bal & ((1ull << lane) - 1ull));
+      dst[cnt + pos] = j;
+    }
+    cnt += __popcll(bal);
+  }
+  if (lane == 0) A.n_ext[unit] = cnt;
+}
+
+hipError_t launch_plan(const PlanArgs& A, hipStream_t stream) {
+  hipLaunchKernelGGL(plan_intervals_kernel, dim3(A.h_q), dim3(1024), 0, stream, A);
+  hipLaunchKernelGGL(plan_cov_clear_kernel, dim3(256), dim3(256), 0, stream, A);
+  const int ivb = (A.iv_stride + 255) / 256;
+  hipLaunchKernelGGL(plan_cov_kernel, dim3(ivb, A.h_q), dim3(256), 0, stream, A);
+  const int units = A.h_q * A.nb;
+  hipLaunchKernelGGL(plan_ext_kernel, dim3((units + 3) / 4), dim3(256), 0, stream, A);
+  return hipGetLastError();
+}
+
+}  // namespace dca

@@ -1,0 +1,214 @@
+"""GPU parity of the HIP path (through the C ABI) against the fp64 oracle, small shapes.
+
+Attention outputs: max-abs <= 2e-2 and mean-abs <= 2e-3 on the bf16 output.
+Index selections: bit-exact.  Sizes span several 64-row blocks and 64-key tiles,
+ragged tails, several DCA chunks, sinks (the split-precision tiles), split-K.
+"""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import dca_oracle as O
+from workloads import f32_to_bf16_bits, bf16_bits_to_f32
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import sparse_dual_chunk_amd as S  # noqa: E402
+from tests.gpu_helpers import (bf16_f64, check_close, oracle_cfg, run_index, run_prefill)  # noqa: E402
+
+# The natural-log LSE comes from logits of bf16-rounded rotated q and k: each
+# logit carries an error of order 2^-9 * scale * |q| |k| (about 0.005 to 0.01 for
+# unit-variance rows, scale 0.115); the LSE inherits at most the largest logit
+# error.  1e-2 bounds it for these inputs.
+LSE_TOL = 1e-2
+
+
+def _inputs(seed, p0, n_q, h_q, h_kv, sinks=False, periodic=0, qscale=1.0):
+    rng = np.random.default_rng(seed)
+    n_k = p0 + n_q
+    q = f32_to_bf16_bits(rng.standard_normal((n_q, h_q, 128)).astype(np.float32) * np.float32(qscale))
+    kf = rng.standard_normal((n_k, h_kv, 128)).astype(np.float32)
+    if sinks:
+        kf[:4] *= 8
+    if periodic:
+        kf[periodic::periodic] *= 4
+    k = f32_to_bf16_bits(kf)
+    v = f32_to_bf16_bits(rng.standard_normal((n_k, h_kv, 128)).astype(np.float32))
+    return dict(q=q, k=k, v=v, positions=np.arange(p0, n_k, dtype=np.int32), p0=p0, n_q=n_q, n_k=n_k)
+
+
+def _cfg(inp, h_q, h_kv, S_, W, base=1e6, s=4.0, **kw):
+    return S.Config(n_q=inp["n_q"], n_k=inp["n_k"], h_q=h_q, h_kv=h_kv, dca_chunk=S_, dca_local=W,
+                    rope_base=base, yarn_s=s, **kw)
+
+
+def _oracle(inp, cfg, v_idx=None, s_off=None):
+    return O.attention(inp["q"], inp["k"], inp["v"], inp["p0"], oracle_cfg(cfg), v_idx=v_idx, s_off=s_off)
+
+
+# ------------------------------------------------------------------ dense
+def test_tiny_dense_all_rows():
+    import workloads as W
+    w = W.C1_TINY
+    inp = W.make(w, 0, seed=0)
+    cfg = S.config_for(w)
+    out, lse = run_prefill(inp, cfg, with_lse=True)
+    ref, ref_lse = _oracle(inp, cfg)
+    check_close(out, ref, "tiny dense")
+    assert np.abs(lse - ref_lse).max() <= LSE_TOL
+
+
+@pytest.mark.parametrize("p0,n_q,split", [(320, 333, 0), (0, 200, 1), (128, 1, 0), (640, 190, 3)])
+def test_dense_ragged_multichunk_with_sinks(p0, n_q, split):
+    inp = _inputs(1 + p0, p0, n_q, 4, 2, sinks=True)
+    cfg = _cfg(inp, 4, 2, 256, 64, split_k=split)
+    out, lse = run_prefill(inp, cfg, with_lse=True)
+    ref, ref_lse = _oracle(inp, cfg)
+    check_close(out, ref, f"dense p0={p0} n_q={n_q}")
+    assert np.abs(lse - ref_lse).max() <= LSE_TOL
+
+
+def test_dense_window_equals_chunk_and_large_base():
+    inp = _inputs(2, 512, 256, 2, 1, sinks=True)
+    cfg = _cfg(inp, 2, 1, 128, 128, base=1e7, s=2.0)
+    out, _ = run_prefill(inp, cfg)
+    check_close(out, _oracle(inp, cfg)[0], "W == S")
+
+
+# ------------------------------------------------------------------ sparse
+def _random_pattern(rng, h_q, n_k, kv, ks, pad=True):
+    v_idx = np.full((h_q, kv), -1, dtype=np.int32)
+    s_off = np.full((h_q, ks), -1, dtype=np.int32)
+    for h in range(h_q):
+        nv = kv - (int(rng.integers(0, 3)) if pad else 0)
+        ns = ks - (int(rng.integers(0, 3)) if pad else 0)
+        v_idx[h, :nv] = np.sort(rng.choice(n_k, size=nv, replace=False))
+        s_off[h, :ns] = np.sort(rng.choice(n_k, size=ns, replace=False))
+    return v_idx, s_off
+
+
+@pytest.mark.parametrize("p0,n_q,kv,ks,split", [(512, 300, 40, 25, 0), (1024, 130, 100, 6, 1),
+                                               (256, 64, 10, 60, 2)])
+def test_sparse_random_pattern(p0, n_q, kv, ks, split):
+    inp = _inputs(10 + p0, p0, n_q, 4, 1, sinks=True, periodic=97)
+    rng = np.random.default_rng(p0 + n_q)
+    v_idx, s_off = _random_pattern(rng, 4, inp["n_k"], kv, ks)
+    cfg = _cfg(inp, 4, 1, 256, 32, vs_k_vertical=kv, vs_k_slash=ks, split_k=split)
+    out, lse = run_prefill(inp, cfg, v_idx=v_idx, s_off=s_off, with_lse=True)
+    ref, ref_lse = _oracle(inp, cfg, v_idx, s_off)
+    check_close(out, ref, "sparse")
+    assert np.abs(lse - ref_lse).max() <= LSE_TOL
+
+
+def test_sparse_all_offsets_equals_dense():
+    inp = _inputs(20, 192, 200, 2, 1, sinks=True)
+    n_k = inp["n_k"]
+    s_off = np.tile(np.arange(n_k, dtype=np.int32), (2, 1))
+    v_idx = np.full((2, 1), -1, dtype=np.int32)
+    cfg = _cfg(inp, 2, 1, 128, 32, vs_k_vertical=1, vs_k_slash=n_k)
+    out_sp, _ = run_prefill(inp, cfg, v_idx=v_idx, s_off=s_off)
+    cfg_d = _cfg(inp, 2, 1, 128, 32)
+    out_d, _ = run_prefill(inp, cfg_d)
+    check_close(out_sp, _oracle(inp, cfg_d)[0], "all offsets")
+    assert np.array_equal(out_sp, out_d)
+
+
+def test_sparse_vertical_only():
+    inp = _inputs(21, 384, 150, 2, 2)
+    rng = np.random.default_rng(5)
+    v_idx, _ = _random_pattern(rng, 2, inp["n_k"], 50, 1, pad=False)
+    s_off = np.full((2, 0), -1, dtype=np.int32)
+    cfg = _cfg(inp, 2, 2, 128, 16, vs_k_vertical=50, vs_k_slash=0)
+    out, _ = run_prefill(inp, cfg, v_idx=v_idx, s_off=np.full((2, 1), -1, np.int32))
+    check_close(out, _oracle(inp, cfg, v_idx, s_off)[0], "vertical only")
+
+
+def test_determinism_bitwise():
+    inp = _inputs(30, 256, 256, 4, 2, sinks=True)
+    rng = np.random.default_rng(1)
+    v_idx, s_off = _random_pattern(rng, 4, inp["n_k"], 30, 20)
+    cfg = _cfg(inp, 4, 2, 128, 32, vs_k_vertical=30, vs_k_slash=20, split_k=2)
+    a, la = run_prefill(inp, cfg, v_idx=v_idx, s_off=s_off, with_lse=True)
+    b, lb = run_prefill(inp, cfg, v_idx=v_idx, s_off=s_off, with_lse=True)
+    assert np.array_equal(a, b) and np.array_equal(la, lb)
+
+
+# ------------------------------------------------------------------ index
+def _check_index(inp, cfg, heads=None):
+    v_gpu, s_gpu = run_index(inp, cfg)
+    v_ref, s_ref, gaps = O.vs_index(inp["q"], inp["k"], inp["p0"], oracle_cfg(cfg), heads=heads)
+    for h, gv, gs in gaps:
+        assert gv is None or gv >= 1e-9, f"oracle gap too small at head {h}: {gv}"
+        assert gs is None or gs >= 1e-9, f"oracle gap too small at head {h}: {gs}"
+        assert np.array_equal(v_gpu[h], v_ref[h]), f"vertical mismatch head {h}"
+        assert np.array_equal(s_gpu[h], s_ref[h]), f"slash mismatch head {h}"
+    return v_gpu, s_gpu
+
+
+@pytest.mark.parametrize("p0,n_q,S_,last", [(192, 200, 128, 64), (192, 100, 256, 64), (0, 40, 64, 64),
+                                             (1024, 256, 512, 32)])
+def test_index_bit_exact(p0, n_q, S_, last):
+    inp = _inputs(40 + p0 + n_q, p0, n_q, 4, 2, sinks=True, periodic=128)
+    cfg = _cfg(inp, 4, 2, S_, 32, vs_k_vertical=20, vs_k_slash=40, vs_last_q=last)
+    _check_index(inp, cfg)
+
+
+def test_index_zero_query_ties():
+    inp = _inputs(50, 256, 128, 2, 1)
+    inp["q"][:] = 0
+    cfg = _cfg(inp, 2, 1, 128, 32, vs_k_vertical=20, vs_k_slash=33)
+    v_gpu, s_gpu = run_index(inp, cfg)
+    for h in range(2):
+        assert v_gpu[h].tolist() == list(range(20))
+        assert s_gpu[h].tolist() == list(range(33))
+
+
+def test_index_k_at_least_candidates():
+    inp = _inputs(51, 0, 40, 2, 1)
+    cfg = _cfg(inp, 2, 1, 64, 16, vs_k_vertical=50, vs_k_slash=45)
+    v_gpu, s_gpu = run_index(inp, cfg)
+    for h in range(2):
+        assert v_gpu[h].tolist() == list(range(40)) + [-1] * 10
+        assert s_gpu[h].tolist() == list(range(40)) + [-1] * 5
+
+
+def test_index_planted_structure():
+    rng = np.random.default_rng(13)
+    p0, n_q = 4096, 256
+    inp = _inputs(52, p0, n_q, 1, 1)
+    one = lambda x: f32_to_bf16_bits(np.array([x], np.float32))[0]
+    inp["q"] = f32_to_bf16_bits(rng.standard_normal((n_q, 1, 128)).astype(np.float32) * np.float32(0.05))
+    inp["k"] = f32_to_bf16_bits(rng.standard_normal((p0 + n_q, 1, 128)).astype(np.float32) * np.float32(0.05))
+    inp["q"][:, 0, 63] = one(10.0)
+    strong, weak = [777, 2900], [100, 1500, 3333]
+    inp["k"][strong, 0, 63] = one(10.0)
+    inp["k"][weak, 0, 63] = one(8.0)
+    cfg = _cfg(inp, 1, 1, 8192, 512, vs_k_vertical=5, vs_k_slash=129)
+    v_gpu, s_gpu = run_index(inp, cfg)
+    assert v_gpu[0].tolist() == sorted(strong + weak)
+    p_rows = p0 + np.arange(n_q - 64, n_q)
+    expect = sorted({0} | set((p_rows - strong[0]).tolist()) | set((p_rows - strong[1]).tolist()))
+    assert s_gpu[0].tolist() == expect
+
+
+def test_index_deterministic():
+    inp = _inputs(53, 512, 128, 2, 1, sinks=True)
+    cfg = _cfg(inp, 2, 1, 256, 32, vs_k_vertical=30, vs_k_slash=50)
+    a = run_index(inp, cfg)
+    b = run_index(inp, cfg)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_index_then_prefill_end_to_end():
+    """The GPU index fed to the GPU attention equals the oracle path end to end."""
+    inp = _inputs(54, 768, 256, 4, 2, sinks=True, periodic=64)
+    cfg = _cfg(inp, 4, 2, 256, 64, vs_k_vertical=24, vs_k_slash=48)
+    v_gpu, s_gpu = _check_index(inp, cfg)
+    out, _ = run_prefill(inp, cfg, v_idx=v_gpu, s_off=s_gpu)
+    v_ref, s_ref, _ = O.vs_index(inp["q"], inp["k"], inp["p0"], oracle_cfg(cfg))
+    check_close(out, _oracle(inp, cfg, v_ref, s_ref)[0], "index + prefill")
