@@ -1,0 +1,280 @@
+#!/usr/bin/env python3
+"""Benchmark of the DCA + vertical-slash sparse prefill attention on one MI355X.
+
+One step is one layer's prefill attention of one workload: for each prefill
+chunk, the vertical-slash index build followed by the DCA attention
+(key rotation, sparse plan, attention, LSE merge).  Inputs are seeded
+synthetic tensors already resident in HBM; the timed region holds exactly
+``--steps`` steps between two device synchronisations.
+
+Prints one JSON line:  value = computed-block TFLOP/s of the whole step
+(F_blocks / step time), ms_per_step = ms per layer.  The roofline object
+reports the attention kernel alone (HIP events around it on the stream it
+runs on); the cpu_baseline object times the fp64 oracle on a bounded sample
+of the same workload on the host cores and extrapolates to the full step.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads as W  # noqa: E402
+
+METRIC = "prefill attention TFLOP/s on computed blocks + ms/layer, 7B heads, 128K–1M"
+PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def log(msg: str) -> None:
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """hipEvent_t handles through libamdhip64 (torch's events see only its current stream)."""
+
+    def __init__(self):
+        self.h = ctypes.CDLL("libamdhip64.so")
+        self.h.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n: int):
+        evs = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            rc = self.h.hipEventCreate(ctypes.byref(e))
+            if rc != 0:
+                raise RuntimeError(f"hipEventCreate failed: {rc}")
+            evs.append(e.value)
+        return evs
+
+    def elapsed_ms(self, a, b) -> float:
+        t = ctypes.c_float()
+        rc = self.h.hipEventElapsedTime(ctypes.byref(t), ctypes.c_void_p(a), ctypes.c_void_p(b))
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed: {rc}")
+        return float(t.value)
+
+
+def kernel_source_hash() -> str:
+    src = os.path.join(ROOT, "sparse_dual_chunk_amd", "csrc", "attn.hip")
+    return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+
+
+def traffic_from_profile(units_per_launch: float):
+    """HBM bytes per attention launch from the committed counter summary, if it was taken
+    on the current attention kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "attn_traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        d = json.load(open(path))
+    except Exception:
+        return None
+    if d.get("attn_source_sha256_16") != kernel_source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, inputs, p0s, f_blocks_total: float, n_blocks_total: int):
+    """Oracle timing on a bounded sample: index scores of one head, attention of two blocks."""
+    from oracle import dca_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    inp = inputs[-1]
+    cfg = dict(h_q=w.h_q, h_kv=w.h_kv, dca_chunk=w.dca_chunk, dca_local=w.dca_local, rope_base=w.rope_base,
+               yarn_s=w.yarn_s, vs_k_vertical=w.k_vertical, vs_k_slash=w.k_slash, vs_last_q=w.vs_last_q)
+    t0 = time.perf_counter()
+    v_idx = s_off = None
+    t_index_head = 0.0
+    if w.sparse:
+        v_idx, s_off, _ = O.vs_index(inp["q"], inp["k"], inp["p0"], cfg, heads=[0])
+        t_index_head = time.perf_counter() - t0
+    nb = (inp["n_q"] + 63) // 64
+    blocks = [nb - 1, nb // 2]
+    t1 = time.perf_counter()
+    fb_sample = 0
+    for b in blocks:
+        _, _, keys = O.attention_block(inp["q"], inp["k"], inp["v"], inp["p0"], 0, b, cfg, v_idx, s_off)
+        rows = min(64, inp["n_q"] - 64 * b)
+        fb_sample += 4 * 128 * rows * len(keys)
+    t_att = time.perf_counter() - t1
+    n_calls = len(p0s)
+    # extrapolate: index per head x heads x calls, attention by the computed-block share
+    t_step = t_index_head * w.h_q * n_calls + t_att * (f_blocks_total / max(fb_sample, 1))
+    return {
+        "value": f_blocks_total / t_step / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": (f"fp64 oracle on the host: index scores of query head 0 of the last chunk "
+                   f"({t_index_head:.1f} s) and attention of query blocks {blocks} of head 0 "
+                   f"({t_att:.1f} s, {fb_sample / 1e9:.1f} GFLOP); step time extrapolated to "
+                   f"{w.h_q} heads x {n_calls} call(s) and to F_blocks"),
+        "seconds_measured": round(time.perf_counter() - t0, 2),
+        "ms_per_step_extrapolated": round(t_step * 1e3, 1),
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default=W.C5_7B_1M.name, choices=sorted(W.WORKLOADS))
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (the path is measured on one MI355X; --gpus {args.gpus} "
+              "is not supported; collectives and sharding are outside this build)", file=sys.stderr)
+        return 2
+
+    import torch
+    import sparse_dual_chunk_amd as S
+
+    w = W.WORKLOADS[args.workload]
+    log(f"workload {w.name}: generating inputs (seed {args.seed})")
+    kv = W.make_keys_values(w, w.n_k_total, args.seed)
+    calls = []
+    for c in range(len(w.chunks)):
+        inp = W.make(w, c, seed=args.seed, kv=kv)
+        cfg = S.config_for(w, c)
+        calls.append((inp, cfg))
+    log("uploading to HBM")
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
+    K = dev(kv[0])
+    V = dev(kv[1])
+    ws_bytes = max(S.dca_workspace_size(cfg) for _, cfg in calls)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    gpu_calls = []
+    for inp, cfg in calls:
+        n_k = inp["n_k"]
+        q = dev(inp["q"])
+        out = torch.empty(q.shape, dtype=torch.int16, device="cuda")
+        vi = torch.empty((w.h_q, max(w.k_vertical, 1)), dtype=torch.int32, device="cuda")
+        so = torch.empty((w.h_q, max(w.k_slash, 1)), dtype=torch.int32, device="cuda")
+        pairs = torch.zeros(1, dtype=torch.int64, device="cuda")
+        gpu_calls.append(dict(q=q, k=K[:n_k], v=V[:n_k], out=out, vi=vi, so=so, pairs=pairs,
+                              pos=inp["positions"], cfg=cfg))
+    torch.cuda.synchronize()
+
+    hev = HipEvents()
+    n_stage_ev = 2 * S.DCA_STAGE_COUNT
+
+    def step(stage_events=None, index_events=None):
+        for ci, g in enumerate(gpu_calls):
+            if w.sparse:
+                if index_events is not None:
+                    index_events[ci][0].record()
+                S.vs_index_build(g["q"], g["k"], g["pos"], g["cfg"], g["vi"], g["so"], ws)
+                if index_events is not None:
+                    index_events[ci][1].record()
+            S.dca_sparse_prefill(g["q"], g["k"], g["v"], g["pos"], g["cfg"], g["out"], ws,
+                                 v_idx=g["vi"] if w.sparse else None, s_off=g["so"] if w.sparse else None,
+                                 cover_pairs=g["pairs"],
+                                 stage_events=None if stage_events is None else stage_events[ci])
+
+    log(f"warmup {args.warmup} step(s)")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    stage_ev = [[hev.create(n_stage_ev) for _ in gpu_calls] for _ in range(args.steps)]
+    index_ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                 for _ in gpu_calls] for _ in range(args.steps)]
+    log(f"timing {args.steps} step(s)")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(stage_ev[s], index_ev[s])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+
+    # per-stage times (ms per step, summed over the chunk calls)
+    stage_ms = {name: 0.0 for name in S.STAGES}
+    attn_launch_ms = []
+    index_ms = 0.0
+    for s in range(args.steps):
+        for ci in range(len(gpu_calls)):
+            ev = stage_ev[s][ci]
+            for si, name in enumerate(S.STAGES):
+                stage_ms[name] += hev.elapsed_ms(ev[2 * si], ev[2 * si + 1]) / args.steps
+            attn_launch_ms.append(hev.elapsed_ms(ev[4], ev[5]))
+            if w.sparse:
+                a, b = index_ev[s][ci]
+                index_ms += a.elapsed_time(b) / args.steps
+
+    pairs_per_call = [int(g["pairs"].item()) for g in gpu_calls]
+    f_blocks = 4 * 128 * sum(pairs_per_call)
+    value = f_blocks / (ms_per_step / 1e3) / 1e12
+    # dominant kernel: the attention launch; algorithmic flops per launch = 4 d * cover pairs of that call
+    attn_avg_ms = float(np.mean(attn_launch_ms))
+    f_per_launch = f_blocks / len(gpu_calls)
+    achieved = f_per_launch / (attn_avg_ms / 1e3) / 1e12
+    traffic = traffic_from_profile(f_per_launch)
+    dense_pairs = sum(
+        sum(min(64, inp["n_q"] - 64 * b) * (inp["p0"] + 64 * b + min(64, inp["n_q"] - 64 * b))
+            for b in range((inp["n_q"] + 63) // 64)) * w.h_q for inp, _ in calls)
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "prefill_calls": [[p0, nq] for p0, nq in w.chunks],
+            "h_q": w.h_q, "h_kv": w.h_kv, "head_dim": w.head_dim,
+            "dca_chunk": w.dca_chunk, "dca_local": w.dca_local, "rope_base": w.rope_base, "yarn_s": w.yarn_s,
+            "k_vertical": w.k_vertical, "k_slash": w.k_slash, "seed": args.seed,
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+            "kernel": "dca_attn_kernel",
+            "avg_launch_ms": round(attn_avg_ms, 4),
+            "algorithmic_flops_per_launch": f_per_launch,
+        },
+        "f_blocks": f_blocks,
+        "cover_fraction_of_dense": round(sum(pairs_per_call) / dense_pairs, 4),
+        "stage_ms": {"index_build": round(index_ms, 3), **{k: round(v, 3) for k, v in stage_ms.items()}},
+        "attention_tflops": round(achieved, 2),
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline: timing the oracle on a sample")
+        result["cpu_baseline"] = cpu_baseline(w, [c[0] for c in calls], [p0 for p0, _ in w.chunks],
+                                              f_blocks, 0)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -91,6 +91,9 @@ typedef struct dca_cfg {
   const int32_t *v_idx;
   const int32_t *s_off;
   float   *lse_out;       /* optional device [h_q][n_q] natural-log LSE of each row; NULL: not written */
+  int64_t *cover_pairs;   /* optional device int64: dca_sparse_prefill writes sum over heads and query
+                             blocks of rows(block) * |cover(block)|, the (row, key) pairs of the computed
+                             blocks; 4 * head_dim * cover_pairs is the computed-block FLOP count.  NULL: not written */
   float   precise_norm;   /* keys whose L2 norm exceeds this get split-bf16 (hi+lo) logits;
                              0: default 2*sqrt(head_dim); < 0: never */
   int32_t split_k;        /* key-range splits per query block, merged by LSE: 0 = library's choice */

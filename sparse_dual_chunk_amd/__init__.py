@@ -51,6 +51,7 @@ class dca_cfg(ctypes.Structure):
         ("v_idx", ctypes.c_void_p),
         ("s_off", ctypes.c_void_p),
         ("lse_out", ctypes.c_void_p),
+        ("cover_pairs", ctypes.c_void_p),
         ("precise_norm", ctypes.c_float),
         ("split_k", ctypes.c_int32),
         ("workspace", ctypes.c_void_p),
@@ -160,7 +161,7 @@ def vs_index_build(q, k, positions, cfg: Config, v_idx, s_off, workspace, stream
 
 
 def dca_sparse_prefill(q, k, v, positions, cfg: Config, out, workspace, v_idx=None, s_off=None, lse_out=None,
-                       stream=None, stage_events: Optional[Sequence[int]] = None) -> None:
+                       cover_pairs=None, stream=None, stage_events: Optional[Sequence[int]] = None) -> None:
     """DCA prefill attention of one chunk (dense when v_idx and s_off are None)."""
     pos, pos_p = _positions(positions)
     ev_arr = None
@@ -168,6 +169,7 @@ def dca_sparse_prefill(q, k, v, positions, cfg: Config, out, workspace, v_idx=No
         ev_arr = (ctypes.c_void_p * (2 * DCA_STAGE_COUNT))(*[int(e) for e in stage_events])
     c = cfg.to_c(workspace=_ptr(workspace), workspace_bytes=workspace.numel() * workspace.element_size(),
                  stream=_stream(stream), v_idx=_ptr(v_idx), s_off=_ptr(s_off), lse_out=_ptr(lse_out),
+                 cover_pairs=_ptr(cover_pairs),
                  stage_events=ctypes.cast(ev_arr, ctypes.c_void_p) if ev_arr is not None else None)
     rc = lib().dca_sparse_prefill(_ptr(q), _ptr(k), _ptr(v), pos_p, ctypes.byref(c), _ptr(out))
     if rc != DCA_OK:

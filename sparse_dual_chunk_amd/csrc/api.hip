@@ -1,6 +1,7 @@
 // C ABI of the DCA sparse prefill library: validation, workspace layout and
 // launch sequences.  Declared in include/dcasparse.h.
 #include <cmath>
+#include <algorithm>
 #include <cstring>
 
 #include "../../include/dcasparse.h"
@@ -27,6 +28,7 @@ using namespace dca;
 struct Freqs { double v[HALF]; };
 
 __global__ void write_freqs_kernel(Freqs f, double* dst) { dst[threadIdx.x] = f.v[threadIdx.x]; }
+__global__ void write_i64_kernel(long long* dst, long long v) { *dst = v; }
 
 constexpr size_t ALIGN = 256;
 inline size_t up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
@@ -38,7 +40,7 @@ struct Layout {
   // shared
   Region freqs;
   // prefill
-  Region khi, klo, kflag, iv, n_iv, cov, ext, n_ext, part_o, part_lse;
+  Region khi, klo, kflag, iv, iv_pre, n_iv, cov, ext, n_ext, part_o, part_lse;
   // index
   Region qs, part_ms, lse, vert, slash, edge, hist, prefix, krem, bcount;
   size_t prefill_bytes = 0, index_bytes = 0;
@@ -96,6 +98,7 @@ Layout make_layout(const dca_cfg* c) {
   place(L.klo, cur, (size_t)n_k * h_kv * D * 2);
   place(L.kflag, cur, (size_t)n_k * h_kv);
   place(L.iv, cur, (size_t)h_q * (c->vs_k_slash + 1) * 2 * 4);
+  place(L.iv_pre, cur, (size_t)h_q * (c->vs_k_slash + 2) * 4);
   place(L.n_iv, cur, (size_t)h_q * 4);
   L.cov_words = (p_last + 64 + 31) / 32;
   place(L.cov, cur, (size_t)h_q * L.cov_words * 4);
@@ -245,13 +248,22 @@ int dca_sparse_prefill(const dca_bf16* q, const dca_bf16* k, const dca_bf16* v, 
   if (sparse) {
     PlanArgs P;
     P.v_idx = cfg->v_idx; P.s_off = cfg->s_off;
-    P.iv = at<int32_t>(cfg, L.iv); P.n_iv = at<int32_t>(cfg, L.n_iv);
+    P.iv = at<int32_t>(cfg, L.iv); P.iv_pre = at<int32_t>(cfg, L.iv_pre); P.n_iv = at<int32_t>(cfg, L.n_iv);
+    P.cover_pairs = (long long*)cfg->cover_pairs;
     P.cov = at<uint32_t>(cfg, L.cov);
     P.ext = at<int32_t>(cfg, L.ext); P.n_ext = at<int32_t>(cfg, L.n_ext);
     P.h_q = h_q; P.k_v = cfg->vs_k_vertical; P.k_s = cfg->vs_k_slash; P.p_last = p_last; P.p0 = p0;
     P.n_q = n_q; P.nb = L.nb; P.iv_stride = cfg->vs_k_slash + 1;
     P.ext_stride = cfg->vs_k_vertical > 0 ? cfg->vs_k_vertical : 1; P.cov_words = L.cov_words;
     if (launch_plan(P, st) != hipSuccess) return DCA_EHIP;
+  } else if (cfg->cover_pairs) {
+    // dense: every block covers its whole causal extent [0, i0 + rows)
+    long long pairs = 0;
+    for (int b = 0; b < L.nb; ++b) {
+      const long long rows = std::min(64, n_q - 64 * b);
+      pairs += rows * (long long)(p0 + 64 * b + rows);
+    }
+    hipLaunchKernelGGL(write_i64_kernel, dim3(1), dim3(1), 0, st, (long long*)cfg->cover_pairs, pairs * h_q);
   }
   record(cfg, 1, 1);
   // stage 2: attention

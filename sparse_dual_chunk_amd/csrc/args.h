@@ -53,10 +53,12 @@ struct PlanArgs {
   const int32_t* v_idx;    // [h_q][k_v]
   const int32_t* s_off;    // [h_q][k_s]
   int32_t* iv;             // [h_q][iv_stride][2]
+  int32_t* iv_pre;         // [h_q][iv_stride + 1] covered offsets before interval k
   int32_t* n_iv;           // [h_q]
   uint32_t* cov;           // [h_q][cov_words] bitmap over offsets o in [-p_last, 64)
   int32_t* ext;            // [h_q][nb][ext_stride]
   int32_t* n_ext;          // [h_q][nb]
+  long long* cover_pairs;  // optional: sum of rows * |cover| over all (head, block)
   int h_q, k_v, k_s, p_last, p0, n_q, nb, iv_stride, ext_stride, cov_words;
 };
 

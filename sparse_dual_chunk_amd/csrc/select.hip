@@ -262,6 +262,11 @@ __global__ void __launch_bounds__(1024) plan_intervals_kernel(PlanArgs A) {
   if (threadIdx.x == 0) {
     if (carry_count > 0) ivh[2 * (carry_count - 1) + 1] = -carry_last + 64;
     A.n_iv[h] = carry_count;
+    int32_t* pre = A.iv_pre + (long long)h * (A.iv_stride + 1);
+    int acc = 0;
+    for (int u = 0; u < carry_count; ++u) { pre[u] = acc; acc += ivh[2 * u + 1] - ivh[2 * u]; }
+    pre[carry_count] = acc;
+    if (A.cover_pairs && h == 0) *A.cover_pairs = 0;
   }
 }
 
@@ -323,7 +328,28 @@ __global__ void __launch_bounds__(256) plan_ext_kernel(PlanArgs A) {
     }
     cnt += __popcll(bal);
   }
-  if (lane == 0) A.n_ext[unit] = cnt;
+  if (lane == 0) {
+    A.n_ext[unit] = cnt;
+    if (A.cover_pairs) {
+      // covered offsets below x: prefix of whole intervals plus the part of the one holding x
+      const int32_t* ivh = A.iv + (long long)h * A.iv_stride * 2;
+      const int32_t* pre = A.iv_pre + (long long)h * (A.iv_stride + 1);
+      const int n_iv = A.n_iv[h];
+      const int rows = hi_key - i0;
+      long long below[2];
+      const int xs[2] = {-i0, rows};
+      for (int t = 0; t < 2; ++t) {
+        const int x = xs[t];
+        int a = 0, z = n_iv;
+        while (a < z) { const int mid = (a + z) >> 1; if (ivh[2 * mid + 1] > x) z = mid; else a = mid + 1; }
+        long long c = pre[a];
+        if (a < n_iv && x > ivh[2 * a]) c += x - ivh[2 * a];
+        below[t] = c;
+      }
+      const long long cover = (below[1] - below[0]) + cnt;
+      atomicAdd((unsigned long long*)A.cover_pairs, (unsigned long long)(cover * rows));
+    }
+  }
 }
 
 hipError_t launch_plan(const PlanArgs& A, hipStream_t stream) {
