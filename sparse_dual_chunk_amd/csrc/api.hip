@@ -10,8 +10,9 @@
 
 namespace dca {
 
-hipError_t launch_rotate_keys(const uint16_t* k, uint16_t* khi, uint16_t* klo, uint8_t* kflag,
-                              const double* inv_freq, int n_k, int h_kv, int S, float thr2, hipStream_t stream);
+hipError_t launch_rotate_keys(const uint16_t* k, uint16_t* khi, uint16_t* klo, uint32_t* kbits,
+                              const double* inv_freq, int n_k, int h_kv, int S, float thr2, int kbits_words,
+                              hipStream_t stream);
 hipError_t launch_attn(const AttnArgs& A, hipStream_t stream);
 hipError_t launch_lse_merge(const float* part_o, const float* part_lse, uint16_t* out, float* lse_out,
                             int P, int n_q, int h_q, hipStream_t stream);
@@ -40,11 +41,12 @@ struct Layout {
   // shared
   Region freqs;
   // prefill
-  Region khi, klo, kflag, iv, iv_pre, n_iv, cov, ext, n_ext, part_o, part_lse;
+  Region khi, klo, kbits, iv, iv_pre, n_iv, cov, ext, n_ext, tiles, n_tiles, t_first, part_o, part_lse;
   // index
   Region qs, part_ms, lse, vert, slash, edge, hist, prefix, krem, bcount;
   size_t prefill_bytes = 0, index_bytes = 0;
-  int split = 1, nb = 0, n_ranges = 0, range_keys = 0, cov_words = 0, max_blocks = 0;
+  int split = 1, nb = 0, n_ranges = 0, range_keys = 0, cov_words = 0, max_blocks = 0, kbits_words = 0,
+      tile_stride = 0;
 };
 
 inline void place(Region& r, size_t& cur, size_t bytes) { r.off = cur; r.bytes = bytes; cur += up(bytes); }
@@ -96,7 +98,8 @@ Layout make_layout(const dca_cfg* c) {
   // --- prefill
   place(L.khi, cur, (size_t)n_k * h_kv * D * 2);
   place(L.klo, cur, (size_t)n_k * h_kv * D * 2);
-  place(L.kflag, cur, (size_t)n_k * h_kv);
+  L.kbits_words = (n_k + 31) / 32 + 1;
+  place(L.kbits, cur, (size_t)h_kv * L.kbits_words * 4);
   place(L.iv, cur, (size_t)h_q * (c->vs_k_slash + 1) * 2 * 4);
   place(L.iv_pre, cur, (size_t)h_q * (c->vs_k_slash + 2) * 4);
   place(L.n_iv, cur, (size_t)h_q * 4);
@@ -104,6 +107,11 @@ Layout make_layout(const dca_cfg* c) {
   place(L.cov, cur, (size_t)h_q * L.cov_words * 4);
   place(L.ext, cur, (size_t)h_q * L.nb * (size_t)(c->vs_k_vertical > 0 ? c->vs_k_vertical : 1) * 4);
   place(L.n_ext, cur, (size_t)h_q * L.nb * 4);
+  // range tiles of 32 covered offsets: every merged interval is at least 64 long
+  L.tile_stride = 2 * (c->vs_k_slash + 1) + 1;
+  place(L.tiles, cur, (size_t)h_q * L.tile_stride * 16);
+  place(L.n_tiles, cur, (size_t)h_q * 4);
+  place(L.t_first, cur, (size_t)h_q * L.nb * 4);
   if (L.split > 1) {
     place(L.part_o, cur, (size_t)L.split * n_q * h_q * D * 4);
     place(L.part_lse, cur, (size_t)L.split * h_q * n_q * 4);
@@ -239,8 +247,8 @@ int dca_sparse_prefill(const dca_bf16* q, const dca_bf16* k, const dca_bf16* v, 
   record(cfg, 0, 0);
   float thr = cfg->precise_norm == 0.f ? 2.f * std::sqrt((float)D) : cfg->precise_norm;
   const float thr2 = thr < 0.f ? -1.f : thr * thr;
-  if (launch_rotate_keys(k, at<uint16_t>(cfg, L.khi), at<uint16_t>(cfg, L.klo), at<uint8_t>(cfg, L.kflag),
-                         at<double>(cfg, L.freqs), n_k, h_kv, cfg->dca_chunk, thr2, st) != hipSuccess)
+  if (launch_rotate_keys(k, at<uint16_t>(cfg, L.khi), at<uint16_t>(cfg, L.klo), at<uint32_t>(cfg, L.kbits),
+                         at<double>(cfg, L.freqs), n_k, h_kv, cfg->dca_chunk, thr2, L.kbits_words, st) != hipSuccess)
     return DCA_EHIP;
   record(cfg, 0, 1);
   // stage 1: sparse plan
@@ -255,6 +263,9 @@ int dca_sparse_prefill(const dca_bf16* q, const dca_bf16* k, const dca_bf16* v, 
     P.h_q = h_q; P.k_v = cfg->vs_k_vertical; P.k_s = cfg->vs_k_slash; P.p_last = p_last; P.p0 = p0;
     P.n_q = n_q; P.nb = L.nb; P.iv_stride = cfg->vs_k_slash + 1;
     P.ext_stride = cfg->vs_k_vertical > 0 ? cfg->vs_k_vertical : 1; P.cov_words = L.cov_words;
+    P.tiles = at<int4>(cfg, L.tiles); P.n_tiles = at<int32_t>(cfg, L.n_tiles); P.t_first = at<int32_t>(cfg, L.t_first);
+    P.kbits = at<uint32_t>(cfg, L.kbits); P.h_kv = h_kv; P.tile_stride = L.tile_stride;
+    P.kbits_words = L.kbits_words;
     if (launch_plan(P, st) != hipSuccess) return DCA_EHIP;
   } else if (cfg->cover_pairs) {
     // dense: every block covers its whole causal extent [0, i0 + rows)
@@ -270,14 +281,14 @@ int dca_sparse_prefill(const dca_bf16* q, const dca_bf16* k, const dca_bf16* v, 
   record(cfg, 2, 0);
   AttnArgs A;
   A.q = q; A.khi = at<uint16_t>(cfg, L.khi); A.klo = at<uint16_t>(cfg, L.klo); A.v = v;
-  A.kflag = at<uint8_t>(cfg, L.kflag); A.inv_freq = at<double>(cfg, L.freqs);
+  A.kbits = at<uint32_t>(cfg, L.kbits); A.inv_freq = at<double>(cfg, L.freqs);
   A.out = out; A.lse_out = cfg->lse_out;
   A.part_o = L.split > 1 ? at<float>(cfg, L.part_o) : nullptr;
   A.part_lse = L.split > 1 ? at<float>(cfg, L.part_lse) : nullptr;
-  A.iv = at<int32_t>(cfg, L.iv); A.n_iv = at<int32_t>(cfg, L.n_iv);
+  A.tiles = at<int4>(cfg, L.tiles); A.n_tiles = at<int32_t>(cfg, L.n_tiles); A.t_first = at<int32_t>(cfg, L.t_first);
   A.ext = at<int32_t>(cfg, L.ext); A.n_ext = at<int32_t>(cfg, L.n_ext);
   A.n_q = n_q; A.n_k = n_k; A.h_q = h_q; A.h_kv = h_kv; A.p0 = p0; A.S = cfg->dca_chunk; A.W = cfg->dca_local;
-  A.nb = L.nb; A.iv_stride = cfg->vs_k_slash + 1;
+  A.nb = L.nb; A.tile_stride = L.tile_stride; A.kbits_words = L.kbits_words;
   A.ext_stride = cfg->vs_k_vertical > 0 ? cfg->vs_k_vertical : 1;
   A.split = L.split; A.dense = sparse ? 0 : 1;
   A.qscale = (float)(yarn_factor(cfg->yarn_s) / std::sqrt((double)D) * 1.4426950408889634);

@@ -1,5 +1,6 @@
 // Argument blocks of the kernels, shared by the kernels and the host entry points.
 #pragma once
+#include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace dca {
@@ -9,17 +10,18 @@ struct AttnArgs {
   const uint16_t* khi;      // [n_k][h_kv][128] rotated, bf16 hi
   const uint16_t* klo;      // same, lo residual
   const uint16_t* v;        // [n_k][h_kv][128]
-  const uint8_t* kflag;     // [h_kv][n_k]
+  const uint32_t* kbits;    // [h_kv][kbits_words] bit j: key j is high-norm (split-precision logits)
   const double* inv_freq;   // [64]
   uint16_t* out;            // [n_q][h_q][128]
   float* lse_out;           // [h_q][n_q] or null
   float* part_o;            // [P][n_q][h_q][128] (P > 1)
   float* part_lse;          // [P][h_q][n_q]      (P > 1)
-  const int32_t* iv;        // [h_q][iv_stride][2] merged slash intervals (offset space)
-  const int32_t* n_iv;      // [h_q]
-  const int32_t* ext;       // [h_q][nb][ext_stride] vertical keys outside the ranges
+  const int4* tiles;        // [h_q][tile_stride] range tiles in offset space: {o1, o2, len1 | len2 << 8, 0}
+  const int32_t* n_tiles;   // [h_q]
+  const int32_t* t_first;   // [h_q][nb] first range tile of each query block
+  const int32_t* ext;       // [h_q][nb][ext_stride] vertical keys outside the ranges (bit 30: high-norm)
   const int32_t* n_ext;     // [h_q][nb]
-  int n_q, n_k, h_q, h_kv, p0, S, W, nb, iv_stride, ext_stride, split, dense;
+  int n_q, n_k, h_q, h_kv, p0, S, W, nb, tile_stride, ext_stride, split, dense, kbits_words;
   float qscale;             // softmax scale * log2(e), folded into the query rotation
 };
 
@@ -58,8 +60,12 @@ struct PlanArgs {
   uint32_t* cov;           // [h_q][cov_words] bitmap over offsets o in [-p_last, 64)
   int32_t* ext;            // [h_q][nb][ext_stride]
   int32_t* n_ext;          // [h_q][nb]
+  int4* tiles;             // [h_q][tile_stride]
+  int32_t* n_tiles;        // [h_q]
+  int32_t* t_first;        // [h_q][nb]
+  const uint32_t* kbits;   // [h_kv][kbits_words]
   long long* cover_pairs;  // optional: sum of rows * |cover| over all (head, block)
-  int h_q, k_v, k_s, p_last, p0, n_q, nb, iv_stride, ext_stride, cov_words;
+  int h_q, h_kv, k_v, k_s, p_last, p0, n_q, nb, iv_stride, ext_stride, cov_words, tile_stride, kbits_words;
 };
 
 }  // namespace dca

@@ -21,65 +21,96 @@
 namespace dca {
 
 
-// LDS row pitches (bf16 elements).  K rows: 136 (68 dwords) keeps the 16-byte
-// operand reads of 16 consecutive rows on distinct banks.  V rows: 144
-// (72 dwords) keeps the transposed 8-byte reads of 4 consecutive rows apart.
-constexpr int KP = 136;
-constexpr int VP = 144;
+// Tiles of 32 keys staged in LDS by direct global->LDS loads, two stages.
+// A tile of one tensor is 8 groups of 4 key rows; a group is stored
+// chunk-major ([16-byte chunk][row], 1 KiB) followed by 64 bytes of padding.
+// Each direct load instruction fills one group (lane l: chunk l/4, row l%4).
+// With the padding, the K operand reads (16 rows, one chunk) and the
+// transposed V reads (4 rows, two chunks) of a 16-lane group fall on distinct
+// banks, and every read address is a per-lane base plus an immediate offset.
+constexpr int BN = 32;
+constexpr int GRPB = 1024 + 64;                // bytes per 4-row group
+constexpr int TILEB = 8 * GRPB;                // one tensor of one tile
+constexpr int STAGEB = 2 * TILEB;              // K then V
 
-struct __align__(16) AttnSmem {
-  uint16_t k[64 * KP];
-  uint16_t v[64 * VP];
-  uint16_t kl[64 * KP];
-  uint16_t ql[2][8 * 64 * 8];  // per wave: q lo fragments [kk][lane][8]
-  int32_t keys[64];
+struct __align__(16) AttnQlo {
+  bf16x8 ql[2][8][64];       // per wave: query lo fragments [kk][lane] (used by high-norm tiles only)
 };
+
+// byte offset of (row, 16-byte chunk) inside a tensor tile
+__device__ __forceinline__ int tile_off(int row, int chunk) { return (row >> 2) * GRPB + chunk * 64 + (row & 3) * 16; }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// max / sum of a value with the one held by lane ^ 32 (the other half of the row)
+__device__ __forceinline__ float pair_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Rotate this lane's query fragment for one DCA mode.  Lane (row = l%32,
 // half = l/32) holds dims {16kk + 8half + e}: pairs (c, c+64) sit in slots kk
-// and kk+4 of the same lane.
+// and kk+4 of the same lane.  The rotated value times the softmax scale is
+// split into bf16 hi and lo halves.  Angles are reduced in fp64 to a fraction
+// of a turn and evaluated with the hardware sine / cosine of that fraction.
 __device__ __forceinline__ void rotate_q(const AttnArgs& A, int h, int row, bool row_ok, int half,
-                                         double qpos, bf16x8 (&qh)[8], uint16_t* ql_w, int lane) {
+                                         double qpos, bf16x8 (&qh)[8], bf16x8 (*ql)[64], int lane) {
   const uint16_t* src = A.q + ((long long)row * A.h_q + h) * D;
-  uint4 raw[8];
-#pragma unroll
-  for (int kk = 0; kk < 8; ++kk) {
-    if (row_ok) raw[kk] = *(const uint4*)(src + 16 * kk + 8 * half);
-    else raw[kk] = make_uint4(0, 0, 0, 0);
-  }
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
-    const uint16_t* xa = (const uint16_t*)&raw[kk];
-    const uint16_t* xb = (const uint16_t*)&raw[kk + 4];
-    uint16_t hi_a[8], hi_b[8], lo_a[8], lo_b[8];
+    bf16x8 la, lb;
+    uint4 ra = make_uint4(0, 0, 0, 0), rb = make_uint4(0, 0, 0, 0);
+    if (row_ok) {
+      ra = *(const uint4*)(src + 16 * kk + 8 * half);
+      rb = *(const uint4*)(src + 16 * (kk + 4) + 8 * half);
+    }
+    const uint16_t* xa = (const uint16_t*)&ra;
+    const uint16_t* xb = (const uint16_t*)&rb;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int c = 16 * kk + 8 * half + e;
-      float sn, cs;
-      sincosf(reduce_angle(qpos, A.inv_freq[c]), &sn, &cs);
+      const double turns = qpos * A.inv_freq[c] * INV_TWO_PI;
+      const float f = (float)(turns - rint(turns));
+      const float sn = __builtin_amdgcn_sinf(f);
+      const float cs = __builtin_amdgcn_cosf(f);
       const float x = bf16_bits_to_f32(xa[e]);
       const float y = bf16_bits_to_f32(xb[e]);
       const float xr = (x * cs - y * sn) * A.qscale;
       const float yr = (x * sn + y * cs) * A.qscale;
-      hi_a[e] = f32_to_bf16_bits(xr);
-      hi_b[e] = f32_to_bf16_bits(yr);
-      lo_a[e] = f32_to_bf16_bits(xr - bf16_bits_to_f32(hi_a[e]));
-      lo_b[e] = f32_to_bf16_bits(yr - bf16_bits_to_f32(hi_b[e]));
+      const __bf16 ha = (__bf16)xr, hb = (__bf16)yr;
+      qh[kk][e] = ha;
+      qh[kk + 4][e] = hb;
+      la[e] = (__bf16)(xr - (float)ha);
+      lb[e] = (__bf16)(yr - (float)hb);
     }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      qh[kk][e] = bits_as_bf16(hi_a[e]);
-      qh[kk + 4][e] = bits_as_bf16(hi_b[e]);
-      ql_w[(kk * 64 + lane) * 8 + e] = lo_a[e];
-      ql_w[((kk + 4) * 64 + lane) * 8 + e] = lo_b[e];
-    }
+    ql[kk][lane] = la;
+    ql[kk + 4][lane] = lb;
   }
 }
 
+// One tile of the walk, wave-uniform: range tiles hold two runs of keys
+// [a1, a1+len1) ++ [a2, a2+len2) (absolute; a1 < 0 possible in the first tile
+// of a block); extra tiles (cnt > 0) hold entries [eoff, eoff+cnt) of the
+// block's extra-vertical list.
+struct Tile {
+  int a1, a2, len1, len2, eoff, cnt;
+};
+
+__device__ __forceinline__ int tile_count(const Tile& T) { return T.cnt ? T.cnt : T.len1 + T.len2; }
+
+// key of slot t (0..31) of a range tile, or -1 outside the tile
+__device__ __forceinline__ int range_key(const Tile& T, int t) {
+  return t < T.len1 ? T.a1 + t : (t < T.len1 + T.len2 ? T.a2 + (t - T.len1) : -1);
+}
+
 __global__ void __launch_bounds__(128, 2) dca_attn_kernel(AttnArgs A) {
-  __shared__ AttnSmem sm;
+  __shared__ __align__(16) uint8_t stage0[STAGEB];
+  __shared__ __align__(16) uint8_t stage1[STAGEB];
+  __shared__ AttnQlo qsm;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -94,10 +125,10 @@ __global__ void __launch_bounds__(128, 2) dca_attn_kernel(AttnArgs A) {
   const int C = A.h_q * A.split;
   const int die = blockIdx.x % NXCD;
   const int local = blockIdx.x / NXCD;
-  const int c = NXCD * (local / C) + die;
-  if (c >= A.nb) return;
+  const int cidx = NXCD * (local / C) + die;
+  if (cidx >= A.nb) return;
   const int w = local % C;
-  const int b = A.nb - 1 - c;
+  const int b = A.nb - 1 - cidx;
   const int h = w / A.split;
   const int part = w % A.split;
   const int g = h / (A.h_q / A.h_kv);
@@ -110,244 +141,249 @@ __global__ void __launch_bounds__(128, 2) dca_attn_kernel(AttnArgs A) {
   const bool row_ok = rloc < rows;
   const int qrow = QB * b + (row_ok ? rloc : 0);
   const int prow = i0 + rloc;                    // absolute position of this lane's row
+  // DCA mode of a key: 2 intra-chunk [segB, ..), 1 successive [segA, segB), 0 inter-chunk [0, segA)
+  const int segA = max(0, (m_blk - 1) * A.S);
+  const int segB = max(0, m_blk * A.S);
 
-  // key range of this split part (64-aligned)
-  int k_beg = 0, k_end = hi_key;
-  if (A.split > 1) {
-    const int tiles = (hi_key + 63) / 64;
-    k_beg = min(hi_key, (int)(((long long)tiles * part / A.split) * 64));
-    k_end = min(hi_key, (int)(((long long)tiles * (part + 1) / A.split) * 64));
-  }
+  const int unit = h * A.nb + b;
+  const int* tl_h = (const int*)(A.tiles + (long long)h * A.tile_stride);
+  const int t_first = A.dense ? 0 : A.t_first[unit];
+  const int n_range = A.dense ? (hi_key + BN - 1) / BN : A.n_tiles[h] - t_first;
+  const int32_t* ext_h = A.ext + (long long)unit * A.ext_stride;
+  const int n_ext = A.dense ? 0 : A.n_ext[unit];
+  const int n_all = n_range + (n_ext + BN - 1) / BN;
+  const int t_beg = (int)((long long)n_all * part / A.split);
+  const int t_end = (int)((long long)n_all * (part + 1) / A.split);
 
-  // mode segments: inter [0, A), successive [A, B), intra [B, hi_key)
-  const int segA = min(hi_key, max(0, (m_blk - 1) * A.S));
-  const int segB = min(hi_key, max(0, m_blk * A.S));
-  const int seg_lo[3] = {0, segA, segB};
-  const int seg_hi[3] = {segA, segB, hi_key};
-
-  const int32_t* ivh = A.iv + (long long)h * A.iv_stride * 2;
-  const int n_ivh = A.dense ? 0 : A.n_iv[h];
-  const int32_t* exth = A.ext + ((long long)h * A.nb + b) * A.ext_stride;
-  const int n_exth = A.dense ? 0 : A.n_ext[h * A.nb + b];
-
-  const uint16_t* kh_base = A.khi + (long long)g * D;
-  const uint16_t* kl_base = A.klo + (long long)g * D;
-  const uint16_t* v_base = A.v + (long long)g * D;
-  const long long kstride = (long long)A.h_kv * D;
-  const uint8_t* flag_base = A.kflag + (long long)g * A.n_k;
-
-  uint16_t* ql_w = sm.ql[wave];   // [kk][lane][8]: each lane reads back only its own slots
+  const int kstride = A.h_kv * D;
+  const uint16_t* kh_base = A.khi + g * D;
+  const uint16_t* kl_base = A.klo + g * D;
+  const uint16_t* v_base = A.v + g * D;
+  const uint32_t* kb = A.kbits + (long long)g * A.kbits_words;
+  const int grp = l32 >> 4;       // which 16-wide d slice of a 32-d block (transposed V reads)
+  const int s16 = lane & 15;
 
   f32x16 o[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) o[i] = f32x16{};
-  float m_run = -INFINITY;   // running max, log2 domain, shared by the two lanes of a row
+  float m_run = 0.f;         // reference max (log2 domain) of this row; scores enter the MFMA as s - m_run
+  bool started = false;      // the row has met a key
   float l_run = 0.f;         // this lane's partial row sum
-
   bf16x8 qh[8];
+  bf16x8 (*ql)[64] = qsm.ql[wave];
+  int q_mode = -1;
 
-  for (int seg = 0; seg < 3; ++seg) {
-    const int lo = max(seg_lo[seg], k_beg);
-    const int hi = min(seg_hi[seg], k_end);
-    if (lo >= hi) continue;
-    // ---- rotate the query fragment for this mode
-    {
-      const int r = prow % A.S;
-      double qpos;
-      if (seg == 2) qpos = r;
-      else if (seg == 1) qpos = min(A.S + r, A.S + A.W - 1);
-      else qpos = A.S + A.W - 1;
-      rotate_q(A, h, qrow, row_ok, half, qpos, qh, ql_w, lane);
+  // ---- tile metadata.  A range tile's descriptor is read by lanes 0..3 (one
+  // int each, a vector load) two tiles ahead; the slot key (lane & 31) and the
+  // high-norm flag of a tile are loaded one tile ahead, before the tile's
+  // direct-to-LDS loads are issued, so no wait on them stalls those loads.
+  auto desc_load = [&](int idx) -> int {   // per-lane part of the descriptor of tile idx
+    if (A.dense || idx >= n_range || idx >= t_end) return 0;
+    return tl_h[4 * (t_first + idx) + (lane & 3)];
+  };
+  auto make_tile = [&](int idx, int dv) -> Tile {
+    Tile T;
+    T.a2 = 0; T.len2 = 0; T.eoff = 0; T.cnt = 0;
+    if (idx < n_range) {
+      if (A.dense) {
+        T.a1 = BN * idx;
+        T.len1 = min(BN, hi_key - T.a1);
+      } else {
+        const int d0 = __builtin_amdgcn_readlane(dv, 0);
+        const int d1 = __builtin_amdgcn_readlane(dv, 1);
+        const int d2 = __builtin_amdgcn_readlane(dv, 2);
+        T.a1 = i0 + d0;
+        T.a2 = i0 + d1;
+        T.len1 = d2 & 0xFF;
+        T.len2 = (d2 >> 8) & 0xFF;
+      }
+    } else {
+      T.a1 = 0; T.len1 = 0;
+      T.eoff = BN * (idx - n_range);
+      T.cnt = min(BN, n_ext - T.eoff);
     }
-
-    // ---- enumerate the covered keys of [lo, hi): range keys, then extra verticals
-    // range cursor (sparse): interval index and current offset
-    int cur_k = 0, cur_o = 0;
-    if (!A.dense) {
-      const int olo = lo - i0;
-      // first interval with hi > olo (intervals ascending and disjoint)
-      int a = 0, z = n_ivh;
-      while (a < z) {
-        int mid = (a + z) >> 1;
-        if (ivh[2 * mid + 1] > olo) z = mid; else a = mid + 1;
-      }
-      cur_k = a;
-      cur_o = (cur_k < n_ivh) ? max(olo, ivh[2 * cur_k]) : 0;
+    return T;
+  };
+  // slot key of this lane (slot lane & 31): an extra-vertical entry (bit 30
+  // marks a high-norm key) or a range key; -1 for an empty slot
+  auto slot_key = [&](const Tile& T) -> int {
+    if (T.cnt) return (l32 < T.cnt) ? ext_h[T.eoff + l32] : -1;
+    const int key = range_key(T, l32);
+    return (key < 0 || key >= A.n_k) ? -1 : key;
+  };
+  // the bitmap word holding a range slot key's high-norm bit (read one tile ahead)
+  auto flag_word = [&](int key) -> uint32_t { return key >= 0 ? kb[key >> 5] : 0u; };
+  auto issue_tile = [&](uint8_t* stage, const Tile& T, int skey) {
+    // all row keys first, then the loads: no wait lands between two loads
+    int keys[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = 4 * (2 * j + wave) + (lane & 3);
+      int key = T.cnt ? (__shfl(skey, r) & 0x3FFFFFFF) : range_key(T, r);
+      keys[j] = min(max(key, 0), A.n_k - 1) * kstride + 8 * (lane >> 2);
     }
-    int dense_next = lo;
-    // extra verticals inside [lo, hi)
-    int e_beg = 0, e_end = 0;
-    if (!A.dense) {
-      int a = 0, z = n_exth;
-      while (a < z) { int mid = (a + z) >> 1; if (exth[mid] >= lo) z = mid; else a = mid + 1; }
-      e_beg = a;
-      z = n_exth;
-      while (a < z) { int mid = (a + z) >> 1; if (exth[mid] >= hi) z = mid; else a = mid + 1; }
-      e_end = a;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int grp4 = 2 * j + wave;
+      __builtin_amdgcn_global_load_lds((const void*)(kh_base + keys[j]),
+                                       (__attribute__((address_space(3))) void*)(stage + grp4 * GRPB), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(v_base + keys[j]),
+                                       (__attribute__((address_space(3))) void*)(stage + TILEB + grp4 * GRPB), 16,
+                                       0, 0);
     }
-    bool ranges_done = false;
-    int e_next = e_beg;
-    const int ohi = hi - i0;
+  };
 
-    while (true) {
-      // ---- build this tile's key list (every lane computes all 64 keys: lane l -> key l)
-      int key = -1;
-      int count = 0;
-      if (!ranges_done) {
-        if (A.dense) {
-          count = min(64, hi - dense_next);
-          if (count > 0) { key = (lane < count) ? dense_next + lane : -1; dense_next += count; }
-          if (dense_next >= hi) ranges_done = true;
-        } else {
-          if (cur_k < n_ivh && ivh[2 * cur_k] < ohi) {
-            const int end1 = min(ivh[2 * cur_k + 1], ohi);
-            const int run1 = min(64, end1 - cur_o);
-            int run2 = 0, o2 = 0;
-            int nk = cur_k, no = cur_o + run1;
-            if (no >= end1) {
-              nk = cur_k + 1;
-              if (nk < n_ivh && ivh[2 * nk] < ohi) {
-                o2 = ivh[2 * nk];
-                const int end2 = min(ivh[2 * nk + 1], ohi);
-                run2 = min(64 - run1, end2 - o2);
-                no = o2 + run2;
-                if (no >= end2) { nk = nk + 1; no = (nk < n_ivh) ? ivh[2 * nk] : 0; }
-              } else {
-                no = (nk < n_ivh) ? ivh[2 * nk] : 0;
-              }
-            }
-            count = run1 + run2;
-            if (lane < run1) key = i0 + cur_o + lane;
-            else if (lane < count) key = i0 + o2 + (lane - run1);
-            cur_k = nk;
-            cur_o = no;
-          }
-          if (count == 0) ranges_done = true;
-        }
-      }
-      if (count == 0) {
-        if (e_next >= e_end) break;
-        count = min(64, e_end - e_next);
-        key = (lane < count) ? exth[e_next + lane] : -1;
-        e_next += count;
-      }
-      if (count <= 0) break;
-      key = (key >= 0 && key < A.n_k) ? key : -1;
-      const bool precise = __any(key >= 0 && flag_base[key >= 0 ? key : 0] != 0);
-      const bool need_mask = (count < 64) || __any(key >= i0) || __any(key < 0);
+  auto compute_tile = [&](const uint8_t* kt, const uint8_t* vt, const Tile& T, int skey, uint32_t fword) {
+    const int count = tile_count(T);
+    const bool flagged = T.cnt ? (skey >= 0 && ((skey >> 30) & 1)) : (skey >= 0 && ((fword >> (skey & 31)) & 1u));
+    const bool precise = __any(flagged);
+    const int key_first = T.cnt ? (__builtin_amdgcn_readlane(skey, 0) & 0x3FFFFFFF) : T.a1;
+    const int key_last = T.cnt ? (__builtin_amdgcn_readlane(skey, count - 1) & 0x3FFFFFFF)
+                               : (T.len2 ? T.a2 + T.len2 - 1 : T.a1 + T.len1 - 1);
+    const int mode_first = key_first >= segB ? 2 : (key_first >= segA ? 1 : 0);
+    const int mode_last = key_last >= segB ? 2 : (key_last >= segA ? 1 : 0);
+    const bool edge = (count < BN) || (key_first < 0) || (key_last >= i0);
 
-      // ---- stage K (hi, and lo when precise) and V rows in LDS
-      __syncthreads();   // previous tile's LDS reads are done
-      if (wave == 0) sm.keys[lane] = key;
-      {
-        const int c16 = tid & 15;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int r = (tid >> 4) + 8 * i;
-          int kr = __shfl(key, r);
-          kr = kr < 0 ? 0 : kr;
-          const long long off = (long long)kr * kstride + 8 * c16;
-          uint4 kv = *(const uint4*)(kh_base + off);
-          uint4 vv = *(const uint4*)(v_base + off);
-          *(uint4*)&sm.k[r * KP + 8 * c16] = kv;
-          *(uint4*)&sm.v[r * VP + 8 * c16] = vv;
-          if (precise) {
-            uint4 kl = *(const uint4*)(kl_base + off);
-            *(uint4*)&sm.kl[r * KP + 8 * c16] = kl;
-          }
-        }
+    for (int mode = mode_first; mode <= mode_last; ++mode) {
+      // ---- query rotation for this DCA mode
+      if (mode != q_mode) {
+        const int r = prow % A.S;
+        double qpos;
+        if (mode == 2) qpos = r;
+        else if (mode == 1) qpos = min(A.S + r, A.S + A.W - 1);
+        else qpos = A.S + A.W - 1;
+        rotate_q(A, h, qrow, row_ok, half, qpos, qh, ql, lane);
+        q_mode = mode;
       }
-      __syncthreads();
-
-      // ---- S^T = K Q^T for the 64 keys x 32 rows of this wave
-      f32x16 s[2];
+      // ---- S^T - m = K Q^T - m: 32 keys x 32 rows of this wave, the running max preloaded
+      f32x16 s;
 #pragma unroll
-      for (int nbk = 0; nbk < 2; ++nbk) {
-        s[nbk] = f32x16{};
+      for (int vv = 0; vv < 16; ++vv) s[vv] = -m_run;
 #pragma unroll
-        for (int kk = 0; kk < 8; ++kk) {
-          const bf16x8 a = *(const bf16x8*)&sm.k[(32 * nbk + l32) * KP + 16 * kk + 8 * half];
-          s[nbk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qh[kk], s[nbk], 0, 0, 0);
-        }
+      for (int kk = 0; kk < 8; ++kk) {
+        const bf16x8 a = *(const bf16x8*)(kt + tile_off(l32, 2 * kk + half));
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qh[kk], s, 0, 0, 0);
       }
       if (precise) {
+        // + K_lo Q_hi + K_hi Q_lo; K_lo rows come straight from global memory
+        int kr = __shfl(skey, l32);
+        kr = (kr < 0) ? 0 : min(kr & 0x3FFFFFFF, A.n_k - 1);
+        const uint16_t* klrow = kl_base + kr * kstride;
 #pragma unroll
-        for (int nbk = 0; nbk < 2; ++nbk) {
-#pragma unroll
-          for (int kk = 0; kk < 8; ++kk) {
-            const bf16x8 ahi = *(const bf16x8*)&sm.k[(32 * nbk + l32) * KP + 16 * kk + 8 * half];
-            const bf16x8 alo = *(const bf16x8*)&sm.kl[(32 * nbk + l32) * KP + 16 * kk + 8 * half];
-            const bf16x8 qlo = *(const bf16x8*)&ql_w[(kk * 64 + lane) * 8];
-            s[nbk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, qh[kk], s[nbk], 0, 0, 0);
-            s[nbk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, qlo, s[nbk], 0, 0, 0);
-          }
+        for (int kk = 0; kk < 8; ++kk) {
+          const bf16x8 alo = *(const bf16x8*)(klrow + 16 * kk + 8 * half);
+          const bf16x8 ahi = *(const bf16x8*)(kt + tile_off(l32, 2 * kk + half));
+          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, qh[kk], s, 0, 0, 0);
+          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, ql[kk][lane], s, 0, 0, 0);
         }
       }
-
-      // ---- mask: absent keys and keys after the row's position
-      if (need_mask) {
+      // ---- masks: absent slots, keys outside [0, p_row], keys of another DCA mode
+      if (edge || mode_first != mode_last) {
 #pragma unroll
-        for (int nbk = 0; nbk < 2; ++nbk) {
-#pragma unroll
-          for (int vv = 0; vv < 16; ++vv) {
-            const int t = 32 * nbk + 8 * (vv >> 2) + 4 * half + (vv & 3);
-            const int kj = sm.keys[t];
-            if (kj < 0 || kj > prow || !row_ok) s[nbk][vv] = -INFINITY;
+        for (int vv = 0; vv < 16; ++vv) {
+          const int t = 8 * (vv >> 2) + 4 * half + (vv & 3);
+          int kj;
+          if (T.cnt) {
+            kj = __shfl(skey, t);
+            kj = kj < 0 ? -1 : (kj & 0x3FFFFFFF);
+          } else {
+            kj = range_key(T, t);
           }
+          const int km = kj >= segB ? 2 : (kj >= segA ? 1 : 0);
+          if (kj < 0 || kj > prow || km != mode) s[vv] = -INFINITY;
         }
       }
-
-      // ---- online softmax (log2 domain), lazy rescaling
-      float mx = -INFINITY;
+      // ---- online softmax (log2 domain).  The reference max moves only when a
+      // score exceeds it by more than 8 (so p <= 2^8), or at the row's first keys.
+      float mx = fmaxf(fmaxf(s[0], s[1]), s[2]);
 #pragma unroll
-      for (int nbk = 0; nbk < 2; ++nbk)
-#pragma unroll
-        for (int vv = 0; vv < 16; ++vv) mx = fmaxf(mx, s[nbk][vv]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const bool grow = mx > m_run + 8.f;
-      if (__any(grow)) {
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - m_new);
+      for (int vv = 3; vv < 15; vv += 2) mx = fmaxf(fmaxf(mx, s[vv]), s[vv + 1]);
+      mx = fmaxf(mx, s[15]);
+      mx = pair_max(mx);
+      const bool need = (mx > 8.f) || (!started && mx != -INFINITY);
+      if (__any(need)) {
+        const float delta = need ? mx : 0.f;
+        const float alpha = fast_exp2(-delta);
         l_run *= alpha;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int vv = 0; vv < 16; ++vv) o[i][vv] *= alpha;
-        m_run = m_new;
+#pragma unroll
+        for (int vv = 0; vv < 16; ++vv) s[vv] -= delta;
+        m_run += delta;
       }
-      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-      bf16x8 pf[4];
+      started = started || (mx != -INFINITY);
+      bf16x8 pf[2];
 #pragma unroll
-      for (int nbk = 0; nbk < 2; ++nbk) {
-#pragma unroll
-        for (int vv = 0; vv < 16; ++vv) {
-          const float p = fast_exp2(s[nbk][vv] - m_use);
-          l_run += p;
-          pf[2 * nbk + (vv >> 3)][vv & 7] = (__bf16)p;
-        }
+      for (int vv = 0; vv < 16; ++vv) {
+        const float p = fast_exp2(s[vv]);
+        l_run += p;
+        pf[vv >> 3][vv & 7] = (__bf16)p;
       }
-
-      // ---- O^T += V^T P^T: A operand read transposed from the row-major V tile
-      const int grp = l32 >> 4;       // which 16-wide d slice of the 32-d block
-      const int s16 = lane & 15;
+      // ---- O^T += V^T P^T, V^T operand read transposed from the row-major V tile
 #pragma unroll
-      for (int G = 0; G < 4; ++G) {
+      for (int G = 0; G < 2; ++G) {
         const int r1 = 16 * G + 4 * half + (s16 >> 2);
         const int r2 = r1 + 8;
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
-          const int col = 32 * db + 16 * grp + 4 * (s16 & 3);
-          const bf16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, &sm.v[r1 * VP + col]));
-          const bf16x4 t2 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, &sm.v[r2 * VP + col]));
+          const int c = 4 * db + 2 * grp + ((s16 & 3) >> 1);     // 16-byte chunk of the 4 columns read
+          const int bo = 8 * (s16 & 1);                           // byte offset inside the chunk
+          const bf16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, vt + tile_off(r1, c) + bo));
+          const bf16x4 t2 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, vt + tile_off(r2, c) + bo));
           const bf16x8 a = __builtin_shufflevector(t1, t2, 0, 1, 2, 3, 4, 5, 6, 7);
           o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[G], o[db], 0, 0, 0);
         }
       }
     }
+  };
+
+  // ---- prologue: tile t_beg staged, descriptor of t_beg+1 in flight
+  int dv_cur = desc_load(t_beg);
+  Tile T_cur = make_tile(t_beg, dv_cur);
+  int sk_cur = -1;
+  uint32_t fw_cur = 0;
+  if (t_beg < t_end) {
+    sk_cur = slot_key(T_cur);
+    fw_cur = T_cur.cnt ? 0u : flag_word(sk_cur);
+    issue_tile(stage0, T_cur, sk_cur);
+  }
+  int dv_nxt = desc_load(t_beg + 1);
+  __syncthreads();
+
+  // One step: prefetch tile ti+1 into the other stage, then compute tile ti.
+  // The other stage was last read before the previous barrier.  Range tiles
+  // issue their loads before any metadata read they would wait for; an
+  // extra-vertical tile needs its keys first (these tiles are few).
+  auto step = [&](const uint8_t* cur, uint8_t* nxt, int ti) {
+    Tile T_n;
+    int sk_n = -1;
+    uint32_t fw_n = 0;
+    const bool more = ti + 1 < t_end;
+    if (more) {
+      T_n = make_tile(ti + 1, dv_nxt);
+      if (T_n.cnt) {
+        sk_n = slot_key(T_n);
+        issue_tile(nxt, T_n, sk_n);
+      } else {
+        issue_tile(nxt, T_n, 0);
+        sk_n = slot_key(T_n);
+        fw_n = flag_word(sk_n);
+      }
+      dv_nxt = desc_load(ti + 2);
+    }
+    compute_tile(cur, cur + TILEB, T_cur, sk_cur, fw_cur);
+    __syncthreads();   // the prefetched stage has landed; this stage may be overwritten next
+    if (more) { T_cur = T_n; sk_cur = sk_n; fw_cur = fw_n; }
+  };
+  for (int ti = t_beg; ti < t_end; ti += 2) {
+    step(stage0, stage1, ti);
+    if (ti + 1 < t_end) step(stage1, stage0, ti + 1);
   }
 
   // ---- finish: row sum over both halves, normalise, write
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = pair_sum(l_run);
   const float inv_l = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const float lse2 = l_tot > 0.f ? m_run + __log2f(l_tot) : -INFINITY;
   const float lse = lse2 * 0.69314718055994531f;

@@ -4,18 +4,23 @@
 // the position of its offset inside its own chunk, so a key is rotated once and
 // the three query rotations carry the mode.  The rotated key is stored as a
 // bf16 pair (hi, lo) with hi + lo within 2^-16 relative of the fp32 rotation;
-// the attention kernel adds the lo half only for keys flagged as high-norm,
-// whose logits would otherwise carry bf16 rounding errors large enough to move
-// the output (sink keys, periodic high-norm keys).
+// the attention kernel adds the lo half only for tiles holding a key flagged as
+// high-norm (L2 norm above a threshold), whose logits would otherwise carry
+// bf16 rounding errors large enough to move the output (attention sinks).
 #include "common.h"
 
 namespace dca {
 
+__global__ void kbits_clear_kernel(uint32_t* __restrict__ kbits, long long n) {
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (long long)gridDim.x * blockDim.x)
+    kbits[i] = 0u;
+}
+
 // One 16-lane group per (key, kv head) row; lane c16 owns pairs 4*c16 .. 4*c16+3.
 __global__ void __launch_bounds__(256) rotate_keys_kernel(
     const uint16_t* __restrict__ k, uint16_t* __restrict__ khi, uint16_t* __restrict__ klo,
-    uint8_t* __restrict__ kflag, const double* __restrict__ inv_freq,
-    int n_k, int h_kv, int S, float thr2) {
+    uint32_t* __restrict__ kbits, const double* __restrict__ inv_freq,
+    int n_k, int h_kv, int S, float thr2, int kbits_words) {
   const int lane16 = threadIdx.x & 15;
   const long long row = (long long)blockIdx.x * 16 + (threadIdx.x >> 4);
   const long long n_rows = (long long)n_k * h_kv;
@@ -62,16 +67,19 @@ __global__ void __launch_bounds__(256) rotate_keys_kernel(
   *(uint2*)(khi + rrow * D + HALF + 4 * lane16) = ob;
   *(uint2*)(klo + rrow * D + 4 * lane16) = pa;
   *(uint2*)(klo + rrow * D + HALF + 4 * lane16) = pb;
-  if (lane16 == 0) kflag[(long long)g * n_k + j] = (thr2 >= 0.f && ss > thr2) ? 1 : 0;
+  // high-norm keys: one bit per key, OR-ed in (order-independent)
+  if (lane16 == 0 && thr2 >= 0.f && ss > thr2)
+    atomicOr(&kbits[(long long)g * kbits_words + (j >> 5)], 1u << (j & 31));
 }
 
-hipError_t launch_rotate_keys(const uint16_t* k, uint16_t* khi, uint16_t* klo, uint8_t* kflag,
-                              const double* inv_freq, int n_k, int h_kv, int S, float thr2,
+hipError_t launch_rotate_keys(const uint16_t* k, uint16_t* khi, uint16_t* klo, uint32_t* kbits,
+                              const double* inv_freq, int n_k, int h_kv, int S, float thr2, int kbits_words,
                               hipStream_t stream) {
   const long long rows = (long long)n_k * h_kv;
   const int blocks = (int)((rows + 15) / 16);
+  hipLaunchKernelGGL(kbits_clear_kernel, dim3(256), dim3(256), 0, stream, kbits, (long long)h_kv * kbits_words);
   hipLaunchKernelGGL(rotate_keys_kernel, dim3(blocks), dim3(256), 0, stream,
-                     k, khi, klo, kflag, inv_freq, n_k, h_kv, S, thr2);
+                     k, khi, klo, kbits, inv_freq, n_k, h_kv, S, thr2, kbits_words);
   return hipGetLastError();
 }
 

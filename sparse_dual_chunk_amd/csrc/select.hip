@@ -296,17 +296,21 @@ __global__ void plan_cov_kernel(PlanArgs A) {
 }
 
 // One wave per (head, query block): vertical columns inside the block's causal
-// extent that the block's ranges miss, ascending, duplicates dropped.
+// extent that the block's ranges miss, ascending, duplicates dropped; bit 30
+// of an entry marks a high-norm key.  Also the block's first range tile (the
+// one holding its lowest in-range offset) and its cover size.
 __global__ void __launch_bounds__(256) plan_ext_kernel(PlanArgs A) {
   const int unit = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (unit >= A.h_q * A.nb) return;
   const int h = unit / A.nb;
   const int b = unit % A.nb;
+  const int g = h / (A.h_q / A.h_kv);
   const int i0 = A.p0 + 64 * b;
   const int hi_key = i0 + min(64, A.n_q - 64 * b);
   const int32_t* vi = A.v_idx + (long long)h * A.k_v;
   const uint32_t* cv = A.cov + (long long)h * A.cov_words;
+  const uint32_t* kb = A.kbits + (long long)g * A.kbits_words;
   int32_t* dst = A.ext + ((long long)h * A.nb + b) * A.ext_stride;
   int cnt = 0;
   for (int base = 0; base < A.k_v; base += 64) {
@@ -324,32 +328,62 @@ __global__ void __launch_bounds__(256) plan_ext_kernel(PlanArgs A) {
     const unsigned long long bal = __ballot(keep);
     if (keep) {
       const int pos = __popcll(bal & ((1ull << lane) - 1ull));
-      dst[cnt + pos] = j;
+      const int flagged = (kb[j >> 5] >> (j & 31)) & 1u;
+      dst[cnt + pos] = j | (flagged << 30);
     }
     cnt += __popcll(bal);
   }
   if (lane == 0) {
     A.n_ext[unit] = cnt;
+    // covered offsets below x: prefix of whole intervals plus the part of the one holding x
+    const int32_t* ivh = A.iv + (long long)h * A.iv_stride * 2;
+    const int32_t* pre = A.iv_pre + (long long)h * (A.iv_stride + 1);
+    const int n_iv = A.n_iv[h];
+    const int rows = hi_key - i0;
+    long long below[2];
+    const int xs[2] = {-i0, rows};
+    for (int t = 0; t < 2; ++t) {
+      const int x = xs[t];
+      int a = 0, z = n_iv;
+      while (a < z) { const int mid = (a + z) >> 1; if (ivh[2 * mid + 1] > x) z = mid; else a = mid + 1; }
+      long long c = pre[a];
+      if (a < n_iv && x > ivh[2 * a]) c += x - ivh[2 * a];
+      below[t] = c;
+    }
+    A.t_first[unit] = (int)(below[0] / 32);
     if (A.cover_pairs) {
-      // covered offsets below x: prefix of whole intervals plus the part of the one holding x
-      const int32_t* ivh = A.iv + (long long)h * A.iv_stride * 2;
-      const int32_t* pre = A.iv_pre + (long long)h * (A.iv_stride + 1);
-      const int n_iv = A.n_iv[h];
-      const int rows = hi_key - i0;
-      long long below[2];
-      const int xs[2] = {-i0, rows};
-      for (int t = 0; t < 2; ++t) {
-        const int x = xs[t];
-        int a = 0, z = n_iv;
-        while (a < z) { const int mid = (a + z) >> 1; if (ivh[2 * mid + 1] > x) z = mid; else a = mid + 1; }
-        long long c = pre[a];
-        if (a < n_iv && x > ivh[2 * a]) c += x - ivh[2 * a];
-        below[t] = c;
-      }
       const long long cover = (below[1] - below[0]) + cnt;
       atomicAdd((unsigned long long*)A.cover_pairs, (unsigned long long)(cover * rows));
     }
   }
+}
+
+// Range tiles of one head in offset space: tile t holds covered offsets of
+// ranks [32t, 32t+32) of the merged intervals, as at most two runs (every
+// interval is at least 64 long).  One thread per tile.
+__global__ void __launch_bounds__(256) plan_tiles_kernel(PlanArgs A) {
+  const int h = blockIdx.y;
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  const int n_iv = A.n_iv[h];
+  const int32_t* ivh = A.iv + (long long)h * A.iv_stride * 2;
+  const int32_t* pre = A.iv_pre + (long long)h * (A.iv_stride + 1);
+  const int total = pre[n_iv];
+  const int n_t = (total + 31) / 32;
+  if (t == 0) A.n_tiles[h] = n_t;
+  if (t >= n_t) return;
+  const int r0 = 32 * t;
+  int a = 0, z = n_iv;   // last interval with pre <= r0
+  while (z - a > 1) { const int mid = (a + z) >> 1; if (pre[mid] <= r0) a = mid; else z = mid; }
+  const int len_a = ivh[2 * a + 1] - ivh[2 * a];
+  const int off = r0 - pre[a];
+  const int want = min(32, total - r0);
+  const int len1 = min(want, len_a - off);
+  int o2 = 0, len2 = 0;
+  if (len1 < want && a + 1 < n_iv) {
+    o2 = ivh[2 * (a + 1)];
+    len2 = min(want - len1, ivh[2 * (a + 1) + 1] - o2);
+  }
+  A.tiles[(long long)h * A.tile_stride + t] = make_int4(ivh[2 * a] + off, o2, len1 | (len2 << 8), 0);
 }
 
 hipError_t launch_plan(const PlanArgs& A, hipStream_t stream) {
@@ -359,6 +393,7 @@ hipError_t launch_plan(const PlanArgs& A, hipStream_t stream) {
   hipLaunchKernelGGL(plan_cov_kernel, dim3(ivb, A.h_q), dim3(256), 0, stream, A);
   const int units = A.h_q * A.nb;
   hipLaunchKernelGGL(plan_ext_kernel, dim3((units + 3) / 4), dim3(256), 0, stream, A);
+  hipLaunchKernelGGL(plan_tiles_kernel, dim3((A.tile_stride + 255) / 256, A.h_q), dim3(256), 0, stream, A);
   return hipGetLastError();
 }
 

@@ -114,8 +114,12 @@ def test_sparse_all_offsets_equals_dense():
     out_sp, _ = run_prefill(inp, cfg, v_idx=v_idx, s_off=s_off)
     cfg_d = _cfg(inp, 2, 1, 128, 32)
     out_d, _ = run_prefill(inp, cfg_d)
-    check_close(out_sp, _oracle(inp, cfg_d)[0], "all offsets")
-    assert np.array_equal(out_sp, out_d)
+    ref = _oracle(inp, cfg_d)[0]
+    check_close(out_sp, ref, "all offsets")
+    check_close(out_d, ref, "dense")
+    # same key sets, different tile grouping (sparse tiles follow the merged
+    # ranges): the two may differ only by rounding
+    assert np.abs(bf16_f64(out_sp) - bf16_f64(out_d)).max() <= 2e-2
 
 
 def test_sparse_vertical_only():
