@@ -41,7 +41,7 @@ struct Layout {
   // shared
   Region freqs;
   // prefill
-  Region khi, klo, kbits, iv, iv_pre, n_iv, cov, ext, n_ext, tiles, n_tiles, t_first, part_o, part_lse;
+  Region khi, klo, kbits, iv, iv_pre, n_iv, cov, ext, n_ext, tiles, n_tiles, t_first, qlo, part_o, part_lse;
   // index
   Region qs, part_ms, lse, vert, slash, edge, hist, prefix, krem, bcount;
   size_t prefill_bytes = 0, index_bytes = 0;
@@ -70,6 +70,8 @@ int validate(const dca_cfg* c, const int32_t* positions) {
   if (p0 % 64 != 0) return DCA_EUNSUPPORTED;
   // int32 key and offset arithmetic inside the kernels
   if ((long long)c->n_k + 2LL * c->dca_chunk + 128 > (1LL << 30)) return DCA_EUNSUPPORTED;
+  // K / V rows of one KV head are addressed by 32-bit byte offsets
+  if ((long long)c->n_k * c->h_kv * c->head_dim * 2 >= (1LL << 32)) return DCA_EUNSUPPORTED;
   if (positions) {
     for (int i = 0; i < c->n_q; ++i)
       if ((long long)positions[i] != p0 + i) return DCA_EINVAL;
@@ -112,6 +114,8 @@ Layout make_layout(const dca_cfg* c) {
   place(L.tiles, cur, (size_t)h_q * L.tile_stride * 16);
   place(L.n_tiles, cur, (size_t)h_q * 4);
   place(L.t_first, cur, (size_t)h_q * L.nb * 4);
+  // one 16 KiB slot of query lo fragments per attention workgroup (grid as launched)
+  place(L.qlo, cur, (size_t)8 * ((L.nb + 7) / 8) * h_q * L.split * 2 * 8 * 64 * 16);
   if (L.split > 1) {
     place(L.part_o, cur, (size_t)L.split * n_q * h_q * D * 4);
     place(L.part_lse, cur, (size_t)L.split * h_q * n_q * 4);
@@ -287,6 +291,7 @@ int dca_sparse_prefill(const dca_bf16* q, const dca_bf16* k, const dca_bf16* v, 
   A.part_lse = L.split > 1 ? at<float>(cfg, L.part_lse) : nullptr;
   A.tiles = at<int4>(cfg, L.tiles); A.n_tiles = at<int32_t>(cfg, L.n_tiles); A.t_first = at<int32_t>(cfg, L.t_first);
   A.ext = at<int32_t>(cfg, L.ext); A.n_ext = at<int32_t>(cfg, L.n_ext);
+  A.qlo = at<uint4>(cfg, L.qlo);
   A.n_q = n_q; A.n_k = n_k; A.h_q = h_q; A.h_kv = h_kv; A.p0 = p0; A.S = cfg->dca_chunk; A.W = cfg->dca_local;
   A.nb = L.nb; A.tile_stride = L.tile_stride; A.kbits_words = L.kbits_words;
   A.ext_stride = cfg->vs_k_vertical > 0 ? cfg->vs_k_vertical : 1;

@@ -21,6 +21,7 @@ struct AttnArgs {
   const int32_t* t_first;   // [h_q][nb] first range tile of each query block
   const int32_t* ext;       // [h_q][nb][ext_stride] vertical keys outside the ranges (bit 30: high-norm)
   const int32_t* n_ext;     // [h_q][nb]
+  uint4* qlo;               // [workgroups][2 waves][8][64 lanes] query lo fragments (16 B each)
   int n_q, n_k, h_q, h_kv, p0, S, W, nb, tile_stride, ext_stride, split, dense, kbits_words;
   float qscale;             // softmax scale * log2(e), folded into the query rotation
 };

@@ -33,10 +33,6 @@ constexpr int GRPB = 1024 + 64;                // bytes per 4-row group
 constexpr int TILEB = 8 * GRPB;                // one tensor of one tile
 constexpr int STAGEB = 2 * TILEB;              // K then V
 
-struct __align__(16) AttnQlo {
-  bf16x8 ql[2][8][64];       // per wave: query lo fragments [kk][lane] (used by high-norm tiles only)
-};
-
 // byte offset of (row, 16-byte chunk) inside a tensor tile
 __device__ __forceinline__ int tile_off(int row, int chunk) { return (row >> 2) * GRPB + chunk * 64 + (row & 3) * 16; }
 
@@ -58,7 +54,7 @@ __device__ __forceinline__ float pair_sum(float x) {
 // split into bf16 hi and lo halves.  Angles are reduced in fp64 to a fraction
 // of a turn and evaluated with the hardware sine / cosine of that fraction.
 __device__ __forceinline__ void rotate_q(const AttnArgs& A, int h, int row, bool row_ok, int half,
-                                         double qpos, bf16x8 (&qh)[8], bf16x8 (*ql)[64], int lane) {
+                                         double qpos, bf16x8 (&qh)[8], uint4* ql, int lane) {
   const uint16_t* src = A.q + ((long long)row * A.h_q + h) * D;
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
@@ -87,8 +83,8 @@ __device__ __forceinline__ void rotate_q(const AttnArgs& A, int h, int row, bool
       la[e] = (__bf16)(xr - (float)ha);
       lb[e] = (__bf16)(yr - (float)hb);
     }
-    ql[kk][lane] = la;
-    ql[kk + 4][lane] = lb;
+    ql[kk * 64 + lane] = __builtin_bit_cast(uint4, la);
+    ql[(kk + 4) * 64 + lane] = __builtin_bit_cast(uint4, lb);
   }
 }
 
@@ -110,10 +106,9 @@ __device__ __forceinline__ int range_key(const Tile& T, int t) {
 __global__ void __launch_bounds__(128, 2) dca_attn_kernel(AttnArgs A) {
   __shared__ __align__(16) uint8_t stage0[STAGEB];
   __shared__ __align__(16) uint8_t stage1[STAGEB];
-  __shared__ AttnQlo qsm;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: LDS bases stay scalar
   const int half = lane >> 5;
   const int l32 = lane & 31;
 
@@ -166,11 +161,13 @@ __global__ void __launch_bounds__(128, 2) dca_attn_kernel(AttnArgs A) {
   f32x16 o[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) o[i] = f32x16{};
-  float m_run = 0.f;         // reference max (log2 domain) of this row; scores enter the MFMA as s - m_run
+  float m_run = 0.f;         // reference max (log2 domain) of this row
   bool started = false;      // the row has met a key
   float l_run = 0.f;         // this lane's partial row sum
   bf16x8 qh[8];
-  bf16x8 (*ql)[64] = qsm.ql[wave];
+  // query lo fragments go to this workgroup's scratch slot: only high-norm
+  // tiles read them back (each lane its own 16-byte entries)
+  uint4* ql = A.qlo + ((long long)blockIdx.x * 2 + wave) * 8 * 64;
   int q_mode = -1;
 
   // ---- tile metadata.  A range tile's descriptor is read by lanes 0..3 (one
@@ -213,23 +210,31 @@ __global__ void __launch_bounds__(128, 2) dca_attn_kernel(AttnArgs A) {
   };
   // the bitmap word holding a range slot key's high-norm bit (read one tile ahead)
   auto flag_word = [&](int key) -> uint32_t { return key >= 0 ? kb[key >> 5] : 0u; };
+  // K and V rows of this KV head through buffer resources: one 32-bit byte
+  // offset per row serves both tensors (the host bounds n_k * h_kv * 256 < 2^32)
+  const __amdgpu_buffer_rsrc_t rs_k = __builtin_amdgcn_make_buffer_rsrc((void*)kh_base, (short)0, -1, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rs_v = __builtin_amdgcn_make_buffer_rsrc((void*)v_base, (short)0, -1, 0x00020000);
+  const int rowb = kstride * 2;
   auto issue_tile = [&](uint8_t* stage, const Tile& T, int skey) {
-    // all row keys first, then the loads: no wait lands between two loads
-    int keys[4];
+    // all row offsets first, then the loads: no wait lands between two loads
+    int voff[4];
+    const int choff = 16 * (lane >> 2);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int r = 4 * (2 * j + wave) + (lane & 3);
-      int key = T.cnt ? (__shfl(skey, r) & 0x3FFFFFFF) : range_key(T, r);
-      keys[j] = min(max(key, 0), A.n_k - 1) * kstride + 8 * (lane >> 2);
+      int key;
+      if (T.cnt) key = __shfl(skey, r) & 0x3FFFFFFF;
+      else key = (r < T.len1 ? T.a1 : T.a2 - T.len1) + r;   // slots past the count are masked later
+      key = min(max(key, 0), A.n_k - 1);
+      voff[j] = __umul24((unsigned)key, (unsigned)rowb) + choff;
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int grp4 = 2 * j + wave;
-      __builtin_amdgcn_global_load_lds((const void*)(kh_base + keys[j]),
-                                       (__attribute__((address_space(3))) void*)(stage + grp4 * GRPB), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(v_base + keys[j]),
-                                       (__attribute__((address_space(3))) void*)(stage + TILEB + grp4 * GRPB), 16,
-                                       0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_k, (__attribute__((address_space(3))) void*)(stage + grp4 * GRPB),
+                                               16, voff[j], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs_v, (__attribute__((address_space(3))) void*)(stage + TILEB + grp4 * GRPB), 16, voff[j], 0, 0, 0);
     }
   };
 
@@ -255,12 +260,11 @@ __global__ void __launch_bounds__(128, 2) dca_attn_kernel(AttnArgs A) {
         rotate_q(A, h, qrow, row_ok, half, qpos, qh, ql, lane);
         q_mode = mode;
       }
-      // ---- S^T - m = K Q^T - m: 32 keys x 32 rows of this wave, the running max preloaded
-      f32x16 s;
+      // ---- S^T = K Q^T: 32 keys x 32 rows of this wave (scores in log2 units)
+      f32x16 s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(kt + tile_off(l32, half)), qh[0],
+                                                         f32x16{}, 0, 0, 0);
 #pragma unroll
-      for (int vv = 0; vv < 16; ++vv) s[vv] = -m_run;
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
+      for (int kk = 1; kk < 8; ++kk) {
         const bf16x8 a = *(const bf16x8*)(kt + tile_off(l32, 2 * kk + half));
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qh[kk], s, 0, 0, 0);
       }
@@ -274,7 +278,8 @@ __global__ void __launch_bounds__(128, 2) dca_attn_kernel(AttnArgs A) {
           const bf16x8 alo = *(const bf16x8*)(klrow + 16 * kk + 8 * half);
           const bf16x8 ahi = *(const bf16x8*)(kt + tile_off(l32, 2 * kk + half));
           s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, qh[kk], s, 0, 0, 0);
-          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, ql[kk][lane], s, 0, 0, 0);
+          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, __builtin_bit_cast(bf16x8, ql[kk * 64 + lane]), s, 0, 0,
+                                                      0);
         }
       }
       // ---- masks: absent slots, keys outside [0, p_row], keys of another DCA mode
@@ -300,24 +305,22 @@ __global__ void __launch_bounds__(128, 2) dca_attn_kernel(AttnArgs A) {
       for (int vv = 3; vv < 15; vv += 2) mx = fmaxf(fmaxf(mx, s[vv]), s[vv + 1]);
       mx = fmaxf(mx, s[15]);
       mx = pair_max(mx);
-      const bool need = (mx > 8.f) || (!started && mx != -INFINITY);
+      const bool need = (mx > m_run + 8.f) || (!started && mx != -INFINITY);
       if (__any(need)) {
-        const float delta = need ? mx : 0.f;
-        const float alpha = fast_exp2(-delta);
+        const float m_new = need ? mx : m_run;
+        const float alpha = started ? fast_exp2(m_run - m_new) : 0.f;
         l_run *= alpha;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int vv = 0; vv < 16; ++vv) o[i][vv] *= alpha;
-#pragma unroll
-        for (int vv = 0; vv < 16; ++vv) s[vv] -= delta;
-        m_run += delta;
+        m_run = m_new;
       }
       started = started || (mx != -INFINITY);
       bf16x8 pf[2];
 #pragma unroll
       for (int vv = 0; vv < 16; ++vv) {
-        const float p = fast_exp2(s[vv]);
+        const float p = fast_exp2(s[vv] - m_run);
         l_run += p;
         pf[vv >> 3][vv & 7] = (__bf16)p;
       }
