@@ -137,7 +137,24 @@ def main() -> int:
     ap.add_argument("--workload", default=W.C5_7B_1M.name, choices=sorted(W.WORKLOADS))
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--split-k", type=int, default=0,
+                    help="key-range split of each (block, head) unit (0: the library's heuristic)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device-to-device copy of BYTES bytes (3 launches), "
+                         "the reference for scaling the HBM byte counters")
     args = ap.parse_args()
+
+    if args.copy_calibration:
+        import torch
+        n = args.copy_calibration
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
+        return 0
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (the path is measured on one MI355X; --gpus {args.gpus} "
@@ -153,7 +170,7 @@ def main() -> int:
     calls = []
     for c in range(len(w.chunks)):
         inp = W.make(w, c, seed=args.seed, kv=kv)
-        cfg = S.config_for(w, c)
+        cfg = S.config_for(w, c, **({"split_k": args.split_k} if args.split_k else {}))
         calls.append((inp, cfg))
     log("uploading to HBM")
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()

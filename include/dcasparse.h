@@ -68,7 +68,7 @@ extern "C" {
 typedef uint16_t dca_bf16;     /* raw bfloat16 bits */
 
 /* Number of optional timing events dca_sparse_prefill records (see stage_events). */
-#define DCA_STAGE_COUNT 4      /* 0: key rotation, 1: sparse plan, 2: attention, 3: LSE merge */
+#define DCA_STAGE_COUNT 4      /* 0: key and query rotations, 1: sparse plan, 2: attention, 3: LSE merge */
 
 typedef struct dca_cfg {
   int32_t n_q;            /* query rows in this call (>= 1) */

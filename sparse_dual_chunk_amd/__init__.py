@@ -30,7 +30,7 @@ DCA_EUNSUPPORTED = -2
 DCA_EWORKSPACE = -3
 DCA_EHIP = -4
 DCA_STAGE_COUNT = 4
-STAGES = ("rotate_keys", "plan", "attention", "lse_merge")
+STAGES = ("rotate", "plan", "attention", "lse_merge")
 
 
 class dca_cfg(ctypes.Structure):

@@ -13,6 +13,8 @@ namespace dca {
 hipError_t launch_rotate_keys(const uint16_t* k, uint16_t* khi, uint16_t* klo, uint32_t* kbits,
                               const double* inv_freq, int n_k, int h_kv, int S, float thr2, int kbits_words,
                               hipStream_t stream);
+hipError_t launch_rotate_queries(const uint16_t* q, uint16_t* qhi, uint16_t* qlo, const double* inv_freq,
+                                 int n_q, int h_q, int p0, int S, int W, float qscale, hipStream_t stream);
 hipError_t launch_attn(const AttnArgs& A, hipStream_t stream);
 hipError_t launch_lse_merge(const float* part_o, const float* part_lse, uint16_t* out, float* lse_out,
                             int P, int n_q, int h_q, hipStream_t stream);
@@ -41,7 +43,7 @@ struct Layout {
   // shared
   Region freqs;
   // prefill
-  Region khi, klo, kbits, iv, iv_pre, n_iv, cov, ext, n_ext, tiles, n_tiles, t_first, qlo, part_o, part_lse;
+  Region khi, klo, kbits, qhi, qlo, iv, iv_pre, n_iv, cov, ext, n_ext, tiles, n_tiles, t_first, part_o, part_lse;
   // index
   Region qs, part_ms, lse, vert, slash, edge, hist, prefix, krem, bcount;
   size_t prefill_bytes = 0, index_bytes = 0;
@@ -88,9 +90,15 @@ Layout make_layout(const dca_cfg* c) {
   if (c->split_k > 0) {
     L.split = c->split_k;
   } else {
-    // enough independent work items to fill 256 compute units several times over
+    // enough independent work items to fill 256 compute units several times
+    // over, and key shares of about 32K keys: the attention workgroups run
+    // split part by split part, so the keys read by the work in flight stay
+    // within one share (32K keys of K and V per KV head: 16 MiB) and are
+    // served from the dies' caches instead of memory
     L.split = 1;
     while (units * L.split < 2048 && L.split < 16) L.split *= 2;
+    const int by_keys = (int)std::min<long long>(32, ((long long)n_k + 32767) / 32768);
+    L.split = std::max(L.split, by_keys);
     const int tiles = (n_k + 63) / 64;
     while (L.split > 1 && L.split > tiles) L.split /= 2;
   }
@@ -102,6 +110,8 @@ Layout make_layout(const dca_cfg* c) {
   place(L.klo, cur, (size_t)n_k * h_kv * D * 2);
   L.kbits_words = (n_k + 31) / 32 + 1;
   place(L.kbits, cur, (size_t)h_kv * L.kbits_words * 4);
+  place(L.qhi, cur, (size_t)3 * n_q * h_q * D * 2);
+  place(L.qlo, cur, (size_t)3 * n_q * h_q * D * 2);
   place(L.iv, cur, (size_t)h_q * (c->vs_k_slash + 1) * 2 * 4);
   place(L.iv_pre, cur, (size_t)h_q * (c->vs_k_slash + 2) * 4);
   place(L.n_iv, cur, (size_t)h_q * 4);
@@ -114,8 +124,6 @@ Layout make_layout(const dca_cfg* c) {
   place(L.tiles, cur, (size_t)h_q * L.tile_stride * 16);
   place(L.n_tiles, cur, (size_t)h_q * 4);
   place(L.t_first, cur, (size_t)h_q * L.nb * 4);
-  // one 16 KiB slot of query lo fragments per attention workgroup (grid as launched)
-  place(L.qlo, cur, (size_t)8 * ((L.nb + 7) / 8) * h_q * L.split * 2 * 8 * 64 * 16);
   if (L.split > 1) {
     place(L.part_o, cur, (size_t)L.split * n_q * h_q * D * 4);
     place(L.part_lse, cur, (size_t)L.split * h_q * n_q * 4);
@@ -247,12 +255,17 @@ int dca_sparse_prefill(const dca_bf16* q, const dca_bf16* k, const dca_bf16* v, 
 
   hipLaunchKernelGGL(write_freqs_kernel, dim3(1), dim3(HALF), 0, st, make_freqs(cfg->rope_base),
                      at<double>(cfg, L.freqs));
-  // stage 0: chunk-local key rotation
+  // stage 0: chunk-local key rotation, query rotations of the three DCA modes
   record(cfg, 0, 0);
   float thr = cfg->precise_norm == 0.f ? 2.f * std::sqrt((float)D) : cfg->precise_norm;
   const float thr2 = thr < 0.f ? -1.f : thr * thr;
   if (launch_rotate_keys(k, at<uint16_t>(cfg, L.khi), at<uint16_t>(cfg, L.klo), at<uint32_t>(cfg, L.kbits),
                          at<double>(cfg, L.freqs), n_k, h_kv, cfg->dca_chunk, thr2, L.kbits_words, st) != hipSuccess)
+    return DCA_EHIP;
+  // softmax scale sqrt(1/t)^2 / sqrt(d) and log2(e) (the kernel works in base 2)
+  const float qscale = (float)(yarn_factor(cfg->yarn_s) / std::sqrt((double)D) * 1.4426950408889634);
+  if (launch_rotate_queries(q, at<uint16_t>(cfg, L.qhi), at<uint16_t>(cfg, L.qlo), at<double>(cfg, L.freqs), n_q,
+                            h_q, p0, cfg->dca_chunk, cfg->dca_local, qscale, st) != hipSuccess)
     return DCA_EHIP;
   record(cfg, 0, 1);
   // stage 1: sparse plan
@@ -284,19 +297,18 @@ int dca_sparse_prefill(const dca_bf16* q, const dca_bf16* k, const dca_bf16* v, 
   // stage 2: attention
   record(cfg, 2, 0);
   AttnArgs A;
-  A.q = q; A.khi = at<uint16_t>(cfg, L.khi); A.klo = at<uint16_t>(cfg, L.klo); A.v = v;
-  A.kbits = at<uint32_t>(cfg, L.kbits); A.inv_freq = at<double>(cfg, L.freqs);
+  A.qhi = at<uint16_t>(cfg, L.qhi); A.qlo = at<uint16_t>(cfg, L.qlo);
+  A.khi = at<uint16_t>(cfg, L.khi); A.klo = at<uint16_t>(cfg, L.klo); A.v = v;
+  A.kbits = at<uint32_t>(cfg, L.kbits);
   A.out = out; A.lse_out = cfg->lse_out;
   A.part_o = L.split > 1 ? at<float>(cfg, L.part_o) : nullptr;
   A.part_lse = L.split > 1 ? at<float>(cfg, L.part_lse) : nullptr;
   A.tiles = at<int4>(cfg, L.tiles); A.n_tiles = at<int32_t>(cfg, L.n_tiles); A.t_first = at<int32_t>(cfg, L.t_first);
   A.ext = at<int32_t>(cfg, L.ext); A.n_ext = at<int32_t>(cfg, L.n_ext);
-  A.qlo = at<uint4>(cfg, L.qlo);
   A.n_q = n_q; A.n_k = n_k; A.h_q = h_q; A.h_kv = h_kv; A.p0 = p0; A.S = cfg->dca_chunk; A.W = cfg->dca_local;
   A.nb = L.nb; A.tile_stride = L.tile_stride; A.kbits_words = L.kbits_words;
   A.ext_stride = cfg->vs_k_vertical > 0 ? cfg->vs_k_vertical : 1;
   A.split = L.split; A.dense = sparse ? 0 : 1;
-  A.qscale = (float)(yarn_factor(cfg->yarn_s) / std::sqrt((double)D) * 1.4426950408889634);
   if (launch_attn(A, st) != hipSuccess) return DCA_EHIP;
   record(cfg, 2, 1);
   // stage 3: LSE merge of the split partials

@@ -6,12 +6,12 @@
 namespace dca {
 
 struct AttnArgs {
-  const uint16_t* q;        // [n_q][h_q][128] raw
+  const uint16_t* qhi;      // [3 modes][n_q][h_q][128] rotated query * scale * log2(e), bf16 hi
+  const uint16_t* qlo;      // same, lo residual
   const uint16_t* khi;      // [n_k][h_kv][128] rotated, bf16 hi
   const uint16_t* klo;      // same, lo residual
   const uint16_t* v;        // [n_k][h_kv][128]
   const uint32_t* kbits;    // [h_kv][kbits_words] bit j: key j is high-norm (split-precision logits)
-  const double* inv_freq;   // [64]
   uint16_t* out;            // [n_q][h_q][128]
   float* lse_out;           // [h_q][n_q] or null
   float* part_o;            // [P][n_q][h_q][128] (P > 1)
@@ -21,9 +21,7 @@ struct AttnArgs {
   const int32_t* t_first;   // [h_q][nb] first range tile of each query block
   const int32_t* ext;       // [h_q][nb][ext_stride] vertical keys outside the ranges (bit 30: high-norm)
   const int32_t* n_ext;     // [h_q][nb]
-  uint4* qlo;               // [workgroups][2 waves][8][64 lanes] query lo fragments (16 B each)
   int n_q, n_k, h_q, h_kv, p0, S, W, nb, tile_stride, ext_stride, split, dense, kbits_words;
-  float qscale;             // softmax scale * log2(e), folded into the query rotation
 };
 
 struct VsArgs {

@@ -48,46 +48,6 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Rotate this lane's query fragment for one DCA mode.  Lane (row = l%32,
-// half = l/32) holds dims {16kk + 8half + e}: pairs (c, c+64) sit in slots kk
-// and kk+4 of the same lane.  The rotated value times the softmax scale is
-// split into bf16 hi and lo halves.  Angles are reduced in fp64 to a fraction
-// of a turn and evaluated with the hardware sine / cosine of that fraction.
-__device__ __forceinline__ void rotate_q(const AttnArgs& A, int h, int row, bool row_ok, int half,
-                                         double qpos, bf16x8 (&qh)[8], uint4* ql, int lane) {
-  const uint16_t* src = A.q + ((long long)row * A.h_q + h) * D;
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
-    bf16x8 la, lb;
-    uint4 ra = make_uint4(0, 0, 0, 0), rb = make_uint4(0, 0, 0, 0);
-    if (row_ok) {
-      ra = *(const uint4*)(src + 16 * kk + 8 * half);
-      rb = *(const uint4*)(src + 16 * (kk + 4) + 8 * half);
-    }
-    const uint16_t* xa = (const uint16_t*)&ra;
-    const uint16_t* xb = (const uint16_t*)&rb;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int c = 16 * kk + 8 * half + e;
-      const double turns = qpos * A.inv_freq[c] * INV_TWO_PI;
-      const float f = (float)(turns - rint(turns));
-      const float sn = __builtin_amdgcn_sinf(f);
-      const float cs = __builtin_amdgcn_cosf(f);
-      const float x = bf16_bits_to_f32(xa[e]);
-      const float y = bf16_bits_to_f32(xb[e]);
-      const float xr = (x * cs - y * sn) * A.qscale;
-      const float yr = (x * sn + y * cs) * A.qscale;
-      const __bf16 ha = (__bf16)xr, hb = (__bf16)yr;
-      qh[kk][e] = ha;
-      qh[kk + 4][e] = hb;
-      la[e] = (__bf16)(xr - (float)ha);
-      lb[e] = (__bf16)(yr - (float)hb);
-    }
-    ql[kk * 64 + lane] = __builtin_bit_cast(uint4, la);
-    ql[(kk + 4) * 64 + lane] = __builtin_bit_cast(uint4, lb);
-  }
-}
-
 // One tile of the walk, wave-uniform: range tiles hold two runs of keys
 // [a1, a1+len1) ++ [a2, a2+len2) (absolute; a1 < 0 possible in the first tile
 // of a block); extra tiles (cnt > 0) hold entries [eoff, eoff+cnt) of the
@@ -113,19 +73,35 @@ __global__ void __launch_bounds__(128, 2) dca_attn_kernel(AttnArgs A) {
   const int l32 = lane & 31;
 
   // ---- work item.  Workgroups reach the dies round-robin (j -> die j % 8) and
-  // each die starts its share in order, so die x is given query-block rows
-  // x, x+8, ... in descending block order (heavy first, dies balanced), and
-  // all heads (and split parts) of one block row back to back: the 7 or 5 query
-  // heads of a KV group then stream the same keys through that die's L2.
-  const int C = A.h_q * A.split;
+  // each die starts its share in order.  Split parts are outermost in every
+  // die's sequence, so the workgroups in flight all read the same share of
+  // their key ranges.  Where the KV groups divide the dies evenly, a die serves
+  // one KV group per part (the group advancing with the part, which evens out
+  // the per-group work) so that all its workgroups read the same keys through
+  // its L2; otherwise it serves all heads of its query-block rows.  Blocks are
+  // taken in descending order (the longest causal extents first).
   const int die = blockIdx.x % NXCD;
   const int local = blockIdx.x / NXCD;
-  const int cidx = NXCD * (local / C) + die;
-  if (cidx >= A.nb) return;
-  const int w = local % C;
-  const int b = A.nb - 1 - cidx;
-  const int h = w / A.split;
-  const int part = w % A.split;
+  const int hpg = A.h_q / A.h_kv;
+  int b, h, part;
+  if (NXCD % A.h_kv == 0) {
+    const int dpg = NXCD / A.h_kv;                 // dies per KV group
+    const int per_part = ((A.nb + dpg - 1) / dpg) * hpg;
+    part = local / per_part;
+    const int rem = local % per_part;
+    const int cidx = dpg * (rem / hpg) + die / A.h_kv;
+    if (cidx >= A.nb) return;
+    b = A.nb - 1 - cidx;
+    h = ((die + part) % A.h_kv) * hpg + rem % hpg;
+  } else {
+    const int per_part = ((A.nb + NXCD - 1) / NXCD) * A.h_q;
+    part = local / per_part;
+    const int rem = local % per_part;
+    const int cidx = NXCD * (rem / A.h_q) + die;
+    if (cidx >= A.nb) return;
+    b = A.nb - 1 - cidx;
+    h = rem % A.h_q;
+  }
   const int g = h / (A.h_q / A.h_kv);
 
   const int i0 = A.p0 + QB * b;                  // absolute position of the block's first row
@@ -164,10 +140,11 @@ __global__ void __launch_bounds__(128, 2) dca_attn_kernel(AttnArgs A) {
   float m_run = 0.f;         // reference max (log2 domain) of this row
   bool started = false;      // the row has met a key
   float l_run = 0.f;         // this lane's partial row sum
+  // rotated query row of this lane for the current DCA mode: the hi half is
+  // held in registers (qh[kk]: dims 16kk + 8half .. +7), the lo half is read
+  // back from global memory by high-norm tiles only
   bf16x8 qh[8];
-  // query lo fragments go to this workgroup's scratch slot: only high-norm
-  // tiles read them back (each lane its own 16-byte entries)
-  uint4* ql = A.qlo + ((long long)blockIdx.x * 2 + wave) * 8 * 64;
+  const uint16_t* ql_row = A.qlo;
   int q_mode = -1;
 
   // ---- tile metadata.  A range tile's descriptor is read by lanes 0..3 (one
@@ -252,12 +229,11 @@ __global__ void __launch_bounds__(128, 2) dca_attn_kernel(AttnArgs A) {
     for (int mode = mode_first; mode <= mode_last; ++mode) {
       // ---- query rotation for this DCA mode
       if (mode != q_mode) {
-        const int r = prow % A.S;
-        double qpos;
-        if (mode == 2) qpos = r;
-        else if (mode == 1) qpos = min(A.S + r, A.S + A.W - 1);
-        else qpos = A.S + A.W - 1;
-        rotate_q(A, h, qrow, row_ok, half, qpos, qh, ql, lane);
+        const long long qo = (((long long)mode * A.n_q + qrow) * A.h_q + h) * D + 8 * half;
+        const uint16_t* qh_row = A.qhi + qo;
+        ql_row = A.qlo + qo;
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) qh[kk] = row_ok ? *(const bf16x8*)(qh_row + 16 * kk) : bf16x8{};
         q_mode = mode;
       }
       // ---- S^T = K Q^T: 32 keys x 32 rows of this wave (scores in log2 units)
@@ -278,8 +254,8 @@ __global__ void __launch_bounds__(128, 2) dca_attn_kernel(AttnArgs A) {
           const bf16x8 alo = *(const bf16x8*)(klrow + 16 * kk + 8 * half);
           const bf16x8 ahi = *(const bf16x8*)(kt + tile_off(l32, 2 * kk + half));
           s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, qh[kk], s, 0, 0, 0);
-          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, __builtin_bit_cast(bf16x8, ql[kk * 64 + lane]), s, 0, 0,
-                                                      0);
+          const bf16x8 qlo = row_ok ? *(const bf16x8*)(ql_row + 16 * kk) : bf16x8{};
+          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, qlo, s, 0, 0, 0);
         }
       }
       // ---- masks: absent slots, keys outside [0, p_row], keys of another DCA mode
@@ -455,8 +431,10 @@ __global__ void __launch_bounds__(256) lse_merge_kernel(const float* __restrict_
 }
 
 hipError_t launch_attn(const AttnArgs& A, hipStream_t stream) {
-  const int C = A.h_q * A.split;
-  const int blocks = NXCD * ((A.nb + NXCD - 1) / NXCD) * C;
+  // every die runs split * (its block rows) * (heads per row) workgroups
+  const int blocks = NXCD % A.h_kv == 0
+      ? NXCD * A.split * ((A.nb + NXCD / A.h_kv - 1) / (NXCD / A.h_kv)) * (A.h_q / A.h_kv)
+      : NXCD * A.split * ((A.nb + NXCD - 1) / NXCD) * A.h_q;
   hipLaunchKernelGGL(dca_attn_kernel, dim3(blocks), dim3(128), 0, stream, A);
   return hipGetLastError();
 }

@@ -1,8 +1,9 @@
-// Chunk-local key rotation (DCA key positions r_j = j mod S) for the attention kernel.
+// Rotary embeddings of the attention kernel's operands under Dual Chunk
+// Attention (paper-review page, section 4, Figure 2).
 //
-// Dual Chunk Attention (paper-review page, section 4, Figure 2) gives every key
-// the position of its offset inside its own chunk, so a key is rotated once and
-// the three query rotations carry the mode.  The rotated key is stored as a
+// Keys: every key takes the position of its offset inside its own chunk
+// (r_j = j mod S), so a key is rotated once and the three query rotations
+// carry the DCA mode.  The rotated key is stored as a
 // bf16 pair (hi, lo) with hi + lo within 2^-16 relative of the fp32 rotation;
 // the attention kernel adds the lo half only for tiles holding a key flagged as
 // high-norm (L2 norm above a threshold), whose logits would otherwise carry
@@ -70,6 +71,70 @@ __global__ void __launch_bounds__(256) rotate_keys_kernel(
   // high-norm keys: one bit per key, OR-ed in (order-independent)
   if (lane16 == 0 && thr2 >= 0.f && ss > thr2)
     atomicOr(&kbits[(long long)g * kbits_words + (j >> 5)], 1u << (j & 31));
+}
+
+// Queries: one rotation per DCA mode the row takes part in, at the mode's query
+// position: intra-chunk r_i, successive-chunk min(S + r_i, S + W - 1),
+// inter-chunk S + W - 1 (W: local window).  A row of chunk c meets keys of mode
+// m only when c >= 2 - m; the other entries are left unwritten and never read.
+// The rotated row times the softmax scale (log2 units) is stored as bf16 hi
+// plus bf16 lo residual in [3 modes][n_q][h_q][128].  Angles are reduced in
+// fp64 to a fraction of a turn, then evaluated with the hardware sine / cosine
+// of that fraction.  One 16-lane group per (row, head), as for the keys.
+__global__ void __launch_bounds__(256) rotate_queries_kernel(
+    const uint16_t* __restrict__ q, uint16_t* __restrict__ qhi, uint16_t* __restrict__ qlo,
+    const double* __restrict__ inv_freq, int n_q, int h_q, int p0, int S, int W, float qscale) {
+  const int lane16 = threadIdx.x & 15;
+  const long long row = (long long)blockIdx.x * 16 + (threadIdx.x >> 4);
+  if (row >= (long long)n_q * h_q) return;
+  const int i = (int)(row / h_q);
+  const int pos = p0 + i;
+  const int chunk = pos / S;
+  const int r = pos % S;
+  const uint16_t* src = q + row * D;
+  uint2 a = *(const uint2*)(src + 4 * lane16);
+  uint2 b = *(const uint2*)(src + HALF + 4 * lane16);
+  const uint16_t xa[4] = {(uint16_t)(a.x & 0xFFFF), (uint16_t)(a.x >> 16), (uint16_t)(a.y & 0xFFFF), (uint16_t)(a.y >> 16)};
+  const uint16_t xb[4] = {(uint16_t)(b.x & 0xFFFF), (uint16_t)(b.x >> 16), (uint16_t)(b.y & 0xFFFF), (uint16_t)(b.y >> 16)};
+  for (int mode = 2 - min(chunk, 2); mode <= 2; ++mode) {
+    const double qpos = mode == 2 ? (double)r : (mode == 1 ? (double)min(S + r, S + W - 1) : (double)(S + W - 1));
+    uint16_t ha[4], hb[4], la[4], lb[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int c = 4 * lane16 + t;
+      const double turns = qpos * inv_freq[c] * INV_TWO_PI;
+      const float f = (float)(turns - rint(turns));
+      const float sn = __builtin_amdgcn_sinf(f);
+      const float cs = __builtin_amdgcn_cosf(f);
+      const float x = bf16_bits_to_f32(xa[t]);
+      const float y = bf16_bits_to_f32(xb[t]);
+      const float xr = (x * cs - y * sn) * qscale;
+      const float yr = (x * sn + y * cs) * qscale;
+      ha[t] = f32_to_bf16_bits(xr);
+      hb[t] = f32_to_bf16_bits(yr);
+      la[t] = f32_to_bf16_bits(xr - bf16_bits_to_f32(ha[t]));
+      lb[t] = f32_to_bf16_bits(yr - bf16_bits_to_f32(hb[t]));
+    }
+    const long long o = ((long long)mode * n_q * h_q + row) * D;
+    uint2 oa, ob, pa, pb;
+    oa.x = ha[0] | ((uint32_t)ha[1] << 16); oa.y = ha[2] | ((uint32_t)ha[3] << 16);
+    ob.x = hb[0] | ((uint32_t)hb[1] << 16); ob.y = hb[2] | ((uint32_t)hb[3] << 16);
+    pa.x = la[0] | ((uint32_t)la[1] << 16); pa.y = la[2] | ((uint32_t)la[3] << 16);
+    pb.x = lb[0] | ((uint32_t)lb[1] << 16); pb.y = lb[2] | ((uint32_t)lb[3] << 16);
+    *(uint2*)(qhi + o + 4 * lane16) = oa;
+    *(uint2*)(qhi + o + HALF + 4 * lane16) = ob;
+    *(uint2*)(qlo + o + 4 * lane16) = pa;
+    *(uint2*)(qlo + o + HALF + 4 * lane16) = pb;
+  }
+}
+
+hipError_t launch_rotate_queries(const uint16_t* q, uint16_t* qhi, uint16_t* qlo, const double* inv_freq,
+                                 int n_q, int h_q, int p0, int S, int W, float qscale, hipStream_t stream) {
+  const long long rows = (long long)n_q * h_q;
+  const int blocks = (int)((rows + 15) / 16);
+  hipLaunchKernelGGL(rotate_queries_kernel, dim3(blocks), dim3(256), 0, stream, q, qhi, qlo, inv_freq,
+                     n_q, h_q, p0, S, W, qscale);
+  return hipGetLastError();
 }
 
 hipError_t launch_rotate_keys(const uint16_t* k, uint16_t* khi, uint16_t* klo, uint32_t* kbits,
