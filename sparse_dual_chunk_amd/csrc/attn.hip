@@ -77,30 +77,32 @@ __global__ void __launch_bounds__(128, 2) dca_attn_kernel(AttnArgs A) {
   // die's sequence, so the workgroups in flight all read the same share of
   // their key ranges.  Where the KV groups divide the dies evenly, a die serves
   // one KV group per part (the group advancing with the part, which evens out
-  // the per-group work) so that all its workgroups read the same keys through
-  // its L2; otherwise it serves all heads of its query-block rows.  Blocks are
-  // taken in descending order (the longest causal extents first).
+  // the per-group work), else all heads.  Within a part a die takes one query
+  // head at a time, its block rows in descending order (longest causal extent
+  // first): the rows of one head share one cover pattern shifted by 64 keys a
+  // row, so the workgroups in flight do near-equal work, start and end
+  // together and walk the same keys at the same time through the die's L2.
   const int die = blockIdx.x % NXCD;
   const int local = blockIdx.x / NXCD;
   const int hpg = A.h_q / A.h_kv;
   int b, h, part;
   if (NXCD % A.h_kv == 0) {
     const int dpg = NXCD / A.h_kv;                 // dies per KV group
-    const int per_part = ((A.nb + dpg - 1) / dpg) * hpg;
-    part = local / per_part;
-    const int rem = local % per_part;
-    const int cidx = dpg * (rem / hpg) + die / A.h_kv;
+    const int rows = (A.nb + dpg - 1) / dpg;       // block rows of this die
+    part = local / (rows * hpg);
+    const int rem = local % (rows * hpg);
+    const int cidx = dpg * (rem % rows) + die / A.h_kv;
     if (cidx >= A.nb) return;
     b = A.nb - 1 - cidx;
-    h = ((die + part) % A.h_kv) * hpg + rem % hpg;
+    h = ((die + part) % A.h_kv) * hpg + rem / rows;
   } else {
-    const int per_part = ((A.nb + NXCD - 1) / NXCD) * A.h_q;
-    part = local / per_part;
-    const int rem = local % per_part;
-    const int cidx = NXCD * (rem / A.h_q) + die;
+    const int rows = (A.nb + NXCD - 1) / NXCD;
+    part = local / (rows * A.h_q);
+    const int rem = local % (rows * A.h_q);
+    const int cidx = NXCD * (rem % rows) + die;
     if (cidx >= A.nb) return;
     b = A.nb - 1 - cidx;
-    h = rem % A.h_q;
+    h = rem / rows;
   }
   const int g = h / (A.h_q / A.h_kv);
 
