@@ -108,7 +108,7 @@ Layout make_layout(const dca_cfg* c) {
   // --- prefill
   place(L.khi, cur, (size_t)n_k * h_kv * D * 2);
   place(L.klo, cur, (size_t)n_k * h_kv * D * 2);
-  L.kbits_words = (n_k + 31) / 32 + 1;
+  L.kbits_words = (n_k + 31) / 32 + 4;   // guard words: a tile reads the two words of each run
   place(L.kbits, cur, (size_t)h_kv * L.kbits_words * 4);
   place(L.qhi, cur, (size_t)3 * n_q * h_q * D * 2);
   place(L.qlo, cur, (size_t)3 * n_q * h_q * D * 2);

@@ -7,7 +7,7 @@
 // over all tiles equals the log-sum-exp merge of the three modes' partials.
 // Within a mode the covered keys are enumerated in ascending order: first the
 // merged slash ranges (vertical-slash sparsity, Figure 4 of the same page),
-// then the vertical columns that no range covers.  Every 64 enumerated keys
+// then the vertical columns that no range covers.  Every 32 enumerated keys
 // form one tile; tiles that hold a high-norm key add the lo halves of the
 // rotated q and k to their logits (three MFMA passes) to keep the bf16 error
 // of those logits small.
@@ -31,7 +31,6 @@ namespace dca {
 constexpr int BN = 32;
 constexpr int GRPB = 1024 + 64;                // bytes per 4-row group
 constexpr int TILEB = 8 * GRPB;                // one tensor of one tile
-constexpr int STAGEB = 2 * TILEB;              // K then V
 
 // byte offset of (row, 16-byte chunk) inside a tensor tile
 __device__ __forceinline__ int tile_off(int row, int chunk) { return (row >> 2) * GRPB + chunk * 64 + (row & 3) * 16; }
@@ -56,16 +55,21 @@ struct Tile {
   int a1, a2, len1, len2, eoff, cnt;
 };
 
-__device__ __forceinline__ int tile_count(const Tile& T) { return T.cnt ? T.cnt : T.len1 + T.len2; }
+__device__ __forceinline__ int tile_count(Tile T) { return T.cnt ? T.cnt : T.len1 + T.len2; }
 
 // key of slot t (0..31) of a range tile, or -1 outside the tile
-__device__ __forceinline__ int range_key(const Tile& T, int t) {
+__device__ __forceinline__ int range_key(Tile T, int t) {
   return t < T.len1 ? T.a1 + t : (t < T.len1 + T.len2 ? T.a2 + (t - T.len1) : -1);
 }
 
 __global__ void __launch_bounds__(128, 2) dca_attn_kernel(AttnArgs A) {
-  __shared__ __align__(16) uint8_t stage0[STAGEB];
-  __shared__ __align__(16) uint8_t stage1[STAGEB];
+  // K and V of the two stages are four LDS objects: the compiler then tells
+  // the reads of one stage from the direct loads in flight into the other
+  // and places no wait for those loads inside the tile's computation
+  __shared__ __align__(16) uint8_t kst0[TILEB];
+  __shared__ __align__(16) uint8_t vst0[TILEB];
+  __shared__ __align__(16) uint8_t kst1[TILEB];
+  __shared__ __align__(16) uint8_t vst1[TILEB];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: LDS bases stay scalar
@@ -144,20 +148,33 @@ __global__ void __launch_bounds__(128, 2) dca_attn_kernel(AttnArgs A) {
   float l_run = 0.f;         // this lane's partial row sum
   // rotated query row of this lane for the current DCA mode: the hi half is
   // held in registers (qh[kk]: dims 16kk + 8half .. +7), the lo half is read
-  // back from global memory by high-norm tiles only
+  // back from global memory by high-norm tiles only.  Rows past the block's
+  // end read row qrow (clamped) and are never written.
   bf16x8 qh[8];
   const uint16_t* ql_row = A.qlo;
   int q_mode = -1;
+  auto load_q = [&](int mode) __attribute__((always_inline)) {
+    const long long qo = (((long long)mode * A.n_q + qrow) * A.h_q + h) * D + 8 * half;
+    const uint16_t* qh_row = A.qhi + qo;
+    ql_row = A.qlo + qo;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) qh[kk] = *(const bf16x8*)(qh_row + 16 * kk);
+    // a mode change is rare: wait here, so that no wait for these loads is
+    // left on the common path (where it would also drain the tile loads)
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    q_mode = mode;
+  };
 
-  // ---- tile metadata.  A range tile's descriptor is read by lanes 0..3 (one
-  // int each, a vector load) two tiles ahead; the slot key (lane & 31) and the
-  // high-norm flag of a tile are loaded one tile ahead, before the tile's
-  // direct-to-LDS loads are issued, so no wait on them stalls those loads.
-  auto desc_load = [&](int idx) -> int {   // per-lane part of the descriptor of tile idx
+  // ---- tile metadata, read by lanes 0..3 (one int each) with vector loads
+  // issued after a tile's direct-to-LDS loads and consumed a step later: a
+  // range tile's descriptor two tiles ahead, the high-norm bitmap words that
+  // hold its two runs one tile ahead.  An extra-vertical tile reads its keys
+  // (one per slot, lane & 31) before its loads are issued.
+  auto desc_load = [&](int idx) __attribute__((always_inline)) -> int {   // per-lane part of the descriptor of tile idx
     if (A.dense || idx >= n_range || idx >= t_end) return 0;
     return tl_h[4 * (t_first + idx) + (lane & 3)];
   };
-  auto make_tile = [&](int idx, int dv) -> Tile {
+  auto make_tile = [&](int idx, int dv) __attribute__((always_inline)) -> Tile {
     Tile T;
     T.a2 = 0; T.len2 = 0; T.eoff = 0; T.cnt = 0;
     if (idx < n_range) {
@@ -180,144 +197,204 @@ __global__ void __launch_bounds__(128, 2) dca_attn_kernel(AttnArgs A) {
     }
     return T;
   };
-  // slot key of this lane (slot lane & 31): an extra-vertical entry (bit 30
-  // marks a high-norm key) or a range key; -1 for an empty slot
-  auto slot_key = [&](const Tile& T) -> int {
-    if (T.cnt) return (l32 < T.cnt) ? ext_h[T.eoff + l32] : -1;
-    const int key = range_key(T, l32);
-    return (key < 0 || key >= A.n_k) ? -1 : key;
+  // words (a >> 5) and (a >> 5) + 1 of run 1 (lanes 0, 1) and run 2 (lanes 2, 3)
+  // of a range tile, negative keys skipped
+  auto flag_load = [&](Tile T) __attribute__((always_inline)) -> uint32_t {
+    const int a = max((lane & 2) ? T.a2 : T.a1, 0);
+    const int w = min((a >> 5) + (lane & 1), A.kbits_words - 1);
+    return kb[w];
   };
-  // the bitmap word holding a range slot key's high-norm bit (read one tile ahead)
-  auto flag_word = [&](int key) -> uint32_t { return key >= 0 ? kb[key >> 5] : 0u; };
+  // a run [a, a + len) holds a high-norm key (scalar bit test on its two words)
+  auto run_flagged = [&](uint32_t w0, uint32_t w1, int a, int len) __attribute__((always_inline)) -> bool {
+    const int ac = max(a, 0);
+    const int lc = len - (ac - a);
+    if (lc <= 0) return false;
+    const uint64_t bits = (((uint64_t)w1 << 32) | w0) >> (ac & 31);
+    return (bits & ((1ull << lc) - 1)) != 0;
+  };
+  // slot key of an extra-vertical tile (bit 30 marks a high-norm key), -1 past the count
+  auto ext_key = [&](Tile T) __attribute__((always_inline)) -> int { return (l32 < T.cnt) ? ext_h[T.eoff + l32] : -1; };
   // K and V rows of this KV head through buffer resources: one 32-bit byte
   // offset per row serves both tensors (the host bounds n_k * h_kv * 256 < 2^32)
   const __amdgpu_buffer_rsrc_t rs_k = __builtin_amdgcn_make_buffer_rsrc((void*)kh_base, (short)0, -1, 0x00020000);
   const __amdgpu_buffer_rsrc_t rs_v = __builtin_amdgcn_make_buffer_rsrc((void*)v_base, (short)0, -1, 0x00020000);
   const int rowb = kstride * 2;
-  auto issue_tile = [&](uint8_t* stage, const Tile& T, int skey) {
-    // all row offsets first, then the loads: no wait lands between two loads
-    int voff[4];
-    const int choff = 16 * (lane >> 2);
+  const int lane3 = lane & 3;
+  // byte offset of load j's row inside a tile of consecutive keys, plus the lane's chunk
+  unsigned roff[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = 4 * (2 * j + wave) + (lane & 3);
-      int key;
-      if (T.cnt) key = __shfl(skey, r) & 0x3FFFFFFF;
-      else key = (r < T.len1 ? T.a1 : T.a2 - T.len1) + r;   // slots past the count are masked later
-      key = min(max(key, 0), A.n_k - 1);
-      voff[j] = __umul24((unsigned)key, (unsigned)rowb) + choff;
+  for (int j = 0; j < 4; ++j) roff[j] = (unsigned)((4 * (2 * j + wave) + lane3) * rowb + 16 * (lane >> 2));
+  auto issue_tile = [&](uint8_t* kstage, uint8_t* vstage, Tile T, int skey) __attribute__((always_inline)) {
+    // all row offsets first, then the loads: no wait lands between two loads.
+    // Load j of wave w fills rows 4(2j + w) .. +3 of the tile (lane: row
+    // lane & 3, 16-byte chunk lane >> 2).
+    int voff[4];
+    const int last_key = (T.len2 ? T.a2 - T.len1 : T.a1) + BN - 1;   // key read by slot 31
+    if (T.cnt || T.a1 < 0 || last_key >= A.n_k) {
+      // extra-vertical tiles and tiles reaching outside [0, n_k): clamped keys
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = 4 * (2 * j + wave) + lane3;
+        int key;
+        if (T.cnt) key = __shfl(skey, r) & 0x3FFFFFFF;
+        else key = (r < T.len1 ? T.a1 : T.a2 - T.len1) + r;   // slots past the count are masked later
+        key = min(max(key, 0), A.n_k - 1);
+        voff[j] = __umul24((unsigned)key, (unsigned)rowb) + 16 * (lane >> 2);
+      }
+    } else if (T.len2 == 0) {
+      const unsigned base = (unsigned)T.a1 * (unsigned)rowb;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) voff[j] = (int)(base + roff[j]);
+    } else {
+      // rows from slot len1 on belong to run 2, a gap of a2 - a1 - len1 keys later
+      const unsigned base = (unsigned)T.a1 * (unsigned)rowb;
+      const unsigned gap = (unsigned)(T.a2 - T.a1 - T.len1) * (unsigned)rowb;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        voff[j] = (int)(base + roff[j] + (lane3 >= T.len1 - 4 * (2 * j + wave) ? gap : 0u));
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int grp4 = 2 * j + wave;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_k, (__attribute__((address_space(3))) void*)(stage + grp4 * GRPB),
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_k, (__attribute__((address_space(3))) void*)(kstage + grp4 * GRPB),
                                                16, voff[j], 0, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rs_v, (__attribute__((address_space(3))) void*)(stage + TILEB + grp4 * GRPB), 16, voff[j], 0, 0, 0);
+          rs_v, (__attribute__((address_space(3))) void*)(vstage + grp4 * GRPB), 16, voff[j], 0, 0, 0);
     }
   };
 
-  auto compute_tile = [&](const uint8_t* kt, const uint8_t* vt, const Tile& T, int skey, uint32_t fword) {
-    const int count = tile_count(T);
-    const bool flagged = T.cnt ? (skey >= 0 && ((skey >> 30) & 1)) : (skey >= 0 && ((fword >> (skey & 31)) & 1u));
-    const bool precise = __any(flagged);
-    const int key_first = T.cnt ? (__builtin_amdgcn_readlane(skey, 0) & 0x3FFFFFFF) : T.a1;
-    const int key_last = T.cnt ? (__builtin_amdgcn_readlane(skey, count - 1) & 0x3FFFFFFF)
-                               : (T.len2 ? T.a2 + T.len2 - 1 : T.a1 + T.len1 - 1);
-    const int mode_first = key_first >= segB ? 2 : (key_first >= segA ? 1 : 0);
-    const int mode_last = key_last >= segB ? 2 : (key_last >= segA ? 1 : 0);
-    const bool edge = (count < BN) || (key_first < 0) || (key_last >= i0);
+  // DCA mode of a key: 2 intra-chunk [segB, ..), 1 successive [segA, segB),
+  // 0 inter-chunk [0, segA); sign-bit arithmetic keeps it scalar
+  auto key_mode = [&](int key) __attribute__((always_inline)) -> int {
+    return (int)((unsigned)(segA - 1 - key) >> 31) + (int)((unsigned)(segB - 1 - key) >> 31);
+  };
 
-    for (int mode = mode_first; mode <= mode_last; ++mode) {
-      // ---- query rotation for this DCA mode
-      if (mode != q_mode) {
-        const long long qo = (((long long)mode * A.n_q + qrow) * A.h_q + h) * D + 8 * half;
-        const uint16_t* qh_row = A.qhi + qo;
-        ql_row = A.qlo + qo;
+  // One DCA mode's pass over the staged tile: S^T = K Q^T (+ the lo terms of a
+  // high-norm tile), the masks (masked passes only), the online softmax and
+  // O^T += V^T P^T.
+  auto tile_pass = [&](const uint8_t* kt, const uint8_t* vt, Tile T, int skey, int mode, bool precise,
+                       bool masked) __attribute__((always_inline)) {
+    if (mode != q_mode) load_q(mode);
+    // ---- S^T = K Q^T: 32 keys x 32 rows of this wave (scores in log2 units)
+    f32x16 s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(kt + tile_off(l32, half)), qh[0],
+                                                       f32x16{}, 0, 0, 0);
 #pragma unroll
-        for (int kk = 0; kk < 8; ++kk) qh[kk] = row_ok ? *(const bf16x8*)(qh_row + 16 * kk) : bf16x8{};
-        q_mode = mode;
-      }
-      // ---- S^T = K Q^T: 32 keys x 32 rows of this wave (scores in log2 units)
-      f32x16 s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(kt + tile_off(l32, half)), qh[0],
-                                                         f32x16{}, 0, 0, 0);
+    for (int kk = 1; kk < 8; ++kk) {
+      const bf16x8 a = *(const bf16x8*)(kt + tile_off(l32, 2 * kk + half));
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qh[kk], s, 0, 0, 0);
+    }
+    if (precise) {
+      // + K_lo Q_hi + K_hi Q_lo; K_lo rows come straight from global memory
+      int kr = T.cnt ? (skey & 0x3FFFFFFF) : range_key(T, l32);
+      kr = min(max(kr, 0), A.n_k - 1);
+      const uint16_t* klrow = kl_base + kr * kstride;
 #pragma unroll
-      for (int kk = 1; kk < 8; ++kk) {
-        const bf16x8 a = *(const bf16x8*)(kt + tile_off(l32, 2 * kk + half));
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qh[kk], s, 0, 0, 0);
-      }
-      if (precise) {
-        // + K_lo Q_hi + K_hi Q_lo; K_lo rows come straight from global memory
-        int kr = __shfl(skey, l32);
-        kr = (kr < 0) ? 0 : min(kr & 0x3FFFFFFF, A.n_k - 1);
-        const uint16_t* klrow = kl_base + kr * kstride;
-#pragma unroll
-        for (int kk = 0; kk < 8; ++kk) {
-          const bf16x8 alo = *(const bf16x8*)(klrow + 16 * kk + 8 * half);
-          const bf16x8 ahi = *(const bf16x8*)(kt + tile_off(l32, 2 * kk + half));
-          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, qh[kk], s, 0, 0, 0);
-          const bf16x8 qlo = row_ok ? *(const bf16x8*)(ql_row + 16 * kk) : bf16x8{};
-          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, qlo, s, 0, 0, 0);
-        }
-      }
-      // ---- masks: absent slots, keys outside [0, p_row], keys of another DCA mode
-      if (edge || mode_first != mode_last) {
-#pragma unroll
-        for (int vv = 0; vv < 16; ++vv) {
-          const int t = 8 * (vv >> 2) + 4 * half + (vv & 3);
-          int kj;
-          if (T.cnt) {
-            kj = __shfl(skey, t);
-            kj = kj < 0 ? -1 : (kj & 0x3FFFFFFF);
-          } else {
-            kj = range_key(T, t);
-          }
-          const int km = kj >= segB ? 2 : (kj >= segA ? 1 : 0);
-          if (kj < 0 || kj > prow || km != mode) s[vv] = -INFINITY;
-        }
-      }
-      // ---- online softmax (log2 domain).  The reference max moves only when a
-      // score exceeds it by more than 8 (so p <= 2^8), or at the row's first keys.
-      float mx = fmaxf(fmaxf(s[0], s[1]), s[2]);
-#pragma unroll
-      for (int vv = 3; vv < 15; vv += 2) mx = fmaxf(fmaxf(mx, s[vv]), s[vv + 1]);
-      mx = fmaxf(mx, s[15]);
-      mx = pair_max(mx);
-      const bool need = (mx > m_run + 8.f) || (!started && mx != -INFINITY);
-      if (__any(need)) {
-        const float m_new = need ? mx : m_run;
-        const float alpha = started ? fast_exp2(m_run - m_new) : 0.f;
-        l_run *= alpha;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int vv = 0; vv < 16; ++vv) o[i][vv] *= alpha;
-        m_run = m_new;
-      }
-      started = started || (mx != -INFINITY);
-      bf16x8 pf[2];
-#pragma unroll
-      for (int vv = 0; vv < 16; ++vv) {
-        const float p = fast_exp2(s[vv] - m_run);
-        l_run += p;
-        pf[vv >> 3][vv & 7] = (__bf16)p;
-      }
-      // ---- O^T += V^T P^T, V^T operand read transposed from the row-major V tile
-#pragma unroll
-      for (int G = 0; G < 2; ++G) {
-        const int r1 = 16 * G + 4 * half + (s16 >> 2);
-        const int r2 = r1 + 8;
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          const int c = 4 * db + 2 * grp + ((s16 & 3) >> 1);     // 16-byte chunk of the 4 columns read
-          const int bo = 8 * (s16 & 1);                           // byte offset inside the chunk
-          const bf16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, vt + tile_off(r1, c) + bo));
-          const bf16x4 t2 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, vt + tile_off(r2, c) + bo));
-          const bf16x8 a = __builtin_shufflevector(t1, t2, 0, 1, 2, 3, 4, 5, 6, 7);
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[G], o[db], 0, 0, 0);
-        }
+      for (int kk = 0; kk < 8; ++kk) {
+        const bf16x8 alo = *(const bf16x8*)(klrow + 16 * kk + 8 * half);
+        const bf16x8 ahi = *(const bf16x8*)(kt + tile_off(l32, 2 * kk + half));
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, qh[kk], s, 0, 0, 0);
+        const bf16x8 qlo = *(const bf16x8*)(ql_row + 16 * kk);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, qlo, s, 0, 0, 0);
       }
     }
+    if (masked) {
+      // ---- masks.  A tile's keys ascend with the slot, so the slots of this
+      // mode's keys that are >= 0 and <= this lane's row form one interval
+      // [t_lo, t_hi); every other slot is masked.
+      const int lo = mode == 0 ? 0 : (mode == 1 ? segA : segB);
+      const int hi = mode == 0 ? segA : (mode == 1 ? segB : 0x7FFFFFFF);
+      int t_lo, t_hi;
+      if (T.cnt) {
+        // extra-vertical keys all lie below the block (the block's own keys are
+        // range-covered): no causal cut, count keys by ballot
+        const int kj = skey & 0x3FFFFFFF;
+        const bool inl = l32 < T.cnt && half == 0;
+        t_lo = __builtin_popcountll(__ballot(inl && kj < lo));
+        t_hi = __builtin_popcountll(__ballot(inl && kj < hi));
+      } else {
+        auto below = [&](int x) {   // number of the tile's keys below x
+          return min(max(x - T.a1, 0), T.len1) + min(max(x - T.a2, 0), T.len2);
+        };
+        t_lo = below(max(lo, 0));
+        t_hi = below(min(hi, prow + 1));
+      }
+      const int base = t_lo - 4 * half;
+      const unsigned span = (unsigned)max(t_hi - t_lo, 0);
+#pragma unroll
+      for (int vv = 0; vv < 16; ++vv) {
+        const int c = 8 * (vv >> 2) + (vv & 3);   // slot of s[vv] is c + 4 half
+        if ((unsigned)(c - base) >= span) s[vv] = -INFINITY;
+      }
+    }
+    // ---- online softmax (log2 domain).  The reference max moves only when a
+    // score exceeds it by more than 8 (so p <= 2^8), or at the row's first keys.
+    float mx = fmaxf(fmaxf(s[0], s[1]), s[2]);
+#pragma unroll
+    for (int vv = 3; vv < 15; vv += 2) mx = fmaxf(fmaxf(mx, s[vv]), s[vv + 1]);
+    mx = fmaxf(mx, s[15]);
+    mx = pair_max(mx);
+    const bool need = (mx > m_run + 8.f) || (!started && mx != -INFINITY);
+    if (__any(need)) {
+      const float m_new = need ? mx : m_run;
+      const float alpha = started ? fast_exp2(m_run - m_new) : 0.f;
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int vv = 0; vv < 16; ++vv) o[i][vv] *= alpha;
+      m_run = m_new;
+    }
+    started = started || (mx != -INFINITY);
+    bf16x8 pf[2];
+#pragma unroll
+    for (int vv = 0; vv < 16; ++vv) pf[vv >> 3][vv & 7] = (__bf16)fast_exp2(s[vv] - m_run);
+    // row sum of the bf16 weights that enter P V (pairs summed by dot products)
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+    for (int G = 0; G < 2; ++G) {
+      l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[G], pf[G], 0, 1), ones, l_run, false);
+      l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[G], pf[G], 2, 3), ones, l_run, false);
+      l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[G], pf[G], 4, 5), ones, l_run, false);
+      l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[G], pf[G], 6, 7), ones, l_run, false);
+    }
+    // ---- O^T += V^T P^T, V^T operand read transposed from the row-major V tile
+#pragma unroll
+    for (int G = 0; G < 2; ++G) {
+      const int r1 = 16 * G + 4 * half + (s16 >> 2);
+      const int r2 = r1 + 8;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const int c = 4 * db + 2 * grp + ((s16 & 3) >> 1);     // 16-byte chunk of the 4 columns read
+        const int bo = 8 * (s16 & 1);                           // byte offset inside the chunk
+        const bf16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, vt + tile_off(r1, c) + bo));
+        const bf16x4 t2 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, vt + tile_off(r2, c) + bo));
+        const bf16x8 a = __builtin_shufflevector(t1, t2, 0, 1, 2, 3, 4, 5, 6, 7);
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[G], o[db], 0, 0, 0);
+      }
+    }
+  };
+
+  // A tile: one pass per DCA mode it holds, unmasked when the tile is full,
+  // inside [0, i0] and of one mode (the common case).
+  auto compute_tile = [&](const uint8_t* kt, const uint8_t* vt, Tile T, int skey, uint32_t fw) __attribute__((always_inline)) {
+    const int count = tile_count(T);
+    int key_first, key_last;
+    bool precise;
+    if (T.cnt) {
+      key_first = __builtin_amdgcn_readlane(skey, 0) & 0x3FFFFFFF;
+      key_last = __builtin_amdgcn_readlane(skey, count - 1) & 0x3FFFFFFF;
+      precise = __any(skey >= 0 && ((skey >> 30) & 1));
+    } else {
+      key_first = T.a1;
+      key_last = T.len2 ? T.a2 + T.len2 - 1 : T.a1 + T.len1 - 1;
+      const uint32_t w0 = __builtin_amdgcn_readlane(fw, 0), w1 = __builtin_amdgcn_readlane(fw, 1);
+      const uint32_t w2 = __builtin_amdgcn_readlane(fw, 2), w3 = __builtin_amdgcn_readlane(fw, 3);
+      precise = run_flagged(w0, w1, T.a1, T.len1) || run_flagged(w2, w3, T.a2, T.len2);
+    }
+    const int mode_first = key_mode(max(key_first, 0));   // negative keys are masked
+    const int mode_last = key_mode(key_last);
+    const bool masked = count < BN || key_first < 0 || key_last > i0 || mode_first != mode_last;
+    for (int mode = mode_first; mode <= mode_last; ++mode) tile_pass(kt, vt, T, skey, mode, precise, masked);
   };
 
   // ---- prologue: tile t_beg staged, descriptor of t_beg+1 in flight
@@ -326,9 +403,9 @@ __global__ void __launch_bounds__(128, 2) dca_attn_kernel(AttnArgs A) {
   int sk_cur = -1;
   uint32_t fw_cur = 0;
   if (t_beg < t_end) {
-    sk_cur = slot_key(T_cur);
-    fw_cur = T_cur.cnt ? 0u : flag_word(sk_cur);
-    issue_tile(stage0, T_cur, sk_cur);
+    if (T_cur.cnt) sk_cur = ext_key(T_cur);
+    issue_tile(kst0, vst0, T_cur, sk_cur);
+    if (!T_cur.cnt) fw_cur = flag_load(T_cur);
   }
   int dv_nxt = desc_load(t_beg + 1);
   __syncthreads();
@@ -337,7 +414,7 @@ __global__ void __launch_bounds__(128, 2) dca_attn_kernel(AttnArgs A) {
   // The other stage was last read before the previous barrier.  Range tiles
   // issue their loads before any metadata read they would wait for; an
   // extra-vertical tile needs its keys first (these tiles are few).
-  auto step = [&](const uint8_t* cur, uint8_t* nxt, int ti) {
+  auto step = [&](const uint8_t* kcur, const uint8_t* vcur, uint8_t* knxt, uint8_t* vnxt, int ti) __attribute__((always_inline)) {
     Tile T_n;
     int sk_n = -1;
     uint32_t fw_n = 0;
@@ -345,22 +422,21 @@ __global__ void __launch_bounds__(128, 2) dca_attn_kernel(AttnArgs A) {
     if (more) {
       T_n = make_tile(ti + 1, dv_nxt);
       if (T_n.cnt) {
-        sk_n = slot_key(T_n);
-        issue_tile(nxt, T_n, sk_n);
+        sk_n = ext_key(T_n);
+        issue_tile(knxt, vnxt, T_n, sk_n);
       } else {
-        issue_tile(nxt, T_n, 0);
-        sk_n = slot_key(T_n);
-        fw_n = flag_word(sk_n);
+        issue_tile(knxt, vnxt, T_n, 0);
+        fw_n = flag_load(T_n);
       }
       dv_nxt = desc_load(ti + 2);
     }
-    compute_tile(cur, cur + TILEB, T_cur, sk_cur, fw_cur);
+    compute_tile(kcur, vcur, T_cur, sk_cur, fw_cur);
     __syncthreads();   // the prefetched stage has landed; this stage may be overwritten next
     if (more) { T_cur = T_n; sk_cur = sk_n; fw_cur = fw_n; }
   };
   for (int ti = t_beg; ti < t_end; ti += 2) {
-    step(stage0, stage1, ti);
-    if (ti + 1 < t_end) step(stage1, stage0, ti + 1);
+    step(kst0, vst0, kst1, vst1, ti);
+    if (ti + 1 < t_end) step(kst1, vst1, kst0, vst0, ti + 1);
   }
 
   // ---- finish: row sum over both halves, normalise, write
