@@ -165,52 +165,53 @@ __global__ void __launch_bounds__(128, 2) dca_attn_kernel(AttnArgs A) {
     q_mode = mode;
   };
 
-  // ---- tile metadata, read by lanes 0..3 (one int each) with vector loads
-  // issued after a tile's direct-to-LDS loads and consumed a step later: a
-  // range tile's descriptor two tiles ahead, the high-norm bitmap words that
-  // hold its two runs one tile ahead.  An extra-vertical tile reads its keys
-  // (one per slot, lane & 31) before its loads are issued.
-  auto desc_load = [&](int idx) __attribute__((always_inline)) -> int {   // per-lane part of the descriptor of tile idx
-    if (A.dense || idx >= n_range || idx >= t_end) return 0;
-    return tl_h[4 * (t_first + idx) + (lane & 3)];
+  // ---- tile metadata.  Range tiles: descriptor and high-norm bitmap words
+  // through scalar loads (their waits do not hold the vector-memory queue of
+  // the staged K / V loads); an extra-vertical tile's keys (one per slot,
+  // lane & 31) with a vector load.
+  typedef __attribute__((address_space(4))) const int ci32;
+  typedef __attribute__((address_space(4))) const uint32_t cu32;
+  ci32* tl4 = (ci32*)(A.tiles + (long long)h * A.tile_stride);
+  cu32* kb4 = (cu32*)kb;
+  auto desc_load = [&](int idx) __attribute__((always_inline)) -> int4 {
+    if (A.dense || idx >= n_range || idx >= t_end) return make_int4(0, 0, 0, 0);
+    ci32* d = tl4 + 4 * (t_first + idx);
+    return make_int4(d[0], d[1], d[2], d[3]);
   };
-  auto make_tile = [&](int idx, int dv) __attribute__((always_inline)) -> Tile {
+  auto range_tile = [&](int idx, int4 d) __attribute__((always_inline)) -> Tile {
     Tile T;
-    T.a2 = 0; T.len2 = 0; T.eoff = 0; T.cnt = 0;
-    if (idx < n_range) {
-      if (A.dense) {
-        T.a1 = BN * idx;
-        T.len1 = min(BN, hi_key - T.a1);
-      } else {
-        const int d0 = __builtin_amdgcn_readlane(dv, 0);
-        const int d1 = __builtin_amdgcn_readlane(dv, 1);
-        const int d2 = __builtin_amdgcn_readlane(dv, 2);
-        T.a1 = i0 + d0;
-        T.a2 = i0 + d1;
-        T.len1 = d2 & 0xFF;
-        T.len2 = (d2 >> 8) & 0xFF;
-      }
+    T.eoff = 0; T.cnt = 0;
+    if (A.dense) {
+      T.a1 = BN * idx;
+      T.len1 = min(BN, hi_key - T.a1);
+      T.a2 = 0; T.len2 = 0;
     } else {
-      T.a1 = 0; T.len1 = 0;
-      T.eoff = BN * (idx - n_range);
-      T.cnt = min(BN, n_ext - T.eoff);
+      T.a1 = i0 + d.x;
+      T.a2 = i0 + d.y;
+      T.len1 = d.z & 0xFF;
+      T.len2 = (d.z >> 8) & 0xFF;
     }
     return T;
   };
-  // words (a >> 5) and (a >> 5) + 1 of run 1 (lanes 0, 1) and run 2 (lanes 2, 3)
-  // of a range tile, negative keys skipped
-  auto flag_load = [&](Tile T) __attribute__((always_inline)) -> uint32_t {
-    const int a = max((lane & 2) ? T.a2 : T.a1, 0);
-    const int w = min((a >> 5) + (lane & 1), A.kbits_words - 1);
-    return kb[w];
+  auto ext_tile = [&](int idx) __attribute__((always_inline)) -> Tile {
+    Tile T;
+    T.a1 = 0; T.a2 = 0; T.len1 = 0; T.len2 = 0;
+    T.eoff = BN * (idx - n_range);
+    T.cnt = min(BN, n_ext - T.eoff);
+    return T;
   };
-  // a run [a, a + len) holds a high-norm key (scalar bit test on its two words)
-  auto run_flagged = [&](uint32_t w0, uint32_t w1, int a, int len) __attribute__((always_inline)) -> bool {
+  // a run [a, a + len) holds a high-norm key: bit test on the two bitmap words
+  // that hold it (the bitmap has guard words past n_k)
+  auto run_flagged = [&](int a, int len) __attribute__((always_inline)) -> bool {
     const int ac = max(a, 0);
     const int lc = len - (ac - a);
     if (lc <= 0) return false;
-    const uint64_t bits = (((uint64_t)w1 << 32) | w0) >> (ac & 31);
+    const int w = ac >> 5;
+    const uint64_t bits = (((uint64_t)kb4[w + 1] << 32) | kb4[w]) >> (ac & 31);
     return (bits & ((1ull << lc) - 1)) != 0;
+  };
+  auto range_precise = [&](Tile T) __attribute__((always_inline)) -> bool {
+    return run_flagged(T.a1, T.len1) || run_flagged(T.a2, T.len2);
   };
   // slot key of an extra-vertical tile (bit 30 marks a high-norm key), -1 past the count
   auto ext_key = [&](Tile T) __attribute__((always_inline)) -> int { return (l32 < T.cnt) ? ext_h[T.eoff + l32] : -1; };
@@ -224,11 +225,11 @@ __global__ void __launch_bounds__(128, 2) dca_attn_kernel(AttnArgs A) {
   unsigned roff[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) roff[j] = (unsigned)((4 * (2 * j + wave) + lane3) * rowb + 16 * (lane >> 2));
-  auto issue_tile = [&](uint8_t* kstage, uint8_t* vstage, Tile T, int skey) __attribute__((always_inline)) {
-    // all row offsets first, then the loads: no wait lands between two loads.
-    // Load j of wave w fills rows 4(2j + w) .. +3 of the tile (lane: row
-    // lane & 3, 16-byte chunk lane >> 2).
-    int voff[4];
+  // Row offsets of a tile's direct loads: load j of wave w fills rows
+  // 4(2j + w) .. +3 of the tile (lane: row lane & 3, 16-byte chunk lane >> 2).
+  struct Offs { int v[4]; };
+  auto tile_offsets = [&](Tile T, int skey) __attribute__((always_inline)) -> Offs {
+    Offs f;
     const int last_key = (T.len2 ? T.a2 - T.len1 : T.a1) + BN - 1;   // key read by slot 31
     if (T.cnt || T.a1 < 0 || last_key >= A.n_k) {
       // extra-vertical tiles and tiles reaching outside [0, n_k): clamped keys
@@ -239,30 +240,55 @@ __global__ void __launch_bounds__(128, 2) dca_attn_kernel(AttnArgs A) {
         if (T.cnt) key = __shfl(skey, r) & 0x3FFFFFFF;
         else key = (r < T.len1 ? T.a1 : T.a2 - T.len1) + r;   // slots past the count are masked later
         key = min(max(key, 0), A.n_k - 1);
-        voff[j] = __umul24((unsigned)key, (unsigned)rowb) + 16 * (lane >> 2);
+        f.v[j] = __umul24((unsigned)key, (unsigned)rowb) + 16 * (lane >> 2);
       }
     } else if (T.len2 == 0) {
       const unsigned base = (unsigned)T.a1 * (unsigned)rowb;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) voff[j] = (int)(base + roff[j]);
+      for (int j = 0; j < 4; ++j) f.v[j] = (int)(base + roff[j]);
     } else {
       // rows from slot len1 on belong to run 2, a gap of a2 - a1 - len1 keys later
       const unsigned base = (unsigned)T.a1 * (unsigned)rowb;
       const unsigned gap = (unsigned)(T.a2 - T.a1 - T.len1) * (unsigned)rowb;
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        voff[j] = (int)(base + roff[j] + (lane3 >= T.len1 - 4 * (2 * j + wave) ? gap : 0u));
+        f.v[j] = (int)(base + roff[j] + (lane3 >= T.len1 - 4 * (2 * j + wave) ? gap : 0u));
     }
+    return f;
+  };
+  // the 4 direct loads of one tensor of a tile into a stage
+  auto issue = [&](__amdgpu_buffer_rsrc_t rs, uint8_t* stage, Offs f) __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int grp4 = 2 * j + wave;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_k, (__attribute__((address_space(3))) void*)(kstage + grp4 * GRPB),
-                                               16, voff[j], 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rs_v, (__attribute__((address_space(3))) void*)(vstage + grp4 * GRPB), 16, voff[j], 0, 0, 0);
-    }
+    for (int j = 0; j < 4; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(stage + (2 * j + wave) * GRPB),
+                                               16, f.v[j], 0, 0, 0);
   };
 
+  // ---- pipeline.  The K and V stages are released separately: step t
+  //   B1: own loads of K(t) landed, barrier; then V(t+1) is issued into the V
+  //       stage that V(t-1) held;
+  //   S^T = K Q^T of tile t;
+  //   B2: barrier (both waves are done with K(t)); then K(t+2) is issued into
+  //       K(t)'s stage, with the metadata reads of the tiles after it;
+  //   softmax;
+  //   B3: own loads of V(t) landed, barrier; then O += P V.
+  // So K is read about 1.5 steps and V about 2 steps after its loads were
+  // issued.  A wave issues 4 direct loads per tile and tensor, also for tiles
+  // past the end (clamped rows, never read), so the number of these loads
+  // issued after any given one is fixed and the waits below count them (reads
+  // of metadata in between only make a wait longer).  Barriers carry no memory
+  // fence (a fence would wait for every load in flight).
+  auto vm_wait = [&](int n) __attribute__((always_inline)) {   // at most n vector-memory ops outstanding
+    if (n >= 12) __builtin_amdgcn_s_waitcnt(0x0F7C);
+    else if (n >= 8) __builtin_amdgcn_s_waitcnt(0x0F78);
+    else __builtin_amdgcn_s_waitcnt(0x0F70);
+  };
+  auto wg_barrier = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's LDS reads are done
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
   // DCA mode of a key: 2 intra-chunk [segB, ..), 1 successive [segA, segB),
   // 0 inter-chunk [0, segA); sign-bit arithmetic keeps it scalar
   auto key_mode = [&](int key) __attribute__((always_inline)) -> int {
@@ -272,10 +298,12 @@ __global__ void __launch_bounds__(128, 2) dca_attn_kernel(AttnArgs A) {
   // One DCA mode's pass over the staged tile: S^T = K Q^T (+ the lo terms of a
   // high-norm tile), the masks (masked passes only), the online softmax and
   // O^T += V^T P^T.
-  auto tile_pass = [&](const uint8_t* kt, const uint8_t* vt, Tile T, int skey, int mode, bool precise,
-                       bool masked) __attribute__((always_inline)) {
+  // S^T = K Q^T of the staged tile for one DCA mode's query rotation (+ the
+  // lo terms of a high-norm tile)
+  auto qk = [&](const uint8_t* kt, Tile T, int skey, int mode, bool precise) __attribute__((always_inline))
+      -> f32x16 {
     if (mode != q_mode) load_q(mode);
-    // ---- S^T = K Q^T: 32 keys x 32 rows of this wave (scores in log2 units)
+    // 32 keys x 32 rows of this wave (scores in log2 units)
     f32x16 s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(kt + tile_off(l32, half)), qh[0],
                                                        f32x16{}, 0, 0, 0);
 #pragma unroll
@@ -297,35 +325,69 @@ __global__ void __launch_bounds__(128, 2) dca_attn_kernel(AttnArgs A) {
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, qlo, s, 0, 0, 0);
       }
     }
-    if (masked) {
-      // ---- masks.  A tile's keys ascend with the slot, so the slots of this
-      // mode's keys that are >= 0 and <= this lane's row form one interval
-      // [t_lo, t_hi); every other slot is masked.
-      const int lo = mode == 0 ? 0 : (mode == 1 ? segA : segB);
-      const int hi = mode == 0 ? segA : (mode == 1 ? segB : 0x7FFFFFFF);
-      int t_lo, t_hi;
+    return s;
+  };
+
+  // A tile.  Its keys ascend with the slot, so each DCA mode's keys fill one
+  // interval of slots, and so do the keys inside [0, row].  S^T is computed
+  // once per mode the tile holds and merged slot by slot; slots outside
+  // [0, row] or past the count are masked (only tiles at the block's edges
+  // have such slots).  Then one online softmax and one O += P V.  after_qk
+  // runs once S^T is done (B2 and the K issue), B3 before the V reads.
+  auto compute_tile = [&](const uint8_t* kt, const uint8_t* vt, Tile T, int skey, bool precise, auto&& after_qk)
+      __attribute__((always_inline)) {
+    const int count = tile_count(T);
+    int key_first, key_last;
+    if (T.cnt) {
+      key_first = __builtin_amdgcn_readlane(skey, 0) & 0x3FFFFFFF;
+      key_last = __builtin_amdgcn_readlane(skey, count - 1) & 0x3FFFFFFF;
+    } else {
+      key_first = T.a1;
+      key_last = T.len2 ? T.a2 + T.len2 - 1 : T.a1 + T.len1 - 1;
+    }
+    const int mode_first = key_mode(max(key_first, 0));   // negative keys are masked
+    const int mode_last = key_mode(key_last);
+    // number of the tile's keys below x
+    auto below = [&](int x) __attribute__((always_inline)) -> int {
       if (T.cnt) {
-        // extra-vertical keys all lie below the block (the block's own keys are
-        // range-covered): no causal cut, count keys by ballot
         const int kj = skey & 0x3FFFFFFF;
-        const bool inl = l32 < T.cnt && half == 0;
-        t_lo = __builtin_popcountll(__ballot(inl && kj < lo));
-        t_hi = __builtin_popcountll(__ballot(inl && kj < hi));
-      } else {
-        auto below = [&](int x) {   // number of the tile's keys below x
-          return min(max(x - T.a1, 0), T.len1) + min(max(x - T.a2, 0), T.len2);
-        };
-        t_lo = below(max(lo, 0));
-        t_hi = below(min(hi, prow + 1));
+        return __builtin_popcountll(__ballot(l32 < T.cnt && half == 0 && kj < x));
       }
+      return min(max(x - T.a1, 0), T.len1) + min(max(x - T.a2, 0), T.len2);
+    };
+    // keep s[vv] where its slot (c + 4 half) lies in [t_lo, t_hi), else take alt
+    auto select_slots = [&](f32x16& s, int t_lo, int t_hi, float alt) __attribute__((always_inline)) {
       const int base = t_lo - 4 * half;
       const unsigned span = (unsigned)max(t_hi - t_lo, 0);
 #pragma unroll
       for (int vv = 0; vv < 16; ++vv) {
-        const int c = 8 * (vv >> 2) + (vv & 3);   // slot of s[vv] is c + 4 half
-        if ((unsigned)(c - base) >= span) s[vv] = -INFINITY;
+        const int c = 8 * (vv >> 2) + (vv & 3);
+        if ((unsigned)(c - base) >= span) s[vv] = alt;
       }
+    };
+    f32x16 s = qk(kt, T, skey, mode_first, precise);
+    // slots from the first key of mode m on take that mode's scores (the
+    // modes after the first are spelled out: a loop here would make the
+    // compiler wait for the staged loads in flight before every S^T)
+    auto merge_mode = [&](int m) __attribute__((always_inline)) {
+      const int tb = below(m == 2 ? segB : segA);
+      const f32x16 s2 = qk(kt, T, skey, m, precise);
+      const int base = tb - 4 * half;
+#pragma unroll
+      for (int vv = 0; vv < 16; ++vv) {
+        const int c = 8 * (vv >> 2) + (vv & 3);
+        if (c >= base) s[vv] = s2[vv];
+      }
+    };
+    if (mode_first + 1 <= mode_last) merge_mode(mode_first + 1);
+    if (mode_first + 2 <= mode_last) merge_mode(mode_first + 2);
+    if (count < BN || key_first < 0 || key_last > i0) {
+      // extra-vertical keys all lie below the block (its own keys are range-covered)
+      const int t_lo = T.cnt ? 0 : below(0);
+      const int t_hi = T.cnt ? count : below(prow + 1);
+      select_slots(s, t_lo, t_hi, -INFINITY);
     }
+    after_qk();
     // ---- online softmax (log2 domain).  The reference max moves only when a
     // score exceeds it by more than 8 (so p <= 2^8), or at the row's first keys.
     float mx = fmaxf(fmaxf(s[0], s[1]), s[2]);
@@ -357,6 +419,10 @@ __global__ void __launch_bounds__(128, 2) dca_attn_kernel(AttnArgs A) {
       l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[G], pf[G], 4, 5), ones, l_run, false);
       l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[G], pf[G], 6, 7), ones, l_run, false);
     }
+    // B3: this wave's loads of V(t) landed (issued after them: K(t+1), V(t+1)
+    // and K(t+2)); barrier
+    vm_wait(12);
+    wg_barrier();
     // ---- O^T += V^T P^T, V^T operand read transposed from the row-major V tile
 #pragma unroll
     for (int G = 0; G < 2; ++G) {
@@ -374,69 +440,64 @@ __global__ void __launch_bounds__(128, 2) dca_attn_kernel(AttnArgs A) {
     }
   };
 
-  // A tile: one pass per DCA mode it holds, unmasked when the tile is full,
-  // inside [0, i0] and of one mode (the common case).
-  auto compute_tile = [&](const uint8_t* kt, const uint8_t* vt, Tile T, int skey, uint32_t fw) __attribute__((always_inline)) {
-    const int count = tile_count(T);
-    int key_first, key_last;
-    bool precise;
-    if (T.cnt) {
-      key_first = __builtin_amdgcn_readlane(skey, 0) & 0x3FFFFFFF;
-      key_last = __builtin_amdgcn_readlane(skey, count - 1) & 0x3FFFFFFF;
-      precise = __any(skey >= 0 && ((skey >> 30) & 1));
-    } else {
-      key_first = T.a1;
-      key_last = T.len2 ? T.a2 + T.len2 - 1 : T.a1 + T.len1 - 1;
-      const uint32_t w0 = __builtin_amdgcn_readlane(fw, 0), w1 = __builtin_amdgcn_readlane(fw, 1);
-      const uint32_t w2 = __builtin_amdgcn_readlane(fw, 2), w3 = __builtin_amdgcn_readlane(fw, 3);
-      precise = run_flagged(w0, w1, T.a1, T.len1) || run_flagged(w2, w3, T.a2, T.len2);
-    }
-    const int mode_first = key_mode(max(key_first, 0));   // negative keys are masked
-    const int mode_last = key_mode(key_last);
-    const bool masked = count < BN || key_first < 0 || key_last > i0 || mode_first != mode_last;
-    for (int mode = mode_first; mode <= mode_last; ++mode) tile_pass(kt, vt, T, skey, mode, precise, masked);
-  };
+  const Tile T_dummy = {0, 0, BN, 0, 0, 0};   // rows 0..31, for loads past the last tile
 
-  // ---- prologue: tile t_beg staged, descriptor of t_beg+1 in flight
-  int dv_cur = desc_load(t_beg);
-  Tile T_cur = make_tile(t_beg, dv_cur);
-  int sk_cur = -1;
-  uint32_t fw_cur = 0;
-  if (t_beg < t_end) {
-    if (T_cur.cnt) sk_cur = ext_key(T_cur);
-    issue_tile(kst0, vst0, T_cur, sk_cur);
-    if (!T_cur.cnt) fw_cur = flag_load(T_cur);
+  // ---- range tiles [t_beg, r_end), pipelined.  Prologue: K(t0), V(t0),
+  // K(t0+1) in flight, the descriptor of t0+2 requested.
+  const int r_end = min(t_end, n_range);
+  const int t0 = t_beg;
+  Tile T_c = range_tile(t0, desc_load(t0));
+  const Offs f_c = tile_offsets(t0 < r_end ? T_c : T_dummy, -1);
+  issue(rs_k, kst0, f_c);
+  issue(rs_v, vst0, f_c);
+  bool p_c = t0 < r_end && range_precise(T_c);
+  Tile T_n = range_tile(t0 + 1, desc_load(t0 + 1));
+  Offs f_n = tile_offsets(t0 + 1 < r_end ? T_n : T_dummy, -1);
+  issue(rs_k, kst1, f_n);
+  bool p_n = t0 + 1 < r_end && range_precise(T_n);
+  int4 d_2 = desc_load(t0 + 2);
+
+  // One step on range tile ti: its stages kc / vc, and vn, the V stage of tile ti+1.
+  auto step = [&](uint8_t* kc, const uint8_t* vc, uint8_t* vn, int ti) __attribute__((always_inline)) {
+    vm_wait(8);            // K(ti) landed: V(ti) and K(ti+1) were issued after it
+    wg_barrier();          // B1: K(ti) visible; V(ti-1)'s stage is free
+    issue(rs_v, vn, f_n);
+    Tile T_2 = T_dummy;
+    bool p_2 = false;
+    Offs f_2;
+    auto after_qk = [&]() __attribute__((always_inline)) {
+      wg_barrier();        // B2: both waves are done with K(ti)
+      T_2 = range_tile(ti + 2, d_2);
+      f_2 = tile_offsets(ti + 2 < r_end ? T_2 : T_dummy, -1);
+      issue(rs_k, kc, f_2);
+      p_2 = ti + 2 < r_end && range_precise(T_2);
+      d_2 = desc_load(ti + 3);
+    };
+    compute_tile(kc, vc, T_c, -1, p_c, after_qk);
+    T_c = T_n; p_c = p_n;
+    T_n = T_2; p_n = p_2; f_n = f_2;
+  };
+  for (int ti = t_beg; ti < r_end; ti += 2) {
+    step(kst0, vst0, vst1, ti);
+    if (ti + 1 < r_end) step(kst1, vst1, vst0, ti + 1);
   }
-  int dv_nxt = desc_load(t_beg + 1);
-  __syncthreads();
+  // the clamped loads past the last range tile land before the stages are reused
+  vm_wait(0);
+  wg_barrier();
 
-  // One step: prefetch tile ti+1 into the other stage, then compute tile ti.
-  // The other stage was last read before the previous barrier.  Range tiles
-  // issue their loads before any metadata read they would wait for; an
-  // extra-vertical tile needs its keys first (these tiles are few).
-  auto step = [&](const uint8_t* kcur, const uint8_t* vcur, uint8_t* knxt, uint8_t* vnxt, int ti) __attribute__((always_inline)) {
-    Tile T_n;
-    int sk_n = -1;
-    uint32_t fw_n = 0;
-    const bool more = ti + 1 < t_end;
-    if (more) {
-      T_n = make_tile(ti + 1, dv_nxt);
-      if (T_n.cnt) {
-        sk_n = ext_key(T_n);
-        issue_tile(knxt, vnxt, T_n, sk_n);
-      } else {
-        issue_tile(knxt, vnxt, T_n, 0);
-        fw_n = flag_load(T_n);
-      }
-      dv_nxt = desc_load(ti + 2);
-    }
-    compute_tile(kcur, vcur, T_cur, sk_cur, fw_cur);
-    __syncthreads();   // the prefetched stage has landed; this stage may be overwritten next
-    if (more) { T_cur = T_n; sk_cur = sk_n; fw_cur = fw_n; }
-  };
-  for (int ti = t_beg; ti < t_end; ti += 2) {
-    step(kst0, vst0, kst1, vst1, ti);
-    if (ti + 1 < t_end) step(kst1, vst1, kst0, vst0, ti + 1);
+  // ---- extra-vertical tiles (a few per block, after the range tiles): keys,
+  // then K and V, then the tile, one at a time
+  for (int ti = max(t_beg, n_range); ti < t_end; ++ti) {
+    const Tile T = ext_tile(ti);
+    const int sk = ext_key(T);
+    const bool prec = __any(sk >= 0 && ((sk >> 30) & 1));
+    const Offs f = tile_offsets(T, sk);
+    issue(rs_k, kst0, f);
+    issue(rs_v, vst0, f);
+    vm_wait(0);
+    wg_barrier();
+    compute_tile(kst0, vst0, T, sk, prec, [] {});
+    wg_barrier();          // the stage is read; the next tile may overwrite it
   }
 
   // ---- finish: row sum over both halves, normalise, write
