@@ -22,18 +22,23 @@ namespace dca {
 
 
 // Tiles of 32 keys staged in LDS by direct global->LDS loads, two stages.
-// A tile of one tensor is 8 groups of 4 key rows; a group is stored
-// chunk-major ([16-byte chunk][row], 1 KiB) followed by 64 bytes of padding.
-// Each direct load instruction fills one group (lane l: chunk l/4, row l%4).
-// With the padding, the K operand reads (16 rows, one chunk) and the
-// transposed V reads (4 rows, two chunks) of a 16-lane group fall on distinct
-// banks, and every read address is a per-lane base plus an immediate offset.
+// A tile of one tensor is 8 groups of 4 key rows: a group holds its rows one
+// after the other (256 bytes each, 1 KiB) and 64 bytes of padding.  Each
+// direct load instruction fills one group, 16 consecutive lanes per row, so
+// that every 4 lanes read 64 contiguous bytes of one row (the vector memory
+// unit serves such requests several times faster than four rows per 4
+// lanes).  Inside row r of a group the 16-byte chunk c sits at slot
+// c ^ 5(r & 3): with the padding, the K operand reads (16 rows, one chunk)
+// and the transposed V reads (4 rows, four chunks) fall on distinct banks
+// for 32 as for 64 four-byte banks.
 constexpr int BN = 32;
 constexpr int GRPB = 1024 + 64;                // bytes per 4-row group
 constexpr int TILEB = 8 * GRPB;                // one tensor of one tile
 
 // byte offset of (row, 16-byte chunk) inside a tensor tile
-__device__ __forceinline__ int tile_off(int row, int chunk) { return (row >> 2) * GRPB + chunk * 64 + (row & 3) * 16; }
+__device__ __forceinline__ int tile_off(int row, int chunk) {
+  return (row >> 2) * GRPB + (row & 3) * 256 + ((chunk ^ (5 * (row & 3))) << 4);
+}
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -220,13 +225,14 @@ __global__ void __launch_bounds__(128, 2) dca_attn_kernel(AttnArgs A) {
   const __amdgpu_buffer_rsrc_t rs_k = __builtin_amdgcn_make_buffer_rsrc((void*)kh_base, (short)0, -1, 0x00020000);
   const __amdgpu_buffer_rsrc_t rs_v = __builtin_amdgcn_make_buffer_rsrc((void*)v_base, (short)0, -1, 0x00020000);
   const int rowb = kstride * 2;
-  const int lane3 = lane & 3;
+  const int lrow = lane >> 4;                       // row of a load's group this lane fills
+  const int lchunk = 16 * ((lane & 15) ^ (5 * lrow));  // byte offset of the chunk it reads
   // byte offset of load j's row inside a tile of consecutive keys, plus the lane's chunk
   unsigned roff[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) roff[j] = (unsigned)((4 * (2 * j + wave) + lane3) * rowb + 16 * (lane >> 2));
+  for (int j = 0; j < 4; ++j) roff[j] = (unsigned)((4 * (2 * j + wave) + lrow) * rowb + lchunk);
   // Row offsets of a tile's direct loads: load j of wave w fills rows
-  // 4(2j + w) .. +3 of the tile (lane: row lane & 3, 16-byte chunk lane >> 2).
+  // 4(2j + w) .. +3 of the tile (lane: row lane >> 4, chunk (lane & 15) ^ 5(lane >> 4)).
   struct Offs { int v[4]; };
   auto tile_offsets = [&](Tile T, int skey) __attribute__((always_inline)) -> Offs {
     Offs f;
@@ -235,12 +241,12 @@ __global__ void __launch_bounds__(128, 2) dca_attn_kernel(AttnArgs A) {
       // extra-vertical tiles and tiles reaching outside [0, n_k): clamped keys
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int r = 4 * (2 * j + wave) + lane3;
+        const int r = 4 * (2 * j + wave) + lrow;
         int key;
         if (T.cnt) key = __shfl(skey, r) & 0x3FFFFFFF;
         else key = (r < T.len1 ? T.a1 : T.a2 - T.len1) + r;   // slots past the count are masked later
         key = min(max(key, 0), A.n_k - 1);
-        f.v[j] = __umul24((unsigned)key, (unsigned)rowb) + 16 * (lane >> 2);
+        f.v[j] = __umul24((unsigned)key, (unsigned)rowb) + lchunk;
       }
     } else if (T.len2 == 0) {
       const unsigned base = (unsigned)T.a1 * (unsigned)rowb;
@@ -252,7 +258,7 @@ __global__ void __launch_bounds__(128, 2) dca_attn_kernel(AttnArgs A) {
       const unsigned gap = (unsigned)(T.a2 - T.a1 - T.len1) * (unsigned)rowb;
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        f.v[j] = (int)(base + roff[j] + (lane3 >= T.len1 - 4 * (2 * j + wave) ? gap : 0u));
+        f.v[j] = (int)(base + roff[j] + (lrow >= T.len1 - 4 * (2 * j + wave) ? gap : 0u));
     }
     return f;
   };
