@@ -100,7 +100,11 @@ __global__ void __launch_bounds__(128, 2) dca_attn_kernel(AttnArgs A) {
     const int rows = (A.nb + dpg - 1) / dpg;       // block rows of this die
     part = local / (rows * hpg);
     const int rem = local % (rows * hpg);
-    const int cidx = dpg * (rem % rows) + die / A.h_kv;
+    // split calls: each die takes a contiguous half of the block rows (the
+    // halves swap with the part), so the rows in flight on a die are adjacent
+    // and read nearly the same keys; one part: rows interleave (balance)
+    const int sub = die / A.h_kv;
+    const int cidx = A.split > 1 ? ((sub + part) % dpg) * rows + rem % rows : dpg * (rem % rows) + sub;
     if (cidx >= A.nb) return;
     b = A.nb - 1 - cidx;
     h = ((die + part) % A.h_kv) * hpg + rem / rows;
