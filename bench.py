@@ -277,7 +277,7 @@ def main() -> int:
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
-            "kernel": "dca_attn_kernel",
+            "kernel": "dca_attn_kernel" if w.sparse else "dca_attn_dense_kernel",
             "avg_launch_ms": round(attn_avg_ms, 4),
             "algorithmic_flops_per_launch": f_per_launch,
         },

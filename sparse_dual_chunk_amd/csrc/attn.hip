@@ -67,7 +67,8 @@ __device__ __forceinline__ int range_key(Tile T, int t) {
   return t < T.len1 ? T.a1 + t : (t < T.len1 + T.len2 ? T.a2 + (t - T.len1) : -1);
 }
 
-__global__ void __launch_bounds__(128, 2) dca_attn_kernel(AttnArgs A) {
+template <bool DENSE>
+__device__ __forceinline__ void attn_body(const AttnArgs& A) {
   // K and V of the two stages are four LDS objects: the compiler then tells
   // the reads of one stage from the direct loads in flight into the other
   // and places no wait for those loads inside the tile's computation
@@ -133,10 +134,10 @@ __global__ void __launch_bounds__(128, 2) dca_attn_kernel(AttnArgs A) {
 
   const int unit = h * A.nb + b;
   const int* tl_h = (const int*)(A.tiles + (long long)h * A.tile_stride);
-  const int t_first = A.dense ? 0 : A.t_first[unit];
-  const int n_range = A.dense ? (hi_key + BN - 1) / BN : A.n_tiles[h] - t_first;
+  const int t_first = DENSE ? 0 : A.t_first[unit];
+  const int n_range = DENSE ? (hi_key + BN - 1) / BN : A.n_tiles[h] - t_first;
   const int32_t* ext_h = A.ext + (long long)unit * A.ext_stride;
-  const int n_ext = A.dense ? 0 : A.n_ext[unit];
+  const int n_ext = DENSE ? 0 : A.n_ext[unit];
   const int n_all = n_range + (n_ext + BN - 1) / BN;
   const int t_beg = (int)((long long)n_all * part / A.split);
   const int t_end = (int)((long long)n_all * (part + 1) / A.split);
@@ -183,14 +184,14 @@ __global__ void __launch_bounds__(128, 2) dca_attn_kernel(AttnArgs A) {
   ci32* tl4 = (ci32*)(A.tiles + (long long)h * A.tile_stride);
   cu32* kb4 = (cu32*)kb;
   auto desc_load = [&](int idx) __attribute__((always_inline)) -> int4 {
-    if (A.dense || idx >= n_range || idx >= t_end) return make_int4(0, 0, 0, 0);
+    if (DENSE || idx >= n_range || idx >= t_end) return make_int4(0, 0, 0, 0);
     ci32* d = tl4 + 4 * (t_first + idx);
     return make_int4(d[0], d[1], d[2], d[3]);
   };
   auto range_tile = [&](int idx, int4 d) __attribute__((always_inline)) -> Tile {
     Tile T;
     T.eoff = 0; T.cnt = 0;
-    if (A.dense) {
+    if (DENSE) {
       T.a1 = BN * idx;
       T.len1 = min(BN, hi_key - T.a1);
       T.a2 = 0; T.len2 = 0;
@@ -238,11 +239,14 @@ __global__ void __launch_bounds__(128, 2) dca_attn_kernel(AttnArgs A) {
   // Row offsets of a tile's direct loads: load j of wave w fills rows
   // 4(2j + w) .. +3 of the tile (lane: row lane >> 4, chunk (lane & 15) ^ 5(lane >> 4)).
   struct Offs { int v[4]; };
-  auto tile_offsets = [&](Tile T, int skey) __attribute__((always_inline)) -> Offs {
+  // Rows past a tile's count read the keys after its last run; together with
+  // negative keys (only in a block's first range tile) they can leave
+  // [0, n_k) only in the prologue's tiles and in blocks within 95 keys of the
+  // end: there, and for extra-vertical tiles, keys are clamped.
+  const bool clamp_all = 64 * b + 95 >= A.n_q;
+  auto tile_offsets = [&](Tile T, int skey, bool clamp) __attribute__((always_inline)) -> Offs {
     Offs f;
-    const int last_key = (T.len2 ? T.a2 - T.len1 : T.a1) + BN - 1;   // key read by slot 31
-    if (T.cnt || T.a1 < 0 || last_key >= A.n_k) {
-      // extra-vertical tiles and tiles reaching outside [0, n_k): clamped keys
+    if (clamp || T.cnt) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int r = 4 * (2 * j + wave) + lrow;
@@ -433,20 +437,25 @@ __global__ void __launch_bounds__(128, 2) dca_attn_kernel(AttnArgs A) {
     // and K(t+2)); barrier
     vm_wait(12);
     wg_barrier();
-    // ---- O^T += V^T P^T, V^T operand read transposed from the row-major V tile
+    // ---- O^T += V^T P^T, V^T operand read transposed from the row-major V tile.
+    // All 8 reads of a 16-key half are issued before its 4 MFMAs, so their
+    // latency overlaps instead of stalling every MFMA.
 #pragma unroll
     for (int G = 0; G < 2; ++G) {
       const int r1 = 16 * G + 4 * half + (s16 >> 2);
       const int r2 = r1 + 8;
+      bf16x8 a[4];
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
         const int c = 4 * db + 2 * grp + ((s16 & 3) >> 1);     // 16-byte chunk of the 4 columns read
         const int bo = 8 * (s16 & 1);                           // byte offset inside the chunk
         const bf16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, vt + tile_off(r1, c) + bo));
         const bf16x4 t2 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, vt + tile_off(r2, c) + bo));
-        const bf16x8 a = __builtin_shufflevector(t1, t2, 0, 1, 2, 3, 4, 5, 6, 7);
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[G], o[db], 0, 0, 0);
+        a[db] = __builtin_shufflevector(t1, t2, 0, 1, 2, 3, 4, 5, 6, 7);
       }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int db = 0; db < 4; ++db) o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[db], pf[G], o[db], 0, 0, 0);
     }
   };
 
@@ -457,12 +466,12 @@ __global__ void __launch_bounds__(128, 2) dca_attn_kernel(AttnArgs A) {
   const int r_end = min(t_end, n_range);
   const int t0 = t_beg;
   Tile T_c = range_tile(t0, desc_load(t0));
-  const Offs f_c = tile_offsets(t0 < r_end ? T_c : T_dummy, -1);
+  const Offs f_c = tile_offsets(t0 < r_end ? T_c : T_dummy, -1, true);
   issue(rs_k, kst0, f_c);
   issue(rs_v, vst0, f_c);
   bool p_c = t0 < r_end && range_precise(T_c);
   Tile T_n = range_tile(t0 + 1, desc_load(t0 + 1));
-  Offs f_n = tile_offsets(t0 + 1 < r_end ? T_n : T_dummy, -1);
+  Offs f_n = tile_offsets(t0 + 1 < r_end ? T_n : T_dummy, -1, true);
   issue(rs_k, kst1, f_n);
   bool p_n = t0 + 1 < r_end && range_precise(T_n);
   int4 d_2 = desc_load(t0 + 2);
@@ -478,7 +487,7 @@ __global__ void __launch_bounds__(128, 2) dca_attn_kernel(AttnArgs A) {
     auto after_qk = [&]() __attribute__((always_inline)) {
       wg_barrier();        // B2: both waves are done with K(ti)
       T_2 = range_tile(ti + 2, d_2);
-      f_2 = tile_offsets(ti + 2 < r_end ? T_2 : T_dummy, -1);
+      f_2 = tile_offsets(ti + 2 < r_end ? T_2 : T_dummy, -1, clamp_all);
       issue(rs_k, kc, f_2);
       p_2 = ti + 2 < r_end && range_precise(T_2);
       d_2 = desc_load(ti + 3);
@@ -501,7 +510,7 @@ __global__ void __launch_bounds__(128, 2) dca_attn_kernel(AttnArgs A) {
     const Tile T = ext_tile(ti);
     const int sk = ext_key(T);
     const bool prec = __any(sk >= 0 && ((sk >> 30) & 1));
-    const Offs f = tile_offsets(T, sk);
+    const Offs f = tile_offsets(T, sk, true);
     issue(rs_k, kst0, f);
     issue(rs_v, vst0, f);
     vm_wait(0);
@@ -547,6 +556,10 @@ __global__ void __launch_bounds__(128, 2) dca_attn_kernel(AttnArgs A) {
   }
 }
 
+// sparse (vertical-slash) calls and dense calls: one body, the dense tile walk known at compile time
+__global__ void __launch_bounds__(128, 2) dca_attn_kernel(AttnArgs A) { attn_body<false>(A); }
+__global__ void __launch_bounds__(128, 2) dca_attn_dense_kernel(AttnArgs A) { attn_body<true>(A); }
+
 // LSE merge of split partials: m = max lse_p, O = sum e^{lse_p-m} O_p / sum e^{lse_p-m}.
 __global__ void __launch_bounds__(256) lse_merge_kernel(const float* __restrict__ part_o,
                                                         const float* __restrict__ part_lse,
@@ -584,7 +597,11 @@ hipError_t launch_attn(const AttnArgs& A, hipStream_t stream) {
   const int blocks = NXCD % A.h_kv == 0
       ? NXCD * A.split * ((A.nb + NXCD / A.h_kv - 1) / (NXCD / A.h_kv)) * (A.h_q / A.h_kv)
       : NXCD * A.split * ((A.nb + NXCD - 1) / NXCD) * A.h_q;
-  hipLaunchKernelGGL(dca_attn_kernel, dim3(blocks), dim3(128), 0, stream, A);
+  if (A.dense) {
+    hipLaunchKernelGGL(dca_attn_dense_kernel, dim3(blocks), dim3(128), 0, stream, A);
+  } else {
+    hipLaunchKernelGGL(dca_attn_kernel, dim3(blocks), dim3(128), 0, stream, A);
+  }
   return hipGetLastError();
 }
 
