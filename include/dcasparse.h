@@ -96,7 +96,8 @@ typedef struct dca_cfg {
                              blocks; 4 * head_dim * cover_pairs is the computed-block FLOP count.  NULL: not written */
   float   precise_norm;   /* keys whose L2 norm exceeds this get split-bf16 (hi+lo) logits;
                              0: default 2*sqrt(head_dim); < 0: never */
-  int32_t split_k;        /* key-range splits per query block, merged by LSE: 0 = library's choice */
+  int32_t split_k;        /* key-range splits per query block (0..256), merged by LSE: 0 = library's
+                             choice (about one split per 16K keys, at most 64) */
   void   *workspace;      /* device scratch, >= dca_workspace_size bytes, 256-byte aligned */
   size_t  workspace_bytes;
   void   *stream;         /* hipStream_t; NULL = the null stream */

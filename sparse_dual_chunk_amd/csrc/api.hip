@@ -65,7 +65,7 @@ int validate(const dca_cfg* c, const int32_t* positions) {
   if (!(c->yarn_s > 0.0) || !std::isfinite(c->yarn_s)) return DCA_EINVAL;
   if (c->vs_k_vertical < 0 || c->vs_k_slash < 0) return DCA_EINVAL;
   if (c->vs_last_q < 1 || c->vs_last_q > 64) return DCA_EUNSUPPORTED;
-  if (c->split_k < 0 || c->split_k > 64) return DCA_EINVAL;
+  if (c->split_k < 0 || c->split_k > 256) return DCA_EINVAL;
   if (!std::isfinite(c->precise_norm)) return DCA_EINVAL;
   // the chunk of rows must be the tail of the prefix, starting on a 64 boundary
   const long long p0 = (long long)c->n_k - c->n_q;
@@ -91,13 +91,13 @@ Layout make_layout(const dca_cfg* c) {
     L.split = c->split_k;
   } else {
     // enough independent work items to fill 256 compute units several times
-    // over, and key shares of about 32K keys: the attention workgroups run
+    // over, and key shares of about 16K keys: the attention workgroups run
     // split part by split part, so the keys read by the work in flight stay
-    // within one share (32K keys of K and V per KV head: 16 MiB) and are
-    // served from the dies' caches instead of memory
+    // within one share (16K keys of K and V per KV head: 8 MiB) and are
+    // served from the dies' caches rather than memory
     L.split = 1;
     while (units * L.split < 2048 && L.split < 16) L.split *= 2;
-    const int by_keys = (int)std::min<long long>(32, ((long long)n_k + 32767) / 32768);
+    const int by_keys = (int)std::min<long long>(64, ((long long)n_k + 16383) / 16384);
     L.split = std::max(L.split, by_keys);
     const int tiles = (n_k + 63) / 64;
     while (L.split > 1 && L.split > tiles) L.split /= 2;
