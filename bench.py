@@ -87,7 +87,7 @@ def traffic_from_profile(units_per_launch: float):
 
 
 def cpu_baseline(w, inputs, p0s, f_blocks_total: float, n_blocks_total: int):
-    """Oracle timing on a bounded sample (about 10 s): index scores of two heads, attention of
+    """Oracle timing on a bounded sample (about 10-15 s): index scores of three heads, attention of
     four query blocks of one head."""
     from oracle import dca_oracle as O
     try:
@@ -102,8 +102,8 @@ def cpu_baseline(w, inputs, p0s, f_blocks_total: float, n_blocks_total: int):
     v_idx = s_off = None
     t_index_head = 0.0
     if w.sparse:
-        v_idx, s_off, _ = O.vs_index(inp["q"], inp["k"], inp["p0"], cfg, heads=[0, 1])
-        t_index_head = (time.perf_counter() - t0) / 2
+        v_idx, s_off, _ = O.vs_index(inp["q"], inp["k"], inp["p0"], cfg, heads=[0, 1, 2])
+        t_index_head = (time.perf_counter() - t0) / 3
     nb = (inp["n_q"] + 63) // 64
     blocks = [nb - 1, (3 * nb) // 4, nb // 2, nb // 4]
     t1 = time.perf_counter()
@@ -121,7 +121,7 @@ def cpu_baseline(w, inputs, p0s, f_blocks_total: float, n_blocks_total: int):
         "unit": "TFLOP/s",
         "cores": int(cores),
         "kind": "oracle",
-        "sample": (f"fp64 oracle on the host: index scores of query heads 0-1 of the last chunk "
+        "sample": (f"fp64 oracle on the host: index scores of query heads 0-2 of the last chunk "
                    f"({t_index_head:.1f} s per head) and attention of query blocks {blocks} of head 0 "
                    f"({t_att:.1f} s, {fb_sample / 1e9:.1f} GFLOP); step time extrapolated to "
                    f"{w.h_q} heads x {n_calls} call(s) and to F_blocks"),
