@@ -13,6 +13,8 @@ namespace dca {
 hipError_t launch_rotate_keys(const uint16_t* k, uint16_t* khi, uint16_t* klo, uint32_t* kbits,
                               const double* inv_freq, int n_k, int h_kv, int S, float thr2, int kbits_words,
                               hipStream_t stream);
+hipError_t launch_hn_next(const uint32_t* kbits, uint8_t* hn, int n_pad, int h_kv, int kbits_words,
+                          hipStream_t stream);
 hipError_t launch_rotate_queries(const uint16_t* q, uint16_t* qhi, uint16_t* qlo, const double* inv_freq,
                                  int n_q, int h_q, int p0, int S, int W, float qscale, hipStream_t stream);
 hipError_t launch_attn(const AttnArgs& A, hipStream_t stream);
@@ -43,11 +45,11 @@ struct Layout {
   // shared
   Region freqs;
   // prefill
-  Region khi, klo, kbits, qhi, qlo, iv, iv_pre, n_iv, cov, ext, n_ext, tiles, n_tiles, t_first, part_o, part_lse;
+  Region khi, klo, kbits, hn, qhi, qlo, iv, iv_pre, n_iv, cov, ext, n_ext, tiles, n_tiles, t_first, part_o, part_lse;
   // index
   Region qs, part_ms, lse, vert, slash, edge, hist, prefix, krem, bcount;
   size_t prefill_bytes = 0, index_bytes = 0;
-  int split = 1, nb = 0, n_ranges = 0, range_keys = 0, cov_words = 0, max_blocks = 0, kbits_words = 0,
+  int split = 1, nb = 0, n_ranges = 0, range_keys = 0, cov_words = 0, max_blocks = 0, kbits_words = 0, hn_pad = 0,
       tile_stride = 0;
 };
 
@@ -94,10 +96,11 @@ Layout make_layout(const dca_cfg* c) {
     // over, and key shares of about 16K keys: the attention workgroups run
     // split part by split part, so the keys read by the work in flight stay
     // within one share (16K keys of K and V per KV head: 8 MiB) and are
-    // served from the dies' caches rather than memory
+    // served from the dies' caches rather than memory (from 64K keys on;
+    // below that the keys fit the caches whole)
     L.split = 1;
     while (units * L.split < 2048 && L.split < 16) L.split *= 2;
-    const int by_keys = (int)std::min<long long>(64, ((long long)n_k + 16383) / 16384);
+    const int by_keys = n_k < 65536 ? 1 : (int)std::min<long long>(64, ((long long)n_k + 16383) / 16384);
     L.split = std::max(L.split, by_keys);
     const int tiles = (n_k + 63) / 64;
     while (L.split > 1 && L.split > tiles) L.split /= 2;
@@ -110,6 +113,8 @@ Layout make_layout(const dca_cfg* c) {
   place(L.klo, cur, (size_t)n_k * h_kv * D * 2);
   L.kbits_words = (n_k + 31) / 32 + 4;   // guard words: a tile reads the two words of each run
   place(L.kbits, cur, (size_t)h_kv * L.kbits_words * 4);
+  L.hn_pad = (n_k + 128 + 3) / 4 * 4;   // runs may start up to 95 keys past n_k - 1
+  place(L.hn, cur, (size_t)h_kv * L.hn_pad);
   place(L.qhi, cur, (size_t)3 * n_q * h_q * D * 2);
   place(L.qlo, cur, (size_t)3 * n_q * h_q * D * 2);
   place(L.iv, cur, (size_t)h_q * (c->vs_k_slash + 1) * 2 * 4);
@@ -262,6 +267,9 @@ int dca_sparse_prefill(const dca_bf16* q, const dca_bf16* k, const dca_bf16* v, 
   if (launch_rotate_keys(k, at<uint16_t>(cfg, L.khi), at<uint16_t>(cfg, L.klo), at<uint32_t>(cfg, L.kbits),
                          at<double>(cfg, L.freqs), n_k, h_kv, cfg->dca_chunk, thr2, L.kbits_words, st) != hipSuccess)
     return DCA_EHIP;
+  if (launch_hn_next(at<uint32_t>(cfg, L.kbits), at<uint8_t>(cfg, L.hn), L.hn_pad, h_kv, L.kbits_words, st) !=
+      hipSuccess)
+    return DCA_EHIP;
   // softmax scale sqrt(1/t)^2 / sqrt(d) and log2(e) (the kernel works in base 2)
   const float qscale = (float)(yarn_factor(cfg->yarn_s) / std::sqrt((double)D) * 1.4426950408889634);
   if (launch_rotate_queries(q, at<uint16_t>(cfg, L.qhi), at<uint16_t>(cfg, L.qlo), at<double>(cfg, L.freqs), n_q,
@@ -299,7 +307,7 @@ int dca_sparse_prefill(const dca_bf16* q, const dca_bf16* k, const dca_bf16* v, 
   AttnArgs A;
   A.qhi = at<uint16_t>(cfg, L.qhi); A.qlo = at<uint16_t>(cfg, L.qlo);
   A.khi = at<uint16_t>(cfg, L.khi); A.klo = at<uint16_t>(cfg, L.klo); A.v = v;
-  A.kbits = at<uint32_t>(cfg, L.kbits);
+  A.kbits = at<uint32_t>(cfg, L.kbits); A.hn = at<uint8_t>(cfg, L.hn); A.hn_pad = L.hn_pad;
   A.out = out; A.lse_out = cfg->lse_out;
   A.part_o = L.split > 1 ? at<float>(cfg, L.part_o) : nullptr;
   A.part_lse = L.split > 1 ? at<float>(cfg, L.part_lse) : nullptr;

@@ -12,6 +12,7 @@ struct AttnArgs {
   const uint16_t* klo;      // same, lo residual
   const uint16_t* v;        // [n_k][h_kv][128]
   const uint32_t* kbits;    // [h_kv][kbits_words] bit j: key j is high-norm (split-precision logits)
+  const uint8_t* hn;        // [h_kv][hn_pad] distance from key j to the next high-norm key, capped at 64
   uint16_t* out;            // [n_q][h_q][128]
   float* lse_out;           // [h_q][n_q] or null
   float* part_o;            // [P][n_q][h_q][128] (P > 1)
@@ -21,7 +22,7 @@ struct AttnArgs {
   const int32_t* t_first;   // [h_q][nb] first range tile of each query block
   const int32_t* ext;       // [h_q][nb][ext_stride] vertical keys outside the ranges (bit 30: high-norm)
   const int32_t* n_ext;     // [h_q][nb]
-  int n_q, n_k, h_q, h_kv, p0, S, W, nb, tile_stride, ext_stride, split, dense, kbits_words;
+  int n_q, n_k, h_q, h_kv, p0, S, W, nb, tile_stride, ext_stride, split, dense, kbits_words, hn_pad;
 };
 
 struct VsArgs {

@@ -146,7 +146,6 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A) {
   const uint16_t* kh_base = A.khi + g * D;
   const uint16_t* kl_base = A.klo + g * D;
   const uint16_t* v_base = A.v + g * D;
-  const uint32_t* kb = A.kbits + (long long)g * A.kbits_words;
   const int grp = l32 >> 4;       // which 16-wide d slice of a 32-d block (transposed V reads)
   const int s16 = lane & 15;
 
@@ -182,7 +181,6 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A) {
   typedef __attribute__((address_space(4))) const int ci32;
   typedef __attribute__((address_space(4))) const uint32_t cu32;
   ci32* tl4 = (ci32*)(A.tiles + (long long)h * A.tile_stride);
-  cu32* kb4 = (cu32*)kb;
   auto desc_load = [&](int idx) __attribute__((always_inline)) -> int4 {
     if (DENSE || idx >= n_range || idx >= t_end) return make_int4(0, 0, 0, 0);
     ci32* d = tl4 + 4 * (t_first + idx);
@@ -210,15 +208,16 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A) {
     T.cnt = min(BN, n_ext - T.eoff);
     return T;
   };
-  // a run [a, a + len) holds a high-norm key: bit test on the two bitmap words
-  // that hold it (the bitmap has guard words past n_k)
+  // a run [a, a + len) holds a high-norm key: the distance from its first
+  // (non-negative) key to the next high-norm key is below its length (one
+  // byte of the distance table, read through the scalar cache as its dword)
+  cu32* hn4 = (cu32*)(A.hn + (long long)g * A.hn_pad);
   auto run_flagged = [&](int a, int len) __attribute__((always_inline)) -> bool {
     const int ac = max(a, 0);
     const int lc = len - (ac - a);
     if (lc <= 0) return false;
-    const int w = ac >> 5;
-    const uint64_t bits = (((uint64_t)kb4[w + 1] << 32) | kb4[w]) >> (ac & 31);
-    return (bits & ((1ull << lc) - 1)) != 0;
+    const int d = (int)((hn4[ac >> 2] >> (8 * (ac & 3))) & 0xFFu);
+    return d < lc;
   };
   auto range_precise = [&](Tile T) __attribute__((always_inline)) -> bool {
     return run_flagged(T.a1, T.len1) || run_flagged(T.a2, T.len2);

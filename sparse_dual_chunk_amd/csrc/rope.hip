@@ -137,6 +137,38 @@ hipError_t launch_rotate_queries(const uint16_t* q, uint16_t* qhi, uint16_t* qlo
   return hipGetLastError();
 }
 
+// hn[g][j] = distance from key j to the next high-norm key of KV head g,
+// capped at 64 (a run [a, a+len) of len <= 32 holds one iff hn[a] < len).
+// Entries j < n_pad (n_pad = the padded row count, a multiple of 4); the
+// bitmap has guard words past n_k, so the three words read stay inside.
+__global__ void __launch_bounds__(256) hn_next_kernel(const uint32_t* __restrict__ kbits, uint8_t* __restrict__ hn,
+                                                      int n_pad, int h_kv, int kbits_words) {
+  const long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= (long long)h_kv * n_pad) return;
+  const int g = (int)(e / n_pad);
+  const int j = (int)(e % n_pad);
+  const uint32_t* kb = kbits + (long long)g * kbits_words;
+  const int w = j >> 5;
+  int d = 64;
+  if (w < kbits_words) {
+    // bits j .. j+63 of the bitmap, as a 96-bit window starting at word w
+    const uint64_t lo = (uint64_t)kb[w] | ((uint64_t)(w + 1 < kbits_words ? kb[w + 1] : 0u) << 32);
+    const uint32_t hi = w + 2 < kbits_words ? kb[w + 2] : 0u;
+    const int sh = j & 31;
+    const uint64_t win = (lo >> sh) | (sh ? ((uint64_t)hi << (64 - sh)) : 0ull);
+    if (win) d = min(64, __builtin_ctzll(win));
+  }
+  hn[e] = (uint8_t)d;
+}
+
+hipError_t launch_hn_next(const uint32_t* kbits, uint8_t* hn, int n_pad, int h_kv, int kbits_words,
+                          hipStream_t stream) {
+  const long long n = (long long)h_kv * n_pad;
+  hipLaunchKernelGGL(hn_next_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, kbits, hn, n_pad, h_kv,
+                     kbits_words);
+  return hipGetLastError();
+}
+
 hipError_t launch_rotate_keys(const uint16_t* k, uint16_t* khi, uint16_t* klo, uint32_t* kbits,
                               const double* inv_freq, int n_k, int h_kv, int S, float thr2, int kbits_words,
                               hipStream_t stream) {
