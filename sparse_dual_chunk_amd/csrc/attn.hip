@@ -153,6 +153,8 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) o[i] = f32x16{};
   float m_run = 0.f;         // reference max (log2 domain) of this row
+  f32x16 negm = {};          // -m_run in every entry: the S^T MFMAs start from it, so the
+                             // scores come out already shifted by the reference max
   bool started = false;      // the row has met a key
   float l_run = 0.f;         // this lane's partial row sum
   // rotated query row of this lane for the current DCA mode: the hi half is
@@ -318,7 +320,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A) {
     if (mode != q_mode) load_q(mode);
     // 32 keys x 32 rows of this wave (scores in log2 units)
     f32x16 s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(kt + tile_off(l32, half)), qh[0],
-                                                       f32x16{}, 0, 0, 0);
+                                                       negm, 0, 0, 0);
 #pragma unroll
     for (int kk = 1; kk < 8; ++kk) {
       const bf16x8 a = *(const bf16x8*)(kt + tile_off(l32, 2 * kk + half));
@@ -401,28 +403,34 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A) {
       select_slots(s, t_lo, t_hi, -INFINITY);
     }
     after_qk();
-    // ---- online softmax (log2 domain).  The reference max moves only when a
-    // score exceeds it by more than 8 (so p <= 2^8), or at the row's first keys.
+    // ---- online softmax (log2 domain; s already holds score - m_run).  The
+    // reference max moves only when a score exceeds it by more than 8 (so
+    // p <= 2^8), or at the row's first keys.
     float mx = fmaxf(fmaxf(s[0], s[1]), s[2]);
 #pragma unroll
     for (int vv = 3; vv < 15; vv += 2) mx = fmaxf(fmaxf(mx, s[vv]), s[vv + 1]);
     mx = fmaxf(mx, s[15]);
     mx = pair_max(mx);
-    const bool need = (mx > m_run + 8.f) || (!started && mx != -INFINITY);
+    const bool need = (mx > 8.f) || (!started && mx != -INFINITY);
     if (__any(need)) {
-      const float m_new = need ? mx : m_run;
-      const float alpha = started ? fast_exp2(m_run - m_new) : 0.f;
+      const float shift = need ? mx : 0.f;
+      const float alpha = started ? fast_exp2(-shift) : 0.f;
       l_run *= alpha;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int vv = 0; vv < 16; ++vv) o[i][vv] *= alpha;
-      m_run = m_new;
+      m_run += shift;
+#pragma unroll
+      for (int vv = 0; vv < 16; ++vv) {
+        s[vv] -= shift;
+        negm[vv] = -m_run;
+      }
     }
     started = started || (mx != -INFINITY);
     bf16x8 pf[2];
 #pragma unroll
-    for (int vv = 0; vv < 16; ++vv) pf[vv >> 3][vv & 7] = (__bf16)fast_exp2(s[vv] - m_run);
+    for (int vv = 0; vv < 16; ++vv) pf[vv >> 3][vv & 7] = (__bf16)fast_exp2(s[vv]);
     // row sum of the bf16 weights that enter P V (pairs summed by dot products)
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
