@@ -34,6 +34,7 @@ struct VsArgs {
   double* vert;              // [h_q][n_k]
   double* slash;             // [h_q][n_off], n_off = p_last + 1
   double* edge;              // [h_q][n_ranges][2][64][2] double-double partial diagonals at range edges
+  double* logits;            // [h_q][64][n_k] scaled logits of pass 1 (read back by pass 2)
   int n_k, h_q, h_kv, S, n_s, p_first, range_keys, n_ranges, n_off;
   double scale;
 };

@@ -105,6 +105,8 @@ __global__ void __launch_bounds__(256) vs_pass_kernel(VsArgs A) {
   }
 
   for (int t0 = kr0; t0 < kr1; t0 += SUB) {
+    f64x4 acc[2];
+    if constexpr (PASS == 1) {
     // ---- rotate 32 keys into LDS (fp64): one direct sincos per 8 keys, then angle addition
     {
       const int j0 = t0 + 8 * kg;
@@ -138,7 +140,6 @@ __global__ void __launch_bounds__(256) vs_pass_kernel(VsArgs A) {
     __syncthreads();
 
     // ---- logits for 16 rows x 32 keys per wave
-    f64x4 acc[2];
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
       acc[nb] = f64x4{0.0, 0.0, 0.0, 0.0};
@@ -146,6 +147,15 @@ __global__ void __launch_bounds__(256) vs_pass_kernel(VsArgs A) {
       for (int ks = 0; ks < 32; ++ks) {
         const double bop = sm.kt[(16 * nb + (lane & 15)) * KPD + 4 * ks + kd];
         acc[nb] = __builtin_amdgcn_mfma_f64_16x16x4f64(qa[ks], bop, acc[nb], 0, 0, 0);
+      }
+    }
+    } else {
+      // pass 2 reads the scaled logits pass 1 stored (16 lanes: 128 contiguous bytes)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const int j = min(t0 + 16 * nb + (lane & 15), A.n_k - 1);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[nb][v] = A.logits[((long long)h * 64 + 16 * wave + kd + 4 * v) * A.n_k + j];
       }
     }
 
@@ -157,8 +167,9 @@ __global__ void __launch_bounds__(256) vs_pass_kernel(VsArgs A) {
         for (int v = 0; v < 4; ++v) {
           const int crow = 16 * wave + kd + 4 * v;
           const int p = A.p_first + crow;
+          const double l = A.scale * acc[nb][v];
+          if (j < A.n_k) A.logits[((long long)h * 64 + crow) * A.n_k + j] = l;
           if (crow < A.n_s && j <= p && j < A.n_k) {
-            const double l = A.scale * acc[nb][v];
             if (l > row_m[v] + 200.0) {
               row_s[v] = (row_m[v] == -INFINITY) ? 0.0 : row_s[v] * exp(row_m[v] - l);
               row_m[v] = l;
@@ -178,7 +189,7 @@ __global__ void __launch_bounds__(256) vs_pass_kernel(VsArgs A) {
           const int crow = 16 * wave + kd + 4 * v;
           const int p = A.p_first + crow;
           double a = 0.0;
-          if (crow < A.n_s && j <= p && j < A.n_k) a = exp(A.scale * acc[nb][v] - lse_v[v]);
+          if (crow < A.n_s && j <= p && j < A.n_k) a = exp(acc[nb][v] - lse_v[v]);
           sm.at[crow * APD + jj] = a;
         }
       }
