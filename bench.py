@@ -88,7 +88,7 @@ def traffic_from_profile(units_per_launch: float):
 
 def cpu_baseline(w, inputs, p0s, f_blocks_total: float, n_blocks_total: int):
     """Oracle timing on a bounded sample (about 10-15 s): index scores of three heads, attention of
-    four query blocks of one head."""
+    five query blocks of one head."""
     from oracle import dca_oracle as O
     try:
         from threadpoolctl import threadpool_info
@@ -105,7 +105,7 @@ def cpu_baseline(w, inputs, p0s, f_blocks_total: float, n_blocks_total: int):
         v_idx, s_off, _ = O.vs_index(inp["q"], inp["k"], inp["p0"], cfg, heads=[0, 1, 2])
         t_index_head = (time.perf_counter() - t0) / 3
     nb = (inp["n_q"] + 63) // 64
-    blocks = [nb - 1, (3 * nb) // 4, nb // 2, nb // 4]
+    blocks = sorted({nb - 1, (3 * nb) // 4, nb // 2, nb // 4, nb // 8}, reverse=True)
     t1 = time.perf_counter()
     fb_sample = 0
     for b in blocks:
