@@ -137,8 +137,11 @@ __global__ void sel_scan_kernel(SelArgs A) {
 }
 
 // Write selected indices in ascending order; the first block of each list pads with -1.
+// Each wave owns a contiguous quarter of the block's elements and walks it 64
+// at a time (coalesced reads); ballots give every lane the number of selected
+// elements before it.  A pass of counts first gives each wave its start.
 __global__ void __launch_bounds__(256) sel_write_kernel(SelArgs A) {
-  __shared__ uint32_t sg[256], se[256];
+  __shared__ uint32_t wcg[4], wce[4];
   const int list = blockIdx.y;
   const double* s; int32_t* out; int n, k, f;
   sel_list(A, list, s, out, n, k, f);
@@ -146,43 +149,48 @@ __global__ void __launch_bounds__(256) sel_write_kernel(SelArgs A) {
   const int beg = blockIdx.x * SEL_CHUNK;
   const bool all = (k >= n);
   const uint64_t T = A.prefix[list];
-  const int need_eq = all ? 0 : A.krem[list];
+  const uint32_t need_eq = all ? 0u : (uint32_t)A.krem[list];
   if (blockIdx.x == 0) {
     for (int i = min(k, n) + threadIdx.x; i < k; i += 256) out[i] = -1;
   }
   if (beg >= n) return;
   const int end = min(n, beg + SEL_CHUNK);
-  const uint32_t* bc = A.bcount + ((long long)list * A.max_blocks + blockIdx.x) * 2;
-  uint32_t run_g = bc[0], run_e = bc[1];
-  // each thread owns a contiguous run of 32 elements so that index order is kept
-  const int per = SEL_CHUNK / 256;
-  const int my0 = beg + threadIdx.x * per;
-  uint32_t tg = 0, te = 0;
-  for (int i = my0; i < min(end, my0 + per); ++i) {
-    const uint64_t key = sel_key(s, i, f);
-    if (all || key > T) ++tg; else if (key == T) ++te;
-  }
-  sg[threadIdx.x] = tg; se[threadIdx.x] = te;
-  __syncthreads();
-  // exclusive scan over threads (Hillis-Steele on 256 entries)
-  for (int off = 1; off < 256; off <<= 1) {
-    uint32_t a = 0, b2 = 0;
-    if (threadIdx.x >= off) { a = sg[threadIdx.x - off]; b2 = se[threadIdx.x - off]; }
-    __syncthreads();
-    sg[threadIdx.x] += a; se[threadIdx.x] += b2;
-    __syncthreads();
-  }
-  uint32_t gb = run_g + sg[threadIdx.x] - tg;
-  uint32_t eb = run_e + se[threadIdx.x] - te;
-  for (int i = my0; i < min(end, my0 + per); ++i) {
-    const uint64_t key = sel_key(s, i, f);
-    if (all || key > T) {
-      out[gb + min(eb, (uint32_t)need_eq)] = i;
-      ++gb;
-    } else if (key == T) {
-      if (eb < (uint32_t)need_eq) out[gb + eb] = i;
-      ++eb;
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int w0 = beg + w * (SEL_CHUNK / 4);
+  const int w1 = min(end, w0 + SEL_CHUNK / 4);
+  const uint64_t below = (1ull << lane) - 1ull;
+  auto classify = [&](int i, bool& g, bool& e) __attribute__((always_inline)) {
+    g = false; e = false;
+    if (i < w1) {
+      const uint64_t key = sel_key(s, i, f);
+      g = all || key > T;
+      e = !g && key == T;
     }
+  };
+  uint32_t cg = 0, ce = 0;
+  for (int i0 = w0; i0 < w1; i0 += 64) {
+    bool g, e;
+    classify(i0 + lane, g, e);
+    cg += (uint32_t)__popcll(__ballot(g));
+    ce += (uint32_t)__popcll(__ballot(e));
+  }
+  if (lane == 0) { wcg[w] = cg; wce[w] = ce; }
+  __syncthreads();
+  const uint32_t* bc = A.bcount + ((long long)list * A.max_blocks + blockIdx.x) * 2;
+  uint32_t gb = bc[0], eb = bc[1];
+  for (int u = 0; u < w; ++u) { gb += wcg[u]; eb += wce[u]; }
+  for (int i0 = w0; i0 < w1; i0 += 64) {
+    bool g, e;
+    const int i = i0 + lane;
+    classify(i, g, e);
+    const uint64_t bg = __ballot(g), be = __ballot(e);
+    const uint32_t g_before = gb + (uint32_t)__popcll(bg & below);
+    const uint32_t e_before = eb + (uint32_t)__popcll(be & below);
+    if (g) out[g_before + min(e_before, need_eq)] = i;
+    else if (e && e_before < need_eq) out[g_before + e_before] = i;
+    gb += (uint32_t)__popcll(bg);
+    eb += (uint32_t)__popcll(be);
   }
 }
 
@@ -204,70 +212,116 @@ hipError_t launch_select(const SelArgs& A, hipStream_t stream) {
 // Sparse plan
 // ---------------------------------------------------------------------------
 
-// One workgroup per head: valid offsets in descending order (ascending key
-// offset -delta), 0 forced, duplicates dropped, runs merged when consecutive
-// offsets differ by at most 64.
+// One workgroup (1024 threads) per head.  The selected offsets in descending
+// order (ascending key offset -delta) with the forced 0 appended; out-of-range
+// entries (padding -1, delta > p_last) are skipped.  An offset is kept when it
+// lies strictly below the previous valid one (this drops duplicates and a
+// forced 0 the list already held); a kept offset opens a new interval when
+// the previous valid offset lies more than 64 above it, else it extends the
+// current one.  Interval k is [-first kept, -last kept + 64).  Every quantity
+// is a prefix scan over the list (1024 entries per pass, carries between
+// passes); the covered-offset prefix iv_pre is a scan over the intervals.
+__device__ __forceinline__ int scan1024_max(int x, int* wred) {   // inclusive max-scan over the block
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x = max(x, y);
+  }
+  if (lane == 63) wred[w] = x;
+  __syncthreads();
+  int pre = -1;
+  for (int u = 0; u < w; ++u) pre = max(pre, wred[u]);
+  __syncthreads();
+  return max(x, pre);
+}
+__device__ __forceinline__ int scan1024_sum(int x, int* wred) {   // inclusive sum-scan over the block
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) wred[w] = x;
+  __syncthreads();
+  int pre = 0;
+  for (int u = 0; u < w; ++u) pre += wred[u];
+  __syncthreads();
+  return x + pre;
+}
+
 __global__ void __launch_bounds__(1024) plan_intervals_kernel(PlanArgs A) {
-  __shared__ int32_t sd[1024];
-  __shared__ int32_t sflag[1024];
-  __shared__ int32_t carry_last;    // last kept delta of the previous chunk (or -1)
-  __shared__ int32_t carry_count;   // intervals emitted so far
-  __shared__ int32_t open_lo;       // lo of the interval being built
+  __shared__ int32_t sd[1024];      // offsets of this pass (-1: skipped)
+  __shared__ int32_t sx[1024];      // inclusive scan results, read back at tid - 1
+  __shared__ int32_t wred[16];
+  const int tid = threadIdx.x;
   const int h = blockIdx.x;
   const int32_t* so = A.s_off + (long long)h * A.k_s;
   int32_t* ivh = A.iv + (long long)h * A.iv_stride * 2;
-  const int total = A.k_s + 1;      // descending list: s_off reversed, then the forced 0
-  if (threadIdx.x == 0) { carry_last = -1; carry_count = 0; open_lo = 0; }
-  __syncthreads();
+  const int total = A.k_s + 1;
+  int carry_valid = -1;   // last valid offset of the earlier passes
+  int carry_kept = -1;    // last kept offset of the earlier passes
+  int carry_count = 0;    // intervals opened in the earlier passes
   for (int base = 0; base < total; base += 1024) {
-    const int t = base + threadIdx.x;
+    const int t = base + tid;
     int d = -1;
     if (t < A.k_s) d = so[A.k_s - 1 - t];
     else if (t == A.k_s) d = 0;
     if (d < 0 || d > A.p_last) d = -1;
-    sd[threadIdx.x] = d;
+    sd[tid] = d;
+    // previous valid offset
+    const int vi = scan1024_max(d >= 0 ? tid : -1, wred);
+    sx[tid] = vi;
     __syncthreads();
-    // keep d if valid and strictly below every earlier kept value (drops duplicates,
-    // and a forced 0 that the list already held)
-    // previous valid element: scan back within the chunk, else the carry
-    int prev = -1;
-    if (d >= 0) {
-      for (int u = (int)threadIdx.x - 1; u >= 0; --u) { if (sd[u] >= 0) { prev = sd[u]; break; } }
-      if (prev < 0) prev = carry_last;
-    }
-    const bool keep = (d >= 0) && (prev < 0 || d < prev);
-    // a kept value starts a new interval when the gap to the previous kept value exceeds 64
-    sflag[threadIdx.x] = keep ? ((prev < 0 || prev - d > 64) ? 2 : 1) : 0;
+    const int pv_i = tid > 0 ? sx[tid - 1] : -1;
+    const int prev = pv_i >= 0 ? sd[pv_i] : carry_valid;
+    const bool keep = d >= 0 && (prev < 0 || d < prev);
+    const bool start = keep && (prev < 0 || prev - d > 64);
     __syncthreads();
-    if (threadIdx.x == 0) {
-      int cnt = carry_count;
-      int last = carry_last;
-      int lo = open_lo;
-      for (int u = 0; u < 1024 && base + u < total; ++u) {
-        const int fl = sflag[u];
-        if (!fl) continue;
-        const int dv = sd[u];
-        if (fl == 2) {
-          if (last >= 0) { ivh[2 * (cnt - 1) + 1] = -last + 64; }
-          lo = -dv;
-          ivh[2 * cnt] = lo;
-          ++cnt;
-        }
-        last = dv;
-      }
-      carry_count = cnt; carry_last = last; open_lo = lo;
+    // previous kept offset
+    const int ki = scan1024_max(keep ? tid : -1, wred);
+    sx[tid] = ki;
+    __syncthreads();
+    const int pk_i = tid > 0 ? sx[tid - 1] : -1;
+    const int prev_kept = pk_i >= 0 ? sd[pk_i] : carry_kept;
+    // interval ids
+    const int n_start = scan1024_sum(start ? 1 : 0, wred);
+    if (start) {
+      const int id = carry_count + n_start - 1;
+      ivh[2 * id] = -d;
+      if (id > 0) ivh[2 * (id - 1) + 1] = -prev_kept + 64;   // close the interval before it
     }
+    // carries (thread 1023 holds the pass totals)
+    if (tid == 1023) {
+      sx[0] = vi >= 0 ? sd[vi] : carry_valid;
+      sx[1] = ki >= 0 ? sd[ki] : carry_kept;
+      sx[2] = carry_count + n_start;
+    }
+    __syncthreads();
+    carry_valid = sx[0]; carry_kept = sx[1]; carry_count = sx[2];
     __syncthreads();
   }
-  if (threadIdx.x == 0) {
-    if (carry_count > 0) ivh[2 * (carry_count - 1) + 1] = -carry_last + 64;
+  if (tid == 0) {
+    if (carry_count > 0) ivh[2 * (carry_count - 1) + 1] = -carry_kept + 64;
     A.n_iv[h] = carry_count;
-    int32_t* pre = A.iv_pre + (long long)h * (A.iv_stride + 1);
-    int acc = 0;
-    for (int u = 0; u < carry_count; ++u) { pre[u] = acc; acc += ivh[2 * u + 1] - ivh[2 * u]; }
-    pre[carry_count] = acc;
     if (A.cover_pairs && h == 0) *A.cover_pairs = 0;
   }
+  __syncthreads();   // the interval ends are written (global memory, same workgroup)
+  __threadfence_block();
+  // iv_pre[u] = covered offsets of intervals 0..u-1
+  int32_t* pre = A.iv_pre + (long long)h * (A.iv_stride + 1);
+  int acc = 0;
+  for (int base = 0; base < carry_count; base += 1024) {
+    const int u = base + tid;
+    const int len = u < carry_count ? ivh[2 * u + 1] - ivh[2 * u] : 0;
+    const int inc = scan1024_sum(len, wred);
+    if (u < carry_count) pre[u] = acc + inc - len;
+    if (tid == 1023) sx[0] = inc;
+    __syncthreads();
+    acc += sx[0];
+    __syncthreads();
+  }
+  if (tid == 0) pre[carry_count] = acc;
 }
 
 __global__ void plan_cov_clear_kernel(PlanArgs A) {
