@@ -47,7 +47,7 @@ struct Layout {
   // prefill
   Region khi, klo, kbits, hn, qhi, qlo, iv, iv_pre, n_iv, cov, ext, n_ext, tiles, n_tiles, t_first, part_o, part_lse;
   // index
-  Region qs, part_ms, lse, vert, slash, edge, logits, hist, prefix, krem, bcount;
+  Region qs, part_ms, lse, vert, slash, edge, logits, trig, hist, prefix, krem, bcount;
   size_t prefill_bytes = 0, index_bytes = 0;
   int split = 1, nb = 0, n_ranges = 0, range_keys = 0, cov_words = 0, max_blocks = 0, kbits_words = 0, hn_pad = 0,
       tile_stride = 0;
@@ -150,6 +150,7 @@ Layout make_layout(const dca_cfg* c) {
   place(L.slash, cur, (size_t)h_q * (p_last + 1) * 8);
   place(L.edge, cur, (size_t)h_q * L.n_ranges * 2 * 64 * 2 * 8);
   place(L.logits, cur, (size_t)h_q * 64 * n_k * 8);
+  place(L.trig, cur, (size_t)(c->dca_chunk / 8) * HALF * 16);
   place(L.hist, cur, (size_t)2 * h_q * 256 * 4);
   place(L.prefix, cur, (size_t)2 * h_q * 8);
   place(L.krem, cur, (size_t)2 * h_q * 4);
@@ -226,6 +227,7 @@ int vs_index_build(const dca_bf16* q, const dca_bf16* k, const int32_t* position
   V.slash = at<double>(cfg, L.slash);
   V.edge = at<double>(cfg, L.edge);
   V.logits = at<double>(cfg, L.logits);
+  V.trig = at<double2>(cfg, L.trig);
   V.n_k = n_k; V.h_q = h_q; V.h_kv = cfg->h_kv; V.S = cfg->dca_chunk; V.n_s = n_s;
   V.p_first = p_last - n_s + 1; V.range_keys = L.range_keys; V.n_ranges = L.n_ranges; V.n_off = p_last + 1;
   V.scale = yarn_factor(cfg->yarn_s) / std::sqrt((double)D);

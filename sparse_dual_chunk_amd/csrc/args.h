@@ -35,6 +35,7 @@ struct VsArgs {
   double* slash;             // [h_q][n_off], n_off = p_last + 1
   double* edge;              // [h_q][n_ranges][2][64][2] double-double partial diagonals at range edges
   double* logits;            // [h_q][64][n_k] scaled logits of pass 1 (read back by pass 2)
+  double2* trig;             // [S / 8][64] (cos, sin) of the key positions 8a, a < S / 8
   int n_k, h_q, h_kv, S, n_s, p_first, range_keys, n_ranges, n_off;
   double scale;
 };

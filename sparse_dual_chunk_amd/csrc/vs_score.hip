@@ -53,6 +53,20 @@ __global__ void __launch_bounds__(256) vs_prep_q_kernel(const uint16_t* __restri
   }
 }
 
+// Anchor rotations of the key positions that are multiples of 8:
+// trig[p / 8][c] = (cos, sin)(p * inv_freq[c]) for p in [0, S).  A key row is
+// rotated from its anchor by at most 7 steps of angle addition.
+__global__ void __launch_bounds__(256) vs_trig_kernel(const double* __restrict__ inv_freq, double2* __restrict__ trig,
+                                                      int n_anchor) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (long long)n_anchor * HALF) return;
+  const int a = (int)(i / HALF);
+  const int c = (int)(i % HALF);
+  double sn, cs;
+  sincos((double)(8 * a) * inv_freq[c], &sn, &cs);
+  trig[i] = make_double2(cs, sn);
+}
+
 struct __align__(16) VsSmem {
   double kt[SUB * KPD];          // rotated keys of the sub-tile, [key][dim]
   double at[64 * APD];           // pass 2: probabilities [row][key]
@@ -60,7 +74,7 @@ struct __align__(16) VsSmem {
 };
 
 template <int PASS>
-__global__ void __launch_bounds__(256) vs_pass_kernel(VsArgs A) {
+__global__ void __launch_bounds__(256, 3) vs_pass_kernel(VsArgs A) {
   __shared__ VsSmem sm;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -93,6 +107,21 @@ __global__ void __launch_bounds__(256) vs_pass_kernel(VsArgs A) {
   double qa[32];
   int cur_var = -1;
 
+  // raw key values (x | y << 16) of this thread's pair for keys 8kg .. 8kg+7
+  // of a sub-tile and the anchor rotation of the first, loaded a sub-tile ahead
+  uint32_t kraw[8];
+  double2 anc;
+  auto load_raw = [&](int t0) __attribute__((always_inline)) {
+    const int j0 = t0 + 8 * kg;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const uint16_t* p = kbase + (long long)min(j0 + u, A.n_k - 1) * kstride + c;
+      kraw[u] = (uint32_t)p[0] | ((uint32_t)p[HALF] << 16);
+    }
+    anc = A.trig[(long long)((j0 % A.S) >> 3) * HALF + c];
+  };
+  if (PASS == 1) load_raw(kr0);
+
   double row_m[4], row_s[4], lse_v[4];
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
@@ -107,19 +136,18 @@ __global__ void __launch_bounds__(256) vs_pass_kernel(VsArgs A) {
   for (int t0 = kr0; t0 < kr1; t0 += SUB) {
     f64x4 acc[2];
     if constexpr (PASS == 1) {
-    // ---- rotate 32 keys into LDS (fp64): one direct sincos per 8 keys, then angle addition
+    // ---- rotate 32 keys into LDS (fp64): the anchor rotation of each 8 keys
+    // (exact), then angle addition
     {
       const int j0 = t0 + 8 * kg;
-      const double pos0 = (double)(j0 % A.S);
-      double sn, cs;
-      sincos(pos0 * A.inv_freq[c], &sn, &cs);
+      double cs = anc.x, sn = anc.y;
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int j = j0 + u;
         double x = 0.0, y = 0.0;
         if (j < A.n_k) {
-          x = (double)bf16_bits_to_f32(kbase[(long long)j * kstride + c]);
-          y = (double)bf16_bits_to_f32(kbase[(long long)j * kstride + c + HALF]);
+          x = (double)bf16_bits_to_f32((uint16_t)(kraw[u] & 0xFFFFu));
+          y = (double)bf16_bits_to_f32((uint16_t)(kraw[u] >> 16));
         }
         sm.kt[(8 * kg + u) * KPD + c] = x * cs - y * sn;
         sm.kt[(8 * kg + u) * KPD + c + HALF] = x * sn + y * cs;
@@ -128,6 +156,7 @@ __global__ void __launch_bounds__(256) vs_pass_kernel(VsArgs A) {
         cs = cs2; sn = sn2;
       }
     }
+    if (t0 + SUB < kr1) load_raw(t0 + SUB);   // lands while this sub-tile's MFMAs run
     // ---- query variant for this sub-tile (keys of one DCA chunk)
     const int m_key = t0 / A.S;
     const int need_var = (m_key == m_arow) ? 0 : 1;
@@ -135,6 +164,9 @@ __global__ void __launch_bounds__(256) vs_pass_kernel(VsArgs A) {
       const double* src = A.qs + (((long long)need_var * A.h_q + h) * 64 + arow) * D + kd;
 #pragma unroll
       for (int ks = 0; ks < 32; ++ks) qa[ks] = src[4 * ks];
+      // a variant change is rare: wait here, so that no wait for these loads is
+      // left in the MFMA loop (where it would also wait for the logit stores)
+      __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
       cur_var = need_var;
     }
     __syncthreads();
@@ -295,6 +327,9 @@ __global__ void vs_edge_kernel(const double* __restrict__ edge, double* __restri
 }
 
 hipError_t launch_vs_score(const VsArgs& A, const uint16_t* q, int n_q, hipStream_t stream) {
+  const long long n_trig = (long long)(A.S / 8) * HALF;
+  hipLaunchKernelGGL(vs_trig_kernel, dim3((unsigned)((n_trig + 255) / 256)), dim3(256), 0, stream, A.inv_freq,
+                     A.trig, A.S / 8);
   hipLaunchKernelGGL(vs_prep_q_kernel, dim3(A.h_q), dim3(256), 0, stream, q, (double*)A.qs, A.inv_freq, n_q,
                      A.h_q, A.S, A.n_s, A.p_first);
   const int blocks = NXCD * ((A.n_ranges + NXCD - 1) / NXCD) * A.h_q;
