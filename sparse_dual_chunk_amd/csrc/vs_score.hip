@@ -121,6 +121,17 @@ __global__ void __launch_bounds__(256, 3) vs_pass_kernel(VsArgs A) {
     anc = A.trig[(long long)((j0 % A.S) >> 3) * HALF + c];
   };
   if (PASS == 1) load_raw(kr0);
+  // pass 2: the scaled logits of a sub-tile (16 lanes read 128 contiguous bytes), loaded a sub-tile ahead
+  double lg[2][4];
+  auto load_lg = [&](int t0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const int j = min(t0 + 16 * nb + (lane & 15), A.n_k - 1);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) lg[nb][v] = A.logits[((long long)h * 64 + 16 * wave + kd + 4 * v) * A.n_k + j];
+    }
+  };
+  if (PASS == 2) load_lg(kr0);
 
   double row_m[4], row_s[4], lse_v[4];
 #pragma unroll
@@ -182,13 +193,12 @@ __global__ void __launch_bounds__(256, 3) vs_pass_kernel(VsArgs A) {
       }
     }
     } else {
-      // pass 2 reads the scaled logits pass 1 stored (16 lanes: 128 contiguous bytes)
+      // pass 2 reads the scaled logits pass 1 stored
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        const int j = min(t0 + 16 * nb + (lane & 15), A.n_k - 1);
+      for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) acc[nb][v] = A.logits[((long long)h * 64 + 16 * wave + kd + 4 * v) * A.n_k + j];
-      }
+        for (int v = 0; v < 4; ++v) acc[nb][v] = lg[nb][v];
+      if (t0 + SUB < kr1) load_lg(t0 + SUB);
     }
 
     if (PASS == 1) {
@@ -240,10 +250,9 @@ __global__ void __launch_bounds__(256, 3) vs_pass_kernel(VsArgs A) {
         if (e <= A.p_first) {
           const int slot = (e + (1 << 30)) & (RING - 1);
           double hi = sm.ring_hi[slot], lo = sm.ring_lo[slot];
-          for (int i = 0; i < 64; ++i) {
-            const int col = e + i - t0;
-            if (col >= 0 && col < SUB) dd_add(hi, lo, sm.at[i * APD + col]);
-          }
+          // rows i of the diagonal inside the sub-tile: 0 <= e + i - t0 < SUB
+          const int i_lo = max(0, t0 - e), i_hi = min(64, t0 + SUB - e);
+          for (int i = i_lo; i < i_hi; ++i) dd_add(hi, lo, sm.at[i * APD + (e + i - t0)]);
           const bool last_sub = (t0 + SUB >= kr1);
           const bool complete = (e + 63 < t0 + SUB) || (last_sub && kr1 == A.n_k);
           const bool started_here = (e >= kr0) || (kr0 == 0);
