@@ -37,6 +37,9 @@ in the design notes lists every one):
     covers keys [i0 - delta, i0 - delta + 63]; the vertical columns are added;
     the union is clipped to [0, i0 + 63] and each row then attends its causal
     part.  Empty sets give O = 0, lse = -inf.
+  * Generation step (decode): the newest tokens attend every cached key up to
+    their own position with the same DCA positions, densely (the pages apply
+    the sparse attention to the prefill).
 """
 from __future__ import annotations
 
@@ -265,6 +268,40 @@ def attention(q, k, v, p0: int, cfg: dict, v_idx=None, s_off=None, heads=None):
             r0 = b * QBLOCK
             out[r0:r0 + len(l), h] = o
             lse[h, r0:r0 + len(l)] = l
+    return out, lse
+
+
+def decode_attention(q, k, v, cfg: dict, heads=None, key_block: int = 1 << 18):
+    """One generation step: the n_t rows of ``q`` are the newest tokens, at
+    positions n_k - n_t .. n_k - 1, and each attends every cached key j <= its
+    position with the DCA positions of its (row, key) pairs (the generation
+    side of the same attention: no sparsity, which the pages apply to the
+    prefill).  q [n_t][h_q][d], k, v [n_k][h_kv][d] bf16 bits.
+
+    Keys are taken ``key_block`` at a time and the blocks' softmax partials
+    merged by ``lse_merge`` (exact), so a million-key cache fits in memory.
+    Returns (out [n_t][h_q][d] fp64, lse [h_q][n_t] fp64).
+    """
+    n_t, h_q, d = q.shape
+    n_k = k.shape[0]
+    G = h_q // cfg["h_kv"]
+    S, W, base = cfg["dca_chunk"], cfg["dca_local"], cfg["rope_base"]
+    scale = softmax_scale(cfg["yarn_s"], d)
+    p_rows = np.arange(n_k - n_t, n_k)
+    out = np.zeros((n_t, h_q, d))
+    lse = np.full((h_q, n_t), -np.inf)
+    for h in (range(h_q) if heads is None else heads):
+        g = h // G
+        qr = bf16_to_f64(q[:, h])
+        parts = []
+        for j0 in range(0, n_k, key_block):
+            keys = np.arange(j0, min(n_k, j0 + key_block))
+            allowed = keys[None, :] <= p_rows[:, None]
+            parts.append(attend_rows(qr, p_rows, bf16_to_f64(k[keys, g]), bf16_to_f64(v[keys, g]), keys, allowed,
+                                     S, W, base, scale))
+        o, l = lse_merge(parts) if len(parts) > 1 else parts[0]
+        out[:, h] = o
+        lse[h] = l
     return out, lse
 
 

@@ -400,3 +400,51 @@ def test_bf16_rounding_matches_torch():
     x = np.random.default_rng(16).standard_normal(100000).astype(np.float32) * 7
     ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     assert np.array_equal(f32_to_bf16_bits(x), ref)
+
+
+# ---------------------------------------------------------------- decode (generation step)
+@pytest.mark.parametrize("n_k,n_t", [(45, 1), (45, 3), (37, 2)])
+def test_decode_matches_brute_force(n_k, n_t):
+    """Newest tokens at positions n_k - n_t .. n_k - 1 (not on a 64 boundary), several DCA
+    chunks, a sink; key blocks of 16 exercise the partial merge."""
+    rng = np.random.default_rng(40 + n_k + n_t)
+    d = 8
+    q = _bf16(rng, (n_t, 2, d))
+    k = _bf16(rng, (n_k, 1, d))
+    k[:2] = f32_to_bf16_bits(bf16_bits_to_f32(k[:2]) * 8)
+    v = _bf16(rng, (n_k, 1, d))
+    cfg = _cfg(2, 1, 8, 3, base=1e4)
+    out, lse = O.decode_attention(q, k, v, cfg, key_block=16)
+    bo, bl = brute.attention(_nested(q), _nested(k), _nested(v), n_k - n_t, cfg)
+    assert np.abs(out - np.array(bo)).max() <= 1e-12
+    assert np.abs(lse - np.array(bl)).max() <= 1e-12
+
+
+def test_decode_within_window_is_plain_rope_attention():
+    """n_k <= S + W: the DCA positions of every pair equal the true ones."""
+    rng = np.random.default_rng(41)
+    S, W, n_k, n_t, d = 256, 64, 300, 3, 128
+    q, k, v = _bf16(rng, (n_t, 4, d)), _bf16(rng, (n_k, 2, d)), _bf16(rng, (n_k, 2, d))
+    cfg = _cfg(4, 2, S, W, base=1e6, s=4.0)
+    out, _ = O.decode_attention(q, k, v, cfg)
+    p_rows = np.arange(n_k - n_t, n_k)
+    mask = np.where(np.arange(n_k)[None, :] <= p_rows[:, None], 0.0, -np.inf)
+    for h in range(4):
+        g = h // 2
+        qr = _rope_complex(O.bf16_to_f64(q[:, h]), p_rows, 1e6)
+        kr = _rope_complex(O.bf16_to_f64(k[:, g]), np.arange(n_k), 1e6)
+        ref = _sdpa_causal_fp64(qr, kr, O.bf16_to_f64(v[:, g]), O.softmax_scale(4.0, d), mask=mask)
+        assert np.abs(out[:, h] - ref).max() <= 1e-12
+
+
+def test_decode_zero_query_gives_mean_and_log_count():
+    rng = np.random.default_rng(42)
+    n_k, n_t, d = 1000, 4, 128
+    q = np.zeros((n_t, 2, d), dtype=np.uint16)
+    k, v = _bf16(rng, (n_k, 1, d), 3.0), _bf16(rng, (n_k, 1, d))
+    out, lse = O.decode_attention(q, k, v, _cfg(2, 1, 64, 16), key_block=256)
+    vf = O.bf16_to_f64(v[:, 0])
+    for t in range(n_t):
+        p = n_k - n_t + t
+        assert np.allclose(out[t, 1], vf[: p + 1].mean(axis=0), rtol=0, atol=1e-13)
+        assert abs(lse[1, t] - math.log(p + 1)) <= 1e-12
