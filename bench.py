@@ -130,6 +130,105 @@ def cpu_baseline(w, inputs, p0s, f_blocks_total: float, n_blocks_total: int):
     }
 
 
+DECODE_METRIC = "decode-step attention over a 1M-key KV cache, 7B heads: cache GB/s (K + V read per step)"
+
+
+def bench_decode(args) -> int:
+    """One step = the attention of ``--decode-tokens`` new tokens over the whole 1,048,576-key
+    cache of the 1M workload's layer (7B heads).  The rotated key cache is built before
+    the timed region (its keys enter the cache once, at prefill time)."""
+    import torch
+    import sparse_dual_chunk_amd as S
+    from oracle import dca_oracle as O
+
+    w = W.C5_7B_1M
+    n_k, n_t = w.n_k_total, args.decode_tokens
+    log(f"decode: {n_t} token(s) over {n_k} cached keys, generating inputs (seed {args.seed})")
+    k, v = W.make_keys_values(w, n_k, args.seed)
+    q = W.make_queries(w, n_k - n_t, n_t, seed=args.seed + 1)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
+    cfg = S.Config(n_q=n_t, n_k=n_k, h_q=w.h_q, h_kv=w.h_kv, dca_chunk=w.dca_chunk, dca_local=w.dca_local,
+                   rope_base=w.rope_base, yarn_s=w.yarn_s, split_k=args.split_k)
+    K, V, Q = dev(k), dev(v), dev(q)
+    cache = S.KeyCache.allocate(n_k, w.h_kv)
+    S.dca_key_cache_append(K, 0, cfg, cache)
+    del K
+    out = torch.empty(Q.shape, dtype=torch.int16, device="cuda")
+    ws = torch.empty(S.dca_decode_workspace_size(cfg), dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    hev = HipEvents()
+    n_ev = 2 * S.DCA_STAGE_COUNT
+    for _ in range(args.warmup):
+        S.dca_decode(Q, cache, V, cfg, out, ws)
+    torch.cuda.synchronize()
+    evs = [hev.create(n_ev) for _ in range(args.steps)]
+    log(f"timing {args.steps} step(s)")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for st in range(args.steps):
+        S.dca_decode(Q, cache, V, cfg, out, ws, stage_events=evs[st])
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    stage_ms = {name: float(np.mean([hev.elapsed_ms(e[2 * i], e[2 * i + 1]) for e in evs]))
+                for i, name in enumerate(S.STAGES)}
+    attn_ms = stage_ms["attention"]
+    # algorithmic bytes of the attention kernel: every K (rotated, hi) and V row once,
+    # the query rows, and the parts' fp32 partials written
+    ws_parts = S.dca_decode_workspace_size(cfg)
+    kv_bytes = 2 * n_k * w.h_kv * w.head_dim * 2
+    part_bytes = ws_parts - 2 * 3 * n_t * w.h_q * w.head_dim * 2
+    algo_bytes = kv_bytes + 3 * n_t * w.h_q * w.head_dim * 2 + part_bytes
+    achieved = algo_bytes / (attn_ms / 1e3) / 1e9
+    result = {
+        "metric": DECODE_METRIC,
+        "value": round(kv_bytes / (ms_per_step / 1e3) / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "7b_decode_1m_cache", "n_tokens": n_t, "n_k": n_k, "h_q": w.h_q, "h_kv": w.h_kv,
+                   "head_dim": w.head_dim, "dca_chunk": w.dca_chunk, "dca_local": w.dca_local,
+                   "rope_base": w.rope_base, "yarn_s": w.yarn_s, "seed": args.seed},
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "traffic": None,
+            "kernel": "dca_decode_kernel",
+            "avg_launch_ms": round(attn_ms, 5),
+            "algorithmic_bytes_per_launch": algo_bytes,
+        },
+        "tokens_per_s_per_layer": round(n_t / (ms_per_step / 1e3), 1),
+        "stage_ms": {k2: round(v2, 5) for k2, v2 in stage_ms.items()},
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline: the oracle's decode of one query head")
+        t1 = time.perf_counter()
+        O.decode_attention(q, k, v, dict(h_q=w.h_q, h_kv=w.h_kv, dca_chunk=w.dca_chunk, dca_local=w.dca_local,
+                                         rope_base=w.rope_base, yarn_s=w.yarn_s), heads=[0])
+        t_head = time.perf_counter() - t1
+        try:
+            from threadpoolctl import threadpool_info
+            cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        except Exception:
+            cores = os.cpu_count() or 1
+        t_step = t_head * w.h_q
+        result["cpu_baseline"] = {"value": round(kv_bytes / t_step / 1e9, 4), "unit": "GB/s", "cores": int(cores),
+                                  "kind": "oracle",
+                                  "sample": f"fp64 oracle decode of query head 0 over the whole cache "
+                                            f"({t_head:.1f} s), extrapolated to {w.h_q} heads"}
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -143,6 +242,9 @@ def main() -> int:
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes (3 launches), "
                          "the reference for scaling the HBM byte counters")
+    ap.add_argument("--decode", action="store_true",
+                    help="measure the generation-step attention over the 1M-key cache instead of the prefill")
+    ap.add_argument("--decode-tokens", type=int, default=1)
     args = ap.parse_args()
 
     if args.copy_calibration:
@@ -161,6 +263,9 @@ def main() -> int:
         print(f"bench.py runs on one GPU only (the path is measured on one MI355X; --gpus {args.gpus} "
               "is not supported; collectives and sharding are outside this build)", file=sys.stderr)
         return 2
+
+    if args.decode:
+        return bench_decode(args)
 
     import torch
     import sparse_dual_chunk_amd as S

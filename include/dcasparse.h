@@ -1,7 +1,8 @@
 /*
  * dcasparse.h — C ABI of the MI355X (gfx950) library for long-context prefill
  * attention with Dual Chunk Attention (DCA), YaRN logit scaling and
- * vertical-slash sparsity chosen per prefill chunk.
+ * vertical-slash sparsity chosen per prefill chunk, and the generation-step
+ * (decode) attention over a rotated key cache.
  *
  * What is computed (sources: "Qwen2.5-1M Technical Report" as summarised on
  * the xllm-io paper-review page, section 4 "Inference & deployment":
@@ -35,7 +36,8 @@
  *     KV prefix ends with the chunk), with p0 a multiple of 64.  It is read
  *     before anything is enqueued so that malformed calls fail synchronously.
  *   - Every buffer belongs to the caller.  No entry point allocates device
- *     memory: scratch comes from cfg->workspace, sized by dca_workspace_size.
+ *     memory: scratch comes from cfg->workspace, sized by dca_workspace_size
+ *     (dca_decode_workspace_size for dca_decode).
  *   - Work is enqueued on cfg->stream and the call returns without waiting.
  *     Outputs are bitwise deterministic for identical inputs.
  *   - Calls sharing one workspace must not overlap in time (same stream, or
@@ -133,6 +135,49 @@ DCA_API int vs_index_build(const dca_bf16 *q, const dca_bf16 *k, const int32_t *
  * natural-log LSE of every row.  bf16 inputs, fp32 accumulation. */
 DCA_API int dca_sparse_prefill(const dca_bf16 *q, const dca_bf16 *k, const dca_bf16 *v,
                        const int32_t *positions, const dca_cfg *cfg, dca_bf16 *out);
+
+/* ---- Generation step (decode) ------------------------------------------
+ * After a prefill, each generated token attends the whole key cache with the
+ * same DCA positions, densely (the pages apply the sparse attention to the
+ * prefill only).  A key's rotation depends only on r_j = j mod S, not on the
+ * query, so keys are rotated once, when they enter the cache, into the three
+ * arrays below (caller-owned device memory of the given capacity):
+ *   k_hi    [capacity][h_kv][head_dim]  RoPE(k_j, r_j) rounded to bf16
+ *   k_lo    [capacity][h_kv][head_dim]  bf16 residual of that rounding
+ *   k_flags [h_kv][(capacity + 31) / 32] bit j set: key j's L2 norm exceeds
+ *           cfg->precise_norm (its logits then use hi + lo). */
+typedef struct dca_key_cache {
+  dca_bf16 *k_hi;
+  dca_bf16 *k_lo;
+  uint32_t *k_flags;
+  int32_t   capacity;     /* keys the arrays hold; capacity * h_kv * head_dim * 2 < 2^32 */
+} dca_key_cache;
+
+/* Rotates keys j0 .. j0+n-1 into the cache (k points at key j0, layout
+ * [n][h_kv][head_dim] raw bf16 before rotation) and rewrites their flag bits
+ * (other bits are kept).  Reads cfg->h_kv, head_dim, dca_chunk, rope_base,
+ * precise_norm and stream; needs no workspace.  Requires 0 <= j0,
+ * 1 <= n, j0 + n <= capacity.  Asynchronous on cfg->stream. */
+DCA_API int dca_key_cache_append(const dca_bf16 *k, int32_t j0, int32_t n, const dca_cfg *cfg,
+                                 const dca_key_cache *cache);
+
+/* Workspace bytes of dca_decode for this configuration (cfg->n_q new tokens,
+ * cfg->n_k cached keys).  Pure host computation. */
+DCA_API int dca_decode_workspace_size(const dca_cfg *cfg, size_t *bytes);
+
+/* Attention of the n_q = cfg->n_q newest tokens, at positions
+ * n_k - n_q .. n_k - 1, over cache keys 0 .. n_k - 1 (all appended): dense
+ * DCA, A(i) = { j <= p_i } in the definition at the top.  q [n_q][h_q][128]
+ * raw bf16 before rotation; v [capacity][h_kv][128] (rows < n_k are read).
+ * Writes out [n_q][h_q][128] bf16 and, when cfg->lse_out is set, the
+ * natural-log LSE [h_q][n_q].  1 <= n_q <= 64 and n_q <= n_k <= capacity;
+ * cfg->v_idx and cfg->s_off must be NULL; cfg->split_k (0..4096) sets the
+ * number of key parts (0: the library's choice, ~2048 workgroups); positions
+ * are implied.  bf16 inputs, fp32 accumulation; deterministic.
+ * cfg->stage_events, when set, are recorded as for dca_sparse_prefill:
+ * 0 query rotations, 1 (empty), 2 attention over the cache, 3 LSE merge. */
+DCA_API int dca_decode(const dca_bf16 *q, const dca_key_cache *cache, const dca_bf16 *v, const dca_cfg *cfg,
+                       dca_bf16 *out);
 
 /* Static message for an error code; never NULL. */
 DCA_API const char *dca_strerror(int code);

@@ -10,6 +10,9 @@ Names follow the C ABI in ``include/dcasparse.h``:
 * :func:`dca_workspace_size`
 * :func:`vs_index_build`
 * :func:`dca_sparse_prefill`
+* :func:`dca_key_cache_append`
+* :func:`dca_decode_workspace_size`
+* :func:`dca_decode`
 * :func:`dca_strerror`
 """
 from __future__ import annotations
@@ -61,6 +64,16 @@ class dca_cfg(ctypes.Structure):
     ]
 
 
+class dca_key_cache(ctypes.Structure):
+    """Mirror of ``struct dca_key_cache``."""
+    _fields_ = [
+        ("k_hi", ctypes.c_void_p),
+        ("k_lo", ctypes.c_void_p),
+        ("k_flags", ctypes.c_void_p),
+        ("capacity", ctypes.c_int32),
+    ]
+
+
 class DcaError(RuntimeError):
     def __init__(self, code: int, where: str):
         super().__init__(f"{where}: error {code} ({dca_strerror(code)})")
@@ -86,6 +99,14 @@ def lib() -> ctypes.CDLL:
         L.dca_sparse_prefill.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                          ctypes.POINTER(dca_cfg), ctypes.c_void_p]
         L.dca_sparse_prefill.restype = ctypes.c_int
+        L.dca_key_cache_append.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(dca_cfg),
+                                           ctypes.POINTER(dca_key_cache)]
+        L.dca_key_cache_append.restype = ctypes.c_int
+        L.dca_decode_workspace_size.argtypes = [ctypes.POINTER(dca_cfg), ctypes.POINTER(ctypes.c_size_t)]
+        L.dca_decode_workspace_size.restype = ctypes.c_int
+        L.dca_decode.argtypes = [ctypes.c_void_p, ctypes.POINTER(dca_key_cache), ctypes.c_void_p,
+                                 ctypes.POINTER(dca_cfg), ctypes.c_void_p]
+        L.dca_decode.restype = ctypes.c_int
         L.dca_strerror.argtypes = [ctypes.c_int]
         L.dca_strerror.restype = ctypes.c_char_p
         _lib = L
@@ -185,3 +206,59 @@ def config_for(w, chunk: int = 0, **overrides) -> Config:
     for k2, v2 in overrides.items():
         setattr(cfg, k2, v2)
     return cfg
+
+
+# ---------------------------------------------------------------- generation step (decode)
+@dataclasses.dataclass
+class KeyCache:
+    """Device arrays of a rotated key cache (see ``struct dca_key_cache``)."""
+    k_hi: object       # int16 tensor [capacity][h_kv][128]
+    k_lo: object       # int16 tensor [capacity][h_kv][128]
+    k_flags: object    # int32 tensor [h_kv][(capacity + 31) // 32], zero before the first append
+    capacity: int
+
+    @staticmethod
+    def allocate(capacity: int, h_kv: int, head_dim: int = 128, device: str = "cuda") -> "KeyCache":
+        import torch
+        return KeyCache(k_hi=torch.empty((capacity, h_kv, head_dim), dtype=torch.int16, device=device),
+                        k_lo=torch.empty((capacity, h_kv, head_dim), dtype=torch.int16, device=device),
+                        k_flags=torch.zeros((h_kv, (capacity + 31) // 32), dtype=torch.int32, device=device),
+                        capacity=capacity)
+
+    def to_c(self) -> dca_key_cache:
+        c = dca_key_cache()
+        c.k_hi, c.k_lo, c.k_flags, c.capacity = _ptr(self.k_hi), _ptr(self.k_lo), _ptr(self.k_flags), self.capacity
+        return c
+
+
+def dca_key_cache_append(k, j0: int, cfg: Config, cache: KeyCache, stream=None) -> None:
+    """Rotate keys j0 .. j0 + k.shape[0] - 1 (k: [n][h_kv][128] raw bf16 bits) into the cache."""
+    c = cfg.to_c(stream=_stream(stream))
+    kc = cache.to_c()
+    rc = lib().dca_key_cache_append(_ptr(k), int(j0), int(k.shape[0]), ctypes.byref(c), ctypes.byref(kc))
+    if rc != DCA_OK:
+        raise DcaError(rc, "dca_key_cache_append")
+
+
+def dca_decode_workspace_size(cfg: Config) -> int:
+    c = cfg.to_c()
+    n = ctypes.c_size_t(0)
+    rc = lib().dca_decode_workspace_size(ctypes.byref(c), ctypes.byref(n))
+    if rc != DCA_OK:
+        raise DcaError(rc, "dca_decode_workspace_size")
+    return int(n.value)
+
+
+def dca_decode(q, cache: KeyCache, v, cfg: Config, out, workspace, lse_out=None, stream=None,
+               stage_events: Optional[Sequence[int]] = None) -> None:
+    """Attention of the cfg.n_q newest tokens (q [n_q][h_q][128]) over cache keys 0 .. cfg.n_k - 1."""
+    ev_arr = None
+    if stage_events is not None:
+        ev_arr = (ctypes.c_void_p * (2 * DCA_STAGE_COUNT))(*[int(e) for e in stage_events])
+    c = cfg.to_c(workspace=_ptr(workspace), workspace_bytes=workspace.numel() * workspace.element_size(),
+                 stream=_stream(stream), lse_out=_ptr(lse_out),
+                 stage_events=ctypes.cast(ev_arr, ctypes.c_void_p) if ev_arr is not None else None)
+    kc = cache.to_c()
+    rc = lib().dca_decode(_ptr(q), ctypes.byref(kc), _ptr(v), ctypes.byref(c), _ptr(out))
+    if rc != DCA_OK:
+        raise DcaError(rc, "dca_decode")

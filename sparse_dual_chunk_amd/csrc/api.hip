@@ -11,8 +11,8 @@
 namespace dca {
 
 hipError_t launch_rotate_keys(const uint16_t* k, uint16_t* khi, uint16_t* klo, uint32_t* kbits,
-                              const double* inv_freq, int n_k, int h_kv, int S, float thr2, int kbits_words,
-                              hipStream_t stream);
+                              const Freqs& f, int j0, int n, int h_kv, int S, float thr2, int kbits_words,
+                              bool clear_all, hipStream_t stream);
 hipError_t launch_hn_next(const uint32_t* kbits, uint8_t* hn, int n_pad, int h_kv, int kbits_words,
                           hipStream_t stream);
 hipError_t launch_rotate_queries(const uint16_t* q, uint16_t* qhi, uint16_t* qlo, const double* inv_freq,
@@ -23,14 +23,14 @@ hipError_t launch_lse_merge(const float* part_o, const float* part_lse, uint16_t
 hipError_t launch_vs_score(const VsArgs& A, const uint16_t* q, int n_q, hipStream_t stream);
 hipError_t launch_select(const SelArgs& A, hipStream_t stream);
 hipError_t launch_plan(const PlanArgs& A, hipStream_t stream);
+hipError_t launch_decode_attn(const DecArgs& A, hipStream_t stream);
+hipError_t launch_decode_merge(const DecArgs& A, uint16_t* out, float* lse_out, hipStream_t stream);
 
 }  // namespace dca
 
 namespace {
 
 using namespace dca;
-
-struct Freqs { double v[HALF]; };
 
 __global__ void write_freqs_kernel(Freqs f, double* dst) { dst[threadIdx.x] = f.v[threadIdx.x]; }
 __global__ void write_i64_kernel(long long* dst, long long v) { *dst = v; }
@@ -160,6 +160,55 @@ Layout make_layout(const dca_cfg* c) {
   return L;
 }
 
+// ---- generation step (decode)
+int validate_decode(const dca_cfg* c) {
+  if (!c) return DCA_EINVAL;
+  if (c->n_q < 1 || c->n_k < c->n_q || c->h_q < 1 || c->h_kv < 1) return DCA_EINVAL;
+  if (c->h_q % c->h_kv != 0) return DCA_EINVAL;
+  if (c->n_q > 64) return DCA_EUNSUPPORTED;
+  if (c->head_dim != 128) return DCA_EUNSUPPORTED;
+  if (c->dca_chunk < 64 || c->dca_chunk % 64 != 0) return DCA_EUNSUPPORTED;
+  if (c->dca_local < 1 || c->dca_local > c->dca_chunk) return DCA_EUNSUPPORTED;
+  if (!(c->rope_base > 1.0) || !std::isfinite(c->rope_base)) return DCA_EINVAL;
+  if (!(c->yarn_s > 0.0) || !std::isfinite(c->yarn_s)) return DCA_EINVAL;
+  if (c->v_idx || c->s_off) return DCA_EINVAL;
+  if (c->split_k < 0 || c->split_k > 4096) return DCA_EINVAL;
+  if ((long long)c->n_k + 2LL * c->dca_chunk + 128 > (1LL << 30)) return DCA_EUNSUPPORTED;
+  if ((long long)c->n_k * c->h_kv * c->head_dim * 2 >= (1LL << 32)) return DCA_EUNSUPPORTED;
+  return DCA_OK;
+}
+
+struct DecLayout {
+  Region freqs, qhi, qlo, part_o, part_lse;
+  int n_cb = 1, part_keys = 32, n_parts = 1;
+  size_t bytes = 0;
+};
+
+DecLayout make_dec_layout(const dca_cfg* c) {
+  DecLayout L;
+  const int G = c->h_q / c->h_kv;
+  L.n_cb = (c->n_q * G + 31) / 32;
+  long long pk;
+  if (c->split_k > 0) {
+    pk = ((long long)c->n_k + c->split_k - 1) / c->split_k;
+  } else {
+    // about 2048 one-wave workgroups: two per SIMD of the 256 compute units
+    pk = ((long long)c->n_k * c->h_kv * L.n_cb + 2047) / 2048;
+    pk = std::max(pk, 256LL);
+  }
+  pk = (pk + 31) / 32 * 32;
+  L.part_keys = (int)pk;
+  L.n_parts = (int)((c->n_k + pk - 1) / pk);
+  size_t cur = 0;
+  place(L.freqs, cur, HALF * sizeof(double));
+  place(L.qhi, cur, (size_t)3 * c->n_q * c->h_q * D * 2);
+  place(L.qlo, cur, (size_t)3 * c->n_q * c->h_q * D * 2);
+  place(L.part_o, cur, (size_t)L.n_parts * c->n_q * c->h_q * D * 4);
+  place(L.part_lse, cur, (size_t)L.n_parts * c->h_q * c->n_q * 4);
+  L.bytes = cur;
+  return L;
+}
+
 template <class T>
 T* at(const dca_cfg* c, const Region& r) { return (T*)((char*)c->workspace + r.off); }
 
@@ -269,7 +318,8 @@ int dca_sparse_prefill(const dca_bf16* q, const dca_bf16* k, const dca_bf16* v, 
   float thr = cfg->precise_norm == 0.f ? 2.f * std::sqrt((float)D) : cfg->precise_norm;
   const float thr2 = thr < 0.f ? -1.f : thr * thr;
   if (launch_rotate_keys(k, at<uint16_t>(cfg, L.khi), at<uint16_t>(cfg, L.klo), at<uint32_t>(cfg, L.kbits),
-                         at<double>(cfg, L.freqs), n_k, h_kv, cfg->dca_chunk, thr2, L.kbits_words, st) != hipSuccess)
+                         make_freqs(cfg->rope_base), 0, n_k, h_kv, cfg->dca_chunk, thr2, L.kbits_words, true,
+                         st) != hipSuccess)
     return DCA_EHIP;
   if (launch_hn_next(at<uint32_t>(cfg, L.kbits), at<uint8_t>(cfg, L.hn), L.hn_pad, h_kv, L.kbits_words, st) !=
       hipSuccess)
@@ -329,6 +379,71 @@ int dca_sparse_prefill(const dca_bf16* q, const dca_bf16* k, const dca_bf16* v, 
     if (launch_lse_merge(A.part_o, A.part_lse, out, cfg->lse_out, L.split, n_q, h_q, st) != hipSuccess)
       return DCA_EHIP;
   }
+  record(cfg, 3, 1);
+  return DCA_OK;
+}
+
+int dca_key_cache_append(const dca_bf16* k, int32_t j0, int32_t n, const dca_cfg* cfg, const dca_key_cache* cache) {
+  if (!cfg || !cache || !k) return DCA_EINVAL;
+  if (!cache->k_hi || !cache->k_lo || !cache->k_flags || cache->capacity < 1) return DCA_EINVAL;
+  if (cfg->h_kv < 1) return DCA_EINVAL;
+  if (cfg->head_dim != 128) return DCA_EUNSUPPORTED;
+  if (cfg->dca_chunk < 64 || cfg->dca_chunk % 64 != 0) return DCA_EUNSUPPORTED;
+  if (!(cfg->rope_base > 1.0) || !std::isfinite(cfg->rope_base)) return DCA_EINVAL;
+  if (!std::isfinite(cfg->precise_norm)) return DCA_EINVAL;
+  if (j0 < 0 || n < 1 || (long long)j0 + n > cache->capacity) return DCA_EINVAL;
+  if ((long long)cache->capacity + 2LL * cfg->dca_chunk + 128 > (1LL << 30)) return DCA_EUNSUPPORTED;
+  if ((long long)cache->capacity * cfg->h_kv * cfg->head_dim * 2 >= (1LL << 32)) return DCA_EUNSUPPORTED;
+  const float thr = cfg->precise_norm == 0.f ? 2.f * std::sqrt((float)D) : cfg->precise_norm;
+  const float thr2 = thr < 0.f ? -1.f : thr * thr;
+  const int words = (cache->capacity + 31) / 32;
+  if (launch_rotate_keys(k, cache->k_hi, cache->k_lo, cache->k_flags, make_freqs(cfg->rope_base), j0, n, cfg->h_kv,
+                         cfg->dca_chunk, thr2, words, false, (hipStream_t)cfg->stream) != hipSuccess)
+    return DCA_EHIP;
+  return DCA_OK;
+}
+
+int dca_decode_workspace_size(const dca_cfg* cfg, size_t* bytes) {
+  if (!bytes) return DCA_EINVAL;
+  const int rc = validate_decode(cfg);
+  if (rc != DCA_OK) return rc;
+  *bytes = make_dec_layout(cfg).bytes;
+  return DCA_OK;
+}
+
+int dca_decode(const dca_bf16* q, const dca_key_cache* cache, const dca_bf16* v, const dca_cfg* cfg, dca_bf16* out) {
+  int rc = validate_decode(cfg);
+  if (rc != DCA_OK) return rc;
+  if (!q || !cache || !v || !out) return DCA_EINVAL;
+  if (!cache->k_hi || !cache->k_lo || !cache->k_flags || cache->capacity < cfg->n_k) return DCA_EINVAL;
+  if ((long long)cache->capacity * cfg->h_kv * cfg->head_dim * 2 >= (1LL << 32)) return DCA_EUNSUPPORTED;
+  const DecLayout L = make_dec_layout(cfg);
+  rc = check_workspace(cfg, L.bytes);
+  if (rc != DCA_OK) return rc;
+  hipStream_t st = (hipStream_t)cfg->stream;
+  const int n_t = cfg->n_q, n_k = cfg->n_k, h_q = cfg->h_q;
+  record(cfg, 0, 0);
+  hipLaunchKernelGGL(write_freqs_kernel, dim3(1), dim3(HALF), 0, st, make_freqs(cfg->rope_base),
+                     at<double>(cfg, L.freqs));
+  const float qscale = (float)(yarn_factor(cfg->yarn_s) / std::sqrt((double)D) * 1.4426950408889634);
+  if (launch_rotate_queries(q, at<uint16_t>(cfg, L.qhi), at<uint16_t>(cfg, L.qlo), at<double>(cfg, L.freqs), n_t,
+                            h_q, n_k - n_t, cfg->dca_chunk, cfg->dca_local, qscale, st) != hipSuccess)
+    return DCA_EHIP;
+  record(cfg, 0, 1);
+  record(cfg, 1, 0);
+  record(cfg, 1, 1);
+  DecArgs A;
+  A.qhi = at<uint16_t>(cfg, L.qhi); A.qlo = at<uint16_t>(cfg, L.qlo);
+  A.khi = cache->k_hi; A.klo = cache->k_lo; A.kflags = cache->k_flags; A.v = v;
+  A.part_o = at<float>(cfg, L.part_o); A.part_lse = at<float>(cfg, L.part_lse);
+  A.n_t = n_t; A.n_k = n_k; A.h_q = h_q; A.h_kv = cfg->h_kv; A.S = cfg->dca_chunk;
+  A.kflag_words = (cache->capacity + 31) / 32;
+  A.part_keys = L.part_keys; A.n_parts = L.n_parts; A.n_cb = L.n_cb;
+  record(cfg, 2, 0);
+  if (launch_decode_attn(A, st) != hipSuccess) return DCA_EHIP;
+  record(cfg, 2, 1);
+  record(cfg, 3, 0);
+  if (launch_decode_merge(A, out, cfg->lse_out, st) != hipSuccess) return DCA_EHIP;
   record(cfg, 3, 1);
   return DCA_OK;
 }

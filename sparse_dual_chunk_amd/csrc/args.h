@@ -25,6 +25,18 @@ struct AttnArgs {
   int n_q, n_k, h_q, h_kv, p0, S, W, nb, tile_stride, ext_stride, split, dense, kbits_words, hn_pad;
 };
 
+struct DecArgs {
+  const uint16_t* qhi;      // [3 modes][n_t][h_q][128] rotated token rows * scale * log2(e), bf16 hi
+  const uint16_t* qlo;      // same, lo residual
+  const uint16_t* khi;      // key cache [capacity][h_kv][128] rotated, bf16 hi
+  const uint16_t* klo;      // same, lo residual
+  const uint32_t* kflags;   // [h_kv][kflag_words] bit j: key j is high-norm
+  const uint16_t* v;        // [capacity][h_kv][128]
+  float* part_o;            // [P][n_t][h_q][128] normalised partial outputs
+  float* part_lse;          // [P][h_q][n_t] natural-log partial LSE
+  int n_t, n_k, h_q, h_kv, S, kflag_words, part_keys, n_parts, n_cb;
+};
+
 struct VsArgs {
   const uint16_t* k;         // raw keys [n_k][h_kv][128]
   const double* qs;          // [2][h_q][64][128] scoring rows rotated at r_i ([0]) and S + r_i ([1])

@@ -18,6 +18,9 @@ namespace dca {
 
 constexpr int D = 128;          // head dimension
 constexpr int HALF = 64;        // RoPE pairs (c, c + 64)
+
+// RoPE frequencies theta_c = base^(-2c/d), c < 64, computed on the host in fp64
+struct Freqs { double v[HALF]; };
 constexpr int QB = 64;          // rows of a query block (sparse-cover granule)
 constexpr int NXCD = 8;         // MI355X: 8 accelerator dies, workgroups dispatched round-robin
 

@@ -18,19 +18,22 @@ __global__ void kbits_clear_kernel(uint32_t* __restrict__ kbits, long long n) {
 }
 
 // One 16-lane group per (key, kv head) row; lane c16 owns pairs 4*c16 .. 4*c16+3.
+// Keys j0 .. j0+n-1: k points at key j0, the outputs and bits are indexed by
+// the absolute key.
 __global__ void __launch_bounds__(256) rotate_keys_kernel(
     const uint16_t* __restrict__ k, uint16_t* __restrict__ khi, uint16_t* __restrict__ klo,
-    uint32_t* __restrict__ kbits, const double* __restrict__ inv_freq,
-    int n_k, int h_kv, int S, float thr2, int kbits_words) {
+    uint32_t* __restrict__ kbits, Freqs fq, int j0,
+    int n, int h_kv, int S, float thr2, int kbits_words) {
   const int lane16 = threadIdx.x & 15;
   const long long row = (long long)blockIdx.x * 16 + (threadIdx.x >> 4);
-  const long long n_rows = (long long)n_k * h_kv;
+  const long long n_rows = (long long)n * h_kv;
   const bool active = row < n_rows;
   const long long rrow = active ? row : 0;
-  const int j = (int)(rrow / h_kv);
+  const int j = j0 + (int)(rrow / h_kv);
   const int g = (int)(rrow % h_kv);
   const double pos = (double)(j % S);
   const uint16_t* src = k + rrow * D;
+  const long long orow = (long long)j0 * h_kv + rrow;
   // two 8-byte loads: dims 4c..4c+3 and 64+4c..64+4c+3
   uint2 a = *(const uint2*)(src + 4 * lane16);
   uint2 b = *(const uint2*)(src + HALF + 4 * lane16);
@@ -42,7 +45,7 @@ __global__ void __launch_bounds__(256) rotate_keys_kernel(
   for (int t = 0; t < 4; ++t) {
     const int c = 4 * lane16 + t;
     float sn, cs;
-    sincosf(reduce_angle(pos, inv_freq[c]), &sn, &cs);
+    sincosf(reduce_angle(pos, fq.v[c]), &sn, &cs);
     const float x = bf16_bits_to_f32(xa[t]);
     const float y = bf16_bits_to_f32(xb[t]);
     ss += x * x + y * y;
@@ -64,10 +67,10 @@ __global__ void __launch_bounds__(256) rotate_keys_kernel(
   ob.x = hb[0] | ((uint32_t)hb[1] << 16); ob.y = hb[2] | ((uint32_t)hb[3] << 16);
   pa.x = la[0] | ((uint32_t)la[1] << 16); pa.y = la[2] | ((uint32_t)la[3] << 16);
   pb.x = lb[0] | ((uint32_t)lb[1] << 16); pb.y = lb[2] | ((uint32_t)lb[3] << 16);
-  *(uint2*)(khi + rrow * D + 4 * lane16) = oa;
-  *(uint2*)(khi + rrow * D + HALF + 4 * lane16) = ob;
-  *(uint2*)(klo + rrow * D + 4 * lane16) = pa;
-  *(uint2*)(klo + rrow * D + HALF + 4 * lane16) = pb;
+  *(uint2*)(khi + orow * D + 4 * lane16) = oa;
+  *(uint2*)(khi + orow * D + HALF + 4 * lane16) = ob;
+  *(uint2*)(klo + orow * D + 4 * lane16) = pa;
+  *(uint2*)(klo + orow * D + HALF + 4 * lane16) = pb;
   // high-norm keys: one bit per key, OR-ed in (order-independent)
   if (lane16 == 0 && thr2 >= 0.f && ss > thr2)
     atomicOr(&kbits[(long long)g * kbits_words + (j >> 5)], 1u << (j & 31));
@@ -169,14 +172,33 @@ hipError_t launch_hn_next(const uint32_t* kbits, uint8_t* hn, int n_pad, int h_k
   return hipGetLastError();
 }
 
+// Clear the bits of keys [j0, j0 + n) of every KV head (partial words keep their other bits).
+__global__ void kbits_clear_range_kernel(uint32_t* __restrict__ kbits, int kbits_words, int h_kv, int j0, int n) {
+  const int w0 = j0 >> 5, w1 = (j0 + n - 1) >> 5;
+  const long long nw = (long long)(w1 - w0 + 1) * h_kv;
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < nw; i += (long long)gridDim.x * blockDim.x) {
+    const int g = (int)(i / (w1 - w0 + 1));
+    const int w = w0 + (int)(i % (w1 - w0 + 1));
+    const int lo = max(j0, 32 * w) - 32 * w;             // first bit of the range in this word
+    const int hi = min(j0 + n, 32 * w + 32) - 32 * w;    // one past the last
+    const uint32_t m = (hi - lo == 32) ? 0xFFFFFFFFu : (((1u << (hi - lo)) - 1u) << lo);
+    atomicAnd(&kbits[(long long)g * kbits_words + w], ~m);
+  }
+}
+
+// Rotates keys [j0, j0 + n) (k points at key j0).  clear_all: the whole bitmap
+// is cleared first (a fresh prefix), else only the bits of the range.
 hipError_t launch_rotate_keys(const uint16_t* k, uint16_t* khi, uint16_t* klo, uint32_t* kbits,
-                              const double* inv_freq, int n_k, int h_kv, int S, float thr2, int kbits_words,
-                              hipStream_t stream) {
-  const long long rows = (long long)n_k * h_kv;
+                              const Freqs& f, int j0, int n, int h_kv, int S, float thr2, int kbits_words,
+                              bool clear_all, hipStream_t stream) {
+  const long long rows = (long long)n * h_kv;
   const int blocks = (int)((rows + 15) / 16);
-  hipLaunchKernelGGL(kbits_clear_kernel, dim3(256), dim3(256), 0, stream, kbits, (long long)h_kv * kbits_words);
+  if (clear_all)
+    hipLaunchKernelGGL(kbits_clear_kernel, dim3(256), dim3(256), 0, stream, kbits, (long long)h_kv * kbits_words);
+  else
+    hipLaunchKernelGGL(kbits_clear_range_kernel, dim3(64), dim3(256), 0, stream, kbits, kbits_words, h_kv, j0, n);
   hipLaunchKernelGGL(rotate_keys_kernel, dim3(blocks), dim3(256), 0, stream,
-                     k, khi, klo, kbits, inv_freq, n_k, h_kv, S, thr2, kbits_words);
+                     k, khi, klo, kbits, f, j0, n, h_kv, S, thr2, kbits_words);
   return hipGetLastError();
 }
 

@@ -27,7 +27,8 @@ def _declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = _declared_functions()
-    assert set(names) == {"dca_workspace_size", "vs_index_build", "dca_sparse_prefill", "dca_strerror"}
+    assert set(names) == {"dca_workspace_size", "vs_index_build", "dca_sparse_prefill", "dca_key_cache_append",
+                          "dca_decode_workspace_size", "dca_decode", "dca_strerror"}
     out = subprocess.run(["nm", "-D", "--defined-only", S.LIB_PATH], capture_output=True, text=True).stdout
     exported = {l.split()[-1] for l in out.splitlines() if l.strip()}
     for n in names:
@@ -47,6 +48,20 @@ def test_struct_layout_matches_header(tmp_path):
     vals = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True).stdout.split()]
     assert vals[0] == ctypes.sizeof(S.dca_cfg)
     assert vals[1:] == [getattr(S.dca_cfg, f).offset for f, _ in S.dca_cfg._fields_]
+
+
+def test_key_cache_struct_layout_matches_header(tmp_path):
+    prog = tmp_path / "kc.c"
+    prog.write_text(
+        '#include <stdio.h>\n#include <stddef.h>\n#include "%s"\n'
+        'int main(void){printf("%%zu", sizeof(dca_key_cache));\n' % HEADER
+        + "".join('printf(" %%zu", offsetof(dca_key_cache, %s));\n' % f for f, _ in S.dca_key_cache._fields_)
+        + "return 0;}\n")
+    exe = tmp_path / "kc"
+    subprocess.run(["gcc", str(prog), "-o", str(exe)], check=True)
+    vals = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True).stdout.split()]
+    assert vals[0] == ctypes.sizeof(S.dca_key_cache)
+    assert vals[1:] == [getattr(S.dca_key_cache, f).offset for f, _ in S.dca_key_cache._fields_]
 
 
 def _cfg(**kw):
@@ -152,3 +167,72 @@ def test_index_rejects_missing_outputs():
 def test_strerror_covers_codes():
     for code in (0, -1, -2, -3, -4, 7):
         assert isinstance(S.dca_strerror(code), str) and S.dca_strerror(code)
+
+
+
+# ---------------------------------------------------------------- decode entry points
+def _dcfg(**kw):
+    base = dict(n_q=1, n_k=5000, h_q=28, h_kv=4, dca_chunk=1024, dca_local=256, rope_base=1e7, yarn_s=4.0)
+    base.update(kw)
+    return S.Config(**base)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(head_dim=64), S.DCA_EUNSUPPORTED),
+    (dict(dca_chunk=96), S.DCA_EUNSUPPORTED),
+    (dict(dca_local=2000), S.DCA_EUNSUPPORTED),
+    (dict(n_q=0), S.DCA_EINVAL),
+    (dict(n_q=65, n_k=100), S.DCA_EUNSUPPORTED),
+    (dict(n_q=10, n_k=5), S.DCA_EINVAL),
+    (dict(h_q=30), S.DCA_EINVAL),
+    (dict(split_k=5000), S.DCA_EINVAL),
+    (dict(yarn_s=-1.0), S.DCA_EINVAL),
+])
+def test_decode_workspace_size_validation(kw, code):
+    with pytest.raises(S.DcaError) as ei:
+        S.dca_decode_workspace_size(_dcfg(**kw))
+    assert ei.value.code == code
+
+
+def test_decode_workspace_holds_the_parts():
+    # any positions work (no 64-row alignment); the parts' fp32 partials dominate
+    small = S.dca_decode_workspace_size(_dcfg())
+    big = S.dca_decode_workspace_size(_dcfg(n_k=1 << 20, dca_chunk=262144, dca_local=4096, n_q=4))
+    assert 0 < small < big
+    parts = (S.dca_decode_workspace_size(_dcfg(n_k=65536, split_k=64))
+             - S.dca_decode_workspace_size(_dcfg(n_k=65536, split_k=32)))
+    assert parts >= 32 * 28 * 128 * 4
+
+
+class _FakeCache(S.KeyCache):
+    def __init__(self, capacity):
+        t = _FakeTensor()
+        super().__init__(k_hi=t, k_lo=t, k_flags=t, capacity=capacity)
+
+
+def test_decode_rejects_bad_calls_before_any_launch():
+    cfg = _dcfg()
+    t = _FakeTensor(S.dca_decode_workspace_size(cfg))
+    with pytest.raises(S.DcaError) as ei:                      # cache smaller than n_k
+        S.dca_decode(t, _FakeCache(4999), t, cfg, t, t, stream=0)
+    assert ei.value.code == S.DCA_EINVAL
+    with pytest.raises(S.DcaError) as ei:                      # workspace too small
+        S.dca_decode(t, _FakeCache(5000), t, cfg, t, _FakeTensor(t.numel() - 1), stream=0)
+    assert ei.value.code == S.DCA_EWORKSPACE
+    c = cfg.to_c(workspace=0x1000, workspace_bytes=1 << 30, v_idx=0x1000)
+    kc = _FakeCache(5000).to_c()
+    assert S.lib().dca_decode(0x1000, ctypes.byref(kc), 0x1000, ctypes.byref(c), 0x1000) == S.DCA_EINVAL
+    c = cfg.to_c(workspace=0x1000, workspace_bytes=1 << 30)
+    assert S.lib().dca_decode(0x1000, None, 0x1000, ctypes.byref(c), 0x1000) == S.DCA_EINVAL
+
+
+def test_key_cache_append_validation():
+    cfg = _dcfg()
+    t = _FakeTensor()
+    for j0, n, cap, code in [(-1, 4, 100, S.DCA_EINVAL), (0, 0, 100, S.DCA_EINVAL), (90, 20, 100, S.DCA_EINVAL)]:
+        c = cfg.to_c(stream=0)
+        kc = _FakeCache(cap).to_c()
+        assert S.lib().dca_key_cache_append(0x1000, j0, n, ctypes.byref(c), ctypes.byref(kc)) == code
+    c = _dcfg(dca_chunk=100).to_c(stream=0)
+    kc = _FakeCache(100).to_c()
+    assert S.lib().dca_key_cache_append(0x1000, 0, 10, ctypes.byref(c), ctypes.byref(kc)) == S.DCA_EUNSUPPORTED
