@@ -210,31 +210,31 @@ __global__ void __launch_bounds__(64) dca_decode_kernel(DecArgs A) {
   };
 
   // ---- the part's tiles, two stages: tile ti+2 is loaded into the stage of
-  // tile ti once ti is computed.  The waits count this wave's loads: 16 per
-  // tile (8 K, 8 V), issued in tile order (other vector loads in between only
-  // make a wait longer).
+  // tile ti once ti is computed.  Every step issues its 16 loads (8 K, 8 V),
+  // past the part's end as repeats of its last tile (served by the L2), so
+  // the number of loads issued after any tile is fixed: a tile has landed
+  // when at most 16 of this wave's vector loads are outstanding (other loads
+  // in between only make that wait longer).
+  const int t_last = t_end - 1;
   issue(rs_k, kst0, BN * t_beg);
   issue(rs_v, vst0, BN * t_beg);
-  if (t_beg + 1 < t_end) {
-    issue(rs_k, kst1, BN * (t_beg + 1));
-    issue(rs_v, vst1, BN * (t_beg + 1));
-  }
+  issue(rs_k, kst1, BN * min(t_beg + 1, t_last));
+  issue(rs_v, vst1, BN * min(t_beg + 1, t_last));
   auto step = [&](uint8_t* kc, uint8_t* vc, int ti) __attribute__((always_inline)) {
-    if (ti + 1 < t_end) __builtin_amdgcn_s_waitcnt(0x4F70);   // vmcnt(16): tile ti+1 may be in flight
-    else __builtin_amdgcn_s_waitcnt(0x0F70);                  // vmcnt(0)
+    __builtin_amdgcn_s_waitcnt(0x4F70);   // vmcnt(16): tile ti landed, tile ti+1 may be in flight
     asm volatile("" ::: "memory");
     compute_tile(kc, vc, BN * ti);
-    if (ti + 2 < t_end) {
-      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this stage's reads are done
-      asm volatile("" ::: "memory");
-      issue(rs_k, kc, BN * (ti + 2));
-      issue(rs_v, vc, BN * (ti + 2));
-    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this stage's reads are done
+    asm volatile("" ::: "memory");
+    issue(rs_k, kc, BN * min(ti + 2, t_last));
+    issue(rs_v, vc, BN * min(ti + 2, t_last));
   };
   for (int ti = t_beg; ti < t_end; ti += 2) {
     step(kst0, vst0, ti);
     if (ti + 1 < t_end) step(kst1, vst1, ti + 1);
   }
+  // the repeats land before the workgroup's LDS is released
+  __builtin_amdgcn_s_waitcnt(0x0F70);
 
   // ---- the part's partial of this column: O normalised, natural-log lse
   const float l_tot = pair_sum(l_run);
@@ -257,24 +257,25 @@ __global__ void __launch_bounds__(64) dca_decode_kernel(DecArgs A) {
 }
 
 // LSE merge of the parts of one (token, head): m = max_p lse_p,
-// O = sum_p e^{lse_p - m} O_p / sum_p e^{lse_p - m}.  Eight 32-lane groups take
-// every eighth part (lane: 4 dims); the groups' sums are combined in order.
-__global__ void __launch_bounds__(256) dca_decode_merge_kernel(const float* __restrict__ part_o,
-                                                               const float* __restrict__ part_lse,
-                                                               uint16_t* __restrict__ out, float* __restrict__ lse_out,
-                                                               int P, int n_t, int h_q) {
-  __shared__ float sm_m[8], sm_w[8];
-  __shared__ float4 sm_acc[8][32];
+// O = sum_p e^{lse_p - m} O_p / sum_p e^{lse_p - m}.  32 groups of 32 lanes
+// take every 32nd part (lane: 4 dims); the groups' sums are combined in order.
+constexpr int MERGE_GROUPS = 32;
+__global__ void __launch_bounds__(1024) dca_decode_merge_kernel(const float* __restrict__ part_o,
+                                                                const float* __restrict__ part_lse,
+                                                                uint16_t* __restrict__ out, float* __restrict__ lse_out,
+                                                                int P, int n_t, int h_q) {
+  __shared__ float sm_m[MERGE_GROUPS], sm_w[MERGE_GROUPS];
+  __shared__ float4 sm_acc[MERGE_GROUPS][32];
   const int t = blockIdx.x / h_q;
   const int h = blockIdx.x % h_q;
   const int sg = threadIdx.x >> 5;
   const int l = threadIdx.x & 31;
   float m = -INFINITY;
-  for (int p = sg; p < P; p += 8) m = fmaxf(m, part_lse[((long long)p * h_q + h) * n_t + t]);
+  for (int p = sg; p < P; p += MERGE_GROUPS) m = fmaxf(m, part_lse[((long long)p * h_q + h) * n_t + t]);
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   float w = 0.f;
   if (m != -INFINITY) {
-    for (int p = sg; p < P; p += 8) {
+    for (int p = sg; p < P; p += MERGE_GROUPS) {
       const float lp = part_lse[((long long)p * h_q + h) * n_t + t];
       const float wt = (lp == -INFINITY) ? 0.f : __expf(lp - m);
       const float4 x = *(const float4*)(part_o + (((long long)p * n_t + t) * h_q + h) * D + 4 * l);
@@ -287,11 +288,11 @@ __global__ void __launch_bounds__(256) dca_decode_merge_kernel(const float* __re
   __syncthreads();
   if (sg != 0) return;
   float M = -INFINITY;
-  for (int u = 0; u < 8; ++u) M = fmaxf(M, sm_m[u]);
+  for (int u = 0; u < MERGE_GROUPS; ++u) M = fmaxf(M, sm_m[u]);
   float4 tot = make_float4(0.f, 0.f, 0.f, 0.f);
   float wsum = 0.f;
   if (M != -INFINITY) {
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < MERGE_GROUPS; ++u) {
       const float e = (sm_m[u] == -INFINITY) ? 0.f : __expf(sm_m[u] - M);
       const float4 a = sm_acc[u][l];
       tot.x += e * a.x; tot.y += e * a.y; tot.z += e * a.z; tot.w += e * a.w;
@@ -313,7 +314,7 @@ hipError_t launch_decode_attn(const DecArgs& A, hipStream_t stream) {
 }
 
 hipError_t launch_decode_merge(const DecArgs& A, uint16_t* out, float* lse_out, hipStream_t stream) {
-  hipLaunchKernelGGL(dca_decode_merge_kernel, dim3((unsigned)(A.n_t * A.h_q)), dim3(256), 0, stream, A.part_o,
+  hipLaunchKernelGGL(dca_decode_merge_kernel, dim3((unsigned)(A.n_t * A.h_q)), dim3(1024), 0, stream, A.part_o,
                      A.part_lse, out, lse_out, A.n_parts, A.n_t, A.h_q);
   return hipGetLastError();
 }
