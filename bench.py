@@ -130,6 +130,22 @@ def cpu_baseline(w, inputs, p0s, f_blocks_total: float, n_blocks_total: int):
     }
 
 
+def decode_traffic_from_profile():
+    """HBM bytes per decode launch from the committed counter summary, if it was taken on
+    the current decode kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "decode_traffic.json")
+    src = os.path.join(ROOT, "sparse_dual_chunk_amd", "csrc", "decode.hip")
+    if not os.path.exists(path):
+        return None
+    try:
+        d = json.load(open(path))
+    except Exception:
+        return None
+    if d.get("decode_source_sha256_16") != hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]:
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
 DECODE_METRIC = "decode-step attention over a 1M-key KV cache, 7B heads: cache GB/s (K + V read per step)"
 
 
@@ -201,7 +217,7 @@ def bench_decode(args) -> int:
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
-            "traffic": None,
+            "traffic": decode_traffic_from_profile(),
             "kernel": "dca_decode_kernel",
             "avg_launch_ms": round(attn_ms, 5),
             "algorithmic_bytes_per_launch": algo_bytes,
