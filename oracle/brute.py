@@ -63,8 +63,20 @@ def _cover(i0: int, n_k: int, vcols, soffs) -> List[int]:
     return sorted(keys)
 
 
-def attention(q, k, v, p0: int, cfg: dict, v_idx=None, s_off=None):
-    """q [n_q][h_q][d], k, v [n_k][h_kv][d] as nested float lists.
+def _exact_keys(p: int, vcols, soffs) -> List[int]:
+    keys = set()
+    for delta in [0] + [x for x in soffs if x >= 0]:
+        if p - delta >= 0:
+            keys.add(p - delta)
+    for c in vcols:
+        if 0 <= c <= p:
+            keys.add(c)
+    return sorted(keys)
+
+
+def attention(q, k, v, p0: int, cfg: dict, v_idx=None, s_off=None, exact: bool = False):
+    """q [n_q][h_q][d], k, v [n_k][h_kv][d] as nested float lists.  ``exact``: a row
+    attends the keys exactly on its selected diagonals and vertical columns.
 
     Returns (out [n_q][h_q][d], lse [h_q][n_q]).
     """
@@ -80,8 +92,11 @@ def attention(q, k, v, p0: int, cfg: dict, v_idx=None, s_off=None):
         for i in range(n_q):
             p = p0 + i
             i0 = p0 + (i // 64) * 64
-            cov = _cover(i0, n_k, None if v_idx is None else v_idx[h], None if s_off is None else s_off[h])
-            keys = [j for j in cov if j <= p]
+            if exact and v_idx is not None:
+                keys = _exact_keys(p, v_idx[h], s_off[h])
+            else:
+                cov = _cover(i0, n_k, None if v_idx is None else v_idx[h], None if s_off is None else s_off[h])
+                keys = [j for j in cov if j <= p]
             if not keys:
                 continue
             logits = []
@@ -98,8 +113,9 @@ def attention(q, k, v, p0: int, cfg: dict, v_idx=None, s_off=None):
     return out, lse
 
 
-def vs_index(q, k, p0: int, cfg: dict):
-    """Vertical / slash scores and top-k selections, by loops over (row, key)."""
+def vs_index(q, k, p0: int, cfg: dict, budgets=None):
+    """Vertical / slash scores and top-k selections, by loops over (row, key).
+    ``budgets``: per-head (k_v, k_s), padded to the config's k with -1."""
     n_q, h_q, d = len(q), len(q[0]), len(q[0][0])
     n_k = len(k)
     S, base = cfg["dca_chunk"], cfg["rope_base"]
@@ -127,8 +143,9 @@ def vs_index(q, k, p0: int, cfg: dict):
                 slash[p - j] += w[j] / z
         verts.append(vert)
         slashes.append(slash)
-        vsel.append(_topk(vert, kv, forced=()))
-        ssel.append(_topk(slash, ks, forced=(0,)))
+        kvh, ksh = (kv, ks) if budgets is None else budgets[h]
+        vsel.append(_topk(vert, kvh, forced=()) + [-1] * (kv - kvh))
+        ssel.append(_topk(slash, ksh, forced=(0,)) + [-1] * (ks - ksh))
     return vsel, ssel, verts, slashes
 
 

@@ -37,6 +37,10 @@ in the design notes lists every one):
     covers keys [i0 - delta, i0 - delta + 63]; the vertical columns are added;
     the union is clipped to [0, i0 + 63] and each row then attends its causal
     part.  Empty sets give O = 0, lse = -inf.
+  * Exact-diagonal variant (optional): a row at position p attends key j <= p
+    when p - j is a selected offset (or 0) or j a selected vertical column,
+    with no 64-row granule.  Per-head budgets (optional): each head keeps its
+    own k best of each list, padded to the configured k with -1.
   * Generation step (decode): the newest tokens attend every cached key up to
     their own position with the same DCA positions, densely (the pages apply
     the sparse attention to the prefill).
@@ -192,6 +196,21 @@ def block_cover(i0: int, n_k: int, v_idx_h: Optional[np.ndarray], s_off_h: Optio
     return np.flatnonzero(covered).astype(np.int64)
 
 
+def exact_cover_mask(p_rows: np.ndarray, keys: np.ndarray, v_idx_h: Optional[np.ndarray],
+                     s_off_h: Optional[np.ndarray]) -> np.ndarray:
+    """Exact-diagonal semantics: row at position p attends key j <= p iff p - j is a
+    selected slash offset (or 0), or j is a selected vertical column.  Returns the
+    [R][N] bool mask over ``keys``; negative entries are padding."""
+    offs = np.asarray(s_off_h if s_off_h is not None else [], dtype=np.int64)
+    offs = np.unique(np.concatenate([[0], offs[offs >= 0]]))
+    cols = np.asarray(v_idx_h if v_idx_h is not None else [], dtype=np.int64)
+    cols = cols[cols >= 0]
+    delta = p_rows[:, None] - keys[None, :]
+    on_slash = np.isin(delta, offs)
+    on_vert = np.isin(keys, cols)[None, :]
+    return (delta >= 0) & (on_slash | on_vert)
+
+
 def slash_intervals(s_off_h: Optional[np.ndarray]) -> np.ndarray:
     """Union of the slash footprints [-delta, -delta+64) (and delta = 0) as disjoint
     half-open intervals in offset space relative to a block start, ascending."""
@@ -232,9 +251,11 @@ def cover_sizes(n_q: int, p0: int, n_k: int, v_idx_h, s_off_h) -> np.ndarray:
 
 
 def attention_block(q: np.ndarray, k: np.ndarray, v: np.ndarray, p0: int, h: int, b: int, cfg: dict,
-                    v_idx: Optional[np.ndarray] = None, s_off: Optional[np.ndarray] = None):
+                    v_idx: Optional[np.ndarray] = None, s_off: Optional[np.ndarray] = None, exact: bool = False):
     """Output rows of query block b for query head h.  q, k, v are bf16 bit arrays.
 
+    ``exact``: the exact-diagonal semantics of :func:`exact_cover_mask` instead of
+    the 64-row block cover (sparse calls only).
     Returns (out [rows][d], lse [rows], cover keys).
     """
     n_q = q.shape[0]
@@ -246,15 +267,19 @@ def attention_block(q: np.ndarray, k: np.ndarray, v: np.ndarray, p0: int, h: int
     i0 = p0 + r0
     dense = v_idx is None and s_off is None
     keys = block_cover(i0, n_k, None if dense else v_idx[h], None if dense else s_off[h], dense)
-    allowed = keys[None, :] <= p_rows[:, None]
+    if exact and not dense:
+        allowed = exact_cover_mask(p_rows, keys, v_idx[h], s_off[h])
+    else:
+        allowed = keys[None, :] <= p_rows[:, None]
     out, lse = attend_rows(bf16_to_f64(q[r0:r1, h]), p_rows, bf16_to_f64(k[keys, g]), bf16_to_f64(v[keys, g]),
                            keys, allowed, cfg["dca_chunk"], cfg["dca_local"], cfg["rope_base"],
                            softmax_scale(cfg["yarn_s"], q.shape[2]))
     return out, lse, keys
 
 
-def attention(q, k, v, p0: int, cfg: dict, v_idx=None, s_off=None, heads=None):
-    """Full prefill attention for one call (dense if v_idx and s_off are None).
+def attention(q, k, v, p0: int, cfg: dict, v_idx=None, s_off=None, heads=None, exact: bool = False):
+    """Full prefill attention for one call (dense if v_idx and s_off are None;
+    ``exact`` selects the exact-diagonal semantics for sparse calls).
 
     Returns (out [n_q][h_q][d] fp64, lse [h_q][n_q] fp64).
     """
@@ -264,7 +289,7 @@ def attention(q, k, v, p0: int, cfg: dict, v_idx=None, s_off=None, heads=None):
     nb = (n_q + QBLOCK - 1) // QBLOCK
     for h in (range(h_q) if heads is None else heads):
         for b in range(nb):
-            o, l, _ = attention_block(q, k, v, p0, h, b, cfg, v_idx, s_off)
+            o, l, _ = attention_block(q, k, v, p0, h, b, cfg, v_idx, s_off, exact)
             r0 = b * QBLOCK
             out[r0:r0 + len(l), h] = o
             lse[h, r0:r0 + len(l)] = l
@@ -400,8 +425,12 @@ def topk_ascending(scores: np.ndarray, k: int, forced: Sequence[int] = ()):
     return out, gap
 
 
-def vs_index(q, k, p0: int, cfg: dict, heads=None):
-    """Vertical column ids [h_q][k_v] and slash offsets [h_q][k_s], plus the cut gaps."""
+def vs_index(q, k, p0: int, cfg: dict, heads=None, budgets=None):
+    """Vertical column ids [h_q][k_v] and slash offsets [h_q][k_s], plus the cut gaps.
+
+    ``budgets`` [h_q][2] (optional): per-head (k_v, k_s), each at most the
+    config's k_v, k_s; a head's row holds its own k best, padded with -1.
+    """
     h_q = q.shape[1]
     kv, ks = cfg["vs_k_vertical"], cfg["vs_k_slash"]
     vert, slash, _ = vs_scores(q, k, p0, cfg, heads)
@@ -409,8 +438,9 @@ def vs_index(q, k, p0: int, cfg: dict, heads=None):
     s_off = np.full((h_q, ks), -1, dtype=np.int32)
     gaps = []
     for h in (range(h_q) if heads is None else heads):
-        v_idx[h], gv = topk_ascending(vert[h], kv)
-        s_off[h], gs = topk_ascending(slash[h], ks, forced=(0,))
+        kv_h, ks_h = (kv, ks) if budgets is None else (int(budgets[h][0]), int(budgets[h][1]))
+        v_idx[h, :kv_h], gv = topk_ascending(vert[h], kv_h)
+        s_off[h, :ks_h], gs = topk_ascending(slash[h], ks_h, forced=(0,))
         gaps.append((h, gv, gs))
     return v_idx, s_off, gaps
 

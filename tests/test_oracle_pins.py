@@ -448,3 +448,87 @@ def test_decode_zero_query_gives_mean_and_log_count():
         p = n_k - n_t + t
         assert np.allclose(out[t, 1], vf[: p + 1].mean(axis=0), rtol=0, atol=1e-13)
         assert abs(lse[1, t] - math.log(p + 1)) <= 1e-12
+
+
+# ---------------------------------------------------------------- exact-diagonal slashes, per-head budgets
+def _pattern(rng, h_q, n_k, kv, ks):
+    v_idx = np.full((h_q, kv), -1, np.int32)
+    s_off = np.full((h_q, ks), -1, np.int32)
+    for h in range(h_q):
+        nv, ns = kv - int(rng.integers(0, 2)), ks - int(rng.integers(0, 2))
+        v_idx[h, :nv] = np.sort(rng.choice(n_k, nv, replace=False))
+        s_off[h, :ns] = np.sort(rng.choice(n_k, ns, replace=False))
+    return v_idx, s_off
+
+
+@pytest.mark.parametrize("p0,n_q", [(0, 48), (128, 40)])
+def test_exact_diagonals_match_brute_force(p0, n_q):
+    q, k, v = _tiny(60 + p0, n_q, p0, sink=True)
+    n_k = p0 + n_q
+    v_idx, s_off = _pattern(np.random.default_rng(p0), 2, n_k, 5, 9)
+    cfg = _cfg(2, 1, 8, 3, base=1e4, kv=5, ks=9)
+    out, lse = O.attention(q, k, v, p0, cfg, v_idx=v_idx, s_off=s_off, exact=True)
+    bo, bl = brute.attention(_nested(q), _nested(k), _nested(v), p0, cfg, v_idx.tolist(), s_off.tolist(),
+                             exact=True)
+    assert np.abs(out - np.array(bo)).max() <= 1e-12
+    assert np.abs(lse - np.array(bl)).max() <= 1e-12
+
+
+def test_exact_self_diagonal_only_returns_own_value():
+    """Only delta = 0 and no vertical: each row attends itself, out = v_i, lse = its own logit."""
+    rng = np.random.default_rng(61)
+    p0, n_q, d = 64, 70, 128
+    n_k = p0 + n_q
+    q, k, v = _bf16(rng, (n_q, 2, d)), _bf16(rng, (n_k, 1, d)), _bf16(rng, (n_k, 1, d))
+    cfg = _cfg(2, 1, 32, 8, kv=1, ks=1)
+    none = np.full((2, 1), -1, np.int32)
+    out, lse = O.attention(q, k, v, p0, cfg, v_idx=none, s_off=none, exact=True)
+    vf = O.bf16_to_f64(v[:, 0])
+    assert np.array_equal(out[:, 0], vf[p0:]) and np.array_equal(out[:, 1], vf[p0:])
+    # r_i = p_i mod 32 for both query and key: the logit is scale * |q|.|k| turned by the same angle
+    for i in (0, 33, 69):
+        p = p0 + i
+        ql = O.rope(O.bf16_to_f64(q[i, 0]), p % 32, 1e6)
+        kl = O.rope(O.bf16_to_f64(k[p, 0]), p % 32, 1e6)
+        assert abs(lse[0, i] - O.softmax_scale(4.0, d) * float(ql @ kl)) <= 1e-12
+
+
+def test_exact_all_offsets_equals_dense():
+    rng = np.random.default_rng(62)
+    p0, n_q, d = 128, 100, 128
+    n_k = p0 + n_q
+    q, k, v = _bf16(rng, (n_q, 2, d)), _bf16(rng, (n_k, 1, d)), _bf16(rng, (n_k, 1, d))
+    cfg = _cfg(2, 1, 64, 16, kv=1, ks=n_k)
+    s_off = np.tile(np.arange(n_k, dtype=np.int32), (2, 1))
+    out, lse = O.attention(q, k, v, p0, cfg, v_idx=np.full((2, 1), -1, np.int32), s_off=s_off, exact=True)
+    ref, ref_lse = O.attention(q, k, v, p0, _cfg(2, 1, 64, 16))
+    assert np.abs(out - ref).max() <= 1e-12 and np.abs(lse - ref_lse).max() <= 1e-12
+
+
+def test_exact_zero_query_gives_mean_over_the_exact_set():
+    rng = np.random.default_rng(63)
+    p0, n_q, d = 64, 60, 128
+    n_k = p0 + n_q
+    q = np.zeros((n_q, 1, d), np.uint16)
+    k, v = _bf16(rng, (n_k, 1, d)), _bf16(rng, (n_k, 1, d))
+    v_idx = np.array([[2, 50, 90]], np.int32)
+    s_off = np.array([[1, 7, 64, -1]], np.int32)
+    out, lse = O.attention(q, k, v, p0, _cfg(1, 1, 32, 8, kv=3, ks=4), v_idx=v_idx, s_off=s_off, exact=True)
+    vf = O.bf16_to_f64(v[:, 0])
+    for i in range(n_q):
+        p = p0 + i
+        A = sorted({p - dl for dl in (0, 1, 7, 64) if p - dl >= 0} | {c for c in (2, 50, 90) if c <= p})
+        assert np.allclose(out[i, 0], vf[A].mean(axis=0), rtol=0, atol=1e-13)
+        assert abs(lse[0, i] - math.log(len(A))) <= 1e-13
+
+
+def test_index_per_head_budgets_match_brute_force():
+    q, k, _ = _tiny(70, 40, 64)
+    cfg = _cfg(2, 1, 8, 3, base=1e4, kv=6, ks=9, last=16)
+    budgets = [(6, 9), (2, 4)]
+    v_idx, s_off, _ = O.vs_index(q, k, 64, cfg, budgets=budgets)
+    bv, bs, _, _ = brute.vs_index(_nested(q), _nested(k), 64, cfg, budgets=budgets)
+    assert v_idx.tolist() == bv and s_off.tolist() == bs
+    assert (v_idx[1, 2:] == -1).all() and (s_off[1, 4:] == -1).all()
+    full_v, full_s, _ = O.vs_index(q, k, 64, cfg)
+    assert np.array_equal(full_v[0], v_idx[0]) and np.array_equal(full_s[0], s_off[0])
