@@ -258,6 +258,8 @@ def main() -> int:
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes (3 launches), "
                          "the reference for scaling the HBM byte counters")
+    ap.add_argument("--slash-exact", action="store_true",
+                    help="sparse calls with the exact-diagonal semantics instead of the 64-row block cover")
     ap.add_argument("--decode", action="store_true",
                     help="measure the generation-step attention over the 1M-key cache instead of the prefill")
     ap.add_argument("--decode-tokens", type=int, default=1)
@@ -292,7 +294,8 @@ def main() -> int:
     calls = []
     for c in range(len(w.chunks)):
         inp = W.make(w, c, seed=args.seed, kv=kv)
-        cfg = S.config_for(w, c, **({"split_k": args.split_k} if args.split_k else {}))
+        cfg = S.config_for(w, c, **({"split_k": args.split_k} if args.split_k else {}),
+                           **({"slash_exact": 1} if args.slash_exact else {}))
         calls.append((inp, cfg))
     log("uploading to HBM")
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
@@ -390,6 +393,7 @@ def main() -> int:
             "h_q": w.h_q, "h_kv": w.h_kv, "head_dim": w.head_dim,
             "dca_chunk": w.dca_chunk, "dca_local": w.dca_local, "rope_base": w.rope_base, "yarn_s": w.yarn_s,
             "k_vertical": w.k_vertical, "k_slash": w.k_slash, "seed": args.seed,
+            **({"slash_semantics": "exact diagonals"} if args.slash_exact else {}),
         },
         "roofline": {
             "bound": "mfma",
@@ -398,7 +402,8 @@ def main() -> int:
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
-            "kernel": "dca_attn_kernel" if w.sparse else "dca_attn_dense_kernel",
+            "kernel": ("dca_attn_exact_kernel" if args.slash_exact else "dca_attn_kernel") if w.sparse
+                      else "dca_attn_dense_kernel",
             "avg_launch_ms": round(attn_avg_ms, 4),
             "algorithmic_flops_per_launch": f_per_launch,
         },

@@ -107,6 +107,17 @@ typedef struct dca_cfg {
    * that dca_sparse_prefill records on cfg->stream around each stage; NULL =
    * no timing.  Stages that do not run still get both events recorded. */
   void  **stage_events;
+  /* Sparse semantics of dca_sparse_prefill.  0: the block cover above (64-row
+   * granule).  1: exact diagonals: row i attends key j <= p_i when p_i - j is a
+   * selected offset (or 0) or j a selected vertical column.  Both compute the
+   * same covered tiles (cover_pairs is the block cover in both); the exact
+   * reading masks each row to its own diagonals. */
+  int32_t slash_exact;
+  /* Optional device int32 [h_q][2]: per-head budgets (k_v, k_s) for
+   * vs_index_build, each clamped to [0, vs_k_vertical] / [0, vs_k_slash]; a
+   * head's rows hold its own k best, padded with -1.  NULL: every head takes
+   * vs_k_vertical and vs_k_slash. */
+  const int32_t *vs_k_per_head;
 } dca_cfg;
 
 /* Bytes of workspace both entry points need for this configuration (the

@@ -61,6 +61,8 @@ class dca_cfg(ctypes.Structure):
         ("workspace_bytes", ctypes.c_size_t),
         ("stream", ctypes.c_void_p),
         ("stage_events", ctypes.c_void_p),
+        ("slash_exact", ctypes.c_int32),
+        ("vs_k_per_head", ctypes.c_void_p),
     ]
 
 
@@ -130,6 +132,7 @@ class Config:
     vs_k_slash: int = 0
     precise_norm: float = 0.0
     split_k: int = 0
+    slash_exact: int = 0
 
     def to_c(self, **ptrs) -> dca_cfg:
         c = dca_cfg()
@@ -171,11 +174,12 @@ def dca_workspace_size(cfg: Config) -> int:
     return int(n.value)
 
 
-def vs_index_build(q, k, positions, cfg: Config, v_idx, s_off, workspace, stream=None) -> None:
-    """Vertical-slash index of one chunk; writes v_idx [h_q][k_v] and s_off [h_q][k_s] (int32, device)."""
+def vs_index_build(q, k, positions, cfg: Config, v_idx, s_off, workspace, stream=None, k_per_head=None) -> None:
+    """Vertical-slash index of one chunk; writes v_idx [h_q][k_v] and s_off [h_q][k_s] (int32, device).
+    k_per_head: optional device int32 [h_q][2] per-head budgets (k_v, k_s)."""
     pos, pos_p = _positions(positions)
     c = cfg.to_c(workspace=_ptr(workspace), workspace_bytes=workspace.numel() * workspace.element_size(),
-                 stream=_stream(stream))
+                 stream=_stream(stream), vs_k_per_head=_ptr(k_per_head))
     rc = lib().vs_index_build(_ptr(q), _ptr(k), pos_p, ctypes.byref(c), _ptr(v_idx), _ptr(s_off))
     if rc != DCA_OK:
         raise DcaError(rc, "vs_index_build")

@@ -46,6 +46,8 @@ struct Layout {
   Region freqs;
   // prefill
   Region khi, klo, kbits, hn, qhi, qlo, iv, iv_pre, n_iv, cov, ext, n_ext, tiles, n_tiles, t_first, part_o, part_lse;
+  Region dbits, vbits;
+  int dbits_words = 0, vbits_words = 0;
   // index
   Region qs, part_ms, lse, vert, slash, edge, logits, trig, hist, prefix, krem, bcount;
   size_t prefill_bytes = 0, index_bytes = 0;
@@ -69,6 +71,7 @@ int validate(const dca_cfg* c, const int32_t* positions) {
   if (c->vs_last_q < 1 || c->vs_last_q > 64) return DCA_EUNSUPPORTED;
   if (c->split_k < 0 || c->split_k > 256) return DCA_EINVAL;
   if (!std::isfinite(c->precise_norm)) return DCA_EINVAL;
+  if (c->slash_exact != 0 && c->slash_exact != 1) return DCA_EINVAL;
   // the chunk of rows must be the tail of the prefix, starting on a 64 boundary
   const long long p0 = (long long)c->n_k - c->n_q;
   if (p0 % 64 != 0) return DCA_EUNSUPPORTED;
@@ -129,6 +132,14 @@ Layout make_layout(const dca_cfg* c) {
   place(L.tiles, cur, (size_t)h_q * L.tile_stride * 16);
   place(L.n_tiles, cur, (size_t)h_q * 4);
   place(L.t_first, cur, (size_t)h_q * L.nb * 4);
+  if (c->slash_exact) {
+    // windows of up to 8 words start between bit 34 and bit p_last + 160
+    L.dbits_words = (p_last + 160) / 32 + 9;
+    // 2-word windows start at key bit a + 128, a <= n_k + 95
+    L.vbits_words = (n_k + 254) / 32 + 3;
+    place(L.dbits, cur, (size_t)h_q * L.dbits_words * 4);
+    place(L.vbits, cur, (size_t)h_q * L.vbits_words * 4);
+  }
   if (L.split > 1) {
     place(L.part_o, cur, (size_t)L.split * n_q * h_q * D * 4);
     place(L.part_lse, cur, (size_t)L.split * h_q * n_q * 4);
@@ -291,6 +302,7 @@ int vs_index_build(const dca_bf16* q, const dca_bf16* k, const int32_t* position
   S.krem = at<int32_t>(cfg, L.krem);
   S.bcount = at<uint32_t>(cfg, L.bcount);
   S.max_blocks = L.max_blocks;
+  S.k_head = cfg->vs_k_per_head;
   if (launch_select(S, st) != hipSuccess) return DCA_EHIP;
   return DCA_OK;
 }
@@ -345,6 +357,9 @@ int dca_sparse_prefill(const dca_bf16* q, const dca_bf16* k, const dca_bf16* v, 
     P.tiles = at<int4>(cfg, L.tiles); P.n_tiles = at<int32_t>(cfg, L.n_tiles); P.t_first = at<int32_t>(cfg, L.t_first);
     P.kbits = at<uint32_t>(cfg, L.kbits); P.h_kv = h_kv; P.tile_stride = L.tile_stride;
     P.kbits_words = L.kbits_words;
+    P.dbits = cfg->slash_exact ? at<uint32_t>(cfg, L.dbits) : nullptr;
+    P.vbits = cfg->slash_exact ? at<uint32_t>(cfg, L.vbits) : nullptr;
+    P.dbits_words = L.dbits_words; P.vbits_words = L.vbits_words;
     if (launch_plan(P, st) != hipSuccess) return DCA_EHIP;
   } else if (cfg->cover_pairs) {
     // dense: every block covers its whole causal extent [0, i0 + rows)
@@ -371,6 +386,10 @@ int dca_sparse_prefill(const dca_bf16* q, const dca_bf16* k, const dca_bf16* v, 
   A.nb = L.nb; A.tile_stride = L.tile_stride; A.kbits_words = L.kbits_words;
   A.ext_stride = cfg->vs_k_vertical > 0 ? cfg->vs_k_vertical : 1;
   A.split = L.split; A.dense = sparse ? 0 : 1;
+  A.exact = (sparse && cfg->slash_exact) ? 1 : 0;
+  A.dbits = A.exact ? at<uint32_t>(cfg, L.dbits) : nullptr;
+  A.vbits = A.exact ? at<uint32_t>(cfg, L.vbits) : nullptr;
+  A.dbits_words = L.dbits_words; A.vbits_words = L.vbits_words;
   if (launch_attn(A, st) != hipSuccess) return DCA_EHIP;
   record(cfg, 2, 1);
   // stage 3: LSE merge of the split partials

@@ -22,7 +22,10 @@ struct AttnArgs {
   const int32_t* t_first;   // [h_q][nb] first range tile of each query block
   const int32_t* ext;       // [h_q][nb][ext_stride] vertical keys outside the ranges (bit 30: high-norm)
   const int32_t* n_ext;     // [h_q][nb]
+  const uint32_t* dbits;    // exact diagonals: [h_q][dbits_words] bit delta + 128 = selected offset (and 0)
+  const uint32_t* vbits;    // exact diagonals: [h_q][vbits_words] bit j + 128 = selected vertical column
   int n_q, n_k, h_q, h_kv, p0, S, W, nb, tile_stride, ext_stride, split, dense, kbits_words, hn_pad;
+  int exact, dbits_words, vbits_words;
 };
 
 struct DecArgs {
@@ -63,6 +66,7 @@ struct SelArgs {
   int32_t* krem;           // [2*h_q]
   uint32_t* bcount;        // [2*h_q][max_blocks][2] (gt, eq)
   int max_blocks;
+  const int32_t* k_head;   // optional [h_q][2] per-head (k_v, k_s), clamped to [0, k_v / k_s]
 };
 
 struct PlanArgs {
@@ -79,7 +83,10 @@ struct PlanArgs {
   int32_t* t_first;        // [h_q][nb]
   const uint32_t* kbits;   // [h_kv][kbits_words]
   long long* cover_pairs;  // optional: sum of rows * |cover| over all (head, block)
+  uint32_t* dbits;         // exact diagonals (or null): [h_q][dbits_words], bit delta + 128
+  uint32_t* vbits;         // exact diagonals (or null): [h_q][vbits_words], bit j + 128
   int h_q, h_kv, k_v, k_s, p_last, p0, n_q, nb, iv_stride, ext_stride, cov_words, tile_stride, kbits_words;
+  int dbits_words, vbits_words;
 };
 
 }  // namespace dca

@@ -37,7 +37,7 @@ __device__ __forceinline__ int range_key(Tile T, int t) {
   return t < T.len1 ? T.a1 + t : (t < T.len1 + T.len2 ? T.a2 + (t - T.len1) : -1);
 }
 
-template <bool DENSE>
+template <bool DENSE, bool EXACT>
 __device__ __forceinline__ void attn_body(const AttnArgs& A) {
   // K and V of the two stages are four LDS objects: the compiler then tells
   // the reads of one stage from the direct loads in flight into the other
@@ -193,6 +193,35 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A) {
   };
   auto range_precise = [&](Tile T) __attribute__((always_inline)) -> bool {
     return run_flagged(T.a1, T.len1) || run_flagged(T.a2, T.len2);
+  };
+  // Exact-diagonal semantics: the slots of run [a, a + len) (placed at slots
+  // so ..) that this lane's row attends: its offset prow - key is selected
+  // (or 0), or the key is a selected vertical column.  The offset bits of a
+  // row form a 32-bit window inside 6 words that the whole wave shares
+  // (scalar loads); the run's vertical bits are the same for every row.
+  typedef __attribute__((address_space(4))) const uint32_t cu32b;
+  cu32b* db4 = (cu32b*)(A.dbits + (long long)h * A.dbits_words);
+  cu32b* vb4 = (cu32b*)(A.vbits + (long long)h * A.vbits_words);
+  auto exact_run = [&](int a, int len, int so) __attribute__((always_inline)) -> uint32_t {
+    if (len <= 0) return 0u;
+    const uint32_t runmask = (len >= 32 ? 0xFFFFFFFFu : ((1u << len) - 1u)) << so;
+    const int bw = (i0 - a - 31 + 128) >> 5;
+    uint32_t w[6];
+#pragma unroll
+    for (int k = 0; k < 6; ++k) w[k] = db4[bw + k];
+    const int sh = prow - a - (len - 1) + 128 - 32 * bw;   // 0 .. 125
+    const int kx = sh >> 5;
+    uint32_t lo = w[0], hi = w[1];
+#pragma unroll
+    for (int k = 1; k < 5; ++k)
+      if (kx == k) { lo = w[k]; hi = w[k + 1]; }
+    const uint32_t win = (uint32_t)((((uint64_t)hi << 32) | lo) >> (sh & 31));
+    // window bit x is offset prow - a - (len - 1) + x, i.e. slot so + len - 1 - x
+    const uint32_t md = __builtin_bitreverse32(win) >> (32 - len - so);
+    const int vbit = a + 128;
+    const uint32_t v0 = vb4[vbit >> 5], v1 = vb4[(vbit >> 5) + 1];
+    const uint32_t vw = (uint32_t)((((uint64_t)v1 << 32) | v0) >> (vbit & 31));
+    return (md | (vw << so)) & runmask;
   };
   // slot key of an extra-vertical tile (bit 30 marks a high-norm key), -1 past the count
   auto ext_key = [&](Tile T) __attribute__((always_inline)) -> int { return (l32 < T.cnt) ? ext_h[T.eoff + l32] : -1; };
@@ -372,6 +401,14 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A) {
       const int t_hi = T.cnt ? count : below(prow + 1);
       select_slots(s, t_lo, t_hi, -INFINITY);
     }
+    if (EXACT && !T.cnt) {
+      const uint32_t m = exact_run(T.a1, T.len1, 0) | exact_run(T.a2, T.len2, T.len1);
+#pragma unroll
+      for (int vv = 0; vv < 16; ++vv) {
+        const int slot = 8 * (vv >> 2) + (vv & 3) + 4 * half;
+        if (!((m >> slot) & 1u)) s[vv] = -INFINITY;
+      }
+    }
     after_qk();
     // ---- online softmax (log2 domain; s already holds score - m_run).  The
     // reference max moves only when a score exceeds it by more than 8 (so
@@ -533,9 +570,12 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A) {
   }
 }
 
-// sparse (vertical-slash) calls and dense calls: one body, the dense tile walk known at compile time
-__global__ void __launch_bounds__(128, 2) dca_attn_kernel(AttnArgs A) { attn_body<false>(A); }
-__global__ void __launch_bounds__(128, 2) dca_attn_dense_kernel(AttnArgs A) { attn_body<true>(A); }
+// sparse (vertical-slash) calls, sparse calls with exact diagonals, and dense
+// calls: one body, the variant known at compile time (the exact masks cost
+// registers the other two do not pay for)
+__global__ void __launch_bounds__(128, 2) dca_attn_kernel(AttnArgs A) { attn_body<false, false>(A); }
+__global__ void __launch_bounds__(128, 2) dca_attn_exact_kernel(AttnArgs A) { attn_body<false, true>(A); }
+__global__ void __launch_bounds__(128, 2) dca_attn_dense_kernel(AttnArgs A) { attn_body<true, false>(A); }
 
 // LSE merge of split partials: m = max lse_p, O = sum e^{lse_p-m} O_p / sum e^{lse_p-m}.
 __global__ void __launch_bounds__(256) lse_merge_kernel(const float* __restrict__ part_o,
@@ -576,6 +616,8 @@ hipError_t launch_attn(const AttnArgs& A, hipStream_t stream) {
       : NXCD * A.split * ((A.nb + NXCD - 1) / NXCD) * A.h_q;
   if (A.dense) {
     hipLaunchKernelGGL(dca_attn_dense_kernel, dim3(blocks), dim3(128), 0, stream, A);
+  } else if (A.exact) {
+    hipLaunchKernelGGL(dca_attn_exact_kernel, dim3(blocks), dim3(128), 0, stream, A);
   } else {
     hipLaunchKernelGGL(dca_attn_kernel, dim3(blocks), dim3(128), 0, stream, A);
   }

@@ -21,14 +21,24 @@ constexpr int SEL_CHUNK = 8192;           // list elements per histogram / compa
 constexpr uint64_t FORCED_KEY = 0x7FF0000000000000ull;   // +inf
 
 
+// List `list` (2h: vertical scores of head h, 2h+1: slash scores): scores s[n],
+// output row out of length kcap, and the number k of picks (the head's own
+// budget when per-head budgets are given, at most kcap).
 __device__ __forceinline__ void sel_list(const SelArgs& A, int list, const double*& s, int32_t*& out, int& n,
-                                         int& k, int& forced0) {
+                                         int& k, int& forced0, int& kcap) {
   const int h = list >> 1;
   if ((list & 1) == 0) {
-    s = A.vert + (long long)h * A.n_v; out = A.v_out + (long long)h * A.k_v; n = A.n_v; k = A.k_v; forced0 = 0;
+    s = A.vert + (long long)h * A.n_v; out = A.v_out + (long long)h * A.k_v; n = A.n_v; kcap = A.k_v; forced0 = 0;
   } else {
-    s = A.slash + (long long)h * A.n_sl; out = A.s_out + (long long)h * A.k_s; n = A.n_sl; k = A.k_s; forced0 = 1;
+    s = A.slash + (long long)h * A.n_sl; out = A.s_out + (long long)h * A.k_s; n = A.n_sl; kcap = A.k_s; forced0 = 1;
   }
+  k = kcap;
+  if (A.k_head) k = min(max(A.k_head[2 * h + (list & 1)], 0), kcap);
+}
+__device__ __forceinline__ void sel_list(const SelArgs& A, int list, const double*& s, int32_t*& out, int& n,
+                                         int& k, int& forced0) {
+  int kcap;
+  sel_list(A, list, s, out, n, k, forced0, kcap);
 }
 
 __device__ __forceinline__ uint64_t sel_key(const double* s, int i, int forced0) {
@@ -143,16 +153,16 @@ __global__ void sel_scan_kernel(SelArgs A) {
 __global__ void __launch_bounds__(256) sel_write_kernel(SelArgs A) {
   __shared__ uint32_t wcg[4], wce[4];
   const int list = blockIdx.y;
-  const double* s; int32_t* out; int n, k, f;
-  sel_list(A, list, s, out, n, k, f);
+  const double* s; int32_t* out; int n, k, f, kcap;
+  sel_list(A, list, s, out, n, k, f, kcap);
+  if (blockIdx.x == 0) {
+    for (int i = min(k, n) + threadIdx.x; i < kcap; i += 256) out[i] = -1;
+  }
   if (k <= 0) return;
   const int beg = blockIdx.x * SEL_CHUNK;
   const bool all = (k >= n);
   const uint64_t T = A.prefix[list];
   const uint32_t need_eq = all ? 0u : (uint32_t)A.krem[list];
-  if (blockIdx.x == 0) {
-    for (int i = min(k, n) + threadIdx.x; i < k; i += 256) out[i] = -1;
-  }
   if (beg >= n) return;
   const int end = min(n, beg + SEL_CHUNK);
   const int lane = threadIdx.x & 63;
@@ -440,7 +450,41 @@ __global__ void __launch_bounds__(256) plan_tiles_kernel(PlanArgs A) {
   A.tiles[(long long)h * A.tile_stride + t] = make_int4(ivh[2 * a] + off, o2, len1 | (len2 << 8), 0);
 }
 
+// Exact-diagonal semantics: the selected offsets (and 0) and vertical columns
+// of each head as bitmaps, bit delta + 128 and bit j + 128 (the 128 leading
+// zero bits let a window start below 0).
+__global__ void plan_bits_clear_kernel(PlanArgs A) {
+  const long long nd = (long long)A.h_q * A.dbits_words, nv = (long long)A.h_q * A.vbits_words;
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < nd + nv; i += (long long)gridDim.x * blockDim.x) {
+    if (i < nd) A.dbits[i] = 0u;
+    else A.vbits[i - nd] = 0u;
+  }
+}
+
+__global__ void plan_bits_kernel(PlanArgs A) {
+  const int h = blockIdx.y;
+  uint32_t* db = A.dbits + (long long)h * A.dbits_words;
+  uint32_t* vb = A.vbits + (long long)h * A.vbits_words;
+  const int n = A.k_s + A.k_v + 1;
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) {
+    if (i < A.k_s) {
+      const int d = A.s_off[(long long)h * A.k_s + i];
+      if (d >= 0 && d <= A.p_last) atomicOr(&db[(d + 128) >> 5], 1u << ((d + 128) & 31));
+    } else if (i < A.k_s + A.k_v) {
+      const int c = A.v_idx[(long long)h * A.k_v + (i - A.k_s)];
+      if (c >= 0 && c <= A.p_last) atomicOr(&vb[(c + 128) >> 5], 1u << ((c + 128) & 31));
+    } else {
+      atomicOr(&db[128 >> 5], 1u);   // offset 0
+    }
+  }
+}
+
 hipError_t launch_plan(const PlanArgs& A, hipStream_t stream) {
+  if (A.dbits) {
+    hipLaunchKernelGGL(plan_bits_clear_kernel, dim3(256), dim3(256), 0, stream, A);
+    const int n = A.k_s + A.k_v + 1;
+    hipLaunchKernelGGL(plan_bits_kernel, dim3((n + 255) / 256, A.h_q), dim3(256), 0, stream, A);
+  }
   hipLaunchKernelGGL(plan_intervals_kernel, dim3(A.h_q), dim3(1024), 0, stream, A);
   hipLaunchKernelGGL(plan_cov_clear_kernel, dim3(256), dim3(256), 0, stream, A);
   const int ivb = (A.iv_stride + 255) / 256;

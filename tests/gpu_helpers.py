@@ -37,13 +37,14 @@ def run_prefill(inp: dict, cfg: S.Config, v_idx=None, s_off=None, with_lse=False
     return host_u16(out), (lse.cpu().numpy() if lse is not None else None)
 
 
-def run_index(inp: dict, cfg: S.Config, ws=None):
+def run_index(inp: dict, cfg: S.Config, ws=None, budgets=None):
     import torch
     q, k = dev(inp["q"]), dev(inp["k"])
     vi = torch.empty((cfg.h_q, max(cfg.vs_k_vertical, 1)), dtype=torch.int32, device="cuda")
     so = torch.empty((cfg.h_q, max(cfg.vs_k_slash, 1)), dtype=torch.int32, device="cuda")
     ws = workspace(cfg) if ws is None else ws
-    S.vs_index_build(q, k, inp["positions"], cfg, vi, so, ws)
+    kh = dev(np.asarray(budgets, dtype=np.int32)) if budgets is not None else None
+    S.vs_index_build(q, k, inp["positions"], cfg, vi, so, ws, k_per_head=kh)
     torch.cuda.synchronize()
     return vi.cpu().numpy()[:, :cfg.vs_k_vertical], so.cpu().numpy()[:, :cfg.vs_k_slash]
 

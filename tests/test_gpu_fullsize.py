@@ -6,7 +6,8 @@ oracle computes one by one:
   * the vertical-slash index of sampled query heads, bit-exact;
   * the exact F_blocks cover count of every head from the GPU's own index;
   * the attention rows of sampled (head, query block) pairs (blocks 0, 1, middle,
-    last and two seeded random ones), within the bf16 output tolerance, plus lse;
+    last and two seeded random ones), within the bf16 output tolerance, plus lse
+    (for the 128K chunk also with the exact-diagonal semantics);
   * properties that hold at any size on all rows (finite outputs, |o| <= max |v|).
 """
 from __future__ import annotations
@@ -26,10 +27,11 @@ pytestmark = pytest.mark.gpu
 
 LSE_TOL = 1e-2
 CASES = [
-    ("7b_dense_32k", 0),
-    ("7b_chunk_at_98304_of_128k", 0),
-    ("14b_256k_in_8_chunks", 7),
-    ("7b_last_chunk_of_1m", 0),
+    ("7b_dense_32k", 0, 0),
+    ("7b_chunk_at_98304_of_128k", 0, 0),
+    ("7b_chunk_at_98304_of_128k", 0, 1),
+    ("14b_256k_in_8_chunks", 7, 0),
+    ("7b_last_chunk_of_1m", 0, 0),
 ]
 _cache: dict = {}
 
@@ -38,9 +40,9 @@ def log(msg: str) -> None:
     print(f"[fullsize] {msg}", file=sys.stderr, flush=True)
 
 
-def gpu_call(name: str, chunk: int) -> dict:
-    """Run index build + prefill of one call on the GPU once per (workload, chunk)."""
-    key = (name, chunk)
+def gpu_call(name: str, chunk: int, exact: int = 0) -> dict:
+    """Run index build + prefill of one call on the GPU once per (workload, chunk, semantics)."""
+    key = (name, chunk, exact)
     if key in _cache:
         return _cache[key]
     _cache.clear()
@@ -51,7 +53,7 @@ def gpu_call(name: str, chunk: int) -> dict:
     w = W.WORKLOADS[name]
     log(f"{name} chunk {chunk}: generating inputs")
     inp = W.make(w, chunk, seed=0)
-    cfg = S.config_for(w, chunk)
+    cfg = S.config_for(w, chunk, slash_exact=exact)
     log(f"{name} chunk {chunk}: GPU index + prefill (n_q {cfg.n_q}, n_k {cfg.n_k})")
     q, k, v = dev(inp["q"]), dev(inp["k"]), dev(inp["v"])
     ws = torch.empty(S.dca_workspace_size(cfg), dtype=torch.uint8, device="cuda")
@@ -66,7 +68,7 @@ def gpu_call(name: str, chunk: int) -> dict:
     S.dca_sparse_prefill(q, k, v, inp["positions"], cfg, out, ws, v_idx=vi, s_off=so, lse_out=lse,
                          cover_pairs=pairs)
     torch.cuda.synchronize()
-    res = dict(w=w, inp=inp, cfg=cfg, out=host_u16(out), lse=lse.cpu().numpy(), pairs=int(pairs.item()),
+    res = dict(w=w, inp=inp, cfg=cfg, exact=bool(exact), out=host_u16(out), lse=lse.cpu().numpy(), pairs=int(pairs.item()),
                v_idx=None if vi is None else vi.cpu().numpy(), s_off=None if so is None else so.cpu().numpy())
     del q, k, v, ws, out, lse, pairs, vi, so
     torch.cuda.empty_cache()
@@ -103,7 +105,7 @@ def check_sampled_blocks(r):
     worst, tot, cnt = 0.0, 0.0, 0
     for h, b in pairs:
         ref, lse_ref, _ = O.attention_block(inp["q"], inp["k"], inp["v"], inp["p0"], h, b, ocfg,
-                                            r["v_idx"], r["s_off"])
+                                            r["v_idx"], r["s_off"], exact=r["exact"])
         r0 = 64 * b
         got = bf16_f64(r["out"][r0:r0 + ref.shape[0], h])
         err = np.abs(got - ref)
@@ -132,9 +134,9 @@ def check_all_rows_bounded(r):
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("name,chunk", CASES)
-def test_fullsize(name, chunk):
-    r = gpu_call(name, chunk)
+@pytest.mark.parametrize("name,chunk,exact", CASES)
+def test_fullsize(name, chunk, exact):
+    r = gpu_call(name, chunk, exact)
     if r["w"].sparse:
         check_index(r)
     check_cover_pairs(r)

@@ -216,3 +216,58 @@ def test_index_then_prefill_end_to_end():
     out, _ = run_prefill(inp, cfg, v_idx=v_gpu, s_off=s_gpu)
     v_ref, s_ref, _ = O.vs_index(inp["q"], inp["k"], inp["p0"], oracle_cfg(cfg))
     check_close(out, _oracle(inp, cfg, v_ref, s_ref)[0], "index + prefill")
+
+
+# ------------------------------------------------------------------ exact diagonals, per-head budgets
+@pytest.mark.parametrize("p0,n_q,kv,ks,split", [(512, 300, 40, 25, 0), (1024, 130, 100, 6, 1),
+                                               (256, 64, 10, 60, 2), (768, 200, 7, 90, 3)])
+def test_sparse_exact_diagonals(p0, n_q, kv, ks, split):
+    inp = _inputs(80 + p0, p0, n_q, 4, 1, sinks=True, periodic=97)
+    rng = np.random.default_rng(p0 + n_q + 1)
+    v_idx, s_off = _random_pattern(rng, 4, inp["n_k"], kv, ks)
+    cfg = _cfg(inp, 4, 1, 256, 32, vs_k_vertical=kv, vs_k_slash=ks, split_k=split, slash_exact=1)
+    out, lse = run_prefill(inp, cfg, v_idx=v_idx, s_off=s_off, with_lse=True)
+    ref, ref_lse = _oracle_exact(inp, cfg, v_idx, s_off)
+    check_close(out, ref, "exact diagonals")
+    assert np.abs(lse - ref_lse).max() <= LSE_TOL
+
+
+def _oracle_exact(inp, cfg, v_idx, s_off):
+    return O.attention(inp["q"], inp["k"], inp["v"], inp["p0"], oracle_cfg(cfg), v_idx=v_idx, s_off=s_off,
+                       exact=True)
+
+
+def test_exact_self_diagonal_returns_own_values():
+    """Offset 0 only, no vertical column: every row attends itself alone, so the output
+    is its own value row, bit for bit."""
+    inp = _inputs(81, 640, 200, 2, 1, sinks=True)
+    none = np.full((2, 1), -1, np.int32)
+    cfg = _cfg(inp, 2, 1, 256, 32, vs_k_vertical=1, vs_k_slash=1, slash_exact=1)
+    out, _ = run_prefill(inp, cfg, v_idx=none, s_off=none)
+    for h in range(2):
+        assert np.array_equal(out[:, h], inp["v"][inp["p0"]:, 0])
+
+
+def test_exact_all_offsets_equals_dense():
+    inp = _inputs(82, 192, 200, 2, 1, sinks=True)
+    n_k = inp["n_k"]
+    s_off = np.tile(np.arange(n_k, dtype=np.int32), (2, 1))
+    cfg = _cfg(inp, 2, 1, 128, 32, vs_k_vertical=1, vs_k_slash=n_k, slash_exact=1)
+    out, _ = run_prefill(inp, cfg, v_idx=np.full((2, 1), -1, np.int32), s_off=s_off)
+    check_close(out, _oracle(inp, _cfg(inp, 2, 1, 128, 32))[0], "exact, all offsets")
+
+
+def test_index_per_head_budgets():
+    inp = _inputs(83, 1024, 256, 4, 2, sinks=True, periodic=128)
+    cfg = _cfg(inp, 4, 2, 512, 32, vs_k_vertical=20, vs_k_slash=40)
+    budgets = [[20, 40], [5, 12], [0, 1], [20, 3]]
+    v_gpu, s_gpu = run_index(inp, cfg, budgets=budgets)
+    v_ref, s_ref, gaps = O.vs_index(inp["q"], inp["k"], inp["p0"], oracle_cfg(cfg), budgets=budgets)
+    for h, gv, gs in gaps:
+        assert gv is None or gv >= 1e-9
+        assert gs is None or gs >= 1e-9
+    assert np.array_equal(v_gpu, v_ref) and np.array_equal(s_gpu, s_ref)
+    # the exact-diagonal prefill from this index, end to end
+    ecfg = _cfg(inp, 4, 2, 512, 32, vs_k_vertical=20, vs_k_slash=40, slash_exact=1)
+    out, _ = run_prefill(inp, ecfg, v_idx=v_gpu, s_off=s_gpu)
+    check_close(out, _oracle_exact(inp, ecfg, v_ref, s_ref)[0], "budgets + exact")
