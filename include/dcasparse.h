@@ -172,6 +172,15 @@ typedef struct dca_key_cache {
 DCA_API int dca_key_cache_append(const dca_bf16 *k, int32_t j0, int32_t n, const dca_cfg *cfg,
                                  const dca_key_cache *cache);
 
+/* dca_sparse_prefill with the keys taken from a rotated key cache instead of
+ * raw k: keys 0 .. n_k-1 must have been appended (the chunk's own keys
+ * included), so a chunked prefill rotates every key once rather than its
+ * whole prefix per chunk.  Same definition, outputs and workspace
+ * (dca_workspace_size) as dca_sparse_prefill; with the same keys the outputs
+ * are bitwise equal. */
+DCA_API int dca_sparse_prefill_cached(const dca_bf16 *q, const dca_key_cache *cache, const dca_bf16 *v,
+                                      const int32_t *positions, const dca_cfg *cfg, dca_bf16 *out);
+
 /* Workspace bytes of dca_decode for this configuration (cfg->n_q new tokens,
  * cfg->n_k cached keys).  Pure host computation. */
 DCA_API int dca_decode_workspace_size(const dca_cfg *cfg, size_t *bytes);

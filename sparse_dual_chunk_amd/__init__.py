@@ -11,6 +11,7 @@ Names follow the C ABI in ``include/dcasparse.h``:
 * :func:`vs_index_build`
 * :func:`dca_sparse_prefill`
 * :func:`dca_key_cache_append`
+* :func:`dca_sparse_prefill_cached`
 * :func:`dca_decode_workspace_size`
 * :func:`dca_decode`
 * :func:`dca_strerror`
@@ -104,6 +105,9 @@ def lib() -> ctypes.CDLL:
         L.dca_key_cache_append.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(dca_cfg),
                                            ctypes.POINTER(dca_key_cache)]
         L.dca_key_cache_append.restype = ctypes.c_int
+        L.dca_sparse_prefill_cached.argtypes = [ctypes.c_void_p, ctypes.POINTER(dca_key_cache), ctypes.c_void_p,
+                                                ctypes.c_void_p, ctypes.POINTER(dca_cfg), ctypes.c_void_p]
+        L.dca_sparse_prefill_cached.restype = ctypes.c_int
         L.dca_decode_workspace_size.argtypes = [ctypes.POINTER(dca_cfg), ctypes.POINTER(ctypes.c_size_t)]
         L.dca_decode_workspace_size.restype = ctypes.c_int
         L.dca_decode.argtypes = [ctypes.c_void_p, ctypes.POINTER(dca_key_cache), ctypes.c_void_p,
@@ -266,3 +270,21 @@ def dca_decode(q, cache: KeyCache, v, cfg: Config, out, workspace, lse_out=None,
     rc = lib().dca_decode(_ptr(q), ctypes.byref(kc), _ptr(v), ctypes.byref(c), _ptr(out))
     if rc != DCA_OK:
         raise DcaError(rc, "dca_decode")
+
+
+def dca_sparse_prefill_cached(q, cache: KeyCache, v, positions, cfg: Config, out, workspace, v_idx=None, s_off=None,
+                              lse_out=None, cover_pairs=None, stream=None,
+                              stage_events: Optional[Sequence[int]] = None) -> None:
+    """dca_sparse_prefill with keys 0 .. cfg.n_k - 1 from a rotated key cache."""
+    pos, pos_p = _positions(positions)
+    ev_arr = None
+    if stage_events is not None:
+        ev_arr = (ctypes.c_void_p * (2 * DCA_STAGE_COUNT))(*[int(e) for e in stage_events])
+    c = cfg.to_c(workspace=_ptr(workspace), workspace_bytes=workspace.numel() * workspace.element_size(),
+                 stream=_stream(stream), v_idx=_ptr(v_idx), s_off=_ptr(s_off), lse_out=_ptr(lse_out),
+                 cover_pairs=_ptr(cover_pairs),
+                 stage_events=ctypes.cast(ev_arr, ctypes.c_void_p) if ev_arr is not None else None)
+    kc = cache.to_c()
+    rc = lib().dca_sparse_prefill_cached(_ptr(q), ctypes.byref(kc), _ptr(v), pos_p, ctypes.byref(c), _ptr(out))
+    if rc != DCA_OK:
+        raise DcaError(rc, "dca_sparse_prefill_cached")

@@ -307,11 +307,21 @@ int vs_index_build(const dca_bf16* q, const dca_bf16* k, const int32_t* position
   return DCA_OK;
 }
 
-int dca_sparse_prefill(const dca_bf16* q, const dca_bf16* k, const dca_bf16* v, const int32_t* positions,
-                       const dca_cfg* cfg, dca_bf16* out) {
+}  // extern "C"
+
+namespace {
+
+// The prefill of one chunk.  Keys come either raw (k: rotated here into the
+// workspace) or from a rotated key cache (cache: rotated when they entered it).
+int prefill_impl(const dca_bf16* q, const dca_bf16* k, const dca_key_cache* cache, const dca_bf16* v,
+                 const int32_t* positions, const dca_cfg* cfg, dca_bf16* out) {
   int rc = validate(cfg, positions);
   if (rc != DCA_OK) return rc;
-  if (!q || !k || !v || !out || !positions) return DCA_EINVAL;
+  if (!q || !(k || cache) || !v || !out || !positions) return DCA_EINVAL;
+  if (cache) {
+    if (!cache->k_hi || !cache->k_lo || !cache->k_flags || cache->capacity < cfg->n_k) return DCA_EINVAL;
+    if ((long long)cache->capacity * cfg->h_kv * cfg->head_dim * 2 >= (1LL << 32)) return DCA_EUNSUPPORTED;
+  }
   const bool sparse = cfg->v_idx || cfg->s_off;
   if (sparse && ((cfg->vs_k_vertical > 0 && !cfg->v_idx) || (cfg->vs_k_slash > 0 && !cfg->s_off)))
     return DCA_EINVAL;
@@ -325,16 +335,22 @@ int dca_sparse_prefill(const dca_bf16* q, const dca_bf16* k, const dca_bf16* v, 
 
   hipLaunchKernelGGL(write_freqs_kernel, dim3(1), dim3(HALF), 0, st, make_freqs(cfg->rope_base),
                      at<double>(cfg, L.freqs));
+  // rotated keys and their high-norm bits: this call's own rotation, or the cache's
+  const uint16_t* khi = cache ? cache->k_hi : at<uint16_t>(cfg, L.khi);
+  const uint16_t* klo = cache ? cache->k_lo : at<uint16_t>(cfg, L.klo);
+  const uint32_t* kbits = cache ? cache->k_flags : at<uint32_t>(cfg, L.kbits);
+  const int kbits_words = cache ? (cache->capacity + 31) / 32 : L.kbits_words;
   // stage 0: chunk-local key rotation, query rotations of the three DCA modes
   record(cfg, 0, 0);
-  float thr = cfg->precise_norm == 0.f ? 2.f * std::sqrt((float)D) : cfg->precise_norm;
-  const float thr2 = thr < 0.f ? -1.f : thr * thr;
-  if (launch_rotate_keys(k, at<uint16_t>(cfg, L.khi), at<uint16_t>(cfg, L.klo), at<uint32_t>(cfg, L.kbits),
-                         make_freqs(cfg->rope_base), 0, n_k, h_kv, cfg->dca_chunk, thr2, L.kbits_words, true,
-                         st) != hipSuccess)
-    return DCA_EHIP;
-  if (launch_hn_next(at<uint32_t>(cfg, L.kbits), at<uint8_t>(cfg, L.hn), L.hn_pad, h_kv, L.kbits_words, st) !=
-      hipSuccess)
+  if (!cache) {
+    float thr = cfg->precise_norm == 0.f ? 2.f * std::sqrt((float)D) : cfg->precise_norm;
+    const float thr2 = thr < 0.f ? -1.f : thr * thr;
+    if (launch_rotate_keys(k, at<uint16_t>(cfg, L.khi), at<uint16_t>(cfg, L.klo), at<uint32_t>(cfg, L.kbits),
+                           make_freqs(cfg->rope_base), 0, n_k, h_kv, cfg->dca_chunk, thr2, L.kbits_words, true,
+                           st) != hipSuccess)
+      return DCA_EHIP;
+  }
+  if (launch_hn_next(kbits, at<uint8_t>(cfg, L.hn), L.hn_pad, h_kv, kbits_words, st) != hipSuccess)
     return DCA_EHIP;
   // softmax scale sqrt(1/t)^2 / sqrt(d) and log2(e) (the kernel works in base 2)
   const float qscale = (float)(yarn_factor(cfg->yarn_s) / std::sqrt((double)D) * 1.4426950408889634);
@@ -355,8 +371,8 @@ int dca_sparse_prefill(const dca_bf16* q, const dca_bf16* k, const dca_bf16* v, 
     P.n_q = n_q; P.nb = L.nb; P.iv_stride = cfg->vs_k_slash + 1;
     P.ext_stride = cfg->vs_k_vertical > 0 ? cfg->vs_k_vertical : 1; P.cov_words = L.cov_words;
     P.tiles = at<int4>(cfg, L.tiles); P.n_tiles = at<int32_t>(cfg, L.n_tiles); P.t_first = at<int32_t>(cfg, L.t_first);
-    P.kbits = at<uint32_t>(cfg, L.kbits); P.h_kv = h_kv; P.tile_stride = L.tile_stride;
-    P.kbits_words = L.kbits_words;
+    P.kbits = kbits; P.h_kv = h_kv; P.tile_stride = L.tile_stride;
+    P.kbits_words = kbits_words;
     P.dbits = cfg->slash_exact ? at<uint32_t>(cfg, L.dbits) : nullptr;
     P.vbits = cfg->slash_exact ? at<uint32_t>(cfg, L.vbits) : nullptr;
     P.dbits_words = L.dbits_words; P.vbits_words = L.vbits_words;
@@ -375,15 +391,15 @@ int dca_sparse_prefill(const dca_bf16* q, const dca_bf16* k, const dca_bf16* v, 
   record(cfg, 2, 0);
   AttnArgs A;
   A.qhi = at<uint16_t>(cfg, L.qhi); A.qlo = at<uint16_t>(cfg, L.qlo);
-  A.khi = at<uint16_t>(cfg, L.khi); A.klo = at<uint16_t>(cfg, L.klo); A.v = v;
-  A.kbits = at<uint32_t>(cfg, L.kbits); A.hn = at<uint8_t>(cfg, L.hn); A.hn_pad = L.hn_pad;
+  A.khi = khi; A.klo = klo; A.v = v;
+  A.kbits = kbits; A.hn = at<uint8_t>(cfg, L.hn); A.hn_pad = L.hn_pad;
   A.out = out; A.lse_out = cfg->lse_out;
   A.part_o = L.split > 1 ? at<float>(cfg, L.part_o) : nullptr;
   A.part_lse = L.split > 1 ? at<float>(cfg, L.part_lse) : nullptr;
   A.tiles = at<int4>(cfg, L.tiles); A.n_tiles = at<int32_t>(cfg, L.n_tiles); A.t_first = at<int32_t>(cfg, L.t_first);
   A.ext = at<int32_t>(cfg, L.ext); A.n_ext = at<int32_t>(cfg, L.n_ext);
   A.n_q = n_q; A.n_k = n_k; A.h_q = h_q; A.h_kv = h_kv; A.p0 = p0; A.S = cfg->dca_chunk; A.W = cfg->dca_local;
-  A.nb = L.nb; A.tile_stride = L.tile_stride; A.kbits_words = L.kbits_words;
+  A.nb = L.nb; A.tile_stride = L.tile_stride; A.kbits_words = kbits_words;
   A.ext_stride = cfg->vs_k_vertical > 0 ? cfg->vs_k_vertical : 1;
   A.split = L.split; A.dense = sparse ? 0 : 1;
   A.exact = (sparse && cfg->slash_exact) ? 1 : 0;
@@ -400,6 +416,22 @@ int dca_sparse_prefill(const dca_bf16* q, const dca_bf16* k, const dca_bf16* v, 
   }
   record(cfg, 3, 1);
   return DCA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dca_sparse_prefill(const dca_bf16* q, const dca_bf16* k, const dca_bf16* v, const int32_t* positions,
+                       const dca_cfg* cfg, dca_bf16* out) {
+  if (!k) return DCA_EINVAL;
+  return prefill_impl(q, k, nullptr, v, positions, cfg, out);
+}
+
+int dca_sparse_prefill_cached(const dca_bf16* q, const dca_key_cache* cache, const dca_bf16* v,
+                              const int32_t* positions, const dca_cfg* cfg, dca_bf16* out) {
+  if (!cache) return DCA_EINVAL;
+  return prefill_impl(q, nullptr, cache, v, positions, cfg, out);
 }
 
 int dca_key_cache_append(const dca_bf16* k, int32_t j0, int32_t n, const dca_cfg* cfg, const dca_key_cache* cache) {

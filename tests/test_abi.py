@@ -28,7 +28,7 @@ def _declared_functions():
 def test_library_exports_every_declared_symbol():
     names = _declared_functions()
     assert set(names) == {"dca_workspace_size", "vs_index_build", "dca_sparse_prefill", "dca_key_cache_append",
-                          "dca_decode_workspace_size", "dca_decode", "dca_strerror"}
+                          "dca_sparse_prefill_cached", "dca_decode_workspace_size", "dca_decode", "dca_strerror"}
     out = subprocess.run(["nm", "-D", "--defined-only", S.LIB_PATH], capture_output=True, text=True).stdout
     exported = {l.split()[-1] for l in out.splitlines() if l.strip()}
     for n in names:
@@ -236,3 +236,16 @@ def test_key_cache_append_validation():
     c = _dcfg(dca_chunk=100).to_c(stream=0)
     kc = _FakeCache(100).to_c()
     assert S.lib().dca_key_cache_append(0x1000, 0, 10, ctypes.byref(c), ctypes.byref(kc)) == S.DCA_EUNSUPPORTED
+
+
+
+def test_cached_prefill_rejects_small_cache_before_any_launch():
+    cfg = _cfg()
+    t = _FakeTensor(S.dca_workspace_size(cfg))
+    with pytest.raises(S.DcaError) as ei:
+        S.dca_sparse_prefill_cached(t, _FakeCache(511), t, np.arange(256, 512, dtype=np.int32), cfg, t, t, stream=0)
+    assert ei.value.code == S.DCA_EINVAL
+    c = cfg.to_c(workspace=0x1000, workspace_bytes=1 << 30)
+    pos = np.arange(256, 512, dtype=np.int32)
+    assert S.lib().dca_sparse_prefill_cached(0x1000, None, 0x1000, pos.ctypes.data_as(ctypes.c_void_p),
+                                             ctypes.byref(c), 0x1000) == S.DCA_EINVAL
