@@ -245,6 +245,134 @@ def bench_decode(args) -> int:
     return 0
 
 
+SEQUENCE_METRIC = "whole-prompt chunked prefill ms per layer (index + attention of every chunk)"
+
+
+def bench_sequence(args) -> int:
+    """One step = the chunked prefill of a whole prompt (default: the 14B 256K prompt of 8
+    chunks), every chunk's key append, index build and attention, through
+    dca_prefill_sequence.  Compared: fixed 32K-row chunks against the equal-time schedule
+    (the library's cost coefficients, the same number of chunks), each with the index
+    builds in order on one stream and one chunk ahead on a second stream."""
+    import torch
+    import sparse_dual_chunk_amd as S
+
+    w = W.WORKLOADS[args.workload] if args.workload != W.C5_7B_1M.name else W.C4_14B_256K
+    n = w.n_k_total
+    fixed = list(range(0, n, 32768)) + [n]
+    log(f"sequence: {w.name}, {n} tokens, generating inputs (seed {args.seed})")
+    k, v = W.make_keys_values(w, n, args.seed)
+    q = np.concatenate([W.make_queries(w, a, b - a, args.seed) for a, b in zip(fixed[:-1], fixed[1:])])
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
+    Q, K, V = dev(q), dev(k), dev(v)
+    del q, k, v
+    cfg = S.Config(n_q=n, n_k=n, h_q=w.h_q, h_kv=w.h_kv, dca_chunk=w.dca_chunk, dca_local=w.dca_local,
+                   rope_base=w.rope_base, yarn_s=w.yarn_s, head_dim=w.head_dim, vs_last_q=w.vs_last_q,
+                   vs_k_vertical=w.k_vertical, vs_k_slash=w.k_slash, split_k=args.split_k)
+    sparse = w.sparse
+    cost = S.dca_chunk_cost_default(cfg, sparse)
+    equal, _ = S.dca_chunk_schedule(n, len(fixed) - 1, n, cost)
+    schedules = {"fixed_32k": fixed, "equal_time": equal}
+    fitted_cost = None
+    cache = S.KeyCache.allocate(n, w.h_kv)
+    out = torch.empty(Q.shape, dtype=torch.int16, device="cuda")
+    side = torch.cuda.Stream()
+    hev = HipEvents()
+    results = {}
+    def model_pairs(a, b, cap):
+        e = np.arange(a, b, 64, dtype=np.float64)
+        r = np.minimum(64, b - e)
+        e = e + r
+        if cap > 0:
+            e = -e * np.expm1(-cap / e)
+        return float((r * e).sum())
+
+    def fit_cost(bounds, chunk_ms, index_ms):
+        """Least-squares (non-negative) fit of the cost coefficients to measured chunk times (us)."""
+        from scipy.optimize import nnls
+        ab = list(zip(bounds[:-1], bounds[1:]))
+        A = np.array([[1.0, b - a, model_pairs(a, b, cost.cover_cap)] for a, b in ab])
+        x, _ = nnls(A, 1e3 * np.asarray(chunk_ms))
+        ki = np.array([[1.0, b] for a, b in ab])
+        y, _ = nnls(ki, 1e3 * np.asarray(index_ms))
+        return S.chunk_cost(per_call=x[0] + y[0], per_row=x[1], per_index_key=y[1] if sparse else 0.0,
+                            per_pair=x[2], cover_cap=cost.cover_cap)
+
+    order = list(schedules)
+    while order:
+        name = order.pop(0)
+        bounds = schedules[name]
+        nc = len(bounds) - 1
+        ws = torch.empty(max(S.dca_prefill_sequence_workspace_size(cfg, bounds, sparse, ov) for ov in (False, True)),
+                         dtype=torch.uint8, device="cuda")
+        pairs = torch.zeros(nc, dtype=torch.int64, device="cuda")
+        for overlap in (False, True):
+            tag = f"{name}{'_overlap' if overlap else ''}"
+            istream = side.cuda_stream if overlap else None
+            for _ in range(args.warmup):
+                S.dca_prefill_sequence(Q, K, V, bounds, cfg, cache, out, ws, sparse=sparse, index_stream=istream)
+            torch.cuda.synchronize()
+            tot, ch, ix = [], [], []
+            for _ in range(args.steps):
+                ev = hev.create(2)
+                cev = hev.create(2 * nc)
+                iev = hev.create(2 * nc)
+                st = torch.cuda.current_stream().cuda_stream
+                hev.h.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+                hev.h.hipEventRecord(ctypes.c_void_p(ev[0]), ctypes.c_void_p(st))
+                S.dca_prefill_sequence(Q, K, V, bounds, cfg, cache, out, ws, sparse=sparse, index_stream=istream,
+                                       cover_pairs=pairs, chunk_events=cev, index_events=iev)
+                hev.h.hipEventRecord(ctypes.c_void_p(ev[1]), ctypes.c_void_p(st))
+                torch.cuda.synchronize()
+                tot.append(hev.elapsed_ms(ev[0], ev[1]))
+                ch.append([hev.elapsed_ms(cev[2 * c], cev[2 * c + 1]) for c in range(nc)])
+                ix.append([hev.elapsed_ms(iev[2 * c], iev[2 * c + 1]) for c in range(nc)])
+            chunk_ms = np.median(np.array(ch), axis=0)
+            index_ms = np.median(np.array(ix), axis=0)
+            f_blocks = 4 * w.head_dim * float(pairs.sum().item())
+            results[tag] = {
+                "bounds": bounds,
+                "total_ms": round(float(np.median(tot)), 3),
+                "chunk_attention_ms": [round(float(x), 3) for x in chunk_ms],
+                "chunk_index_ms": [round(float(x), 3) for x in index_ms],
+                "chunk_max_over_mean": round(float(chunk_ms.max() / chunk_ms.mean()), 4),
+                "attention_tflops_on_computed_blocks": round(f_blocks / (float(chunk_ms.sum()) / 1e3) / 1e12, 1),
+            }
+            log(f"{tag}: total {results[tag]['total_ms']} ms, chunk max/mean {results[tag]['chunk_max_over_mean']}")
+            if name == "fixed_32k" and not overlap:
+                # the cost model refitted to this GPU's measured chunk times, then scheduled again
+                fitted_cost = fit_cost(bounds, chunk_ms, index_ms)
+                schedules["equal_time_fitted"], _ = S.dca_chunk_schedule(n, nc, n, fitted_cost)
+                order.append("equal_time_fitted")
+        del ws
+    best = min(results, key=lambda t: results[t]["total_ms"])
+    result = {
+        "metric": SEQUENCE_METRIC,
+        "value": results[best]["total_ms"],
+        "unit": "ms",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": results[best]["total_ms"],
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}_whole_prompt", "n_tokens": n, "h_q": w.h_q, "h_kv": w.h_kv,
+                   "k_vertical": w.k_vertical, "k_slash": w.k_slash, "best": best,
+                   "cost_model": {"per_call": cost.per_call, "per_row": cost.per_row,
+                                  "per_index_key": cost.per_index_key, "per_pair": cost.per_pair,
+                                  "cover_cap": int(cost.cover_cap)},
+                   "fitted_cost_model": None if fitted_cost is None else
+                   {"per_call": fitted_cost.per_call, "per_row": fitted_cost.per_row,
+                    "per_index_key": fitted_cost.per_index_key, "per_pair": fitted_cost.per_pair}},
+        "runs": results,
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -263,6 +391,9 @@ def main() -> int:
     ap.add_argument("--decode", action="store_true",
                     help="measure the generation-step attention over the 1M-key cache instead of the prefill")
     ap.add_argument("--decode-tokens", type=int, default=1)
+    ap.add_argument("--sequence", action="store_true",
+                    help="measure the whole-prompt chunked prefill (default prompt: the 14B 256K one), "
+                         "fixed 32K chunks against the equal-time schedule, index builds in order or overlapped")
     args = ap.parse_args()
 
     if args.copy_calibration:
@@ -284,6 +415,8 @@ def main() -> int:
 
     if args.decode:
         return bench_decode(args)
+    if args.sequence:
+        return bench_sequence(args)
 
     import torch
     import sparse_dual_chunk_amd as S

@@ -199,6 +199,86 @@ DCA_API int dca_decode_workspace_size(const dca_cfg *cfg, size_t *bytes);
 DCA_API int dca_decode(const dca_bf16 *q, const dca_key_cache *cache, const dca_bf16 *v, const dca_cfg *cfg,
                        dca_bf16 *out);
 
+/* ---- Whole-sequence prefill ----------------------------------------------
+ * The pages' chunked prefill runs a long prompt chunk by chunk: chunk c holds
+ * query rows [b_c, b_{c+1}) and attends the prefix [0, b_{c+1}).  Dynamic
+ * chunked pipeline parallelism (paper-review page, section 4, "Pipeline
+ * parallelism", Figure 9) sizes the chunks by the attention kernel's cost so
+ * that every chunk takes about the same time.  The pages give no cost
+ * formula; the model below prices a chunk of rows [a, b) at
+ *   per_call + per_row * (b - a) + per_index_key * b
+ *     + per_pair * sum over its 64-row blocks [i0, i0 + r) of r * cover(i0 + r)
+ * where cover(E) = E for a dense block (its causal extent) and, with
+ * cap = cover_cap > 0, E (1 - exp(-cap / E)) for a sparse one: the expected
+ * union of cap keys' worth of 64-key footprints scattered over the extent
+ * (E while cap >> E, tending to cap when E >> cap). */
+typedef struct dca_chunk_cost {
+  double  per_call;       /* fixed cost of one chunk (launches, LSE merge) */
+  double  per_row;        /* per query row of the chunk (query rotations, key append, output) */
+  double  per_index_key;  /* per key of the chunk's prefix (the index build scores the whole prefix) */
+  double  per_pair;       /* per computed (query row, key) pair, all query heads together */
+  int64_t cover_cap;      /* keys of a sparse block's budget, 64 k_s + k_v; <= 0: dense (no bound) */
+} dca_chunk_cost;
+
+/* Cost coefficients, in microseconds, measured for this library on MI355X
+ * for the heads and budgets of cfg (n_q, n_k are ignored): the attention at
+ * its measured rate per (row, key, head), the index build and sparse plan per
+ * prefix key and head, and cover_cap = 64 * vs_k_slash + vs_k_vertical for a
+ * sparse prefill (sparse = 1), no cap and no index cost for a dense one. */
+DCA_API int dca_chunk_cost_default(const dca_cfg *cfg, int32_t sparse, dca_chunk_cost *cost);
+
+/* Equal-time chunk schedule: splits tokens [0, n_tokens) into exactly
+ * min(n_chunks, ceil(n_tokens / 64)) chunks, each starting on a multiple of
+ * 64 and at most max_rows rows long (max_rows >= 64), minimising the largest
+ * chunk cost under *cost (exact optimum of that min-max problem, found by a
+ * bisection over greedy packings).  Writes bounds[0 .. *n_out] (host int32,
+ * room for n_chunks + 1 entries): 0 = bounds[0] < ... < bounds[*n_out] =
+ * n_tokens; and, when max_cost is not NULL, the largest chunk cost.  Pure
+ * host computation.  DCA_EINVAL when n_chunks chunks of max_rows rows cannot
+ * hold n_tokens, or on negative coefficients. */
+DCA_API int dca_chunk_schedule(int32_t n_tokens, int32_t n_chunks, int32_t max_rows, const dca_chunk_cost *cost,
+                               int32_t *bounds, int32_t *n_out, double *max_cost);
+
+/* How dca_prefill_sequence runs a prompt. */
+typedef struct dca_sequence_plan {
+  const int32_t *bounds;  /* host int32 [n_chunks + 1]: 0 = bounds[0] < ... < bounds[n_chunks] = cfg->n_k,
+                             bounds[c] % 64 == 0 for c < n_chunks (e.g. from dca_chunk_schedule) */
+  int32_t  n_chunks;      /* >= 1 */
+  int32_t  sparse;        /* 1: every chunk builds its vertical-slash index (vs_index_build) and runs the
+                             block-sparse prefill with it; a chunk whose prefix has at most vs_k_slash keys
+                             (with no per-head budgets) selects every offset, so its cover is the dense causal
+                             set and it runs dense.  0: every chunk dense */
+  void    *index_stream;  /* hipStream_t: index builds run on it, one chunk ahead of the attention on
+                             cfg->stream, so the index of chunk c+1 overlaps the attention of chunk c.  NULL:
+                             everything runs on cfg->stream in order */
+  void   **chunk_events;  /* optional 2 * n_chunks hipEvent_t recorded on cfg->stream around chunk c's key
+                             append and prefill (start 2c, stop 2c+1); NULL: none */
+  void   **index_events;  /* optional 2 * n_chunks hipEvent_t recorded around chunk c's index build, on the
+                             stream it runs on (recorded empty for dense chunks); NULL: none */
+  int64_t *cover_pairs;   /* optional device int64 [n_chunks]: each chunk's cover_pairs (see dca_cfg) */
+} dca_sequence_plan;
+
+/* Workspace bytes of dca_prefill_sequence for cfg (the whole prompt: n_q =
+ * n_k = its length) and plan: one chunk's workspace and index buffers, twice
+ * when plan->index_stream is set.  Pure host computation. */
+DCA_API int dca_prefill_sequence_workspace_size(const dca_cfg *cfg, const dca_sequence_plan *plan, size_t *bytes);
+
+/* Chunked prefill of a whole prompt of n = cfg->n_k tokens (cfg->n_q must
+ * equal n; positions are implied: 0 .. n-1).  For each chunk c in order:
+ * appends its keys to the rotated key cache (dca_key_cache_append), builds
+ * its index when sparse (vs_index_build on raw q and k), and runs its
+ * attention from the cache (dca_sparse_prefill_cached), writing rows
+ * [b_c, b_{c+1}) of out [n][h_q][128] and, when cfg->lse_out is set, columns
+ * [b_c, b_{c+1}) of lse_out [h_q][n].  Every key is rotated once.  The outputs
+ * are bitwise those of the per-chunk calls.  cfg->v_idx, s_off, cover_pairs
+ * and stage_events must be NULL (plan->cover_pairs takes the role of the
+ * latter); cache->capacity >= n.  Work is ordered on cfg->stream: when it
+ * reaches the end of the call there, every chunk is done.  Events are created
+ * and released inside the call. */
+DCA_API int dca_prefill_sequence(const dca_bf16 *q, const dca_bf16 *k, const dca_bf16 *v,
+                                 const dca_sequence_plan *plan, const dca_cfg *cfg, const dca_key_cache *cache,
+                                 dca_bf16 *out);
+
 /* Static message for an error code; never NULL. */
 DCA_API const char *dca_strerror(int code);
 

@@ -14,6 +14,10 @@ Names follow the C ABI in ``include/dcasparse.h``:
 * :func:`dca_sparse_prefill_cached`
 * :func:`dca_decode_workspace_size`
 * :func:`dca_decode`
+* :func:`dca_chunk_cost_default`
+* :func:`dca_chunk_schedule`
+* :func:`dca_prefill_sequence_workspace_size`
+* :func:`dca_prefill_sequence`
 * :func:`dca_strerror`
 """
 from __future__ import annotations
@@ -77,6 +81,30 @@ class dca_key_cache(ctypes.Structure):
     ]
 
 
+class dca_chunk_cost(ctypes.Structure):
+    """Mirror of ``struct dca_chunk_cost``."""
+    _fields_ = [
+        ("per_call", ctypes.c_double),
+        ("per_row", ctypes.c_double),
+        ("per_index_key", ctypes.c_double),
+        ("per_pair", ctypes.c_double),
+        ("cover_cap", ctypes.c_int64),
+    ]
+
+
+class dca_sequence_plan(ctypes.Structure):
+    """Mirror of ``struct dca_sequence_plan``."""
+    _fields_ = [
+        ("bounds", ctypes.c_void_p),
+        ("n_chunks", ctypes.c_int32),
+        ("sparse", ctypes.c_int32),
+        ("index_stream", ctypes.c_void_p),
+        ("chunk_events", ctypes.c_void_p),
+        ("index_events", ctypes.c_void_p),
+        ("cover_pairs", ctypes.c_void_p),
+    ]
+
+
 class DcaError(RuntimeError):
     def __init__(self, code: int, where: str):
         super().__init__(f"{where}: error {code} ({dca_strerror(code)})")
@@ -113,6 +141,19 @@ def lib() -> ctypes.CDLL:
         L.dca_decode.argtypes = [ctypes.c_void_p, ctypes.POINTER(dca_key_cache), ctypes.c_void_p,
                                  ctypes.POINTER(dca_cfg), ctypes.c_void_p]
         L.dca_decode.restype = ctypes.c_int
+        L.dca_chunk_cost_default.argtypes = [ctypes.POINTER(dca_cfg), ctypes.c_int32, ctypes.POINTER(dca_chunk_cost)]
+        L.dca_chunk_cost_default.restype = ctypes.c_int
+        L.dca_chunk_schedule.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                         ctypes.POINTER(dca_chunk_cost), ctypes.c_void_p,
+                                         ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_double)]
+        L.dca_chunk_schedule.restype = ctypes.c_int
+        L.dca_prefill_sequence_workspace_size.argtypes = [ctypes.POINTER(dca_cfg), ctypes.POINTER(dca_sequence_plan),
+                                                          ctypes.POINTER(ctypes.c_size_t)]
+        L.dca_prefill_sequence_workspace_size.restype = ctypes.c_int
+        L.dca_prefill_sequence.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                           ctypes.POINTER(dca_sequence_plan), ctypes.POINTER(dca_cfg),
+                                           ctypes.POINTER(dca_key_cache), ctypes.c_void_p]
+        L.dca_prefill_sequence.restype = ctypes.c_int
         L.dca_strerror.argtypes = [ctypes.c_int]
         L.dca_strerror.restype = ctypes.c_char_p
         _lib = L
@@ -288,3 +329,77 @@ def dca_sparse_prefill_cached(q, cache: KeyCache, v, positions, cfg: Config, out
     rc = lib().dca_sparse_prefill_cached(_ptr(q), ctypes.byref(kc), _ptr(v), pos_p, ctypes.byref(c), _ptr(out))
     if rc != DCA_OK:
         raise DcaError(rc, "dca_sparse_prefill_cached")
+
+
+# ---------------------------------------------------------------- whole-prompt chunked prefill
+def dca_chunk_cost_default(cfg: Config, sparse: bool) -> dca_chunk_cost:
+    """The library's MI355X cost coefficients (microseconds) for cfg's heads and budgets."""
+    c = cfg.to_c()
+    m = dca_chunk_cost()
+    rc = lib().dca_chunk_cost_default(ctypes.byref(c), int(bool(sparse)), ctypes.byref(m))
+    if rc != DCA_OK:
+        raise DcaError(rc, "dca_chunk_cost_default")
+    return m
+
+
+def chunk_cost(per_call=0.0, per_row=0.0, per_index_key=0.0, per_pair=0.0, cover_cap=0) -> dca_chunk_cost:
+    m = dca_chunk_cost()
+    m.per_call, m.per_row, m.per_index_key, m.per_pair, m.cover_cap = per_call, per_row, per_index_key, per_pair, \
+        int(cover_cap)
+    return m
+
+
+def dca_chunk_schedule(n_tokens: int, n_chunks: int, max_rows: int, cost: dca_chunk_cost):
+    """Equal-time chunk bounds: returns (bounds list of n_out + 1 ints, largest chunk cost)."""
+    b = np.zeros(n_chunks + 1, dtype=np.int32)
+    n_out = ctypes.c_int32(0)
+    mx = ctypes.c_double(0.0)
+    rc = lib().dca_chunk_schedule(int(n_tokens), int(n_chunks), int(max_rows), ctypes.byref(cost),
+                                  b.ctypes.data_as(ctypes.c_void_p), ctypes.byref(n_out), ctypes.byref(mx))
+    if rc != DCA_OK:
+        raise DcaError(rc, "dca_chunk_schedule")
+    return [int(x) for x in b[: n_out.value + 1]], float(mx.value)
+
+
+def _seq_plan(bounds, sparse, index_stream=None, chunk_events=None, index_events=None, cover_pairs=None):
+    b = np.ascontiguousarray(np.asarray(bounds, dtype=np.int32))
+    n = len(b) - 1
+    keep = [b]
+    p = dca_sequence_plan()
+    p.bounds = b.ctypes.data_as(ctypes.c_void_p)
+    p.n_chunks = n
+    p.sparse = int(bool(sparse))
+    p.index_stream = int(index_stream) if index_stream is not None else None
+    for name, evs in (("chunk_events", chunk_events), ("index_events", index_events)):
+        if evs is not None:
+            arr = (ctypes.c_void_p * (2 * n))(*[int(e) for e in evs])
+            keep.append(arr)
+            setattr(p, name, ctypes.cast(arr, ctypes.c_void_p))
+    p.cover_pairs = _ptr(cover_pairs)
+    return p, keep
+
+
+def dca_prefill_sequence_workspace_size(cfg: Config, bounds, sparse: bool, overlap: bool) -> int:
+    """Workspace bytes of dca_prefill_sequence (overlap: an index stream will be passed)."""
+    p, _keep = _seq_plan(bounds, sparse, index_stream=1 if overlap else None)
+    c = cfg.to_c()
+    n = ctypes.c_size_t(0)
+    rc = lib().dca_prefill_sequence_workspace_size(ctypes.byref(c), ctypes.byref(p), ctypes.byref(n))
+    if rc != DCA_OK:
+        raise DcaError(rc, "dca_prefill_sequence_workspace_size")
+    return int(n.value)
+
+
+def dca_prefill_sequence(q, k, v, bounds, cfg: Config, cache: KeyCache, out, workspace, sparse: bool = True,
+                         index_stream=None, lse_out=None, cover_pairs=None, chunk_events=None, index_events=None,
+                         stream=None) -> None:
+    """Chunked prefill of a whole prompt (cfg.n_q == cfg.n_k == its length) over the given chunk bounds.
+    index_stream: a second stream (int handle) for the index builds, or None to run everything in order."""
+    p, _keep = _seq_plan(bounds, sparse, index_stream, chunk_events, index_events, cover_pairs)
+    c = cfg.to_c(workspace=_ptr(workspace), workspace_bytes=workspace.numel() * workspace.element_size(),
+                 stream=_stream(stream), lse_out=_ptr(lse_out))
+    kc = cache.to_c()
+    rc = lib().dca_prefill_sequence(_ptr(q), _ptr(k), _ptr(v), ctypes.byref(p), ctypes.byref(c), ctypes.byref(kc),
+                                    _ptr(out))
+    if rc != DCA_OK:
+        raise DcaError(rc, "dca_prefill_sequence")

@@ -28,7 +28,9 @@ def _declared_functions():
 def test_library_exports_every_declared_symbol():
     names = _declared_functions()
     assert set(names) == {"dca_workspace_size", "vs_index_build", "dca_sparse_prefill", "dca_key_cache_append",
-                          "dca_sparse_prefill_cached", "dca_decode_workspace_size", "dca_decode", "dca_strerror"}
+                          "dca_sparse_prefill_cached", "dca_decode_workspace_size", "dca_decode", "dca_strerror",
+                          "dca_chunk_cost_default", "dca_chunk_schedule", "dca_prefill_sequence_workspace_size",
+                          "dca_prefill_sequence"}
     out = subprocess.run(["nm", "-D", "--defined-only", S.LIB_PATH], capture_output=True, text=True).stdout
     exported = {l.split()[-1] for l in out.splitlines() if l.strip()}
     for n in names:
@@ -50,18 +52,20 @@ def test_struct_layout_matches_header(tmp_path):
     assert vals[1:] == [getattr(S.dca_cfg, f).offset for f, _ in S.dca_cfg._fields_]
 
 
-def test_key_cache_struct_layout_matches_header(tmp_path):
-    prog = tmp_path / "kc.c"
+@pytest.mark.parametrize("name", ["dca_key_cache", "dca_chunk_cost", "dca_sequence_plan"])
+def test_other_struct_layouts_match_header(tmp_path, name):
+    st = getattr(S, name)
+    prog = tmp_path / "st.c"
     prog.write_text(
         '#include <stdio.h>\n#include <stddef.h>\n#include "%s"\n'
-        'int main(void){printf("%%zu", sizeof(dca_key_cache));\n' % HEADER
-        + "".join('printf(" %%zu", offsetof(dca_key_cache, %s));\n' % f for f, _ in S.dca_key_cache._fields_)
+        'int main(void){printf("%%zu", sizeof(%s));\n' % (HEADER, name)
+        + "".join('printf(" %%zu", offsetof(%s, %s));\n' % (name, f) for f, _ in st._fields_)
         + "return 0;}\n")
-    exe = tmp_path / "kc"
+    exe = tmp_path / "st"
     subprocess.run(["gcc", str(prog), "-o", str(exe)], check=True)
     vals = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True).stdout.split()]
-    assert vals[0] == ctypes.sizeof(S.dca_key_cache)
-    assert vals[1:] == [getattr(S.dca_key_cache, f).offset for f, _ in S.dca_key_cache._fields_]
+    assert vals[0] == ctypes.sizeof(st)
+    assert vals[1:] == [getattr(st, f).offset for f, _ in st._fields_]
 
 
 def _cfg(**kw):
@@ -249,3 +253,54 @@ def test_cached_prefill_rejects_small_cache_before_any_launch():
     pos = np.arange(256, 512, dtype=np.int32)
     assert S.lib().dca_sparse_prefill_cached(0x1000, None, 0x1000, pos.ctypes.data_as(ctypes.c_void_p),
                                              ctypes.byref(c), 0x1000) == S.DCA_EINVAL
+
+
+# ---- whole-prompt chunked prefill
+def _scfg(n=960, **kw):
+    return _cfg(n_q=n, n_k=n, **kw)
+
+
+def test_sequence_workspace_size_and_slots():
+    cfg = _scfg(vs_k_vertical=24, vs_k_slash=40)
+    bounds = [0, 320, 704, 960]
+    one = S.dca_prefill_sequence_workspace_size(cfg, bounds, True, overlap=False)
+    two = S.dca_prefill_sequence_workspace_size(cfg, bounds, True, overlap=True)
+    assert two == 2 * one
+    # one slot holds the largest chunk call's workspace
+    biggest = max(S.dca_workspace_size(_cfg(n_q=b - a, n_k=b, vs_k_vertical=24, vs_k_slash=40))
+                  for a, b in zip(bounds[:-1], bounds[1:]))
+    assert one >= biggest
+
+
+@pytest.mark.parametrize("bounds,code", [([0, 320, 900], S.DCA_EINVAL),        # does not end at n
+                                         ([0, 320, 320, 960], S.DCA_EINVAL),   # empty chunk
+                                         ([0, 100, 960], S.DCA_EUNSUPPORTED),  # chunk start not a multiple of 64
+                                         ([64, 960], S.DCA_EINVAL)])           # does not start at 0
+def test_sequence_rejects_bad_bounds(bounds, code):
+    with pytest.raises(S.DcaError) as ei:
+        S.dca_prefill_sequence_workspace_size(_scfg(), bounds, False, overlap=False)
+    assert ei.value.code == code
+
+
+def test_sequence_rejects_bad_calls_before_any_launch():
+    cfg = _scfg()
+    bounds = [0, 320, 960]
+    ws = S.dca_prefill_sequence_workspace_size(cfg, bounds, False, overlap=False)
+    t = _FakeTensor(ws)
+    # too small a workspace, too small a cache, n_q != n_k, a pattern pointer in cfg
+    with pytest.raises(S.DcaError) as ei:
+        S.dca_prefill_sequence(t, t, t, bounds, cfg, _FakeCache(960), t, _FakeTensor(ws - 256), sparse=False,
+                               stream=0)
+    assert ei.value.code == S.DCA_EWORKSPACE
+    with pytest.raises(S.DcaError) as ei:
+        S.dca_prefill_sequence(t, t, t, bounds, cfg, _FakeCache(959), t, t, sparse=False, stream=0)
+    assert ei.value.code == S.DCA_EINVAL
+    with pytest.raises(S.DcaError) as ei:
+        S.dca_prefill_sequence(t, t, t, bounds, _cfg(n_q=900, n_k=960), _FakeCache(960), t, t, sparse=False,
+                               stream=0)
+    assert ei.value.code == S.DCA_EINVAL
+    p, _keep = S._seq_plan(bounds, False)
+    c = cfg.to_c(workspace=0x1000, workspace_bytes=ws, stream=0, v_idx=0x2000)
+    kc = _FakeCache(960).to_c()
+    assert S.lib().dca_prefill_sequence(0x1000, 0x1000, 0x1000, ctypes.byref(p), ctypes.byref(c), ctypes.byref(kc),
+                                        0x1000) == S.DCA_EINVAL
