@@ -220,11 +220,11 @@ typedef struct dca_chunk_cost {
   int64_t cover_cap;      /* keys of a sparse block's budget, 64 k_s + k_v; <= 0: dense (no bound) */
 } dca_chunk_cost;
 
-/* Cost coefficients, in microseconds, measured for this library on MI355X
- * for the heads and budgets of cfg (n_q, n_k are ignored): the attention at
- * its measured rate per (row, key, head), the index build and sparse plan per
- * prefix key and head, and cover_cap = 64 * vs_k_slash + vs_k_vertical for a
- * sparse prefill (sparse = 1), no cap and no index cost for a dense one. */
+/* Cost coefficients, in microseconds, fitted to this library's measured
+ * chunk times on MI355X, scaled to the heads of cfg (n_q, n_k are ignored):
+ * per (row, key, head) of attention, per (row, head), per (prefix key, head)
+ * of index build, per chunk; cover_cap = 64 * vs_k_slash + vs_k_vertical for
+ * a sparse prefill (sparse = 1), no cap and no index cost for a dense one. */
 DCA_API int dca_chunk_cost_default(const dca_cfg *cfg, int32_t sparse, dca_chunk_cost *cost);
 
 /* Equal-time chunk schedule: splits tokens [0, n_tokens) into exactly

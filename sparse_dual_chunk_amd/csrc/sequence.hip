@@ -72,15 +72,14 @@ int dca_chunk_cost_default(const dca_cfg* cfg, int32_t sparse, dca_chunk_cost* c
   if (cfg->vs_k_vertical < 0 || cfg->vs_k_slash < 0) return DCA_EINVAL;
   if (sparse != 0 && sparse != 1) return DCA_EINVAL;
   const double h = cfg->h_q;
-  // measured on MI355X (7B heads, 32K-row chunks of 32K to 1M-key prefixes):
-  // attention ~850 TFLOP/s on 4 * 128 flops per (row, key, head) pair; index
-  // build + sparse plan ~25 ms per million prefix keys for 28 heads; query
-  // rotations, key append and LSE merge ~2 ns per (row, head); ~60 us of
-  // launches and small kernels per chunk
-  cost->per_call = 60.0;
-  cost->per_row = 2.0e-3 * h;
-  cost->per_pair = 512.0 / 850.0e12 * 1.0e6 * h;
-  cost->per_index_key = sparse ? 9.0e-4 * h : 0.0;
+  // least-squares fit to the chunk times of a 256K-token, 40-head prompt in
+  // eight 32K-row chunks on MI355X (the fit reproduces them within 3%):
+  // 0.55 ns per modelled (row, key, head) pair, 3.8 ns per (row, head),
+  // 0.62 ns per (prefix key, head) of index build, 0.4 ms per chunk
+  cost->per_call = 400.0;
+  cost->per_row = 3.8e-3 * h;
+  cost->per_pair = 5.5e-7 * h;
+  cost->per_index_key = sparse ? 6.2e-4 * h : 0.0;
   cost->cover_cap = sparse ? 64LL * cfg->vs_k_slash + cfg->vs_k_vertical : 0;
   return DCA_OK;
 }

@@ -154,6 +154,6 @@ def test_default_costs_follow_the_heads_and_budgets():
     s = S.dca_chunk_cost_default(cfg, True)
     assert d.cover_cap == 0 and d.per_index_key == 0.0
     assert s.cover_cap == 64 * 16384 + 4096 and s.per_index_key > 0
-    assert d.per_pair == pytest.approx(28 * 512 / 850e12 * 1e6)
+    assert d.per_pair == pytest.approx(28 * 5.5e-7)
     half = S.dca_chunk_cost_default(S.Config(**{**cfg.__dict__, "h_q": 14, "h_kv": 2}), False)
     assert half.per_pair == pytest.approx(d.per_pair / 2)
