@@ -373,6 +373,127 @@ def bench_sequence(args) -> int:
     return 0
 
 
+MOE_METRIC = "fused MoE layer memory bandwidth (routed experts' weights + activations / layer time)"
+
+
+def bench_moe(args) -> int:
+    """One step = one fused MoE layer (64 experts, top-8, d_model 3584, d_ff 2560) over a
+    generation batch of --moe-tokens tokens: slot sort, gate/up product + SwiGLU, down
+    product, weighted sum.  Weights resident in HBM before the timed region."""
+    import torch
+    import sparse_dual_chunk_amd as S
+    from oracle import moe_oracle as M
+    from workloads import moe as WM
+
+    w = WM.MOE_DECODE_64.scaled(n_tokens=args.moe_tokens)
+    log(f"moe: {w.n_tokens} tokens, {w.n_experts} experts top-{w.top_k}, {w.d_model} x {w.d_ff}; generating")
+    w13, w2 = WM.make_weights(w, args.seed)
+    x, ids, wts = WM.make_tokens(w, args.seed)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16) if a.dtype == np.uint16
+                                     else np.ascontiguousarray(a)).cuda()
+    X, IDS, WTS = dev(x), dev(ids), dev(wts)
+    cfg = S.MoeConfig(n_tokens=w.n_tokens, n_experts=w.n_experts, top_k=w.top_k, d_model=w.d_model, d_ff=w.d_ff)
+    # the weights enter HBM once, in the packed layout the layer streams
+    U13, U2 = dev(w13), dev(w2)
+    W13, W2 = torch.empty_like(U13), torch.empty_like(U2)
+    S.moe_pack_weights(U13, U2, cfg, W13, W2)
+    torch.cuda.synchronize()
+    del U13, U2
+    out = torch.empty((w.n_tokens, w.d_model), dtype=torch.int16, device="cuda")
+    ws = torch.empty(S.moe_workspace_size(cfg), dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    hev = HipEvents()
+    n_ev = 2 * S.MOE_STAGE_COUNT
+    for _ in range(args.warmup):
+        S.moe_forward(X, IDS, WTS, W13, W2, cfg, out, ws)
+    torch.cuda.synchronize()
+    evs = [hev.create(n_ev) for _ in range(args.steps)]
+    log(f"timing {args.steps} step(s)")
+    t0 = time.perf_counter()
+    for st in range(args.steps):
+        S.moe_forward(X, IDS, WTS, W13, W2, cfg, out, ws, stage_events=evs[st])
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    stage_ms = {name: float(np.median([hev.elapsed_ms(e[2 * i], e[2 * i + 1]) for e in evs]))
+                for i, name in enumerate(S.MOE_STAGES)}
+    layer_ms = float(np.median([hev.elapsed_ms(e[0], e[-1]) for e in evs]))
+    active = len(set(int(i) for i in ids.ravel() if 0 <= i < w.n_experts))
+    N = int(((ids >= 0) & (ids < w.n_experts)).sum())
+    d, dff = w.d_model, w.d_ff
+    # algorithmic bytes: each routed expert's weights once, each token row once,
+    # activations written and read once, weighted outputs written and read once
+    gate_up_bytes = active * 2 * dff * d * 2 + w.n_tokens * d * 2 + N * dff * 2
+    down_bytes = active * d * dff * 2 + N * dff * 2 + N * d * 4
+    sum_bytes = N * d * 4 + w.n_tokens * d * 2
+    layer_bytes = gate_up_bytes + down_bytes + sum_bytes
+    achieved = gate_up_bytes / (stage_ms["gate_up"] / 1e3) / 1e9
+    result = {
+        "metric": MOE_METRIC,
+        "value": round(layer_bytes / (layer_ms / 1e3) / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "n_tokens": w.n_tokens, "n_experts": w.n_experts, "top_k": w.top_k,
+                   "d_model": d, "d_ff": dff, "routed_experts": active, "seed": args.seed},
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "traffic": moe_traffic_from_profile(gate_up_bytes),
+            "kernel": "moe_mma_kernel<true> (gate/up + SwiGLU)",
+            "avg_launch_ms": round(stage_ms["gate_up"], 5),
+            "algorithmic_bytes_per_launch": gate_up_bytes,
+        },
+        "layer_ms": round(layer_ms, 5),
+        "stage_ms": {k2: round(v2, 5) for k2, v2 in stage_ms.items()},
+        "down_GBps": round(down_bytes / (stage_ms["down"] / 1e3) / 1e9, 1),
+    }
+    if not args.no_cpu_baseline:
+        sample = list(range(min(8, w.n_tokens)))
+        log(f"cpu baseline: the oracle on tokens {sample[0]}..{sample[-1]}")
+        t1 = time.perf_counter()
+        M.moe_forward(x, ids, wts, w13, w2, tokens=sample)
+        t_s = time.perf_counter() - t1
+        try:
+            from threadpoolctl import threadpool_info
+            cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        except Exception:
+            cores = os.cpu_count() or 1
+        e_s = len(set(int(i) for t in sample for i in ids[t] if 0 <= i < w.n_experts))
+        s_bytes = e_s * 3 * d * dff * 2 + len(sample) * d * 2
+        result["cpu_baseline"] = {"value": round(s_bytes / t_s / 1e9, 3), "unit": "GB/s", "cores": int(cores),
+                                  "kind": "oracle",
+                                  "sample": f"fp64 oracle on tokens 0..{len(sample) - 1} ({e_s} routed experts, "
+                                            f"{t_s:.1f} s): their experts' weight bytes over the time"}
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def moe_traffic_from_profile(algo_bytes: float):
+    """HBM bytes per gate/up launch from the committed FETCH_SIZE / WRITE_SIZE summary, if it
+    was taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", "moe_traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+        src = os.path.join(ROOT, "sparse_dual_chunk_amd", "csrc", "moe.hip")
+        if rec.get("source_sha256_16") != hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]:
+            return None
+        return rec.get("gate_up_bytes_per_launch")
+    except Exception:
+        return None
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -391,6 +512,9 @@ def main() -> int:
     ap.add_argument("--decode", action="store_true",
                     help="measure the generation-step attention over the 1M-key cache instead of the prefill")
     ap.add_argument("--decode-tokens", type=int, default=1)
+    ap.add_argument("--moe", action="store_true",
+                    help="measure the fused MoE layer (64 experts, top-8, 3584 x 2560) instead of the prefill")
+    ap.add_argument("--moe-tokens", type=int, default=64)
     ap.add_argument("--sequence", action="store_true",
                     help="measure the whole-prompt chunked prefill (default prompt: the 14B 256K one), "
                          "fixed 32K chunks against the equal-time schedule, index builds in order or overlapped")
@@ -417,6 +541,8 @@ def main() -> int:
         return bench_decode(args)
     if args.sequence:
         return bench_sequence(args)
+    if args.moe:
+        return bench_moe(args)
 
     import torch
     import sparse_dual_chunk_amd as S

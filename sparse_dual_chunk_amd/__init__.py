@@ -19,6 +19,12 @@ Names follow the C ABI in ``include/dcasparse.h``:
 * :func:`dca_prefill_sequence_workspace_size`
 * :func:`dca_prefill_sequence`
 * :func:`dca_strerror`
+
+and ``include/moe.h`` (the fused MoE layer, in the same library):
+
+* :func:`moe_workspace_size`
+* :func:`moe_pack_weights`
+* :func:`moe_forward`
 """
 from __future__ import annotations
 
@@ -105,6 +111,25 @@ class dca_sequence_plan(ctypes.Structure):
     ]
 
 
+class moe_cfg(ctypes.Structure):
+    """Mirror of ``struct moe_cfg``."""
+    _fields_ = [
+        ("n_tokens", ctypes.c_int32),
+        ("n_experts", ctypes.c_int32),
+        ("top_k", ctypes.c_int32),
+        ("d_model", ctypes.c_int32),
+        ("d_ff", ctypes.c_int32),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
+        ("stream", ctypes.c_void_p),
+        ("stage_events", ctypes.c_void_p),
+    ]
+
+
+MOE_STAGE_COUNT = 4
+MOE_STAGES = ("sort", "gate_up", "down", "sum")
+
+
 class DcaError(RuntimeError):
     def __init__(self, code: int, where: str):
         super().__init__(f"{where}: error {code} ({dca_strerror(code)})")
@@ -154,6 +179,14 @@ def lib() -> ctypes.CDLL:
                                            ctypes.POINTER(dca_sequence_plan), ctypes.POINTER(dca_cfg),
                                            ctypes.POINTER(dca_key_cache), ctypes.c_void_p]
         L.dca_prefill_sequence.restype = ctypes.c_int
+        L.moe_workspace_size.argtypes = [ctypes.POINTER(moe_cfg), ctypes.POINTER(ctypes.c_size_t)]
+        L.moe_workspace_size.restype = ctypes.c_int
+        L.moe_pack_weights.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(moe_cfg), ctypes.c_void_p,
+                                       ctypes.c_void_p]
+        L.moe_pack_weights.restype = ctypes.c_int
+        L.moe_forward.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                  ctypes.POINTER(moe_cfg), ctypes.c_void_p]
+        L.moe_forward.restype = ctypes.c_int
         L.dca_strerror.argtypes = [ctypes.c_int]
         L.dca_strerror.restype = ctypes.c_char_p
         _lib = L
@@ -403,3 +436,53 @@ def dca_prefill_sequence(q, k, v, bounds, cfg: Config, cache: KeyCache, out, wor
                                     _ptr(out))
     if rc != DCA_OK:
         raise DcaError(rc, "dca_prefill_sequence")
+
+
+# ---------------------------------------------------------------- fused MoE layer (include/moe.h)
+@dataclasses.dataclass
+class MoeConfig:
+    n_tokens: int
+    n_experts: int
+    top_k: int
+    d_model: int
+    d_ff: int
+
+    def to_c(self, **ptrs) -> moe_cfg:
+        c = moe_cfg()
+        for f in dataclasses.fields(self):
+            setattr(c, f.name, getattr(self, f.name))
+        for k, v in ptrs.items():
+            setattr(c, k, v)
+        return c
+
+
+def moe_workspace_size(cfg: MoeConfig) -> int:
+    c = cfg.to_c()
+    n = ctypes.c_size_t(0)
+    rc = lib().moe_workspace_size(ctypes.byref(c), ctypes.byref(n))
+    if rc != DCA_OK:
+        raise DcaError(rc, "moe_workspace_size")
+    return int(n.value)
+
+
+def moe_pack_weights(w13, w2, cfg: MoeConfig, w13_packed, w2_packed, stream=None) -> None:
+    """Write the packed weight layout moe_forward streams (same shapes as w13 / w2)."""
+    c = cfg.to_c(stream=_stream(stream))
+    rc = lib().moe_pack_weights(_ptr(w13), _ptr(w2), ctypes.byref(c), _ptr(w13_packed), _ptr(w2_packed))
+    if rc != DCA_OK:
+        raise DcaError(rc, "moe_pack_weights")
+
+
+def moe_forward(x, topk_ids, topk_weights, w13_packed, w2_packed, cfg: MoeConfig, out, workspace, stream=None,
+                stage_events: Optional[Sequence[int]] = None) -> None:
+    """Fused MoE layer: out [T][d_model] bf16 from x, routing ids / weights and the packed expert weights."""
+    ev_arr = None
+    if stage_events is not None:
+        ev_arr = (ctypes.c_void_p * (2 * MOE_STAGE_COUNT))(*[int(e) for e in stage_events])
+    c = cfg.to_c(workspace=_ptr(workspace), workspace_bytes=workspace.numel() * workspace.element_size(),
+                 stream=_stream(stream),
+                 stage_events=ctypes.cast(ev_arr, ctypes.c_void_p) if ev_arr is not None else None)
+    rc = lib().moe_forward(_ptr(x), _ptr(topk_ids), _ptr(topk_weights), _ptr(w13_packed), _ptr(w2_packed),
+                           ctypes.byref(c), _ptr(out))
+    if rc != DCA_OK:
+        raise DcaError(rc, "moe_forward")

@@ -11,7 +11,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libdcasparse.so")
-SOURCES = ["api.hip", "rope.hip", "attn.hip", "decode.hip", "vs_score.hip", "select.hip", "sequence.hip"]
+SOURCES = ["api.hip", "rope.hip", "attn.hip", "decode.hip", "vs_score.hip", "select.hip", "sequence.hip", "moe.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

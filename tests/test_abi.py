@@ -20,8 +20,11 @@ if not os.path.exists(S.LIB_PATH):
     pytest.skip("libdcasparse.so not built (python -m sparse_dual_chunk_amd.build)", allow_module_level=True)
 
 
+MOE_HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
 def _declared_functions():
-    src = open(HEADER).read()
+    src = open(HEADER).read() + open(MOE_HEADER).read()
     return re.findall(r"DCA_API\s+[\w\s\*]+?\b(\w+)\s*\(", src)
 
 
@@ -30,7 +33,8 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == {"dca_workspace_size", "vs_index_build", "dca_sparse_prefill", "dca_key_cache_append",
                           "dca_sparse_prefill_cached", "dca_decode_workspace_size", "dca_decode", "dca_strerror",
                           "dca_chunk_cost_default", "dca_chunk_schedule", "dca_prefill_sequence_workspace_size",
-                          "dca_prefill_sequence"}
+                          "dca_prefill_sequence", "moe_workspace_size", "moe_forward",
+                          "moe_pack_weights"}
     out = subprocess.run(["nm", "-D", "--defined-only", S.LIB_PATH], capture_output=True, text=True).stdout
     exported = {l.split()[-1] for l in out.splitlines() if l.strip()}
     for n in names:
@@ -52,13 +56,13 @@ def test_struct_layout_matches_header(tmp_path):
     assert vals[1:] == [getattr(S.dca_cfg, f).offset for f, _ in S.dca_cfg._fields_]
 
 
-@pytest.mark.parametrize("name", ["dca_key_cache", "dca_chunk_cost", "dca_sequence_plan"])
+@pytest.mark.parametrize("name", ["dca_key_cache", "dca_chunk_cost", "dca_sequence_plan", "moe_cfg"])
 def test_other_struct_layouts_match_header(tmp_path, name):
     st = getattr(S, name)
     prog = tmp_path / "st.c"
     prog.write_text(
         '#include <stdio.h>\n#include <stddef.h>\n#include "%s"\n'
-        'int main(void){printf("%%zu", sizeof(%s));\n' % (HEADER, name)
+        'int main(void){printf("%%zu", sizeof(%s));\n' % (MOE_HEADER, name)
         + "".join('printf(" %%zu", offsetof(%s, %s));\n' % (name, f) for f, _ in st._fields_)
         + "return 0;}\n")
     exe = tmp_path / "st"
@@ -304,3 +308,46 @@ def test_sequence_rejects_bad_calls_before_any_launch():
     kc = _FakeCache(960).to_c()
     assert S.lib().dca_prefill_sequence(0x1000, 0x1000, 0x1000, ctypes.byref(p), ctypes.byref(c), ctypes.byref(kc),
                                         0x1000) == S.DCA_EINVAL
+
+
+# ---- fused MoE layer
+def _mcfg(**kw):
+    base = dict(n_tokens=64, n_experts=64, top_k=8, d_model=3584, d_ff=2560)
+    base.update(kw)
+    return S.MoeConfig(**base)
+
+
+@pytest.mark.parametrize("kw,code", [(dict(n_tokens=0), S.DCA_EINVAL), (dict(top_k=0), S.DCA_EINVAL),
+                                     (dict(top_k=65), S.DCA_EUNSUPPORTED), (dict(n_experts=1024), S.DCA_EUNSUPPORTED),
+                                     (dict(d_model=3500), S.DCA_EUNSUPPORTED), (dict(d_ff=64), S.DCA_EUNSUPPORTED)])
+def test_moe_workspace_size_validation(kw, code):
+    with pytest.raises(S.DcaError) as ei:
+        S.moe_workspace_size(_mcfg(**kw))
+    assert ei.value.code == code
+
+
+def test_moe_workspace_holds_activations_and_outputs():
+    n = S.moe_workspace_size(_mcfg())
+    slots = 64 * 8
+    assert n >= slots * 2560 * 2 + slots * 3584 * 4 + slots * 4 + 65 * 4
+
+
+def test_moe_rejects_bad_calls_before_any_launch():
+    cfg = _mcfg()
+    t = _FakeTensor(S.moe_workspace_size(cfg))
+    small = _FakeTensor(S.moe_workspace_size(cfg) - 256)
+    with pytest.raises(S.DcaError) as ei:
+        S.moe_forward(t, t, t, t, t, cfg, t, small, stream=0)
+    assert ei.value.code == S.DCA_EWORKSPACE
+    c = cfg.to_c(workspace=0x1000, workspace_bytes=1 << 40, stream=0)
+    assert S.lib().moe_forward(0x1000, None, 0x1000, 0x1000, 0x1000, ctypes.byref(c), 0x1000) == S.DCA_EINVAL
+
+
+def test_moe_pack_rejects_overlap_and_bad_shapes():
+    cfg = _mcfg(n_experts=2, d_model=256, d_ff=128)
+    c = cfg.to_c(stream=0)
+    n13 = 2 * 2 * 128 * 256 * 2
+    # packed copy overlapping its source
+    assert S.lib().moe_pack_weights(0x100000, 0x900000, ctypes.byref(c), 0x100000 + n13 // 2, 0xA00000) == S.DCA_EINVAL
+    c2 = _mcfg(d_ff=100).to_c(stream=0)
+    assert S.lib().moe_pack_weights(0x1000, 0x2000, ctypes.byref(c2), 0x3000, 0x4000) == S.DCA_EUNSUPPORTED
