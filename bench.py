@@ -166,8 +166,18 @@ def bench_decode(args) -> int:
     cfg = S.Config(n_q=n_t, n_k=n_k, h_q=w.h_q, h_kv=w.h_kv, dca_chunk=w.dca_chunk, dca_local=w.dca_local,
                    rope_base=w.rope_base, yarn_s=w.yarn_s, split_k=args.split_k)
     K, V, Q = dev(k), dev(v), dev(q)
-    cache = S.KeyCache.allocate(n_k, w.h_kv)
-    S.dca_key_cache_append(K, 0, cfg, cache)
+    if args.page_keys:
+        # a pool of pages in a seeded random order (one spare page per 64)
+        n_table = (n_k + args.page_keys - 1) // args.page_keys
+        n_pages = n_table + n_table // 64 + 1
+        table = np.random.default_rng([args.seed, 9]).permutation(n_pages)[:n_table]
+        cache = S.PagedKV.allocate(n_pages, args.page_keys, w.h_kv, table)
+        S.dca_paged_append(K, V, 0, cfg, cache)
+        run = lambda **kw: S.dca_decode_paged(Q, cache, cfg, out, ws, **kw)
+    else:
+        cache = S.KeyCache.allocate(n_k, w.h_kv)
+        S.dca_key_cache_append(K, 0, cfg, cache)
+        run = lambda **kw: S.dca_decode(Q, cache, V, cfg, out, ws, **kw)
     del K
     out = torch.empty(Q.shape, dtype=torch.int16, device="cuda")
     ws = torch.empty(S.dca_decode_workspace_size(cfg), dtype=torch.uint8, device="cuda")
@@ -175,14 +185,14 @@ def bench_decode(args) -> int:
     hev = HipEvents()
     n_ev = 2 * S.DCA_STAGE_COUNT
     for _ in range(args.warmup):
-        S.dca_decode(Q, cache, V, cfg, out, ws)
+        run()
     torch.cuda.synchronize()
     evs = [hev.create(n_ev) for _ in range(args.steps)]
     log(f"timing {args.steps} step(s)")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for st in range(args.steps):
-        S.dca_decode(Q, cache, V, cfg, out, ws, stage_events=evs[st])
+        run(stage_events=evs[st])
     torch.cuda.synchronize()
     ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
     stage_ms = {name: float(np.mean([hev.elapsed_ms(e[2 * i], e[2 * i + 1]) for e in evs]))
@@ -208,7 +218,8 @@ def bench_decode(args) -> int:
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "7b_decode_1m_cache", "n_tokens": n_t, "n_k": n_k, "h_q": w.h_q, "h_kv": w.h_kv,
+        "config": {"workload": "7b_decode_1m_cache" + (f"_paged_{args.page_keys}" if args.page_keys else ""),
+                   "n_tokens": n_t, "n_k": n_k, "h_q": w.h_q, "h_kv": w.h_kv,
                    "head_dim": w.head_dim, "dca_chunk": w.dca_chunk, "dca_local": w.dca_local,
                    "rope_base": w.rope_base, "yarn_s": w.yarn_s, "seed": args.seed},
         "roofline": {
@@ -512,6 +523,8 @@ def main() -> int:
     ap.add_argument("--decode", action="store_true",
                     help="measure the generation-step attention over the 1M-key cache instead of the prefill")
     ap.add_argument("--decode-tokens", type=int, default=1)
+    ap.add_argument("--page-keys", type=int, default=0,
+                    help="decode over a paged cache with pages of this many keys (0: contiguous cache)")
     ap.add_argument("--moe", action="store_true",
                     help="measure the fused MoE layer (64 experts, top-8, 3584 x 2560) instead of the prefill")
     ap.add_argument("--moe-tokens", type=int, default=64)

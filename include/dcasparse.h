@@ -199,6 +199,43 @@ DCA_API int dca_decode_workspace_size(const dca_cfg *cfg, size_t *bytes);
 DCA_API int dca_decode(const dca_bf16 *q, const dca_key_cache *cache, const dca_bf16 *v, const dca_cfg *cfg,
                        dca_bf16 *out);
 
+/* ---- Paged key / value cache for generation ------------------------------
+ * The same rotated keys, their values and flags, kept in a pool of
+ * fixed-size pages shared by many sequences; a sequence owns a page table.
+ * Pools (caller-owned device memory):
+ *   k_hi, k_lo, v [n_pages][page_keys][h_kv][head_dim]
+ *   k_flags       [n_pages][h_kv][page_keys / 32]  bit j % 32 of word
+ *                 (page, g, (j % page_keys) / 32): key j of KV head g is high-norm
+ * page_table (device int32 [n_table]): logical page p (keys p * page_keys ..
+ * (p+1) * page_keys - 1 of the sequence) lives in pool page page_table[p].
+ * Entries outside [0, n_pages) are never written through and are clamped
+ * when read (that key range then holds unspecified data, never an
+ * out-of-bounds access). */
+typedef struct dca_paged_kv {
+  dca_bf16 *k_hi;
+  dca_bf16 *k_lo;
+  dca_bf16 *v;
+  uint32_t *k_flags;
+  int32_t   n_pages;      /* >= 1; n_pages * page_keys * h_kv * head_dim * 2 < 2^32 */
+  int32_t   page_keys;    /* multiple of 32 */
+  const int32_t *page_table;
+  int32_t   n_table;      /* entries of page_table */
+} dca_paged_kv;
+
+/* Rotates keys j0 .. j0+n-1 of the sequence into their pages (k, v point at
+ * key j0, layout [n][h_kv][head_dim] raw bf16), copies their values and
+ * rewrites their flag bits.  Requires j0 >= 0, n >= 1 and
+ * j0 + n <= n_table * page_keys.  Reads the same cfg fields as
+ * dca_key_cache_append; no workspace. */
+DCA_API int dca_paged_append(const dca_bf16 *k, const dca_bf16 *v, int32_t j0, int32_t n, const dca_cfg *cfg,
+                             const dca_paged_kv *cache);
+
+/* dca_decode over a paged cache: keys and values 0 .. cfg->n_k - 1 of the
+ * sequence through its page table (cfg->n_k <= n_table * page_keys).  Same
+ * workspace (dca_decode_workspace_size), outputs and events; with the same
+ * keys and values the outputs equal dca_decode's bit for bit. */
+DCA_API int dca_decode_paged(const dca_bf16 *q, const dca_paged_kv *cache, const dca_cfg *cfg, dca_bf16 *out);
+
 /* ---- Whole-sequence prefill ----------------------------------------------
  * The pages' chunked prefill runs a long prompt chunk by chunk: chunk c holds
  * query rows [b_c, b_{c+1}) and attends the prefix [0, b_{c+1}).  Dynamic

@@ -14,6 +14,8 @@ Names follow the C ABI in ``include/dcasparse.h``:
 * :func:`dca_sparse_prefill_cached`
 * :func:`dca_decode_workspace_size`
 * :func:`dca_decode`
+* :func:`dca_paged_append`
+* :func:`dca_decode_paged`
 * :func:`dca_chunk_cost_default`
 * :func:`dca_chunk_schedule`
 * :func:`dca_prefill_sequence_workspace_size`
@@ -84,6 +86,20 @@ class dca_key_cache(ctypes.Structure):
         ("k_lo", ctypes.c_void_p),
         ("k_flags", ctypes.c_void_p),
         ("capacity", ctypes.c_int32),
+    ]
+
+
+class dca_paged_kv(ctypes.Structure):
+    """Mirror of ``struct dca_paged_kv``."""
+    _fields_ = [
+        ("k_hi", ctypes.c_void_p),
+        ("k_lo", ctypes.c_void_p),
+        ("v", ctypes.c_void_p),
+        ("k_flags", ctypes.c_void_p),
+        ("n_pages", ctypes.c_int32),
+        ("page_keys", ctypes.c_int32),
+        ("page_table", ctypes.c_void_p),
+        ("n_table", ctypes.c_int32),
     ]
 
 
@@ -166,6 +182,12 @@ def lib() -> ctypes.CDLL:
         L.dca_decode.argtypes = [ctypes.c_void_p, ctypes.POINTER(dca_key_cache), ctypes.c_void_p,
                                  ctypes.POINTER(dca_cfg), ctypes.c_void_p]
         L.dca_decode.restype = ctypes.c_int
+        L.dca_paged_append.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                       ctypes.POINTER(dca_cfg), ctypes.POINTER(dca_paged_kv)]
+        L.dca_paged_append.restype = ctypes.c_int
+        L.dca_decode_paged.argtypes = [ctypes.c_void_p, ctypes.POINTER(dca_paged_kv), ctypes.POINTER(dca_cfg),
+                                       ctypes.c_void_p]
+        L.dca_decode_paged.restype = ctypes.c_int
         L.dca_chunk_cost_default.argtypes = [ctypes.POINTER(dca_cfg), ctypes.c_int32, ctypes.POINTER(dca_chunk_cost)]
         L.dca_chunk_cost_default.restype = ctypes.c_int
         L.dca_chunk_schedule.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
@@ -362,6 +384,63 @@ def dca_sparse_prefill_cached(q, cache: KeyCache, v, positions, cfg: Config, out
     rc = lib().dca_sparse_prefill_cached(_ptr(q), ctypes.byref(kc), _ptr(v), pos_p, ctypes.byref(c), _ptr(out))
     if rc != DCA_OK:
         raise DcaError(rc, "dca_sparse_prefill_cached")
+
+
+# ---------------------------------------------------------------- paged cache
+@dataclasses.dataclass
+class PagedKV:
+    """A page pool plus one sequence's page table (see ``struct dca_paged_kv``)."""
+    k_hi: object        # int16 [n_pages][page_keys][h_kv][128]
+    k_lo: object
+    v: object
+    k_flags: object     # int32 [n_pages][h_kv][page_keys // 32], zero before the first append
+    page_table: object  # int32 [n_table] (device)
+    n_pages: int
+    page_keys: int
+
+    @staticmethod
+    def allocate(n_pages: int, page_keys: int, h_kv: int, page_table, head_dim: int = 128,
+                 device: str = "cuda") -> "PagedKV":
+        import torch
+        shape = (n_pages, page_keys, h_kv, head_dim)
+        pt = torch.as_tensor(np.asarray(page_table, dtype=np.int32)).to(device)
+        return PagedKV(k_hi=torch.empty(shape, dtype=torch.int16, device=device),
+                       k_lo=torch.empty(shape, dtype=torch.int16, device=device),
+                       v=torch.empty(shape, dtype=torch.int16, device=device),
+                       k_flags=torch.zeros((n_pages, h_kv, page_keys // 32), dtype=torch.int32, device=device),
+                       page_table=pt, n_pages=n_pages, page_keys=page_keys)
+
+    def to_c(self) -> dca_paged_kv:
+        c = dca_paged_kv()
+        c.k_hi, c.k_lo, c.v, c.k_flags = _ptr(self.k_hi), _ptr(self.k_lo), _ptr(self.v), _ptr(self.k_flags)
+        c.n_pages, c.page_keys = self.n_pages, self.page_keys
+        c.page_table = _ptr(self.page_table)
+        c.n_table = int(self.page_table.numel())
+        return c
+
+
+def dca_paged_append(k, v, j0: int, cfg: Config, cache: PagedKV, stream=None) -> None:
+    """Rotate keys j0 .. j0 + k.shape[0] - 1 into their pages and copy their values."""
+    c = cfg.to_c(stream=_stream(stream))
+    kc = cache.to_c()
+    rc = lib().dca_paged_append(_ptr(k), _ptr(v), int(j0), int(k.shape[0]), ctypes.byref(c), ctypes.byref(kc))
+    if rc != DCA_OK:
+        raise DcaError(rc, "dca_paged_append")
+
+
+def dca_decode_paged(q, cache: PagedKV, cfg: Config, out, workspace, lse_out=None, stream=None,
+                     stage_events: Optional[Sequence[int]] = None) -> None:
+    """dca_decode over a paged cache."""
+    ev_arr = None
+    if stage_events is not None:
+        ev_arr = (ctypes.c_void_p * (2 * DCA_STAGE_COUNT))(*[int(e) for e in stage_events])
+    c = cfg.to_c(workspace=_ptr(workspace), workspace_bytes=workspace.numel() * workspace.element_size(),
+                 stream=_stream(stream), lse_out=_ptr(lse_out),
+                 stage_events=ctypes.cast(ev_arr, ctypes.c_void_p) if ev_arr is not None else None)
+    kc = cache.to_c()
+    rc = lib().dca_decode_paged(_ptr(q), ctypes.byref(kc), ctypes.byref(c), _ptr(out))
+    if rc != DCA_OK:
+        raise DcaError(rc, "dca_decode_paged")
 
 
 # ---------------------------------------------------------------- whole-prompt chunked prefill

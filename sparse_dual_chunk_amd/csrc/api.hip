@@ -24,6 +24,10 @@ hipError_t launch_vs_score(const VsArgs& A, const uint16_t* q, int n_q, hipStrea
 hipError_t launch_select(const SelArgs& A, hipStream_t stream);
 hipError_t launch_plan(const PlanArgs& A, hipStream_t stream);
 hipError_t launch_decode_attn(const DecArgs& A, hipStream_t stream);
+hipError_t launch_rotate_keys_paged(const uint16_t* k, const uint16_t* v, uint16_t* khi, uint16_t* klo,
+                                    uint16_t* vpool, uint32_t* kflags, const int32_t* ptab, int page_keys,
+                                    int n_pages, const Freqs& f, int j0, int n, int h_kv, int S, float thr2,
+                                    hipStream_t stream);
 hipError_t launch_decode_merge(const DecArgs& A, uint16_t* out, float* lse_out, hipStream_t stream);
 
 }  // namespace dca
@@ -462,12 +466,34 @@ int dca_decode_workspace_size(const dca_cfg* cfg, size_t* bytes) {
   return DCA_OK;
 }
 
-int dca_decode(const dca_bf16* q, const dca_key_cache* cache, const dca_bf16* v, const dca_cfg* cfg, dca_bf16* out) {
+}  // extern "C"
+
+namespace {
+
+int paged_check(const dca_paged_kv* c, int h_kv, int head_dim) {
+  if (!c || !c->k_hi || !c->k_lo || !c->v || !c->k_flags || !c->page_table) return DCA_EINVAL;
+  if (c->n_pages < 1 || c->n_table < 1) return DCA_EINVAL;
+  if (c->page_keys < 32 || c->page_keys % 32) return DCA_EUNSUPPORTED;
+  if ((long long)c->n_pages * c->page_keys * h_kv * head_dim * 2 >= (1LL << 32)) return DCA_EUNSUPPORTED;
+  if ((long long)c->n_table * c->page_keys >= (1LL << 30)) return DCA_EUNSUPPORTED;
+  return DCA_OK;
+}
+
+// The generation step over a contiguous cache (paged == nullptr) or a paged pool.
+int decode_impl(const dca_bf16* q, const dca_key_cache* cache, const dca_paged_kv* paged, const dca_bf16* v,
+                const dca_cfg* cfg, dca_bf16* out) {
   int rc = validate_decode(cfg);
   if (rc != DCA_OK) return rc;
-  if (!q || !cache || !v || !out) return DCA_EINVAL;
-  if (!cache->k_hi || !cache->k_lo || !cache->k_flags || cache->capacity < cfg->n_k) return DCA_EINVAL;
-  if ((long long)cache->capacity * cfg->h_kv * cfg->head_dim * 2 >= (1LL << 32)) return DCA_EUNSUPPORTED;
+  if (!q || !out) return DCA_EINVAL;
+  if (paged) {
+    rc = paged_check(paged, cfg->h_kv, cfg->head_dim);
+    if (rc != DCA_OK) return rc;
+    if ((long long)paged->n_table * paged->page_keys < cfg->n_k) return DCA_EINVAL;
+  } else {
+    if (!cache || !v) return DCA_EINVAL;
+    if (!cache->k_hi || !cache->k_lo || !cache->k_flags || cache->capacity < cfg->n_k) return DCA_EINVAL;
+    if ((long long)cache->capacity * cfg->h_kv * cfg->head_dim * 2 >= (1LL << 32)) return DCA_EUNSUPPORTED;
+  }
   const DecLayout L = make_dec_layout(cfg);
   rc = check_workspace(cfg, L.bytes);
   if (rc != DCA_OK) return rc;
@@ -485,10 +511,17 @@ int dca_decode(const dca_bf16* q, const dca_key_cache* cache, const dca_bf16* v,
   record(cfg, 1, 1);
   DecArgs A;
   A.qhi = at<uint16_t>(cfg, L.qhi); A.qlo = at<uint16_t>(cfg, L.qlo);
-  A.khi = cache->k_hi; A.klo = cache->k_lo; A.kflags = cache->k_flags; A.v = v;
+  if (paged) {
+    A.khi = paged->k_hi; A.klo = paged->k_lo; A.kflags = paged->k_flags; A.v = paged->v;
+    A.ptab = paged->page_table; A.page_keys = paged->page_keys; A.n_pages = paged->n_pages;
+    A.kflag_words = 0;
+  } else {
+    A.khi = cache->k_hi; A.klo = cache->k_lo; A.kflags = cache->k_flags; A.v = v;
+    A.ptab = nullptr; A.page_keys = 32; A.n_pages = 1;
+    A.kflag_words = (cache->capacity + 31) / 32;
+  }
   A.part_o = at<float>(cfg, L.part_o); A.part_lse = at<float>(cfg, L.part_lse);
   A.n_t = n_t; A.n_k = n_k; A.h_q = h_q; A.h_kv = cfg->h_kv; A.S = cfg->dca_chunk;
-  A.kflag_words = (cache->capacity + 31) / 32;
   A.part_keys = L.part_keys; A.n_parts = L.n_parts; A.n_cb = L.n_cb;
   record(cfg, 2, 0);
   if (launch_decode_attn(A, st) != hipSuccess) return DCA_EHIP;
@@ -496,6 +529,40 @@ int dca_decode(const dca_bf16* q, const dca_key_cache* cache, const dca_bf16* v,
   record(cfg, 3, 0);
   if (launch_decode_merge(A, out, cfg->lse_out, st) != hipSuccess) return DCA_EHIP;
   record(cfg, 3, 1);
+  return DCA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dca_decode(const dca_bf16* q, const dca_key_cache* cache, const dca_bf16* v, const dca_cfg* cfg, dca_bf16* out) {
+  if (!cache) return DCA_EINVAL;
+  return decode_impl(q, cache, nullptr, v, cfg, out);
+}
+
+int dca_decode_paged(const dca_bf16* q, const dca_paged_kv* cache, const dca_cfg* cfg, dca_bf16* out) {
+  if (!cache) return DCA_EINVAL;
+  return decode_impl(q, nullptr, cache, nullptr, cfg, out);
+}
+
+int dca_paged_append(const dca_bf16* k, const dca_bf16* v, int32_t j0, int32_t n, const dca_cfg* cfg,
+                     const dca_paged_kv* cache) {
+  if (!cfg || !cache || !k || !v) return DCA_EINVAL;
+  if (cfg->h_kv < 1) return DCA_EINVAL;
+  if (cfg->head_dim != 128) return DCA_EUNSUPPORTED;
+  if (cfg->dca_chunk < 64 || cfg->dca_chunk % 64 != 0) return DCA_EUNSUPPORTED;
+  if (!(cfg->rope_base > 1.0) || !std::isfinite(cfg->rope_base)) return DCA_EINVAL;
+  if (!std::isfinite(cfg->precise_norm)) return DCA_EINVAL;
+  int rc = paged_check(cache, cfg->h_kv, cfg->head_dim);
+  if (rc != DCA_OK) return rc;
+  if (j0 < 0 || n < 1 || (long long)j0 + n > (long long)cache->n_table * cache->page_keys) return DCA_EINVAL;
+  const float thr = cfg->precise_norm == 0.f ? 2.f * std::sqrt((float)D) : cfg->precise_norm;
+  const float thr2 = thr < 0.f ? -1.f : thr * thr;
+  if (launch_rotate_keys_paged(k, v, cache->k_hi, cache->k_lo, cache->v, cache->k_flags, cache->page_table,
+                               cache->page_keys, cache->n_pages, make_freqs(cfg->rope_base), j0, n, cfg->h_kv,
+                               cfg->dca_chunk, thr2, (hipStream_t)cfg->stream) != hipSuccess)
+    return DCA_EHIP;
   return DCA_OK;
 }
 

@@ -38,6 +38,11 @@ struct DecArgs {
   float* part_o;            // [P][n_t][h_q][128] normalised partial outputs
   float* part_lse;          // [P][h_q][n_t] natural-log partial LSE
   int n_t, n_k, h_q, h_kv, S, kflag_words, part_keys, n_parts, n_cb;
+  // paged cache: khi / klo / v are pools of n_pages pages of page_keys rows,
+  // kflags is [n_pages][h_kv][page_keys / 32], logical page p of the sequence
+  // is pool page ptab[p] (clamped into [0, n_pages))
+  const int32_t* ptab;
+  int page_keys, n_pages;
 };
 
 struct VsArgs {

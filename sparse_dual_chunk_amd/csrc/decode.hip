@@ -22,6 +22,10 @@
 
 namespace dca {
 
+// PAGED: keys, values and flags live in pages of a pool (a tile of 32 keys
+// never straddles a page); the tile at logical key kt0 starts at pool row
+// tile_row(kt0).  Otherwise the pool is the contiguous cache (pool row = key).
+template <bool PAGED>
 __global__ void __launch_bounds__(64) dca_decode_kernel(DecArgs A) {
   // two stages of K and V: four LDS objects, so that the compiler tells the
   // reads of one stage from the direct loads in flight into the other
@@ -88,22 +92,37 @@ __global__ void __launch_bounds__(64) dca_decode_kernel(DecArgs A) {
   const unsigned rowb = (unsigned)(A.h_kv * D * 2);
   const int lrow = lane >> 4;
   const unsigned lchunk = 16u * (unsigned)((lane & 15) ^ (5 * lrow));
-  auto issue = [&](__amdgpu_buffer_rsrc_t rs, uint8_t* stage, int kt0) __attribute__((always_inline)) {
+  // pool page of the tile at logical key kt0 (wave-uniform)
+  auto tile_page = [&](int kt0) __attribute__((always_inline)) -> int {
+    const int pg = A.ptab[kt0 / A.page_keys];
+    return min(max(pg, 0), A.n_pages - 1);
+  };
+  auto tile_row = [&](int kt0) __attribute__((always_inline)) -> int {
+    return PAGED ? tile_page(kt0) * A.page_keys + kt0 % A.page_keys : kt0;
+  };
+  auto issue = [&](__amdgpu_buffer_rsrc_t rs, uint8_t* stage, int kt0, int row0) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int key = min(kt0 + 4 * j + lrow, A.n_k - 1);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(stage + j * GRPB), 16,
-                                               (int)((unsigned)key * rowb + lchunk), 0, 0, 0);
+                                               (int)((unsigned)(row0 + key - kt0) * rowb + lchunk), 0, 0, 0);
     }
   };
   typedef __attribute__((address_space(4))) const uint32_t cu32;
   cu32* kf = (cu32*)(A.kflags + (long long)g * A.kflag_words);
+  const int pwords = A.page_keys / 32;
+  // the high-norm flag word of the tile at kt0
+  auto flag_word = [&](int kt0) __attribute__((always_inline)) -> uint32_t {
+    if (PAGED)
+      return ((cu32*)A.kflags)[((long long)tile_page(kt0) * A.h_kv + g) * pwords + (kt0 % A.page_keys) / 32];
+    return kf[kt0 >> 5];
+  };
 
   // S^T of the staged tile for one mode's query rotation, plus the lo terms
   // when the tile holds a high-norm key
   const uint16_t* kl_base = A.klo + g * D;
   const long long kstride = (long long)A.h_kv * D;
-  auto qk = [&](const uint8_t* kt, int mode, int kt0, bool precise) __attribute__((always_inline)) -> f32x16 {
+  auto qk = [&](const uint8_t* kt, int mode, int kt0, int row0, bool precise) __attribute__((always_inline)) -> f32x16 {
     if (mode != q_mode) load_q(mode);
     f32x16 s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(kt + tile_off(l32, half)), qh[0],
                                                        negm, 0, 0, 0);
@@ -113,7 +132,7 @@ __global__ void __launch_bounds__(64) dca_decode_kernel(DecArgs A) {
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qh[kk], s, 0, 0, 0);
     }
     if (precise) {
-      const uint16_t* klrow = kl_base + (long long)min(kt0 + l32, A.n_k - 1) * kstride;
+      const uint16_t* klrow = kl_base + (long long)(row0 + min(kt0 + l32, A.n_k - 1) - kt0) * kstride;
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk) {
         const bf16x8 alo = *(const bf16x8*)(klrow + 16 * kk + 8 * half);
@@ -131,15 +150,16 @@ __global__ void __launch_bounds__(64) dca_decode_kernel(DecArgs A) {
   auto compute_tile = [&](const uint8_t* kt, const uint8_t* vt, int kt0) __attribute__((always_inline)) {
     const int m_k = kt0 / A.S;                 // a tile lies inside one DCA chunk
     const int mode = m_k == m_t ? 2 : (m_k + 1 == m_t ? 1 : 0);
-    const bool precise = kf[kt0 >> 5] != 0u;
+    const bool precise = flag_word(kt0) != 0u;
+    const int row0 = PAGED && precise ? tile_row(kt0) : kt0;
     const bool has0 = __any(col_ok && mode == 0);
     const bool has1 = __any(col_ok && mode == 1);
     const int first = has0 ? 0 : (has1 ? 1 : 2);
-    f32x16 s = qk(kt, first, kt0, precise);
+    f32x16 s = qk(kt, first, kt0, row0, precise);
     // the columns' tokens span at most a few chunks: later modes are spelled
     // out (a loop here would make the compiler wait for the staged loads)
     auto merge_mode = [&](int m) __attribute__((always_inline)) {
-      const f32x16 s2 = qk(kt, m, kt0, precise);
+      const f32x16 s2 = qk(kt, m, kt0, row0, precise);
 #pragma unroll
       for (int vv = 0; vv < 16; ++vv)
         if (mode == m) s[vv] = s2[vv];
@@ -216,18 +236,24 @@ __global__ void __launch_bounds__(64) dca_decode_kernel(DecArgs A) {
   // when at most 16 of this wave's vector loads are outstanding (other loads
   // in between only make that wait longer).
   const int t_last = t_end - 1;
-  issue(rs_k, kst0, BN * t_beg);
-  issue(rs_v, vst0, BN * t_beg);
-  issue(rs_k, kst1, BN * min(t_beg + 1, t_last));
-  issue(rs_v, vst1, BN * min(t_beg + 1, t_last));
+  {
+    const int k0 = BN * t_beg, k1 = BN * min(t_beg + 1, t_last);
+    const int r0 = tile_row(k0), r1 = tile_row(k1);
+    issue(rs_k, kst0, k0, r0);
+    issue(rs_v, vst0, k0, r0);
+    issue(rs_k, kst1, k1, r1);
+    issue(rs_v, vst1, k1, r1);
+  }
   auto step = [&](uint8_t* kc, uint8_t* vc, int ti) __attribute__((always_inline)) {
+    const int kn = BN * min(ti + 2, t_last);
+    const int rn = tile_row(kn);            // scalar page-table load, waited for with the LDS reads below
     __builtin_amdgcn_s_waitcnt(0x4F70);   // vmcnt(16): tile ti landed, tile ti+1 may be in flight
     asm volatile("" ::: "memory");
     compute_tile(kc, vc, BN * ti);
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this stage's reads are done
     asm volatile("" ::: "memory");
-    issue(rs_k, kc, BN * min(ti + 2, t_last));
-    issue(rs_v, vc, BN * min(ti + 2, t_last));
+    issue(rs_k, kc, kn, rn);
+    issue(rs_v, vc, kn, rn);
   };
   for (int ti = t_beg; ti < t_end; ti += 2) {
     step(kst0, vst0, ti);
@@ -309,7 +335,10 @@ __global__ void __launch_bounds__(1024) dca_decode_merge_kernel(const float* __r
 
 hipError_t launch_decode_attn(const DecArgs& A, hipStream_t stream) {
   const long long wgs = (long long)A.n_parts * A.h_kv * A.n_cb;
-  hipLaunchKernelGGL(dca_decode_kernel, dim3((unsigned)wgs), dim3(64), 0, stream, A);
+  if (A.ptab)
+    hipLaunchKernelGGL(dca_decode_kernel<true>, dim3((unsigned)wgs), dim3(64), 0, stream, A);
+  else
+    hipLaunchKernelGGL(dca_decode_kernel<false>, dim3((unsigned)wgs), dim3(64), 0, stream, A);
   return hipGetLastError();
 }
 

@@ -17,13 +17,39 @@ __global__ void kbits_clear_kernel(uint32_t* __restrict__ kbits, long long n) {
     kbits[i] = 0u;
 }
 
+// Destination rows of key j: the contiguous cache (row j), or a paged pool
+// (logical page j / page_keys of the sequence is pool page ptab[..]; keys of
+// a page whose entry lies outside [0, n_pages) are not written).
+struct PageMap {
+  const int32_t* ptab;
+  int page_keys, n_pages;
+};
+
+// pool row of key j, or -1 when its page entry is out of range
+__device__ inline long long pool_row(const PageMap& pm, int j) {
+  if (!pm.ptab) return j;
+  const int pg = pm.ptab[j / pm.page_keys];
+  if (pg < 0 || pg >= pm.n_pages) return -1;
+  return (long long)pg * pm.page_keys + j % pm.page_keys;
+}
+
+// index of the flag word holding key j of KV head g (contiguous: [h_kv][words];
+// paged: [n_pages][h_kv][page_keys / 32]), or -1
+__device__ inline long long flag_index(const PageMap& pm, int g, int j, int kbits_words, int h_kv) {
+  if (!pm.ptab) return (long long)g * kbits_words + (j >> 5);
+  const int pg = pm.ptab[j / pm.page_keys];
+  if (pg < 0 || pg >= pm.n_pages) return -1;
+  return ((long long)pg * h_kv + g) * (pm.page_keys / 32) + (j % pm.page_keys) / 32;
+}
+
 // One 16-lane group per (key, kv head) row; lane c16 owns pairs 4*c16 .. 4*c16+3.
-// Keys j0 .. j0+n-1: k points at key j0, the outputs and bits are indexed by
-// the absolute key.
+// Keys j0 .. j0+n-1: k (and v, when given) point at key j0, the outputs and
+// bits are indexed by the absolute key through the page map.
 __global__ void __launch_bounds__(256) rotate_keys_kernel(
     const uint16_t* __restrict__ k, uint16_t* __restrict__ khi, uint16_t* __restrict__ klo,
     uint32_t* __restrict__ kbits, Freqs fq, int j0,
-    int n, int h_kv, int S, float thr2, int kbits_words) {
+    int n, int h_kv, int S, float thr2, int kbits_words, PageMap pm,
+    const uint16_t* __restrict__ v_src, uint16_t* __restrict__ v_dst) {
   const int lane16 = threadIdx.x & 15;
   const long long row = (long long)blockIdx.x * 16 + (threadIdx.x >> 4);
   const long long n_rows = (long long)n * h_kv;
@@ -33,7 +59,8 @@ __global__ void __launch_bounds__(256) rotate_keys_kernel(
   const int g = (int)(rrow % h_kv);
   const double pos = (double)(j % S);
   const uint16_t* src = k + rrow * D;
-  const long long orow = (long long)j0 * h_kv + rrow;
+  const long long prow = pool_row(pm, j);
+  const long long orow = prow * h_kv + g;
   // two 8-byte loads: dims 4c..4c+3 and 64+4c..64+4c+3
   uint2 a = *(const uint2*)(src + 4 * lane16);
   uint2 b = *(const uint2*)(src + HALF + 4 * lane16);
@@ -61,7 +88,7 @@ __global__ void __launch_bounds__(256) rotate_keys_kernel(
   ss += __shfl_xor(ss, 4, 16);
   ss += __shfl_xor(ss, 2, 16);
   ss += __shfl_xor(ss, 1, 16);
-  if (!active) return;
+  if (!active || prow < 0) return;
   uint2 oa, ob, pa, pb;
   oa.x = ha[0] | ((uint32_t)ha[1] << 16); oa.y = ha[2] | ((uint32_t)ha[3] << 16);
   ob.x = hb[0] | ((uint32_t)hb[1] << 16); ob.y = hb[2] | ((uint32_t)hb[3] << 16);
@@ -71,9 +98,13 @@ __global__ void __launch_bounds__(256) rotate_keys_kernel(
   *(uint2*)(khi + orow * D + HALF + 4 * lane16) = ob;
   *(uint2*)(klo + orow * D + 4 * lane16) = pa;
   *(uint2*)(klo + orow * D + HALF + 4 * lane16) = pb;
+  if (v_src) {
+    // the value row is copied as is: 16 bytes per lane
+    *(uint4*)(v_dst + orow * D + 8 * lane16) = *(const uint4*)(v_src + rrow * D + 8 * lane16);
+  }
   // high-norm keys: one bit per key, OR-ed in (order-independent)
   if (lane16 == 0 && thr2 >= 0.f && ss > thr2)
-    atomicOr(&kbits[(long long)g * kbits_words + (j >> 5)], 1u << (j & 31));
+    atomicOr(&kbits[flag_index(pm, g, j, kbits_words, h_kv)], 1u << (j & 31));
 }
 
 // Queries: one rotation per DCA mode the row takes part in, at the mode's query
@@ -172,8 +203,10 @@ hipError_t launch_hn_next(const uint32_t* kbits, uint8_t* hn, int n_pad, int h_k
   return hipGetLastError();
 }
 
-// Clear the bits of keys [j0, j0 + n) of every KV head (partial words keep their other bits).
-__global__ void kbits_clear_range_kernel(uint32_t* __restrict__ kbits, int kbits_words, int h_kv, int j0, int n) {
+// Clear the bits of keys [j0, j0 + n) of every KV head (partial words keep
+// their other bits); a word never straddles a page (page_keys % 32 == 0).
+__global__ void kbits_clear_range_kernel(uint32_t* __restrict__ kbits, int kbits_words, int h_kv, int j0, int n,
+                                         PageMap pm) {
   const int w0 = j0 >> 5, w1 = (j0 + n - 1) >> 5;
   const long long nw = (long long)(w1 - w0 + 1) * h_kv;
   for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < nw; i += (long long)gridDim.x * blockDim.x) {
@@ -182,7 +215,8 @@ __global__ void kbits_clear_range_kernel(uint32_t* __restrict__ kbits, int kbits
     const int lo = max(j0, 32 * w) - 32 * w;             // first bit of the range in this word
     const int hi = min(j0 + n, 32 * w + 32) - 32 * w;    // one past the last
     const uint32_t m = (hi - lo == 32) ? 0xFFFFFFFFu : (((1u << (hi - lo)) - 1u) << lo);
-    atomicAnd(&kbits[(long long)g * kbits_words + w], ~m);
+    const long long fi = flag_index(pm, g, 32 * w, kbits_words, h_kv);
+    if (fi >= 0) atomicAnd(&kbits[fi], ~m);
   }
 }
 
@@ -193,12 +227,30 @@ hipError_t launch_rotate_keys(const uint16_t* k, uint16_t* khi, uint16_t* klo, u
                               bool clear_all, hipStream_t stream) {
   const long long rows = (long long)n * h_kv;
   const int blocks = (int)((rows + 15) / 16);
+  const PageMap none = {nullptr, 0, 0};
   if (clear_all)
     hipLaunchKernelGGL(kbits_clear_kernel, dim3(256), dim3(256), 0, stream, kbits, (long long)h_kv * kbits_words);
   else
-    hipLaunchKernelGGL(kbits_clear_range_kernel, dim3(64), dim3(256), 0, stream, kbits, kbits_words, h_kv, j0, n);
+    hipLaunchKernelGGL(kbits_clear_range_kernel, dim3(64), dim3(256), 0, stream, kbits, kbits_words, h_kv, j0, n,
+                       none);
   hipLaunchKernelGGL(rotate_keys_kernel, dim3(blocks), dim3(256), 0, stream,
-                     k, khi, klo, kbits, f, j0, n, h_kv, S, thr2, kbits_words);
+                     k, khi, klo, kbits, f, j0, n, h_kv, S, thr2, kbits_words, none, (const uint16_t*)nullptr,
+                     (uint16_t*)nullptr);
+  return hipGetLastError();
+}
+
+// Paged append: keys [j0, j0 + n) rotated into the pool pages of the page
+// table, their values copied, their flag bits rewritten.
+hipError_t launch_rotate_keys_paged(const uint16_t* k, const uint16_t* v, uint16_t* khi, uint16_t* klo,
+                                    uint16_t* vpool, uint32_t* kflags, const int32_t* ptab, int page_keys,
+                                    int n_pages, const Freqs& f, int j0, int n, int h_kv, int S, float thr2,
+                                    hipStream_t stream) {
+  const long long rows = (long long)n * h_kv;
+  const int blocks = (int)((rows + 15) / 16);
+  const PageMap pm = {ptab, page_keys, n_pages};
+  hipLaunchKernelGGL(kbits_clear_range_kernel, dim3(64), dim3(256), 0, stream, kflags, 0, h_kv, j0, n, pm);
+  hipLaunchKernelGGL(rotate_keys_kernel, dim3(blocks), dim3(256), 0, stream,
+                     k, khi, klo, kflags, f, j0, n, h_kv, S, thr2, 0, pm, v, vpool);
   return hipGetLastError();
 }
 

@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
                           "dca_sparse_prefill_cached", "dca_decode_workspace_size", "dca_decode", "dca_strerror",
                           "dca_chunk_cost_default", "dca_chunk_schedule", "dca_prefill_sequence_workspace_size",
                           "dca_prefill_sequence", "moe_workspace_size", "moe_forward",
-                          "moe_pack_weights"}
+                          "moe_pack_weights", "dca_paged_append", "dca_decode_paged"}
     out = subprocess.run(["nm", "-D", "--defined-only", S.LIB_PATH], capture_output=True, text=True).stdout
     exported = {l.split()[-1] for l in out.splitlines() if l.strip()}
     for n in names:
@@ -56,7 +56,7 @@ def test_struct_layout_matches_header(tmp_path):
     assert vals[1:] == [getattr(S.dca_cfg, f).offset for f, _ in S.dca_cfg._fields_]
 
 
-@pytest.mark.parametrize("name", ["dca_key_cache", "dca_chunk_cost", "dca_sequence_plan", "moe_cfg"])
+@pytest.mark.parametrize("name", ["dca_key_cache", "dca_chunk_cost", "dca_sequence_plan", "moe_cfg", "dca_paged_kv"])
 def test_other_struct_layouts_match_header(tmp_path, name):
     st = getattr(S, name)
     prog = tmp_path / "st.c"
@@ -351,3 +351,39 @@ def test_moe_pack_rejects_overlap_and_bad_shapes():
     assert S.lib().moe_pack_weights(0x100000, 0x900000, ctypes.byref(c), 0x100000 + n13 // 2, 0xA00000) == S.DCA_EINVAL
     c2 = _mcfg(d_ff=100).to_c(stream=0)
     assert S.lib().moe_pack_weights(0x1000, 0x2000, ctypes.byref(c2), 0x3000, 0x4000) == S.DCA_EUNSUPPORTED
+
+
+# ---- paged cache
+class _FakePaged(S.PagedKV):
+    def __init__(self, n_pages, page_keys, n_table):
+        t = _FakeTensor()
+        super().__init__(k_hi=t, k_lo=t, v=t, k_flags=t, page_table=_FakeTensor(n_table), n_pages=n_pages,
+                         page_keys=page_keys)
+
+    def to_c(self):
+        c = super().to_c()
+        c.n_table = self.page_table.numel()
+        return c
+
+
+@pytest.mark.parametrize("n_pages,page_keys,n_table,code", [(8, 48, 8, S.DCA_EUNSUPPORTED),   # not a multiple of 32
+                                                             (8, 0, 8, S.DCA_EUNSUPPORTED),
+                                                             (0, 64, 8, S.DCA_EINVAL),
+                                                             (8, 64, 12, S.DCA_EINVAL),      # 768 < 800 keys
+                                                             (1 << 20, 1024, 1, S.DCA_EUNSUPPORTED)])  # pool > 4 GiB
+def test_paged_decode_validation(n_pages, page_keys, n_table, code):
+    cfg = _dcfg(n_q=2, n_k=800)
+    t = _FakeTensor(S.dca_decode_workspace_size(cfg))
+    with pytest.raises(S.DcaError) as ei:
+        S.dca_decode_paged(t, _FakePaged(n_pages, page_keys, n_table), cfg, t, t, stream=0)
+    assert ei.value.code == code
+
+
+def test_paged_append_validation():
+    cfg = _dcfg()
+    c = cfg.to_c(stream=0)
+    for j0, n, code in [(-1, 4, S.DCA_EINVAL), (0, 0, S.DCA_EINVAL), (600, 41, S.DCA_EINVAL)]:
+        kc = _FakePaged(8, 64, 10).to_c()                        # 640 keys of table
+        assert S.lib().dca_paged_append(0x1000, 0x1000, j0, n, ctypes.byref(c), ctypes.byref(kc)) == code
+    kc = _FakePaged(8, 64, 10).to_c()
+    assert S.lib().dca_paged_append(0x1000, None, 0, 4, ctypes.byref(c), ctypes.byref(kc)) == S.DCA_EINVAL
