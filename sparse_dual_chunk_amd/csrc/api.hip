@@ -18,7 +18,7 @@ hipError_t launch_hn_next(const uint32_t* kbits, uint8_t* hn, int n_pad, int h_k
 hipError_t launch_rotate_queries(const uint16_t* q, uint16_t* qhi, uint16_t* qlo, const double* inv_freq,
                                  int n_q, int h_q, int p0, int S, int W, float qscale, hipStream_t stream);
 hipError_t launch_attn(const AttnArgs& A, hipStream_t stream);
-hipError_t launch_lse_merge(const float* part_o, const float* part_lse, uint16_t* out, float* lse_out,
+hipError_t launch_lse_merge(const uint16_t* part_o, const float* part_lse, uint16_t* out, float* lse_out,
                             int P, int n_q, int h_q, hipStream_t stream);
 hipError_t launch_vs_score(const VsArgs& A, const uint16_t* q, int n_q, hipStream_t stream);
 hipError_t launch_select(const SelArgs& A, hipStream_t stream);
@@ -145,7 +145,7 @@ Layout make_layout(const dca_cfg* c) {
     place(L.vbits, cur, (size_t)h_q * L.vbits_words * 4);
   }
   if (L.split > 1) {
-    place(L.part_o, cur, (size_t)L.split * n_q * h_q * D * 4);
+    place(L.part_o, cur, (size_t)L.split * n_q * h_q * D * 2);
     place(L.part_lse, cur, (size_t)L.split * h_q * n_q * 4);
   }
   L.prefill_bytes = cur;
@@ -398,7 +398,7 @@ int prefill_impl(const dca_bf16* q, const dca_bf16* k, const dca_key_cache* cach
   A.khi = khi; A.klo = klo; A.v = v;
   A.kbits = kbits; A.hn = at<uint8_t>(cfg, L.hn); A.hn_pad = L.hn_pad;
   A.out = out; A.lse_out = cfg->lse_out;
-  A.part_o = L.split > 1 ? at<float>(cfg, L.part_o) : nullptr;
+  A.part_o = L.split > 1 ? at<uint16_t>(cfg, L.part_o) : nullptr;
   A.part_lse = L.split > 1 ? at<float>(cfg, L.part_lse) : nullptr;
   A.tiles = at<int4>(cfg, L.tiles); A.n_tiles = at<int32_t>(cfg, L.n_tiles); A.t_first = at<int32_t>(cfg, L.t_first);
   A.ext = at<int32_t>(cfg, L.ext); A.n_ext = at<int32_t>(cfg, L.n_ext);

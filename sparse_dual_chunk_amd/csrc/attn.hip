@@ -576,16 +576,19 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A) {
     }
     if (A.lse_out && half == 0) A.lse_out[(long long)h * A.n_q + qrow] = lse;
   } else {
-    float* dst = A.part_o + (((long long)part * A.n_q + qrow) * A.h_q + h) * D;
+    // the normalised partial in fp16 (values within max |v|; 2^-11 relative,
+    // well below the bf16 rounding of the merged output), half the bytes the
+    // merge reads
+    uint16_t* dst = A.part_o + (((long long)part * A.n_q + qrow) * A.h_q + h) * D;
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
 #pragma unroll
       for (int qd = 0; qd < 4; ++qd) {
         const int d0 = 32 * db + 8 * qd + 4 * half;
-        float4 f;
-        f.x = o[db][4 * qd + 0] * inv_l; f.y = o[db][4 * qd + 1] * inv_l;
-        f.z = o[db][4 * qd + 2] * inv_l; f.w = o[db][4 * qd + 3] * inv_l;
-        *(float4*)(dst + d0) = f;
+        uint2 pk;
+        pk.x = f32_to_f16_bits(o[db][4 * qd + 0] * inv_l) | ((uint32_t)f32_to_f16_bits(o[db][4 * qd + 1] * inv_l) << 16);
+        pk.y = f32_to_f16_bits(o[db][4 * qd + 2] * inv_l) | ((uint32_t)f32_to_f16_bits(o[db][4 * qd + 3] * inv_l) << 16);
+        *(uint2*)(dst + d0) = pk;
       }
     }
     if (half == 0) A.part_lse[((long long)part * A.h_q + h) * A.n_q + qrow] = lse;
@@ -600,7 +603,7 @@ __global__ void __launch_bounds__(128, 2) dca_attn_exact_kernel(AttnArgs A) { at
 __global__ void __launch_bounds__(128, 2) dca_attn_dense_kernel(AttnArgs A) { attn_body<true, false>(A); }
 
 // LSE merge of split partials: m = max lse_p, O = sum e^{lse_p-m} O_p / sum e^{lse_p-m}.
-__global__ void __launch_bounds__(256) lse_merge_kernel(const float* __restrict__ part_o,
+__global__ void __launch_bounds__(256) lse_merge_kernel(const uint16_t* __restrict__ part_o,
                                                         const float* __restrict__ part_lse,
                                                         uint16_t* __restrict__ out, float* __restrict__ lse_out,
                                                         int P, int n_q, int h_q) {
@@ -618,7 +621,9 @@ __global__ void __launch_bounds__(256) lse_merge_kernel(const float* __restrict_
     for (int p = 0; p < P; ++p) {
       const float lp = part_lse[((long long)p * h_q + h) * n_q + row];
       const float w = (lp == -INFINITY) ? 0.f : __expf(lp - m);
-      const float4 x = *(const float4*)(part_o + (((long long)p * n_q + row) * h_q + h) * D + 4 * l);
+      const uint2 hx = *(const uint2*)(part_o + (((long long)p * n_q + row) * h_q + h) * D + 4 * l);
+      const float4 x = make_float4(f16_bits_to_f32(hx.x & 0xFFFFu), f16_bits_to_f32(hx.x >> 16),
+                                   f16_bits_to_f32(hx.y & 0xFFFFu), f16_bits_to_f32(hx.y >> 16));
       acc.x += w * x.x; acc.y += w * x.y; acc.z += w * x.z; acc.w += w * x.w;
       wsum += w;
     }
@@ -646,7 +651,7 @@ hipError_t launch_attn(const AttnArgs& A, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_lse_merge(const float* part_o, const float* part_lse, uint16_t* out, float* lse_out,
+hipError_t launch_lse_merge(const uint16_t* part_o, const float* part_lse, uint16_t* out, float* lse_out,
                             int P, int n_q, int h_q, hipStream_t stream) {
   const long long items = (long long)n_q * h_q;
   const int blocks = (int)((items + 7) / 8);

@@ -42,6 +42,14 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
 
 __device__ __forceinline__ __bf16 bits_as_bf16(uint16_t b) { return __builtin_bit_cast(__bf16, b); }
 
+// IEEE half: round to nearest even, and back (exact)
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float f) {
+  return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t b) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
+}
+
 // Angle pos * theta reduced to [-pi, pi] in fp64, returned as fp32.
 __device__ __forceinline__ float reduce_angle(double pos, double theta) {
   double a = pos * theta;
