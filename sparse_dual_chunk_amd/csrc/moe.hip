@@ -21,6 +21,7 @@
 // (B) are read from the caches.  Loads run ahead of the MFMAs by STG - 1 steps.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 
 #include "../../include/moe.h"
@@ -29,7 +30,6 @@
 namespace {
 
 constexpr int KSTEP = 64;     // k per pipeline step (4 MFMAs of k 16)
-constexpr int ROWS = 128;     // weight rows per workgroup (4 waves x 32)
 
 struct MoeArgs {
   const uint16_t* x;          // [T][d_model]
@@ -250,11 +250,14 @@ __device__ inline void expert_pass(const MoeArgs& A, int e, int beg, int m, int 
   }
 }
 
-// Workgroup (expert e, 128 output rows): 4 waves of 32 rows; passes of up to
-// 64 of the expert's slots.  Experts without slots return at once, so only
-// routed experts' weights are read.
-template <bool GATE_UP>
-__global__ __launch_bounds__(256, 2) void moe_mma_kernel(MoeArgs A) {
+// Workgroup (expert e, 32 * WAVES output rows): WAVES waves of 32 rows;
+// passes of up to 64 of the expert's slots.  Experts without slots return at
+// once, so only routed experts' weights are read.  WAVES = 4 in general; 1
+// when few experts can be routed (a token or two), so that their rows spread
+// over every compute unit.
+template <bool GATE_UP, int WAVES>
+__global__ __launch_bounds__(64 * WAVES, 2) void moe_mma_kernel(MoeArgs A) {
+  constexpr int ROWS = 32 * WAVES;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, l32 = lane & 31, half = lane >> 5;
   const int tiles = (GATE_UP ? A.d_ff : A.d_model) / ROWS;
   const int e = blockIdx.x / tiles, rt = blockIdx.x - e * tiles;
@@ -401,12 +404,22 @@ int moe_forward(const dca_bf16* x, const int32_t* topk_ids, const float* topk_we
   hipLaunchKernelGGL(moe_sort_kernel, dim3(1), dim3(1024), 0, st, A);
   if (hipGetLastError() != hipSuccess) return DCA_EHIP;
   moe_record(cfg, 0, 1);
+  // at most min(E, slots) experts are routed: with fewer than two 4-wave
+  // workgroups per compute unit for them, one-wave workgroups fill the GPU
+  const long long routed = std::min<long long>(cfg->n_experts, (long long)A.n_slots);
+  const bool narrow = routed * (cfg->d_ff / 128) < 512;
   moe_record(cfg, 1, 0);
-  hipLaunchKernelGGL(moe_mma_kernel<true>, dim3(cfg->n_experts * (cfg->d_ff / ROWS)), dim3(256), 0, st, A);
+  if (narrow)
+    hipLaunchKernelGGL((moe_mma_kernel<true, 1>), dim3(cfg->n_experts * (cfg->d_ff / 32)), dim3(64), 0, st, A);
+  else
+    hipLaunchKernelGGL((moe_mma_kernel<true, 4>), dim3(cfg->n_experts * (cfg->d_ff / 128)), dim3(256), 0, st, A);
   if (hipGetLastError() != hipSuccess) return DCA_EHIP;
   moe_record(cfg, 1, 1);
   moe_record(cfg, 2, 0);
-  hipLaunchKernelGGL(moe_mma_kernel<false>, dim3(cfg->n_experts * (cfg->d_model / ROWS)), dim3(256), 0, st, A);
+  if (narrow)
+    hipLaunchKernelGGL((moe_mma_kernel<false, 1>), dim3(cfg->n_experts * (cfg->d_model / 32)), dim3(64), 0, st, A);
+  else
+    hipLaunchKernelGGL((moe_mma_kernel<false, 4>), dim3(cfg->n_experts * (cfg->d_model / 128)), dim3(256), 0, st, A);
   if (hipGetLastError() != hipSuccess) return DCA_EHIP;
   moe_record(cfg, 2, 1);
   moe_record(cfg, 3, 0);

@@ -9,7 +9,8 @@ tokens.  Tolerance (bf16 activations between the products, bf16 output):
 max-abs <= 4e-3 and mean-abs <= 4e-4 on outputs of magnitude up to ~0.5 (the
 bf16 output rounding alone is up to 2^-9 |out| ~ 1e-3; measured max errors
 3e-5 .. 1.6e-3).  More than 1024 slots (600 tokens x 2) takes the slot sort
-through two rounds.
+through two rounds.  Shapes with few routable experts (min(E, slots) x d_ff/128 < 512)
+run one-wave workgroups, the others four-wave ones; both kinds are covered.
 """
 import sys
 
@@ -85,7 +86,8 @@ def check(got_bits, ref, what):
 
 @pytest.mark.parametrize("T,E,k,d,d_ff,skew", [(5, 6, 2, 256, 128, 0.0), (40, 8, 3, 384, 640, 0.0),
                                                 (200, 8, 2, 256, 256, 3.0), (1, 16, 4, 512, 384, 0.0),
-                                                (600, 12, 2, 256, 128, 1.0)])
+                                                (600, 12, 2, 256, 128, 1.0), (64, 128, 2, 256, 512, 0.0),
+                                                (300, 128, 4, 256, 512, 2.0)])
 def test_moe_small_against_oracle(T, E, k, d, d_ff, skew):
     w = WM.MoeWorkload("t", T, E, k, d, d_ff, skew=skew)
     x, ids, wts = WM.make_tokens(w, T + E)
