@@ -114,3 +114,22 @@ def test_paged_decode_against_the_oracle():
     ref, ref_lse = O.decode_attention(q, k, v, oracle_cfg(cfg))
     check_close(a, ref, "paged decode")
     assert np.abs(la - ref_lse).max() <= 1e-2
+
+
+@pytest.mark.timeout(600)
+def test_paged_decode_million_key_cache_equals_contiguous():
+    """7B heads, a 1,048,576-key cache of the benchmark's generator in pages of 256 keys
+    placed by a seeded permutation: 1 and 4 tokens, paged output and LSE equal the
+    contiguous decode bit for bit."""
+    import workloads as W
+    w = W.WORKLOADS["7b_last_chunk_of_1m"]
+    n_k = w.n_k_total
+    k, v = W.make_keys_values(w, n_k, seed=0)
+    cfg = S.Config(n_q=1, n_k=n_k, h_q=w.h_q, h_kv=w.h_kv, dca_chunk=w.dca_chunk, dca_local=w.dca_local,
+                   rope_base=w.rope_base, yarn_s=w.yarn_s)
+    paged, flat, vd, _ = _build(k, v, cfg, 256, 3, cuts=[])
+    for n_t in (1, 4):
+        q = W.make_queries(w, n_k - n_t, n_t, seed=1)
+        c = S.Config(**{**cfg.__dict__, "n_q": n_t})
+        (a, la), (b, lb) = _decode_both(q, paged, flat, vd, c)
+        assert np.array_equal(a, b) and np.array_equal(la, lb), n_t

@@ -142,3 +142,32 @@ def test_sequence_over_the_equal_time_schedule():
     a, la, pa = _sequence(qd, kd, vd, bounds, cfg, True, overlap=True)
     b, lb, pb = _per_chunk(qd, kd, vd, bounds, cfg, True)
     assert torch.equal(a, b) and torch.equal(la, lb) and torch.equal(pa, pb)
+
+
+@pytest.mark.timeout(900)
+def test_sequence_14b_256k_prompt_equals_per_chunk_calls():
+    """The 14B prompt of 262,144 tokens (40 / 8 heads, S = 65536, W = 2048, k_v 2048,
+    k_s 8192) in the eight 32K chunks of the benchmark and in the equal-time chunks of the
+    library's cost model: the driver with the index stream equals the per-chunk calls bit
+    for bit, and every output is finite and bounded by max |v|."""
+    import workloads as W
+    w = W.C4_14B_256K
+    n = w.n_k_total
+    log("generating the 256K prompt")
+    k, v = W.make_keys_values(w, n, seed=0)
+    fixed = list(range(0, n, 32768)) + [n]
+    q = np.concatenate([W.make_queries(w, a, b - a, seed=0) for a, b in zip(fixed[:-1], fixed[1:])])
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    cfg = S.Config(n_q=n, n_k=n, h_q=w.h_q, h_kv=w.h_kv, dca_chunk=w.dca_chunk, dca_local=w.dca_local,
+                   rope_base=w.rope_base, yarn_s=w.yarn_s, vs_k_vertical=w.k_vertical, vs_k_slash=w.k_slash)
+    equal, _ = S.dca_chunk_schedule(n, 8, n, S.dca_chunk_cost_default(cfg, True))
+    vmax = float(np.abs((v.astype(np.uint32) << 16).view(np.float32)).max())
+    for bounds in (fixed, equal):
+        log(f"bounds {bounds}")
+        a, la, pa = _sequence(qd, kd, vd, bounds, cfg, True, overlap=True)
+        b, lb, pb = _per_chunk(qd, kd, vd, bounds, cfg, True)
+        assert torch.equal(a, b) and torch.equal(la, lb) and torch.equal(pa, pb)
+        o = (host_u16(a).astype(np.uint32) << 16).view(np.float32)
+        assert np.isfinite(o).all() and np.abs(o).max() <= vmax * (1 + 2 ** -7)
+        del a, b, la, lb
+        torch.cuda.empty_cache()
