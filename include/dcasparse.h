@@ -202,8 +202,9 @@ DCA_API int dca_decode(const dca_bf16 *q, const dca_key_cache *cache, const dca_
 /* ---- Paged key / value cache for generation ------------------------------
  * The same rotated keys, their values and flags, kept in a pool of
  * fixed-size pages shared by many sequences; a sequence owns a page table.
- * Pools (caller-owned device memory):
- *   k_hi, k_lo, v [n_pages][page_keys][h_kv][head_dim]
+ * Pools (caller-owned device memory), each page laid out head-major so that
+ * the keys of one KV head in a page are consecutive rows:
+ *   k_hi, k_lo, v [n_pages][h_kv][page_keys][head_dim]
  *   k_flags       [n_pages][h_kv][page_keys / 32]  bit j % 32 of word
  *                 (page, g, (j % page_keys) / 32): key j of KV head g is high-norm
  * page_table (device int32 [n_table]): logical page p (keys p * page_keys ..

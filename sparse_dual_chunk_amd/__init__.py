@@ -390,7 +390,7 @@ def dca_sparse_prefill_cached(q, cache: KeyCache, v, positions, cfg: Config, out
 @dataclasses.dataclass
 class PagedKV:
     """A page pool plus one sequence's page table (see ``struct dca_paged_kv``)."""
-    k_hi: object        # int16 [n_pages][page_keys][h_kv][128]
+    k_hi: object        # int16 [n_pages][h_kv][page_keys][128]
     k_lo: object
     v: object
     k_flags: object     # int32 [n_pages][h_kv][page_keys // 32], zero before the first append
@@ -402,7 +402,7 @@ class PagedKV:
     def allocate(n_pages: int, page_keys: int, h_kv: int, page_table, head_dim: int = 128,
                  device: str = "cuda") -> "PagedKV":
         import torch
-        shape = (n_pages, page_keys, h_kv, head_dim)
+        shape = (n_pages, h_kv, page_keys, head_dim)
         pt = torch.as_tensor(np.asarray(page_table, dtype=np.int32)).to(device)
         return PagedKV(k_hi=torch.empty(shape, dtype=torch.int16, device=device),
                        k_lo=torch.empty(shape, dtype=torch.int16, device=device),

@@ -85,11 +85,13 @@ __global__ void __launch_bounds__(64) dca_decode_kernel(DecArgs A) {
   // ---- staged loads: 8 direct loads per tensor and tile, load j filling rows
   // 4j .. 4j+3 (lane: row lane >> 4, chunk (lane & 15) ^ 5(lane >> 4)); rows
   // past the last key read the last key (masked later)
+  // contiguous cache: rows [key][h_kv] from this head's column; paged pool:
+  // pages [h_kv][page_keys], so a tile of one head is 32 consecutive rows
   const __amdgpu_buffer_rsrc_t rs_k =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(A.khi + g * D), (short)0, -1, 0x00020000);
+      __builtin_amdgcn_make_buffer_rsrc((void*)(PAGED ? A.khi : A.khi + g * D), (short)0, -1, 0x00020000);
   const __amdgpu_buffer_rsrc_t rs_v =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(A.v + g * D), (short)0, -1, 0x00020000);
-  const unsigned rowb = (unsigned)(A.h_kv * D * 2);
+      __builtin_amdgcn_make_buffer_rsrc((void*)(PAGED ? A.v : A.v + g * D), (short)0, -1, 0x00020000);
+  const unsigned rowb = (unsigned)((PAGED ? 1 : A.h_kv) * D * 2);
   const int lrow = lane >> 4;
   const unsigned lchunk = 16u * (unsigned)((lane & 15) ^ (5 * lrow));
   // pool page of the tile at logical key kt0 (wave-uniform)
@@ -97,8 +99,9 @@ __global__ void __launch_bounds__(64) dca_decode_kernel(DecArgs A) {
     const int pg = A.ptab[kt0 / A.page_keys];
     return min(max(pg, 0), A.n_pages - 1);
   };
+  // row (in units of rowb) of the tile's first key
   auto tile_row = [&](int kt0) __attribute__((always_inline)) -> int {
-    return PAGED ? tile_page(kt0) * A.page_keys + kt0 % A.page_keys : kt0;
+    return PAGED ? (tile_page(kt0) * A.h_kv + g) * A.page_keys + kt0 % A.page_keys : kt0;
   };
   auto issue = [&](__amdgpu_buffer_rsrc_t rs, uint8_t* stage, int kt0, int row0) __attribute__((always_inline)) {
 #pragma unroll
@@ -120,8 +123,8 @@ __global__ void __launch_bounds__(64) dca_decode_kernel(DecArgs A) {
 
   // S^T of the staged tile for one mode's query rotation, plus the lo terms
   // when the tile holds a high-norm key
-  const uint16_t* kl_base = A.klo + g * D;
-  const long long kstride = (long long)A.h_kv * D;
+  const uint16_t* kl_base = PAGED ? A.klo : A.klo + g * D;
+  const long long kstride = (long long)(PAGED ? 1 : A.h_kv) * D;
   auto qk = [&](const uint8_t* kt, int mode, int kt0, int row0, bool precise) __attribute__((always_inline)) -> f32x16 {
     if (mode != q_mode) load_q(mode);
     f32x16 s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(kt + tile_off(l32, half)), qh[0],

@@ -25,12 +25,14 @@ struct PageMap {
   int page_keys, n_pages;
 };
 
-// pool row of key j, or -1 when its page entry is out of range
-__device__ inline long long pool_row(const PageMap& pm, int j) {
-  if (!pm.ptab) return j;
+// destination row (in rows of head_dim elements) of key j, KV head g:
+// contiguous [capacity][h_kv] rows, or a pool page laid out head-major,
+// [h_kv][page_keys] rows; -1 when the page entry is out of range
+__device__ inline long long out_row(const PageMap& pm, int j, int g, int h_kv) {
+  if (!pm.ptab) return (long long)j * h_kv + g;
   const int pg = pm.ptab[j / pm.page_keys];
   if (pg < 0 || pg >= pm.n_pages) return -1;
-  return (long long)pg * pm.page_keys + j % pm.page_keys;
+  return ((long long)pg * h_kv + g) * pm.page_keys + j % pm.page_keys;
 }
 
 // index of the flag word holding key j of KV head g (contiguous: [h_kv][words];
@@ -59,8 +61,7 @@ __global__ void __launch_bounds__(256) rotate_keys_kernel(
   const int g = (int)(rrow % h_kv);
   const double pos = (double)(j % S);
   const uint16_t* src = k + rrow * D;
-  const long long prow = pool_row(pm, j);
-  const long long orow = prow * h_kv + g;
+  const long long orow = out_row(pm, j, g, h_kv);
   // two 8-byte loads: dims 4c..4c+3 and 64+4c..64+4c+3
   uint2 a = *(const uint2*)(src + 4 * lane16);
   uint2 b = *(const uint2*)(src + HALF + 4 * lane16);
@@ -88,7 +89,7 @@ __global__ void __launch_bounds__(256) rotate_keys_kernel(
   ss += __shfl_xor(ss, 4, 16);
   ss += __shfl_xor(ss, 2, 16);
   ss += __shfl_xor(ss, 1, 16);
-  if (!active || prow < 0) return;
+  if (!active || orow < 0) return;
   uint2 oa, ob, pa, pb;
   oa.x = ha[0] | ((uint32_t)ha[1] << 16); oa.y = ha[2] | ((uint32_t)ha[3] << 16);
   ob.x = hb[0] | ((uint32_t)hb[1] << 16); ob.y = hb[2] | ((uint32_t)hb[3] << 16);

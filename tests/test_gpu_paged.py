@@ -2,8 +2,8 @@
 
 A pool larger than the sequence needs, with the sequence's pages scattered by
 a seeded permutation, filled by appends that cross page boundaries.  Checked:
-every pool page holds bit for bit the rows (rotated K hi / lo, V) and flag
-bits of the contiguous cache for its logical page; the paged decode equals
+every pool page holds bit for bit, head-major, the rows (rotated K hi / lo, V)
+and flag bits of the contiguous cache for its logical page; the paged decode equals
 the contiguous decode bit for bit (output and LSE) for pages of 32, 64 and 256
 keys, several DCA chunks, GQA groups of 2 and 7 and 1-5 tokens; and one case
 against the fp64 oracle.
@@ -82,9 +82,10 @@ def test_pool_pages_hold_the_contiguous_rows():
     pflags = paged.k_flags.cpu().numpy().view(np.uint32)
     for p, pg in enumerate(table):
         a, b = p * P, min(n_k, (p + 1) * P)
-        assert np.array_equal(pk[pg, : b - a], khi[a:b]), p
-        assert np.array_equal(pl[pg, : b - a], klo[a:b]), p
-        assert np.array_equal(pv[pg, : b - a], v[a:b]), p
+        for g in range(h_kv):
+            assert np.array_equal(pk[pg, g, : b - a], khi[a:b, g]), (p, g)
+            assert np.array_equal(pl[pg, g, : b - a], klo[a:b, g]), (p, g)
+            assert np.array_equal(pv[pg, g, : b - a], v[a:b, g]), (p, g)
         for g in range(h_kv):
             for w in range((b - a + 31) // 32):
                 want = flags[g, a // 32 + w]
