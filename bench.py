@@ -86,6 +86,16 @@ def traffic_from_profile(units_per_launch: float):
     return d.get("hbm_bytes_per_launch")
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, inputs, p0s, f_blocks_total: float, n_blocks_total: int):
     """Oracle timing on a bounded sample (about 10-15 s): index scores of three heads, attention of
     five query blocks of one head."""
@@ -120,6 +130,7 @@ def cpu_baseline(w, inputs, p0s, f_blocks_total: float, n_blocks_total: int):
         "value": f_blocks_total / t_step / 1e12,
         "unit": "TFLOP/s",
         "cores": int(cores),
+        "cpu_model": cpu_model(),
         "kind": "oracle",
         "sample": (f"fp64 oracle on the host: index scores of query heads 0-2 of the last chunk "
                    f"({t_index_head:.1f} s per head) and attention of query blocks {blocks} of head 0 "
@@ -249,7 +260,7 @@ def bench_decode(args) -> int:
             cores = os.cpu_count() or 1
         t_step = t_head * w.h_q
         result["cpu_baseline"] = {"value": round(kv_bytes / t_step / 1e9, 4), "unit": "GB/s", "cores": int(cores),
-                                  "kind": "oracle",
+                                  "cpu_model": cpu_model(), "kind": "oracle",
                                   "sample": f"fp64 oracle decode of query head 0 over the whole cache "
                                             f"({t_head:.1f} s), extrapolated to {w.h_q} heads"}
     print(json.dumps(result), flush=True)
@@ -482,7 +493,7 @@ def bench_moe(args) -> int:
         e_s = len(set(int(i) for t in sample for i in ids[t] if 0 <= i < w.n_experts))
         s_bytes = e_s * 3 * d * dff * 2 + len(sample) * d * 2
         result["cpu_baseline"] = {"value": round(s_bytes / t_s / 1e9, 3), "unit": "GB/s", "cores": int(cores),
-                                  "kind": "oracle",
+                                  "cpu_model": cpu_model(), "kind": "oracle",
                                   "sample": f"fp64 oracle on tokens 0..{len(sample) - 1} ({e_s} routed experts, "
                                             f"{t_s:.1f} s): their experts' weight bytes over the time"}
     print(json.dumps(result), flush=True)
