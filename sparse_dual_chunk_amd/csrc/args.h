@@ -15,8 +15,8 @@ struct AttnArgs {
   const uint8_t* hn;        // [h_kv][hn_pad] distance from key j to the next high-norm key, capped at 64
   uint16_t* out;            // [n_q][h_q][128]
   float* lse_out;           // [h_q][n_q] or null
-  uint16_t* part_o;         // [P][n_q][h_q][128] fp16 normalised partials (P > 1)
-  float* part_lse;          // [P][h_q][n_q]      (P > 1)
+  uint16_t* part_o;         // [n_q][h_q][P][128] fp16 normalised partials (P > 1)
+  float* part_lse;          // [h_q][n_q][P]      (P > 1)
   const int4* tiles;        // [h_q][tile_stride] range tiles in offset space: {o1, o2, len1 | len2 << 8, 0}
   const int32_t* n_tiles;   // [h_q]
   const int32_t* t_first;   // [h_q][nb] first range tile of each query block

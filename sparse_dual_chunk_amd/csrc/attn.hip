@@ -579,7 +579,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A) {
     // the normalised partial in fp16 (values within max |v|; 2^-11 relative,
     // well below the bf16 rounding of the merged output), half the bytes the
     // merge reads
-    uint16_t* dst = A.part_o + (((long long)part * A.n_q + qrow) * A.h_q + h) * D;
+    uint16_t* dst = A.part_o + (((long long)qrow * A.h_q + h) * A.split + part) * D;
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
 #pragma unroll
@@ -591,7 +591,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A) {
         *(uint2*)(dst + d0) = pk;
       }
     }
-    if (half == 0) A.part_lse[((long long)part * A.h_q + h) * A.n_q + qrow] = lse;
+    if (half == 0) A.part_lse[((long long)h * A.n_q + qrow) * A.split + part] = lse;
   }
 }
 
@@ -602,38 +602,62 @@ __global__ void __launch_bounds__(128, 2) dca_attn_kernel(AttnArgs A) { attn_bod
 __global__ void __launch_bounds__(128, 2) dca_attn_exact_kernel(AttnArgs A) { attn_body<false, true>(A); }
 __global__ void __launch_bounds__(128, 2) dca_attn_dense_kernel(AttnArgs A) { attn_body<true, false>(A); }
 
-// LSE merge of split partials: m = max lse_p, O = sum e^{lse_p-m} O_p / sum e^{lse_p-m}.
+// LSE merge of the key parts of one (row, head): m = max_p lse_p,
+// O = sum_p e^{lse_p - m} O_p / sum_p e^{lse_p - m}.  One wave per (row, head):
+// the row's parts are contiguous (P x 128 halves), lane l takes dims
+// 8 (l % 16) .. + 7 of parts l / 16, l / 16 + 4, ..., so each load
+// instruction reads 1 KB; the four part groups are combined by shuffles.
 __global__ void __launch_bounds__(256) lse_merge_kernel(const uint16_t* __restrict__ part_o,
                                                         const float* __restrict__ part_lse,
                                                         uint16_t* __restrict__ out, float* __restrict__ lse_out,
                                                         int P, int n_q, int h_q) {
-  // one 32-lane group per (row, head); lane owns 4 dims
-  const long long item = (long long)blockIdx.x * 8 + (threadIdx.x >> 5);
-  const int l = threadIdx.x & 31;
+  const long long item = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
   if (item >= (long long)n_q * h_q) return;
   const int row = (int)(item / h_q);
   const int h = (int)(item % h_q);
+  const int pg = lane >> 4;        // part group
+  const int dc = lane & 15;        // dims 8 dc .. 8 dc + 7
+  const float* lse_row = part_lse + ((long long)h * n_q + row) * P;
+  const uint16_t* o_row = part_o + ((long long)row * h_q + h) * P * D + 8 * dc;
   float m = -INFINITY;
-  for (int p = 0; p < P; ++p) m = fmaxf(m, part_lse[((long long)p * h_q + h) * n_q + row]);
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int p = pg; p < P; p += 4) m = fmaxf(m, lse_row[p]);
+  m = fmaxf(m, __shfl_xor(m, 16));
+  m = fmaxf(m, __shfl_xor(m, 32));
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float wsum = 0.f;
   if (m != -INFINITY) {
-    for (int p = 0; p < P; ++p) {
-      const float lp = part_lse[((long long)p * h_q + h) * n_q + row];
+#pragma unroll 4
+    for (int p = pg; p < P; p += 4) {
+      const float lp = lse_row[p];
       const float w = (lp == -INFINITY) ? 0.f : __expf(lp - m);
-      const uint2 hx = *(const uint2*)(part_o + (((long long)p * n_q + row) * h_q + h) * D + 4 * l);
-      const float4 x = make_float4(f16_bits_to_f32(hx.x & 0xFFFFu), f16_bits_to_f32(hx.x >> 16),
-                                   f16_bits_to_f32(hx.y & 0xFFFFu), f16_bits_to_f32(hx.y >> 16));
-      acc.x += w * x.x; acc.y += w * x.y; acc.z += w * x.z; acc.w += w * x.w;
+      const uint4 hx = *(const uint4*)(o_row + (long long)p * D);
+      const uint32_t wd[4] = {hx.x, hx.y, hx.z, hx.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[2 * i] += w * f16_bits_to_f32(wd[i] & 0xFFFFu);
+        acc[2 * i + 1] += w * f16_bits_to_f32(wd[i] >> 16);
+      }
       wsum += w;
     }
   }
+  // combine the four part groups (lanes dc, dc + 16, dc + 32, dc + 48), in a fixed order
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    acc[i] += __shfl_xor(acc[i], 16);
+    acc[i] += __shfl_xor(acc[i], 32);
+  }
+  wsum += __shfl_xor(wsum, 16);
+  wsum += __shfl_xor(wsum, 32);
+  if (pg != 0) return;
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-  uint2 pk;
-  pk.x = f32_to_bf16_bits(acc.x * inv) | ((uint32_t)f32_to_bf16_bits(acc.y * inv) << 16);
-  pk.y = f32_to_bf16_bits(acc.z * inv) | ((uint32_t)f32_to_bf16_bits(acc.w * inv) << 16);
-  *(uint2*)(out + ((long long)row * h_q + h) * D + 4 * l) = pk;
-  if (lse_out && l == 0) lse_out[(long long)h * n_q + row] = (wsum > 0.f) ? m + __logf(wsum) : -INFINITY;
+  uint4 pk;
+  pk.x = f32_to_bf16_bits(acc[0] * inv) | ((uint32_t)f32_to_bf16_bits(acc[1] * inv) << 16);
+  pk.y = f32_to_bf16_bits(acc[2] * inv) | ((uint32_t)f32_to_bf16_bits(acc[3] * inv) << 16);
+  pk.z = f32_to_bf16_bits(acc[4] * inv) | ((uint32_t)f32_to_bf16_bits(acc[5] * inv) << 16);
+  pk.w = f32_to_bf16_bits(acc[6] * inv) | ((uint32_t)f32_to_bf16_bits(acc[7] * inv) << 16);
+  *(uint4*)(out + ((long long)row * h_q + h) * D + 8 * dc) = pk;
+  if (lse_out && dc == 0) lse_out[(long long)h * n_q + row] = (wsum > 0.f) ? m + __logf(wsum) : -INFINITY;
 }
 
 hipError_t launch_attn(const AttnArgs& A, hipStream_t stream) {
@@ -654,7 +678,7 @@ hipError_t launch_attn(const AttnArgs& A, hipStream_t stream) {
 hipError_t launch_lse_merge(const uint16_t* part_o, const float* part_lse, uint16_t* out, float* lse_out,
                             int P, int n_q, int h_q, hipStream_t stream) {
   const long long items = (long long)n_q * h_q;
-  const int blocks = (int)((items + 7) / 8);
+  const int blocks = (int)((items + 3) / 4);      // one wave per (row, head), four per workgroup
   hipLaunchKernelGGL(lse_merge_kernel, dim3(blocks), dim3(256), 0, stream, part_o, part_lse, out, lse_out,
                      P, n_q, h_q);
   return hipGetLastError();
