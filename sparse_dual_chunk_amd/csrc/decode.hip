@@ -94,9 +94,11 @@ __global__ void __launch_bounds__(64) dca_decode_kernel(DecArgs A) {
   const unsigned rowb = (unsigned)((PAGED ? 1 : A.h_kv) * D * 2);
   const int lrow = lane >> 4;
   const unsigned lchunk = 16u * (unsigned)((lane & 15) ^ (5 * lrow));
-  // pool page of the tile at logical key kt0 (wave-uniform)
+  // pool page of the tile at logical key kt0 (wave-uniform; a scalar load,
+  // so its wait never drains the vector loads in flight)
+  typedef __attribute__((address_space(4))) const int32_t ci32;
   auto tile_page = [&](int kt0) __attribute__((always_inline)) -> int {
-    const int pg = A.ptab[kt0 / A.page_keys];
+    const int pg = ((ci32*)A.ptab)[kt0 / A.page_keys];
     return min(max(pg, 0), A.n_pages - 1);
   };
   // row (in units of rowb) of the tile's first key
