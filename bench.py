@@ -209,6 +209,18 @@ def bench_decode(args) -> int:
     stage_ms = {name: float(np.mean([hev.elapsed_ms(e[2 * i], e[2 * i + 1]) for e in evs]))
                 for i, name in enumerate(S.STAGES)}
     attn_ms = stage_ms["attention"]
+    # the same step captured once in a HIP graph and replayed (a serving loop's launch path)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    for _ in range(args.warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for _ in range(args.steps):
+        g.replay()
+    torch.cuda.synchronize()
+    graph_ms_per_step = (time.perf_counter() - t1) * 1e3 / args.steps
     # algorithmic bytes of the attention kernel: every K (rotated, hi) and V row once,
     # the query rows, and the parts' fp32 partials written
     ws_parts = S.dca_decode_workspace_size(cfg)
@@ -245,6 +257,7 @@ def bench_decode(args) -> int:
             "algorithmic_bytes_per_launch": algo_bytes,
         },
         "tokens_per_s_per_layer": round(n_t / (ms_per_step / 1e3), 1),
+        "graph_ms_per_step": round(graph_ms_per_step, 4),
         "stage_ms": {k2: round(v2, 5) for k2, v2 in stage_ms.items()},
     }
     if not args.no_cpu_baseline:
@@ -439,6 +452,18 @@ def bench_moe(args) -> int:
     stage_ms = {name: float(np.median([hev.elapsed_ms(e[2 * i], e[2 * i + 1]) for e in evs]))
                 for i, name in enumerate(S.MOE_STAGES)}
     layer_ms = float(np.median([hev.elapsed_ms(e[0], e[-1]) for e in evs]))
+    # the layer captured once in a HIP graph and replayed
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        S.moe_forward(X, IDS, WTS, W13, W2, cfg, out, ws)
+    for _ in range(args.warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for _ in range(args.steps):
+        g.replay()
+    torch.cuda.synchronize()
+    graph_ms_per_step = (time.perf_counter() - t1) * 1e3 / args.steps
     active = len(set(int(i) for i in ids.ravel() if 0 <= i < w.n_experts))
     N = int(((ids >= 0) & (ids < w.n_experts)).sum())
     d, dff = w.d_model, w.d_ff
@@ -476,6 +501,7 @@ def bench_moe(args) -> int:
             "algorithmic_bytes_per_launch": gate_up_bytes,
         },
         "layer_ms": round(layer_ms, 5),
+        "graph_ms_per_step": round(graph_ms_per_step, 5),
         "stage_ms": {k2: round(v2, 5) for k2, v2 in stage_ms.items()},
         "down_GBps": round(down_bytes / (stage_ms["down"] / 1e3) / 1e9, 1),
     }
