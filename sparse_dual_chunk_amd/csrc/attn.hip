@@ -37,8 +37,17 @@ __device__ __forceinline__ int range_key(Tile T, int t) {
   return t < T.len1 ? T.a1 + t : (t < T.len1 + T.len2 ? T.a2 + (t - T.len1) : -1);
 }
 
-template <bool DENSE, bool EXACT>
+// NW waves of 32 rows per workgroup: 2 (one 64-row block) for every call; 4
+// (two adjacent blocks, 128 rows, sharing every staged K / V tile) for dense
+// calls whose pairs of blocks lie inside one DCA chunk: their key ranges
+// differ only by the 64 keys of the second block, so the pair walks its
+// union at no extra work and loads half the bytes per MFMA.  The DCA mode
+// boundaries are per workgroup, hence the one-chunk condition.
+template <bool DENSE, bool EXACT, int NW = 2>
 __device__ __forceinline__ void attn_body(const AttnArgs& A) {
+  static_assert(NW == 2 || (NW == 4 && DENSE), "four-wave workgroups serve dense calls");
+  constexpr int RB = 32 * NW;      // rows per workgroup
+  constexpr int LPW = 8 / NW;      // direct loads per wave and tensor of a tile
   // K and V of the two stages are four LDS objects: the compiler then tells
   // the reads of one stage from the direct loads in flight into the other
   // and places no wait for those loads inside the tile's computation
@@ -65,11 +74,12 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A) {
   const int die = blockIdx.x % NXCD;
   const int local = blockIdx.x / NXCD;
   const int hpg = A.h_q / A.h_kv;
+  const int NBW = (A.nb + NW / 2 - 1) / (NW / 2);   // row groups of RB rows
   int b, h, part;
   int mpos = 0;              // the block's place in its die's row sequence (split calls)
   if (NXCD % A.h_kv == 0) {
     const int dpg = NXCD / A.h_kv;                 // dies per KV group
-    const int rows = (A.nb + dpg - 1) / dpg;       // block rows of this die
+    const int rows = (NBW + dpg - 1) / dpg;        // block rows of this die
     part = local / (rows * hpg);
     const int rem = local % (rows * hpg);
     // split calls: each die takes a contiguous half of the block rows (the
@@ -77,28 +87,28 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A) {
     // and read nearly the same keys; one part: rows interleave (balance)
     const int sub = die / A.h_kv;
     const int cidx = A.split > 1 ? ((sub + part) % dpg) * rows + rem % rows : dpg * (rem % rows) + sub;
-    if (cidx >= A.nb) return;
-    b = A.nb - 1 - cidx;
+    if (cidx >= NBW) return;
+    b = NBW - 1 - cidx;
     mpos = A.split > 1 ? rem % rows : 0;
     h = ((die + part) % A.h_kv) * hpg + rem / rows;
   } else {
-    const int rows = (A.nb + NXCD - 1) / NXCD;
+    const int rows = (NBW + NXCD - 1) / NXCD;
     part = local / (rows * A.h_q);
     const int rem = local % (rows * A.h_q);
     const int cidx = NXCD * (rem % rows) + die;
-    if (cidx >= A.nb) return;
-    b = A.nb - 1 - cidx;
+    if (cidx >= NBW) return;
+    b = NBW - 1 - cidx;
     h = rem / rows;
   }
   const int g = h / (A.h_q / A.h_kv);
 
-  const int i0 = A.p0 + QB * b;                  // absolute position of the block's first row
-  const int rows = min(QB, A.n_q - QB * b);
+  const int i0 = A.p0 + RB * b;                  // absolute position of the block's first row
+  const int rows = min(RB, A.n_q - RB * b);
   const int hi_key = i0 + rows;                  // keys [0, hi_key): the block's causal extent
   const int m_blk = i0 / A.S;
   const int rloc = 32 * wave + l32;              // row inside the block owned by this lane
   const bool row_ok = rloc < rows;
-  const int qrow = QB * b + (row_ok ? rloc : 0);
+  const int qrow = RB * b + (row_ok ? rloc : 0);
   const int prow = i0 + rloc;                    // absolute position of this lane's row
   // DCA mode of a key: 2 intra-chunk [segB, ..), 1 successive [segA, segB), 0 inter-chunk [0, segA)
   const int segA = max(0, (m_blk - 1) * A.S);
@@ -235,9 +245,9 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A) {
   const int lrow = lane >> 4;                       // row of a load's group this lane fills
   const int lchunk = 16 * ((lane & 15) ^ (5 * lrow));  // byte offset of the chunk it reads
   // byte offset of load j's row inside a tile of consecutive keys, plus the lane's chunk
-  unsigned roff[4];
+  unsigned roff[LPW];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) roff[j] = (unsigned)((4 * (2 * j + wave) + lrow) * rowb + lchunk);
+  for (int j = 0; j < LPW; ++j) roff[j] = (unsigned)((4 * (NW * j + wave) + lrow) * rowb + lchunk);
   // Row offsets of a tile's direct loads: load j of wave w fills rows
   // 4(2j + w) .. +3 of the tile (lane: row lane >> 4, chunk (lane & 15) ^ 5(lane >> 4)).
   struct Offs { int v[4]; };
@@ -246,13 +256,13 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A) {
   // [0, n_k) only in the prologue's tiles, in the block's first range tile and
   // in blocks within 95 keys of the end: there, and for extra-vertical tiles,
   // keys are clamped.
-  const bool clamp_all = 64 * b + 95 >= A.n_q;
+  const bool clamp_all = RB * b + RB + 31 >= A.n_q;
   auto tile_offsets = [&](Tile T, int skey, bool clamp) __attribute__((always_inline)) -> Offs {
     Offs f;
     if (clamp || T.cnt) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r = 4 * (2 * j + wave) + lrow;
+      for (int j = 0; j < LPW; ++j) {
+        const int r = 4 * (NW * j + wave) + lrow;
         int key;
         if (T.cnt) key = __shfl(skey, r) & 0x3FFFFFFF;
         else key = (r < T.len1 ? T.a1 : T.a2 - T.len1) + r;   // slots past the count are masked later
@@ -262,22 +272,22 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A) {
     } else if (T.len2 == 0) {
       const unsigned base = (unsigned)T.a1 * (unsigned)rowb;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) f.v[j] = (int)(base + roff[j]);
+      for (int j = 0; j < LPW; ++j) f.v[j] = (int)(base + roff[j]);
     } else {
       // rows from slot len1 on belong to run 2, a gap of a2 - a1 - len1 keys later
       const unsigned base = (unsigned)T.a1 * (unsigned)rowb;
       const unsigned gap = (unsigned)(T.a2 - T.a1 - T.len1) * (unsigned)rowb;
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        f.v[j] = (int)(base + roff[j] + (lrow >= T.len1 - 4 * (2 * j + wave) ? gap : 0u));
+      for (int j = 0; j < LPW; ++j)
+        f.v[j] = (int)(base + roff[j] + (lrow >= T.len1 - 4 * (NW * j + wave) ? gap : 0u));
     }
     return f;
   };
   // the 4 direct loads of one tensor of a tile into a stage
   auto issue = [&](__amdgpu_buffer_rsrc_t rs, uint8_t* stage, Offs f) __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(stage + (2 * j + wave) * GRPB),
+    for (int j = 0; j < LPW; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(stage + (NW * j + wave) * GRPB),
                                                16, f.v[j], 0, 0, 0);
   };
 
@@ -298,6 +308,8 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A) {
   auto vm_wait = [&](int n) __attribute__((always_inline)) {   // at most n vector-memory ops outstanding
     if (n >= 12) __builtin_amdgcn_s_waitcnt(0x0F7C);
     else if (n >= 8) __builtin_amdgcn_s_waitcnt(0x0F78);
+    else if (n >= 6) __builtin_amdgcn_s_waitcnt(0x0F76);
+    else if (n >= 4) __builtin_amdgcn_s_waitcnt(0x0F74);
     else __builtin_amdgcn_s_waitcnt(0x0F70);
   };
   auto wg_barrier = [&]() __attribute__((always_inline)) {
@@ -452,7 +464,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A) {
     }
     // B3: this wave's loads of V(t) landed (issued after them: K(t+1), V(t+1)
     // and K(t+2)); barrier
-    vm_wait(12);
+    vm_wait(3 * LPW);
     wg_barrier();
     // ---- O^T += V^T P^T, V^T operand read transposed from the row-major V tile.
     // All 8 reads of a 16-key half are issued before its 4 MFMAs, so their
@@ -512,7 +524,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A) {
 
   // One step on range tile ti: its stages kc / vc, and vn, the V stage of tile ti+1.
   auto step = [&](uint8_t* kc, const uint8_t* vc, uint8_t* vn, int ti) __attribute__((always_inline)) {
-    vm_wait(8);            // K(ti) landed: V(ti) and K(ti+1) were issued after it
+    vm_wait(2 * LPW);      // K(ti) landed: V(ti) and K(ti+1) were issued after it
     wg_barrier();          // B1: K(ti) visible; V(ti-1)'s stage is free
     issue(rs_v, vn, f_n);
     Tile T_2 = T_dummy;
@@ -601,6 +613,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A) {
 __global__ void __launch_bounds__(128, 2) dca_attn_kernel(AttnArgs A) { attn_body<false, false>(A); }
 __global__ void __launch_bounds__(128, 2) dca_attn_exact_kernel(AttnArgs A) { attn_body<false, true>(A); }
 __global__ void __launch_bounds__(128, 2) dca_attn_dense_kernel(AttnArgs A) { attn_body<true, false>(A); }
+__global__ void __launch_bounds__(256, 2) dca_attn_dense4_kernel(AttnArgs A) { attn_body<true, false, 4>(A); }
 
 // LSE merge of the key parts of one (row, head): m = max_p lse_p,
 // O = sum_p e^{lse_p - m} O_p / sum_p e^{lse_p - m}.  One wave per (row, head):
@@ -662,10 +675,17 @@ __global__ void __launch_bounds__(256) lse_merge_kernel(const uint16_t* __restri
 
 hipError_t launch_attn(const AttnArgs& A, hipStream_t stream) {
   // every die runs split * (its block rows) * (heads per row) workgroups
+  // dense calls: workgroups of two blocks (128 rows) when no pair can straddle
+  // a DCA chunk boundary (the workgroup's rows must share one chunk), i.e. S
+  // and p0 multiples of 128; else one block per workgroup
+  const bool pairs = A.dense && A.S % 128 == 0 && A.p0 % 128 == 0;
+  const int nbw = pairs ? (A.nb + 1) / 2 : A.nb;
   const int blocks = NXCD % A.h_kv == 0
-      ? NXCD * A.split * ((A.nb + NXCD / A.h_kv - 1) / (NXCD / A.h_kv)) * (A.h_q / A.h_kv)
-      : NXCD * A.split * ((A.nb + NXCD - 1) / NXCD) * A.h_q;
-  if (A.dense) {
+      ? NXCD * A.split * ((nbw + NXCD / A.h_kv - 1) / (NXCD / A.h_kv)) * (A.h_q / A.h_kv)
+      : NXCD * A.split * ((nbw + NXCD - 1) / NXCD) * A.h_q;
+  if (pairs) {
+    hipLaunchKernelGGL(dca_attn_dense4_kernel, dim3(blocks), dim3(256), 0, stream, A);
+  } else if (A.dense) {
     hipLaunchKernelGGL(dca_attn_dense_kernel, dim3(blocks), dim3(128), 0, stream, A);
   } else if (A.exact) {
     hipLaunchKernelGGL(dca_attn_exact_kernel, dim3(blocks), dim3(128), 0, stream, A);
