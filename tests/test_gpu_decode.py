@@ -86,6 +86,14 @@ def test_decode_multichunk(n_k, n_t, split):
     _check(q, k, v, _cfg(n_k, n_t, 4, 2, 256, 64, split=split), f"n_k {n_k} n_t {n_t} split {split}")
 
 
+@pytest.mark.parametrize("h_q,h_kv,n_t", [(6, 3, 2), (16, 16, 1), (10, 5, 3)])
+def test_decode_head_counts(h_q, h_kv, n_t):
+    """KV-head counts that do not divide the 8 dies, and one query head per KV head."""
+    n_k = 900
+    q, k, v = _inputs(40 + h_kv, n_k, n_t, h_q, h_kv)
+    _check(q, k, v, _cfg(n_k, n_t, h_q, h_kv, 256, 64), f"h_q {h_q} h_kv {h_kv}")
+
+
 def test_decode_tokens_straddle_a_chunk_boundary():
     """Tokens at 510 .. 513 with S = 256: two token chunks, so tiles carry two modes."""
     n_k, n_t = 514, 4

@@ -142,6 +142,37 @@ def test_determinism_bitwise():
     assert np.array_equal(a, b) and np.array_equal(la, lb)
 
 
+# ------------------------------------------------------------------ head counts
+# Workgroups map to the 8 dies per KV group when the KV-head count divides 8
+# (1, 2, 4, 8); other counts (3, 5, 16 here) take the all-heads mapping.  Also
+# one query head per KV head (no grouping).
+@pytest.mark.parametrize("h_q,h_kv,p0,n_q,split", [(6, 3, 0, 200, 0),      # two-block workgroups
+                                                   (6, 3, 192, 150, 2),    # one block per workgroup, split
+                                                   (10, 5, 256, 64, 1),
+                                                   (16, 16, 128, 130, 0)])
+def test_dense_head_counts(h_q, h_kv, p0, n_q, split):
+    inp = _inputs(60 + h_kv + p0, p0, n_q, h_q, h_kv, sinks=True)
+    cfg = _cfg(inp, h_q, h_kv, 256, 64, split_k=split)
+    out, lse = run_prefill(inp, cfg, with_lse=True)
+    ref, ref_lse = _oracle(inp, cfg)
+    check_close(out, ref, f"dense h_q {h_q} h_kv {h_kv}")
+    assert np.abs(lse - ref_lse).max() <= LSE_TOL
+
+
+@pytest.mark.parametrize("h_q,h_kv,p0,n_q,split,exact", [(6, 3, 512, 200, 0, 0), (6, 3, 320, 130, 3, 0),
+                                                         (16, 16, 256, 100, 2, 0), (6, 3, 512, 200, 2, 1)])
+def test_sparse_head_counts(h_q, h_kv, p0, n_q, split, exact):
+    inp = _inputs(70 + h_kv + p0, p0, n_q, h_q, h_kv, sinks=True, periodic=97)
+    rng = np.random.default_rng(h_q + p0)
+    v_idx, s_off = _random_pattern(rng, h_q, inp["n_k"], 30, 25)
+    cfg = _cfg(inp, h_q, h_kv, 256, 32, vs_k_vertical=30, vs_k_slash=25, split_k=split, slash_exact=exact)
+    out, lse = run_prefill(inp, cfg, v_idx=v_idx, s_off=s_off, with_lse=True)
+    ref, ref_lse = O.attention(inp["q"], inp["k"], inp["v"], inp["p0"], oracle_cfg(cfg), v_idx=v_idx,
+                               s_off=s_off, exact=bool(exact))
+    check_close(out, ref, f"sparse h_q {h_q} h_kv {h_kv} exact {exact}")
+    assert np.abs(lse - ref_lse).max() <= LSE_TOL
+
+
 # ------------------------------------------------------------------ index
 def _check_index(inp, cfg, heads=None):
     v_gpu, s_gpu = run_index(inp, cfg)
@@ -159,6 +190,13 @@ def _check_index(inp, cfg, heads=None):
 def test_index_bit_exact(p0, n_q, S_, last):
     inp = _inputs(40 + p0 + n_q, p0, n_q, 4, 2, sinks=True, periodic=128)
     cfg = _cfg(inp, 4, 2, S_, 32, vs_k_vertical=20, vs_k_slash=40, vs_last_q=last)
+    _check_index(inp, cfg)
+
+
+@pytest.mark.parametrize("h_q,h_kv", [(6, 3), (16, 16)])
+def test_index_head_counts(h_q, h_kv):
+    inp = _inputs(45 + h_kv, 448, 160, h_q, h_kv, sinks=True, periodic=128)
+    cfg = _cfg(inp, h_q, h_kv, 256, 32, vs_k_vertical=20, vs_k_slash=40)
     _check_index(inp, cfg)
 
 
