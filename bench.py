@@ -584,7 +584,7 @@ def main() -> int:
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (the path is measured on one MI355X; --gpus {args.gpus} "
-              "is not supported; collectives and sharding are outside this build)", file=sys.stderr)
+              "is not supported: the library has no collectives or sharding)", file=sys.stderr)
         return 2
 
     if args.decode:

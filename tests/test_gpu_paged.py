@@ -97,7 +97,8 @@ def test_pool_pages_hold_the_contiguous_rows():
 
 @pytest.mark.parametrize("n_k,n_t,h_q,h_kv,P,S_,W", [(700, 1, 4, 2, 32, 256, 64), (700, 3, 4, 2, 64, 256, 64),
                                                      (1500, 5, 28, 4, 256, 512, 128), (96, 2, 4, 2, 256, 256, 64),
-                                                     (1030, 4, 14, 2, 64, 256, 64)])
+                                                     (1030, 4, 14, 2, 64, 256, 64), (800, 2, 6, 3, 64, 256, 64),
+                                                     (500, 1, 16, 16, 32, 256, 64)])
 def test_paged_decode_equals_contiguous(n_k, n_t, h_q, h_kv, P, S_, W):
     q, k, v = _inputs(n_k + P, n_k, n_t, h_q, h_kv)
     cfg = _cfg(n_k, n_t, h_q, h_kv, S_, W)
