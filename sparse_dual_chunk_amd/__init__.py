@@ -33,6 +33,7 @@ from __future__ import annotations
 import ctypes
 import dataclasses
 import os
+import sys
 from typing import Optional, Sequence
 
 import numpy as np
@@ -249,6 +250,55 @@ def _ptr(t) -> Optional[int]:
     return int(t.data_ptr())
 
 
+def _dev(t, name: str, nbytes: int = 0, dtype: Optional[str] = None) -> Optional[int]:
+    """Address of a buffer that crosses the boundary.
+
+    The library sees only the address, so a torch tensor is checked here:
+    device memory, contiguous, the element type of its layout ("bf16": any
+    2-byte type holding raw bfloat16 bits; else a torch dtype name such as
+    "int32") and at least ``nbytes`` bytes.  A bad tensor raises ValueError
+    before anything is enqueued.  Other objects exposing data_ptr() pass
+    unchecked."""
+    if t is None:
+        return None
+    torch = sys.modules.get("torch")
+    if torch is not None and isinstance(t, torch.Tensor):
+        if dtype == "bf16":
+            if t.element_size() != 2 or (t.is_floating_point() and t.dtype != torch.bfloat16):
+                raise ValueError(f"{name}: needs raw bfloat16 bits (int16, uint16 or bfloat16), got {t.dtype}")
+        elif dtype is not None and t.dtype != getattr(torch, dtype):
+            raise ValueError(f"{name}: needs {dtype}, got {t.dtype}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name}: the tensor must be contiguous")
+        have = t.numel() * t.element_size()
+        if have < nbytes:
+            raise ValueError(f"{name}: holds {have} bytes, the call's layout covers {nbytes}")
+        if t.device.type != "cuda":
+            raise ValueError(f"{name}: needs a device tensor, got one on {t.device}")
+    return int(t.data_ptr())
+
+
+def _ws(workspace) -> dict:
+    """Workspace fields of a config: address and size (the library checks the size)."""
+    return dict(workspace=_dev(workspace, "workspace"),
+                workspace_bytes=workspace.numel() * workspace.element_size())
+
+
+def _check_cache(cache: "KeyCache", cfg: "Config") -> None:
+    row = cfg.h_kv * cfg.head_dim * 2
+    _dev(cache.k_hi, "cache.k_hi", cache.capacity * row, "bf16")
+    _dev(cache.k_lo, "cache.k_lo", cache.capacity * row, "bf16")
+    _dev(cache.k_flags, "cache.k_flags", cfg.h_kv * ((cache.capacity + 31) // 32) * 4, "int32")
+
+
+def _check_paged(cache: "PagedKV", cfg: "Config") -> None:
+    pool = cache.n_pages * cfg.h_kv * cache.page_keys * cfg.head_dim * 2
+    for nm in ("k_hi", "k_lo", "v"):
+        _dev(getattr(cache, nm), "cache." + nm, pool, "bf16")
+    _dev(cache.k_flags, "cache.k_flags", cache.n_pages * cfg.h_kv * (cache.page_keys // 32) * 4, "int32")
+    _dev(cache.page_table, "cache.page_table", 0, "int32")
+
+
 def _stream(stream) -> Optional[int]:
     if stream is None:
         import torch
@@ -278,9 +328,13 @@ def vs_index_build(q, k, positions, cfg: Config, v_idx, s_off, workspace, stream
     """Vertical-slash index of one chunk; writes v_idx [h_q][k_v] and s_off [h_q][k_s] (int32, device).
     k_per_head: optional device int32 [h_q][2] per-head budgets (k_v, k_s)."""
     pos, pos_p = _positions(positions)
-    c = cfg.to_c(workspace=_ptr(workspace), workspace_bytes=workspace.numel() * workspace.element_size(),
-                 stream=_stream(stream), vs_k_per_head=_ptr(k_per_head))
-    rc = lib().vs_index_build(_ptr(q), _ptr(k), pos_p, ctypes.byref(c), _ptr(v_idx), _ptr(s_off))
+    hd2 = cfg.head_dim * 2
+    c = cfg.to_c(**_ws(workspace), stream=_stream(stream),
+                 vs_k_per_head=_dev(k_per_head, "k_per_head", cfg.h_q * 8, "int32"))
+    rc = lib().vs_index_build(_dev(q, "q", cfg.n_q * cfg.h_q * hd2, "bf16"),
+                              _dev(k, "k", cfg.n_k * cfg.h_kv * hd2, "bf16"), pos_p, ctypes.byref(c),
+                              _dev(v_idx, "v_idx", cfg.h_q * cfg.vs_k_vertical * 4, "int32"),
+                              _dev(s_off, "s_off", cfg.h_q * cfg.vs_k_slash * 4, "int32"))
     if rc != DCA_OK:
         raise DcaError(rc, "vs_index_build")
 
@@ -292,11 +346,15 @@ def dca_sparse_prefill(q, k, v, positions, cfg: Config, out, workspace, v_idx=No
     ev_arr = None
     if stage_events is not None:
         ev_arr = (ctypes.c_void_p * (2 * DCA_STAGE_COUNT))(*[int(e) for e in stage_events])
-    c = cfg.to_c(workspace=_ptr(workspace), workspace_bytes=workspace.numel() * workspace.element_size(),
-                 stream=_stream(stream), v_idx=_ptr(v_idx), s_off=_ptr(s_off), lse_out=_ptr(lse_out),
-                 cover_pairs=_ptr(cover_pairs),
+    c = cfg.to_c(**_ws(workspace), stream=_stream(stream),
+                 v_idx=_dev(v_idx, "v_idx", cfg.h_q * cfg.vs_k_vertical * 4, "int32"),
+                 s_off=_dev(s_off, "s_off", cfg.h_q * cfg.vs_k_slash * 4, "int32"),
+                 lse_out=_dev(lse_out, "lse_out", cfg.h_q * cfg.n_q * 4, "float32"),
+                 cover_pairs=_dev(cover_pairs, "cover_pairs", 8, "int64"),
                  stage_events=ctypes.cast(ev_arr, ctypes.c_void_p) if ev_arr is not None else None)
-    rc = lib().dca_sparse_prefill(_ptr(q), _ptr(k), _ptr(v), pos_p, ctypes.byref(c), _ptr(out))
+    qb, kb = cfg.n_q * cfg.h_q * cfg.head_dim * 2, cfg.n_k * cfg.h_kv * cfg.head_dim * 2
+    rc = lib().dca_sparse_prefill(_dev(q, "q", qb, "bf16"), _dev(k, "k", kb, "bf16"), _dev(v, "v", kb, "bf16"),
+                                  pos_p, ctypes.byref(c), _dev(out, "out", qb, "bf16"))
     if rc != DCA_OK:
         raise DcaError(rc, "dca_sparse_prefill")
 
@@ -338,8 +396,11 @@ class KeyCache:
 def dca_key_cache_append(k, j0: int, cfg: Config, cache: KeyCache, stream=None) -> None:
     """Rotate keys j0 .. j0 + k.shape[0] - 1 (k: [n][h_kv][128] raw bf16 bits) into the cache."""
     c = cfg.to_c(stream=_stream(stream))
+    _check_cache(cache, cfg)
     kc = cache.to_c()
-    rc = lib().dca_key_cache_append(_ptr(k), int(j0), int(k.shape[0]), ctypes.byref(c), ctypes.byref(kc))
+    n = int(k.shape[0])
+    rc = lib().dca_key_cache_append(_dev(k, "k", n * cfg.h_kv * cfg.head_dim * 2, "bf16"), int(j0), n,
+                                    ctypes.byref(c), ctypes.byref(kc))
     if rc != DCA_OK:
         raise DcaError(rc, "dca_key_cache_append")
 
@@ -359,11 +420,15 @@ def dca_decode(q, cache: KeyCache, v, cfg: Config, out, workspace, lse_out=None,
     ev_arr = None
     if stage_events is not None:
         ev_arr = (ctypes.c_void_p * (2 * DCA_STAGE_COUNT))(*[int(e) for e in stage_events])
-    c = cfg.to_c(workspace=_ptr(workspace), workspace_bytes=workspace.numel() * workspace.element_size(),
-                 stream=_stream(stream), lse_out=_ptr(lse_out),
+    c = cfg.to_c(**_ws(workspace), stream=_stream(stream),
+                 lse_out=_dev(lse_out, "lse_out", cfg.h_q * cfg.n_q * 4, "float32"),
                  stage_events=ctypes.cast(ev_arr, ctypes.c_void_p) if ev_arr is not None else None)
+    _check_cache(cache, cfg)
     kc = cache.to_c()
-    rc = lib().dca_decode(_ptr(q), ctypes.byref(kc), _ptr(v), ctypes.byref(c), _ptr(out))
+    qb = cfg.n_q * cfg.h_q * cfg.head_dim * 2
+    rc = lib().dca_decode(_dev(q, "q", qb, "bf16"), ctypes.byref(kc),
+                          _dev(v, "v", cfg.n_k * cfg.h_kv * cfg.head_dim * 2, "bf16"), ctypes.byref(c),
+                          _dev(out, "out", qb, "bf16"))
     if rc != DCA_OK:
         raise DcaError(rc, "dca_decode")
 
@@ -376,12 +441,18 @@ def dca_sparse_prefill_cached(q, cache: KeyCache, v, positions, cfg: Config, out
     ev_arr = None
     if stage_events is not None:
         ev_arr = (ctypes.c_void_p * (2 * DCA_STAGE_COUNT))(*[int(e) for e in stage_events])
-    c = cfg.to_c(workspace=_ptr(workspace), workspace_bytes=workspace.numel() * workspace.element_size(),
-                 stream=_stream(stream), v_idx=_ptr(v_idx), s_off=_ptr(s_off), lse_out=_ptr(lse_out),
-                 cover_pairs=_ptr(cover_pairs),
+    c = cfg.to_c(**_ws(workspace), stream=_stream(stream),
+                 v_idx=_dev(v_idx, "v_idx", cfg.h_q * cfg.vs_k_vertical * 4, "int32"),
+                 s_off=_dev(s_off, "s_off", cfg.h_q * cfg.vs_k_slash * 4, "int32"),
+                 lse_out=_dev(lse_out, "lse_out", cfg.h_q * cfg.n_q * 4, "float32"),
+                 cover_pairs=_dev(cover_pairs, "cover_pairs", 8, "int64"),
                  stage_events=ctypes.cast(ev_arr, ctypes.c_void_p) if ev_arr is not None else None)
+    _check_cache(cache, cfg)
     kc = cache.to_c()
-    rc = lib().dca_sparse_prefill_cached(_ptr(q), ctypes.byref(kc), _ptr(v), pos_p, ctypes.byref(c), _ptr(out))
+    qb = cfg.n_q * cfg.h_q * cfg.head_dim * 2
+    rc = lib().dca_sparse_prefill_cached(_dev(q, "q", qb, "bf16"), ctypes.byref(kc),
+                                         _dev(v, "v", cfg.n_k * cfg.h_kv * cfg.head_dim * 2, "bf16"), pos_p,
+                                         ctypes.byref(c), _dev(out, "out", qb, "bf16"))
     if rc != DCA_OK:
         raise DcaError(rc, "dca_sparse_prefill_cached")
 
@@ -422,8 +493,12 @@ class PagedKV:
 def dca_paged_append(k, v, j0: int, cfg: Config, cache: PagedKV, stream=None) -> None:
     """Rotate keys j0 .. j0 + k.shape[0] - 1 into their pages and copy their values."""
     c = cfg.to_c(stream=_stream(stream))
+    _check_paged(cache, cfg)
     kc = cache.to_c()
-    rc = lib().dca_paged_append(_ptr(k), _ptr(v), int(j0), int(k.shape[0]), ctypes.byref(c), ctypes.byref(kc))
+    n = int(k.shape[0])
+    kb = n * cfg.h_kv * cfg.head_dim * 2
+    rc = lib().dca_paged_append(_dev(k, "k", kb, "bf16"), _dev(v, "v", kb, "bf16"), int(j0), n, ctypes.byref(c),
+                                ctypes.byref(kc))
     if rc != DCA_OK:
         raise DcaError(rc, "dca_paged_append")
 
@@ -434,11 +509,14 @@ def dca_decode_paged(q, cache: PagedKV, cfg: Config, out, workspace, lse_out=Non
     ev_arr = None
     if stage_events is not None:
         ev_arr = (ctypes.c_void_p * (2 * DCA_STAGE_COUNT))(*[int(e) for e in stage_events])
-    c = cfg.to_c(workspace=_ptr(workspace), workspace_bytes=workspace.numel() * workspace.element_size(),
-                 stream=_stream(stream), lse_out=_ptr(lse_out),
+    c = cfg.to_c(**_ws(workspace), stream=_stream(stream),
+                 lse_out=_dev(lse_out, "lse_out", cfg.h_q * cfg.n_q * 4, "float32"),
                  stage_events=ctypes.cast(ev_arr, ctypes.c_void_p) if ev_arr is not None else None)
+    _check_paged(cache, cfg)
     kc = cache.to_c()
-    rc = lib().dca_decode_paged(_ptr(q), ctypes.byref(kc), ctypes.byref(c), _ptr(out))
+    qb = cfg.n_q * cfg.h_q * cfg.head_dim * 2
+    rc = lib().dca_decode_paged(_dev(q, "q", qb, "bf16"), ctypes.byref(kc), ctypes.byref(c),
+                                _dev(out, "out", qb, "bf16"))
     if rc != DCA_OK:
         raise DcaError(rc, "dca_decode_paged")
 
@@ -487,7 +565,7 @@ def _seq_plan(bounds, sparse, index_stream=None, chunk_events=None, index_events
             arr = (ctypes.c_void_p * (2 * n))(*[int(e) for e in evs])
             keep.append(arr)
             setattr(p, name, ctypes.cast(arr, ctypes.c_void_p))
-    p.cover_pairs = _ptr(cover_pairs)
+    p.cover_pairs = _dev(cover_pairs, "cover_pairs", 8 * n, "int64")
     return p, keep
 
 
@@ -508,11 +586,13 @@ def dca_prefill_sequence(q, k, v, bounds, cfg: Config, cache: KeyCache, out, wor
     """Chunked prefill of a whole prompt (cfg.n_q == cfg.n_k == its length) over the given chunk bounds.
     index_stream: a second stream (int handle) for the index builds, or None to run everything in order."""
     p, _keep = _seq_plan(bounds, sparse, index_stream, chunk_events, index_events, cover_pairs)
-    c = cfg.to_c(workspace=_ptr(workspace), workspace_bytes=workspace.numel() * workspace.element_size(),
-                 stream=_stream(stream), lse_out=_ptr(lse_out))
+    c = cfg.to_c(**_ws(workspace), stream=_stream(stream),
+                 lse_out=_dev(lse_out, "lse_out", cfg.h_q * cfg.n_q * 4, "float32"))
+    _check_cache(cache, cfg)
     kc = cache.to_c()
-    rc = lib().dca_prefill_sequence(_ptr(q), _ptr(k), _ptr(v), ctypes.byref(p), ctypes.byref(c), ctypes.byref(kc),
-                                    _ptr(out))
+    qb, kb = cfg.n_q * cfg.h_q * cfg.head_dim * 2, cfg.n_k * cfg.h_kv * cfg.head_dim * 2
+    rc = lib().dca_prefill_sequence(_dev(q, "q", qb, "bf16"), _dev(k, "k", kb, "bf16"), _dev(v, "v", kb, "bf16"),
+                                    ctypes.byref(p), ctypes.byref(c), ctypes.byref(kc), _dev(out, "out", qb, "bf16"))
     if rc != DCA_OK:
         raise DcaError(rc, "dca_prefill_sequence")
 
@@ -547,7 +627,9 @@ def moe_workspace_size(cfg: MoeConfig) -> int:
 def moe_pack_weights(w13, w2, cfg: MoeConfig, w13_packed, w2_packed, stream=None) -> None:
     """Write the packed weight layout moe_forward streams (same shapes as w13 / w2)."""
     c = cfg.to_c(stream=_stream(stream))
-    rc = lib().moe_pack_weights(_ptr(w13), _ptr(w2), ctypes.byref(c), _ptr(w13_packed), _ptr(w2_packed))
+    wb = cfg.n_experts * 2 * cfg.d_ff * cfg.d_model * 2
+    rc = lib().moe_pack_weights(_dev(w13, "w13", wb, "bf16"), _dev(w2, "w2", wb // 2, "bf16"), ctypes.byref(c),
+                                _dev(w13_packed, "w13_packed", wb, "bf16"), _dev(w2_packed, "w2_packed", wb // 2, "bf16"))
     if rc != DCA_OK:
         raise DcaError(rc, "moe_pack_weights")
 
@@ -558,10 +640,13 @@ def moe_forward(x, topk_ids, topk_weights, w13_packed, w2_packed, cfg: MoeConfig
     ev_arr = None
     if stage_events is not None:
         ev_arr = (ctypes.c_void_p * (2 * MOE_STAGE_COUNT))(*[int(e) for e in stage_events])
-    c = cfg.to_c(workspace=_ptr(workspace), workspace_bytes=workspace.numel() * workspace.element_size(),
-                 stream=_stream(stream),
+    c = cfg.to_c(**_ws(workspace), stream=_stream(stream),
                  stage_events=ctypes.cast(ev_arr, ctypes.c_void_p) if ev_arr is not None else None)
-    rc = lib().moe_forward(_ptr(x), _ptr(topk_ids), _ptr(topk_weights), _ptr(w13_packed), _ptr(w2_packed),
-                           ctypes.byref(c), _ptr(out))
+    xb, sb = cfg.n_tokens * cfg.d_model * 2, cfg.n_tokens * cfg.top_k * 4
+    wb = cfg.n_experts * 2 * cfg.d_ff * cfg.d_model * 2
+    rc = lib().moe_forward(_dev(x, "x", xb, "bf16"), _dev(topk_ids, "topk_ids", sb, "int32"),
+                           _dev(topk_weights, "topk_weights", sb, "float32"),
+                           _dev(w13_packed, "w13_packed", wb, "bf16"), _dev(w2_packed, "w2_packed", wb // 2, "bf16"),
+                           ctypes.byref(c), _dev(out, "out", xb, "bf16"))
     if rc != DCA_OK:
         raise DcaError(rc, "moe_forward")

@@ -387,3 +387,33 @@ def test_paged_append_validation():
         assert S.lib().dca_paged_append(0x1000, 0x1000, j0, n, ctypes.byref(c), ctypes.byref(kc)) == code
     kc = _FakePaged(8, 64, 10).to_c()
     assert S.lib().dca_paged_append(0x1000, None, 0, 4, ctypes.byref(c), ctypes.byref(kc)) == S.DCA_EINVAL
+
+
+# ---- the binding's checks of torch tensors (before any pointer crosses the boundary)
+def test_binding_checks_tensors_before_the_call():
+    torch = pytest.importorskip("torch")
+    cfg = _cfg()                                   # n_q 256, n_k 512, h_q 4, h_kv 2
+    pos = np.arange(256, 512, dtype=np.int32)
+    ws = _FakeTensor(S.dca_workspace_size(cfg))
+    k = torch.zeros((512, 2, 128), dtype=torch.int16)
+
+    def call(**kw):                                # fakes (unchecked) except the tensor under test
+        a = {n: _FakeTensor() for n in ("q", "k", "v", "out")}
+        a.update(kw)
+        S.dca_sparse_prefill(a["q"], a["k"], a["v"], pos, cfg, a["out"], ws, stream=0)
+
+    with pytest.raises(ValueError, match="q: needs raw bfloat16"):
+        call(q=torch.zeros((256, 4, 128), dtype=torch.float32))
+    with pytest.raises(ValueError, match="k: the tensor must be contiguous"):
+        call(k=torch.zeros((2, 512, 128), dtype=torch.int16).transpose(0, 1))
+    with pytest.raises(ValueError, match="v: holds"):
+        call(v=k[:511])
+    with pytest.raises(ValueError, match="out: needs a device tensor"):
+        call(out=torch.zeros((256, 4, 128), dtype=torch.bfloat16))   # right size, host memory
+    with pytest.raises(ValueError, match="lse_out: needs float32"):
+        S.dca_sparse_prefill(_FakeTensor(), _FakeTensor(), _FakeTensor(), pos, cfg, _FakeTensor(), ws,
+                             lse_out=torch.zeros((4, 256), dtype=torch.float64), stream=0)
+    m = _mcfg(n_tokens=4, n_experts=8, top_k=2, d_model=256, d_ff=128)
+    with pytest.raises(ValueError, match="topk_ids: needs int32"):
+        S.moe_forward(_FakeTensor(), torch.zeros((4, 2), dtype=torch.int64), _FakeTensor(), _FakeTensor(),
+                      _FakeTensor(), m, _FakeTensor(), _FakeTensor(1 << 30), stream=0)
