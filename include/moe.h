@@ -68,7 +68,9 @@ typedef struct moe_cfg {
 } moe_cfg;
 
 /* Workspace bytes of moe_forward: slot order, the bf16 activations of every
- * (token, slot) and their fp32 expert outputs.  Pure host computation. */
+ * (token, slot) and their fp32 expert outputs; for batches of a few tokens,
+ * whose products run in k parts, the fp32 sums of each part.  Pure host
+ * computation. */
 DCA_API int moe_workspace_size(const moe_cfg *cfg, size_t *bytes);
 
 /* Writes the packed layout of w13 and w2 (above) into w13_packed and

@@ -7,8 +7,9 @@
 //   moe_sort_kernel      slots (token, k) grouped by expert, in slot order
 //   moe_mma_kernel<1>    gate and up products of every routed expert, SwiGLU,
 //                        bf16 activations per slot
+//   moe_swiglu_kernel    (k-split gate/up only) SwiGLU of the summed k parts
 //   moe_mma_kernel<0>    down product, scaled by the slot's routing weight
-//   moe_sum_kernel       out_t = sum over the token's slots, in slot order
+//   moe_sum_kernel       out_t = sum over the token's slots (and k parts), in order
 //
 // The two products use v_mfma_f32_32x32x16_bf16 with the weights as the A
 // operand (32 weight rows per wave) and up to 64 of the expert's tokens as B.
@@ -40,8 +41,10 @@ struct MoeArgs {
   const int32_t* offsets;     // [E + 1] first sorted slot of each expert
   const int32_t* sorted;      // [N] slot ids grouped by expert, slot order inside
   uint16_t* act;              // [N][d_ff] bf16 SwiGLU activations, sorted order
-  float* ys;                  // [N][d_model] weighted expert outputs, slot order
+  float* ys;                  // [ks_dn][N][d_model] weighted expert outputs (per k part), slot order
+  float* part;                // [ks_gu][N][2][d_ff] fp32 gate / up sums per k part (ks_gu > 1 only)
   int n_slots, n_experts, top_k, d_model, d_ff;
+  int ks_gu, ks_dn;           // k parts of the gate/up and down products
 };
 
 __device__ inline uint16_t f2bf(float f) {
@@ -185,19 +188,20 @@ __device__ inline void mma_pass(const uint16_t* const (&wp)[NW], const uint16_t*
 // Rows of the C fragment held by this lane: r(i) = 8 (i / 4) + 4 half + i % 4,
 // column = lane % 32.
 template <bool GATE_UP, int NT>
-__device__ inline void expert_pass(const MoeArgs& A, int e, int beg, int m, int t0, int r0, int l32, int half) {
+__device__ inline void expert_pass(const MoeArgs& A, int e, int beg, int m, int t0, int r0, int l32, int half,
+                                   int ks, int k0, int nks) {
   const int d = A.d_model, dff = A.d_ff;
-  const int K = GATE_UP ? d : dff;
+  const int KS = GATE_UP ? A.ks_gu : A.ks_dn;
   constexpr int NW = GATE_UP ? 2 : 1;
   // packed tiles: tile row r0 / 32 of the expert's matrix, this lane's piece
   const uint16_t* wp[NW];
   const int lane = 32 * half + l32;
   if (GATE_UP) {
-    const uint16_t* g = A.w13 + (size_t)e * 2 * dff * d + (size_t)(r0 / 32) * (d / KSTEP) * TILE_ELEMS + 8 * lane;
+    const uint16_t* g = A.w13 + (size_t)e * 2 * dff * d + ((size_t)(r0 / 32) * (d / KSTEP) + k0) * TILE_ELEMS + 8 * lane;
     wp[0] = g;
     wp[NW - 1] = g + (size_t)dff * d;
   } else {
-    wp[0] = A.w2 + (size_t)e * d * dff + (size_t)(r0 / 32) * (dff / KSTEP) * TILE_ELEMS + 8 * lane;
+    wp[0] = A.w2 + (size_t)e * d * dff + ((size_t)(r0 / 32) * (dff / KSTEP) + k0) * TILE_ELEMS + 8 * lane;
   }
   // token columns: lanes past the expert's last slot read its first slot's row
   // (finite values) and their columns are not stored
@@ -210,16 +214,26 @@ __device__ inline void expert_pass(const MoeArgs& A, int e, int beg, int m, int 
     ok[t] = idx < m;
     const int j = beg + (ok[t] ? idx : 0);
     slot[t] = A.sorted[j];
-    bp[t] = GATE_UP ? A.x + (size_t)(slot[t] / A.top_k) * d + 32 * half : A.act + (size_t)j * dff + 32 * half;
+    bp[t] = (GATE_UP ? A.x + (size_t)(slot[t] / A.top_k) * d : A.act + (size_t)j * dff) + KSTEP * k0 + 32 * half;
   }
   f32x16 c[NW][NT];
   constexpr int STG = (NW * 16 + NT * 16) <= 48 ? 3 : 2;
-  mma_pass<NW, NT, STG>(wp, bp, K / KSTEP, c);
+  mma_pass<NW, NT, STG>(wp, bp, nks, c);
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     if (!ok[t]) continue;
     const int idx = t0 + 32 * t + l32;
-    if (GATE_UP) {
+    if (GATE_UP && KS > 1) {
+      // this k part's gate and up sums; moe_swiglu_kernel adds the parts
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        float* dst = A.part + (((size_t)ks * A.n_slots + beg + idx) * 2 + w) * dff + r0 + 4 * half;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          *(float4*)(dst + 8 * q) = make_float4(c[w][t][4 * q], c[w][t][4 * q + 1], c[w][t][4 * q + 2],
+                                                c[w][t][4 * q + 3]);
+      }
+    } else if (GATE_UP) {
       uint16_t* dst = A.act + (size_t)(beg + idx) * dff + r0 + 4 * half;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -236,7 +250,7 @@ __device__ inline void expert_pass(const MoeArgs& A, int e, int beg, int m, int 
       }
     } else {
       const float wt = A.wts[slot[t]];
-      float* dst = A.ys + (size_t)slot[t] * d + r0 + 4 * half;
+      float* dst = A.ys + ((size_t)ks * A.n_slots + slot[t]) * d + r0 + 4 * half;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         float4 p;
@@ -260,15 +274,22 @@ __global__ __launch_bounds__(64 * WAVES, 2) void moe_mma_kernel(MoeArgs A) {
   constexpr int ROWS = 32 * WAVES;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, l32 = lane & 31, half = lane >> 5;
   const int tiles = (GATE_UP ? A.d_ff : A.d_model) / ROWS;
-  const int e = blockIdx.x / tiles, rt = blockIdx.x - e * tiles;
+  // blockIdx = (k part, expert, row tile); the k parts split the product's
+  // 64-wide k steps evenly
+  const int per = A.n_experts * tiles;
+  const int ks = blockIdx.x / per, rem = blockIdx.x - ks * per;
+  const int e = rem / tiles, rt = rem - e * tiles;
+  const int KS = GATE_UP ? A.ks_gu : A.ks_dn;
+  const int steps = (GATE_UP ? A.d_model : A.d_ff) / KSTEP;
+  const int k0 = (int)((long long)steps * ks / KS), k1 = (int)((long long)steps * (ks + 1) / KS);
   const int beg = A.offsets[e], m = A.offsets[e + 1] - beg;
   if (m <= 0) return;
   const int r0 = rt * ROWS + 32 * wave;
   for (int t0 = 0; t0 < m; t0 += 64) {
     if (m - t0 > 32)
-      expert_pass<GATE_UP, 2>(A, e, beg, m, t0, r0, l32, half);
+      expert_pass<GATE_UP, 2>(A, e, beg, m, t0, r0, l32, half, ks, k0, k1 - k0);
     else
-      expert_pass<GATE_UP, 1>(A, e, beg, m, t0, r0, l32, half);
+      expert_pass<GATE_UP, 1>(A, e, beg, m, t0, r0, l32, half, ks, k0, k1 - k0);
   }
 }
 
@@ -292,6 +313,31 @@ __global__ __launch_bounds__(256) void moe_pack_kernel(const uint16_t* src, uint
 }
 
 // out[t][c .. c+3] = bf16(sum over the token's valid slots, in slot order)
+// SwiGLU of the gate / up sums written in k parts: thread = 4 activations of
+// one sorted slot; the parts are added in order.  Slots past the placed ones
+// (dropped ids) are skipped.
+__global__ __launch_bounds__(256) void moe_swiglu_kernel(MoeArgs A) {
+  const int q = A.d_ff / 4;
+  const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= (long long)A.n_slots * q) return;
+  const int j = (int)(gid / q), r = 4 * (int)(gid - (long long)j * q);
+  if (j >= A.offsets[A.n_experts]) return;
+  float g[4] = {0.f, 0.f, 0.f, 0.f}, u[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int ks = 0; ks < A.ks_gu; ++ks) {
+    const float* p = A.part + ((size_t)ks * A.n_slots + j) * 2 * A.d_ff + r;
+    const float4 a = *(const float4*)p, b = *(const float4*)(p + A.d_ff);
+    g[0] += a.x; g[1] += a.y; g[2] += a.z; g[3] += a.w;
+    u[0] += b.x; u[1] += b.y; u[2] += b.z; u[3] += b.w;
+  }
+  uint16_t v[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = f2bf(g[i] / (1.f + __expf(-g[i])) * u[i]);
+  uint2 p;
+  p.x = (uint32_t)v[0] | ((uint32_t)v[1] << 16);
+  p.y = (uint32_t)v[2] | ((uint32_t)v[3] << 16);
+  *(uint2*)(A.act + (size_t)j * A.d_ff + r) = p;
+}
+
 __global__ __launch_bounds__(256) void moe_sum_kernel(MoeArgs A, uint16_t* out, int n_tokens) {
   const int q = A.d_model / 4;
   const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
@@ -302,8 +348,10 @@ __global__ __launch_bounds__(256) void moe_sum_kernel(MoeArgs A, uint16_t* out, 
     const int slot = t * A.top_k + s;
     const int id = A.ids[slot];
     if (id < 0 || id >= A.n_experts) continue;
-    const float4 y = *(const float4*)(A.ys + (size_t)slot * A.d_model + c);
-    acc.x += y.x; acc.y += y.y; acc.z += y.z; acc.w += y.w;
+    for (int ks = 0; ks < A.ks_dn; ++ks) {
+      const float4 y = *(const float4*)(A.ys + ((size_t)ks * A.n_slots + slot) * A.d_model + c);
+      acc.x += y.x; acc.y += y.y; acc.z += y.z; acc.w += y.w;
+    }
   }
   uint2 p;
   p.x = (uint32_t)f2bf(acc.x) | ((uint32_t)f2bf(acc.y) << 16);
@@ -312,8 +360,34 @@ __global__ __launch_bounds__(256) void moe_sum_kernel(MoeArgs A, uint16_t* out, 
 }
 
 struct MoeLayout {
-  size_t offsets = 0, sorted = 0, act = 0, ys = 0, total = 0;
+  size_t offsets = 0, sorted = 0, act = 0, ys = 0, part = 0, total = 0;
 };
+
+// Launch shape.  At most min(E, slots) experts are routed: with fewer than
+// two 4-wave workgroups per compute unit for them, one-wave workgroups fill
+// the GPU (narrow).  When those waves make a single pass (at most 64 slots)
+// and are still few, each one's k range is split into parts so that about
+// KSPLIT_WAVES waves stream the weights: more loads in flight and an even
+// spread over the compute units.
+constexpr long long KSPLIT_WAVES = 3072;
+struct MoeShape {
+  bool narrow = false;
+  int ks_gu = 1, ks_dn = 1;
+};
+
+MoeShape moe_shape(const moe_cfg* c) {
+  MoeShape S;
+  const long long N = (long long)c->n_tokens * c->top_k;
+  const long long routed = std::min<long long>(c->n_experts, N);
+  S.narrow = routed * (c->d_ff / 128) < 512;
+  if (S.narrow && N <= 64) {
+    S.ks_gu = (int)std::clamp<long long>(KSPLIT_WAVES / (routed * (c->d_ff / 32)), 1,
+                                         std::min(8, c->d_model / KSTEP));
+    S.ks_dn = (int)std::clamp<long long>(KSPLIT_WAVES / (routed * (c->d_model / 32)), 1,
+                                         std::min(8, c->d_ff / KSTEP));
+  }
+  return S;
+}
 
 inline size_t up256(size_t x) { return (x + 255) / 256 * 256; }
 
@@ -333,8 +407,10 @@ MoeLayout moe_layout(const moe_cfg* c) {
   size_t cur = 0;
   L.offsets = cur; cur += up256((size_t)(c->n_experts + 1) * 4);
   L.sorted = cur; cur += up256(N * 4);
+  const MoeShape S = moe_shape(c);
   L.act = cur; cur += up256(N * c->d_ff * 2);
-  L.ys = cur; cur += up256(N * c->d_model * 4);
+  L.ys = cur; cur += up256((size_t)S.ks_dn * N * c->d_model * 4);
+  L.part = cur; cur += S.ks_gu > 1 ? up256((size_t)S.ks_gu * N * 2 * c->d_ff * 4) : 0;
   L.total = cur;
   return L;
 }
@@ -398,26 +474,34 @@ int moe_forward(const dca_bf16* x, const int32_t* topk_ids, const float* topk_we
   A.sorted = (const int32_t*)(ws + L.sorted);
   A.act = (uint16_t*)(ws + L.act);
   A.ys = (float*)(ws + L.ys);
+  A.part = (float*)(ws + L.part);
+  const MoeShape S = moe_shape(cfg);
+  A.ks_gu = S.ks_gu;
+  A.ks_dn = S.ks_dn;
   A.n_slots = cfg->n_tokens * cfg->top_k;
   A.n_experts = cfg->n_experts; A.top_k = cfg->top_k; A.d_model = cfg->d_model; A.d_ff = cfg->d_ff;
   moe_record(cfg, 0, 0);
   hipLaunchKernelGGL(moe_sort_kernel, dim3(1), dim3(1024), 0, st, A);
   if (hipGetLastError() != hipSuccess) return DCA_EHIP;
   moe_record(cfg, 0, 1);
-  // at most min(E, slots) experts are routed: with fewer than two 4-wave
-  // workgroups per compute unit for them, one-wave workgroups fill the GPU
-  const long long routed = std::min<long long>(cfg->n_experts, (long long)A.n_slots);
-  const bool narrow = routed * (cfg->d_ff / 128) < 512;
+  const bool narrow = S.narrow;
   moe_record(cfg, 1, 0);
   if (narrow)
-    hipLaunchKernelGGL((moe_mma_kernel<true, 1>), dim3(cfg->n_experts * (cfg->d_ff / 32)), dim3(64), 0, st, A);
+    hipLaunchKernelGGL((moe_mma_kernel<true, 1>), dim3(cfg->n_experts * (cfg->d_ff / 32) * S.ks_gu), dim3(64), 0,
+                       st, A);
   else
     hipLaunchKernelGGL((moe_mma_kernel<true, 4>), dim3(cfg->n_experts * (cfg->d_ff / 128)), dim3(256), 0, st, A);
   if (hipGetLastError() != hipSuccess) return DCA_EHIP;
+  if (S.ks_gu > 1) {
+    const long long items = (long long)A.n_slots * (cfg->d_ff / 4);
+    hipLaunchKernelGGL(moe_swiglu_kernel, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, st, A);
+    if (hipGetLastError() != hipSuccess) return DCA_EHIP;
+  }
   moe_record(cfg, 1, 1);
   moe_record(cfg, 2, 0);
   if (narrow)
-    hipLaunchKernelGGL((moe_mma_kernel<false, 1>), dim3(cfg->n_experts * (cfg->d_model / 32)), dim3(64), 0, st, A);
+    hipLaunchKernelGGL((moe_mma_kernel<false, 1>), dim3(cfg->n_experts * (cfg->d_model / 32) * S.ks_dn), dim3(64),
+                       0, st, A);
   else
     hipLaunchKernelGGL((moe_mma_kernel<false, 4>), dim3(cfg->n_experts * (cfg->d_model / 128)), dim3(256), 0, st, A);
   if (hipGetLastError() != hipSuccess) return DCA_EHIP;
