@@ -101,17 +101,19 @@ def test_moe_small_against_oracle(T, E, k, d, d_ff, skew):
     log(f"max abs error {mx:.2e}")
 
 
-def test_moe_dropped_slots():
-    w = WM.MoeWorkload("t", 30, 6, 3, 256, 256)
+@pytest.mark.parametrize("T,dead", [(30, 7),      # 90 slots: one pass per expert, no k parts
+                                    (12, 5)])     # 36 slots: the products run in k parts
+def test_moe_dropped_slots(T, dead):
+    w = WM.MoeWorkload("t", T, 6, 3, 256, 256)
     x, ids, wts = WM.make_tokens(w, 1)
     w13, w2 = WM.make_weights(w, 1)
     ids = ids.copy()
     ids[::4, 0] = -1
     ids[1::5, 2] = 6
-    ids[7] = -1                                   # a token with every slot dropped
+    ids[dead] = -1                                # a token with every slot dropped
     got = run(x, ids, wts, w13, w2)
     check(got, M.moe_forward(x, ids, wts, w13, w2), "dropped")
-    assert not M.bf16_to_f64(got[7]).any()
+    assert not M.bf16_to_f64(got[dead]).any()
 
 
 def test_moe_deterministic():
