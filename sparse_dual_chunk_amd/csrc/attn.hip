@@ -136,7 +136,10 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A) {
   for (int i = 0; i < 4; ++i) o[i] = f32x16{};
   float m_run = 0.f;         // reference max (log2 domain) of this row
   f32x16 negm = {};          // -m_run in every entry: the S^T MFMAs start from it, so the
-                             // scores come out already shifted by the reference max
+                             // scores come out already shifted by the reference max.  The
+                             // exact-diagonal kernel, which selects every score anyway,
+                             // starts from zero and subtracts m_run then: its 16
+                             // registers would otherwise be spilled
   bool started = false;      // the row has met a key
   float l_run = 0.f;         // this lane's partial row sum
   // rotated query row of this lane for the current DCA mode: the hi half is
@@ -334,7 +337,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A) {
     if (mode != q_mode) load_q(mode);
     // 32 keys x 32 rows of this wave (scores in log2 units)
     f32x16 s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(kt + tile_off(l32, half)), qh[0],
-                                                       negm, 0, 0, 0);
+                                                       EXACT ? f32x16{} : negm, 0, 0, 0);
 #pragma unroll
     for (int kk = 1; kk < 8; ++kk) {
       const bf16x8 a = *(const bf16x8*)(kt + tile_off(l32, 2 * kk + half));
@@ -421,8 +424,11 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A) {
 #pragma unroll
       for (int vv = 0; vv < 16; ++vv) {
         const int slot = 8 * (vv >> 2) + (vv & 3) + 4 * half;
-        if (!((m >> slot) & 1u)) s[vv] = -INFINITY;
+        s[vv] = ((m >> slot) & 1u) ? s[vv] - m_run : -INFINITY;
       }
+    } else if (EXACT) {
+#pragma unroll
+      for (int vv = 0; vv < 16; ++vv) s[vv] -= m_run;
     }
     after_qk();
     // ---- online softmax (log2 domain; s already holds score - m_run).  The
@@ -446,7 +452,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A) {
 #pragma unroll
       for (int vv = 0; vv < 16; ++vv) {
         s[vv] -= shift;
-        negm[vv] = -m_run;
+        if (!EXACT) negm[vv] = -m_run;
       }
     }
     started = started || (mx != -INFINITY);
