@@ -79,7 +79,8 @@ def _check(q, k, v, cfg, what, **kw):
     return out
 
 
-@pytest.mark.parametrize("n_k,n_t,split", [(700, 1, 0), (700, 3, 0), (700, 3, 5), (64, 1, 0), (33, 2, 0)])
+@pytest.mark.parametrize("n_k,n_t,split", [(700, 1, 0), (700, 3, 0), (700, 3, 5), (64, 1, 0), (33, 2, 0),
+                                            (900, 64, 0), (900, 64, 3)])   # 64 tokens: the most one call takes
 def test_decode_multichunk(n_k, n_t, split):
     """S = 256: keys in up to three chunks before the tokens' one."""
     q, k, v = _inputs(n_k + n_t, n_k, n_t, 4, 2)

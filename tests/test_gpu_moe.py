@@ -87,7 +87,8 @@ def check(got_bits, ref, what):
 @pytest.mark.parametrize("T,E,k,d,d_ff,skew", [(5, 6, 2, 256, 128, 0.0), (40, 8, 3, 384, 640, 0.0),
                                                 (200, 8, 2, 256, 256, 3.0), (1, 16, 4, 512, 384, 0.0),
                                                 (600, 12, 2, 256, 128, 1.0), (64, 128, 2, 256, 512, 0.0),
-                                                (300, 128, 4, 256, 512, 2.0)])
+                                                (300, 128, 4, 256, 512, 2.0),
+                                                (3, 4, 4, 256, 128, 0.0)])   # top_k = n_experts: every expert, every token
 def test_moe_small_against_oracle(T, E, k, d, d_ff, skew):
     w = WM.MoeWorkload("t", T, E, k, d, d_ff, skew=skew)
     x, ids, wts = WM.make_tokens(w, T + E)
