@@ -31,10 +31,16 @@
  *       q, out : [n_q][h_q][head_dim]      k, v : [n_k][h_kv][head_dim]
  *     q and k are BEFORE any rotary embedding: the library applies every
  *     rotation itself.
- *   - positions is a HOST int32 array of n_q entries that must be the
- *     contiguous run p0, p0+1, ..., n_k-1 (a chunk of a chunked prefill whose
- *     KV prefix ends with the chunk), with p0 a multiple of 64.  It is read
- *     before anything is enqueued so that malformed calls fail synchronously.
+ *   - positions is a DEVICE int32 array of n_q entries that must be the
+ *     contiguous run p0, p0+1, ..., n_k-1 with p0 = n_k - n_q (a chunk of a
+ *     chunked prefill whose KV prefix ends with the chunk), p0 a multiple of
+ *     64.  The host checks p0 from n_k and n_q before anything is enqueued.
+ *     The entries are checked on the device by the call's first kernel: if
+ *     any differs from p0 + i, the call writes none of its outputs (out,
+ *     lse_out, v_idx, s_off, cover_pairs, attended_pairs keep their contents)
+ *     and stores DCA_EINVAL in *cfg->status when status is given (DCA_OK
+ *     otherwise).  The workspace holds the check's result, so its contents
+ *     after such a call are unspecified.
  *   - Every buffer belongs to the caller.  No entry point allocates device
  *     memory: scratch comes from cfg->workspace, sized by dca_workspace_size
  *     (dca_decode_workspace_size for dca_decode).
@@ -74,7 +80,7 @@ typedef uint16_t dca_bf16;     /* raw bfloat16 bits */
 
 typedef struct dca_cfg {
   int32_t n_q;            /* query rows in this call (>= 1) */
-  int32_t n_k;            /* keys in the prefix; must equal positions[n_q-1] + 1 */
+  int32_t n_k;            /* keys in the prefix; positions[i] must equal n_k - n_q + i */
   int32_t h_q, h_kv;      /* query / KV heads; h_q % h_kv == 0 (GQA: consecutive grouping) */
   int32_t head_dim;       /* must be 128 */
   int32_t dca_chunk;      /* S: multiple of 64, >= 64 */
@@ -118,6 +124,15 @@ typedef struct dca_cfg {
    * head's rows hold its own k best, padded with -1.  NULL: every head takes
    * vs_k_vertical and vs_k_slash. */
   const int32_t *vs_k_per_head;
+  /* Optional device int64: dca_sparse_prefill writes the sum over heads and
+   * rows of |A(i)|, the (row, key) pairs each row attends (causal, and in the
+   * sparse readings only its covered or exact keys); 4 * head_dim *
+   * attended_pairs is F_attended.  For exact diagonals it costs one pass over
+   * the selected offsets per vertical column.  NULL: not written. */
+  int64_t *attended_pairs;
+  /* Optional device int32: calls that take positions store DCA_OK there, or
+   * DCA_EINVAL when the device check of positions fails.  NULL: not written. */
+  int32_t *status;
 } dca_cfg;
 
 /* Bytes of workspace both entry points need for this configuration (the
@@ -308,9 +323,9 @@ DCA_API int dca_prefill_sequence_workspace_size(const dca_cfg *cfg, const dca_se
  * attention from the cache (dca_sparse_prefill_cached), writing rows
  * [b_c, b_{c+1}) of out [n][h_q][128] and, when cfg->lse_out is set, columns
  * [b_c, b_{c+1}) of lse_out [h_q][n].  Every key is rotated once.  The outputs
- * are bitwise those of the per-chunk calls.  cfg->v_idx, s_off, cover_pairs
- * and stage_events must be NULL (plan->cover_pairs takes the role of the
- * latter); cache->capacity >= n.  Work is ordered on cfg->stream: when it
+ * are bitwise those of the per-chunk calls.  cfg->v_idx, s_off, cover_pairs,
+ * attended_pairs and stage_events must be NULL (plan->cover_pairs takes the
+ * role of cover_pairs); cfg->status is not written; cache->capacity >= n.  Work is ordered on cfg->stream: when it
  * reaches the end of the call there, every chunk is done.  Events are created
  * and released inside the call. */
 DCA_API int dca_prefill_sequence(const dca_bf16 *q, const dca_bf16 *k, const dca_bf16 *v,

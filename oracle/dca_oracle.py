@@ -119,13 +119,6 @@ def dca_key_position(j, S: int):
     return np.asarray(j) % S
 
 
-def scoring_query_position(p_i, j, S: int):
-    """Continuous positions used to choose key tokens: r_i in its own chunk, S + r_i before it."""
-    r = np.asarray(p_i) % S
-    same = (np.asarray(j) // S) == (np.asarray(p_i) // S)
-    return np.where(same, r, S + r)
-
-
 # ----------------------------------------------------------------------------
 # Attention over an explicit key set, one query head and a group of rows
 # ----------------------------------------------------------------------------
@@ -448,13 +441,46 @@ def vs_index(q, k, p0: int, cfg: dict, heads=None, budgets=None):
 # ----------------------------------------------------------------------------
 # Work counts
 # ----------------------------------------------------------------------------
-def flop_counts(n_q: int, h_q: int, d: int, p0: int, n_k: int, v_idx=None, s_off=None):
+def _selected_offsets(s_off_h) -> np.ndarray:
+    offs = np.asarray(s_off_h if s_off_h is not None else [], dtype=np.int64)
+    return np.unique(np.concatenate([[0], offs[offs >= 0]]))
+
+
+def _selected_columns(v_idx_h) -> np.ndarray:
+    cols = np.asarray(v_idx_h if v_idx_h is not None else [], dtype=np.int64)
+    return np.unique(cols[cols >= 0])
+
+
+def exact_attended_pairs(n_q: int, p0: int, v_idx_h, s_off_h) -> int:
+    """sum_i |A(i)| of one head under the exact-diagonal semantics, by inclusion-exclusion:
+    a row at position p attends the keys p - delta (delta a selected offset or 0, delta <= p)
+    and the selected columns j <= p; a key that is both is counted once.  The keys counted
+    twice are the pairs (column j, offset delta) with p0 <= j + delta <= p_last."""
+    offs = _selected_offsets(s_off_h)
+    cols = _selected_columns(v_idx_h)
+    p = np.arange(p0, p0 + n_q, dtype=np.int64)
+    on_diag = int(np.searchsorted(offs, p, side="right").sum())
+    on_col = int(np.searchsorted(cols, p, side="right").sum())
+    p_last = p0 + n_q - 1
+    lo = np.searchsorted(offs, p0 - cols, side="left")
+    hi = np.searchsorted(offs, p_last - cols, side="right")
+    both = int((hi - lo).sum())
+    return on_diag + on_col - both
+
+
+def flop_counts(n_q: int, h_q: int, d: int, p0: int, n_k: int, v_idx=None, s_off=None, exact: bool = False):
     """(F_blocks, F_attended) for one call.
 
     F_blocks = 4 d sum_h sum_b rows(b) |C_h(b)|: the canonical block cover,
     counted over every row of each block.  F_attended = 4 d sum_h sum_i |A_h(i)|
-    counts only the causal pairs each row attends (here for the dense case in
-    closed form; for the sparse case from the covers of each block).
+    counts only the (row, key) pairs each row attends.
+
+    Dense: |A(i)| = p_i + 1.  Block cover: the cover of block b always holds the
+    block's own keys [i0, i0 + rows) (offset 0 is always selected) and nothing
+    above them, so |A(i)| = |C_h(b)| - rows + (p_i - i0 + 1) and a block adds
+    rows (|C_h(b)| - rows) + rows (rows + 1) / 2.  Exact diagonals
+    (``exact``): :func:`exact_attended_pairs`; F_blocks is the block cover in
+    both sparse readings (the same tiles are computed).
     """
     dense = v_idx is None and s_off is None
     nb = (n_q + QBLOCK - 1) // QBLOCK
@@ -465,16 +491,12 @@ def flop_counts(n_q: int, h_q: int, d: int, p0: int, n_k: int, v_idx=None, s_off
         if dense:
             sizes = np.array([min(p0 + b * QBLOCK + QBLOCK, n_k) for b in range(nb)], dtype=np.int64)
             fb += int((rows * sizes).sum())
-            fa += int((np.arange(p0, p0 + n_q) + 1).sum())
+            fa += int((np.arange(p0, p0 + n_q, dtype=np.int64) + 1).sum())
         else:
             sizes = cover_sizes(n_q, p0, n_k, v_idx[h], s_off[h])
             fb += int((rows * sizes).sum())
-    if not dense:
-        fa = None
-    return 4 * d * fb, (4 * d * fa if fa is not None else None)
-
-
-def attended_pairs_block(keys: np.ndarray, i0: int, rows: int) -> int:
-    """Number of (row, key) pairs of one block that are causal: sum_i |C ∩ [0, p_i]|."""
-    p_rows = np.arange(i0, i0 + rows)
-    return int(np.searchsorted(keys, p_rows, side="right").sum())
+            if exact:
+                fa += exact_attended_pairs(n_q, p0, v_idx[h], s_off[h])
+            else:
+                fa += int((rows * (sizes - rows) + rows * (rows + 1) // 2).sum())
+    return 4 * d * fb, 4 * d * fa

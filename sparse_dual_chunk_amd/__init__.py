@@ -77,6 +77,8 @@ class dca_cfg(ctypes.Structure):
         ("stage_events", ctypes.c_void_p),
         ("slash_exact", ctypes.c_int32),
         ("vs_k_per_head", ctypes.c_void_p),
+        ("attended_pairs", ctypes.c_void_p),
+        ("status", ctypes.c_void_p),
     ]
 
 
@@ -306,9 +308,21 @@ def _stream(stream) -> Optional[int]:
     return int(stream)
 
 
-def _positions(positions):
-    a = np.ascontiguousarray(np.asarray(positions, dtype=np.int32))
-    return a, a.ctypes.data_as(ctypes.c_void_p)
+def _positions(positions, n_q: int, stream: Optional[int]):
+    """Device int32 positions of a call: a cuda int32 tensor is checked and passed as is;
+    anything else is copied into a new device tensor (kept alive by the caller until the
+    call has been enqueued; torch's allocator orders its reuse on the stream it was made on,
+    and a call on another stream records it there)."""
+    import torch
+    if isinstance(positions, torch.Tensor):
+        if positions.device.type == "cuda":
+            return positions, _dev(positions, "positions", n_q * 4, "int32")
+    elif hasattr(positions, "data_ptr"):
+        return positions, _dev(positions, "positions", n_q * 4, "int32")
+    t = torch.from_numpy(np.ascontiguousarray(np.asarray(positions, dtype=np.int32))).cuda()
+    if stream is not None and stream != int(torch.cuda.current_stream().cuda_stream):
+        t.record_stream(torch.cuda.ExternalStream(stream))
+    return t, _dev(t, "positions", n_q * 4, "int32")
 
 
 def dca_strerror(code: int) -> str:
@@ -324,13 +338,17 @@ def dca_workspace_size(cfg: Config) -> int:
     return int(n.value)
 
 
-def vs_index_build(q, k, positions, cfg: Config, v_idx, s_off, workspace, stream=None, k_per_head=None) -> None:
+def vs_index_build(q, k, positions, cfg: Config, v_idx, s_off, workspace, stream=None, k_per_head=None,
+                   status=None) -> None:
     """Vertical-slash index of one chunk; writes v_idx [h_q][k_v] and s_off [h_q][k_s] (int32, device).
-    k_per_head: optional device int32 [h_q][2] per-head budgets (k_v, k_s)."""
-    pos, pos_p = _positions(positions)
+    positions: device int32 tensor [n_q] (host arrays are uploaded); k_per_head: optional device
+    int32 [h_q][2] per-head budgets (k_v, k_s); status: optional device int32 [1]."""
+    st = _stream(stream)
+    pos, pos_p = _positions(positions, cfg.n_q, st)
     hd2 = cfg.head_dim * 2
-    c = cfg.to_c(**_ws(workspace), stream=_stream(stream),
-                 vs_k_per_head=_dev(k_per_head, "k_per_head", cfg.h_q * 8, "int32"))
+    c = cfg.to_c(**_ws(workspace), stream=st,
+                 vs_k_per_head=_dev(k_per_head, "k_per_head", cfg.h_q * 8, "int32"),
+                 status=_dev(status, "status", 4, "int32"))
     rc = lib().vs_index_build(_dev(q, "q", cfg.n_q * cfg.h_q * hd2, "bf16"),
                               _dev(k, "k", cfg.n_k * cfg.h_kv * hd2, "bf16"), pos_p, ctypes.byref(c),
                               _dev(v_idx, "v_idx", cfg.h_q * cfg.vs_k_vertical * 4, "int32"),
@@ -340,17 +358,22 @@ def vs_index_build(q, k, positions, cfg: Config, v_idx, s_off, workspace, stream
 
 
 def dca_sparse_prefill(q, k, v, positions, cfg: Config, out, workspace, v_idx=None, s_off=None, lse_out=None,
-                       cover_pairs=None, stream=None, stage_events: Optional[Sequence[int]] = None) -> None:
-    """DCA prefill attention of one chunk (dense when v_idx and s_off are None)."""
-    pos, pos_p = _positions(positions)
+                       cover_pairs=None, stream=None, stage_events: Optional[Sequence[int]] = None,
+                       attended_pairs=None, status=None) -> None:
+    """DCA prefill attention of one chunk (dense when v_idx and s_off are None).
+    positions: device int32 tensor [n_q] (host arrays are uploaded)."""
+    st = _stream(stream)
+    pos, pos_p = _positions(positions, cfg.n_q, st)
     ev_arr = None
     if stage_events is not None:
         ev_arr = (ctypes.c_void_p * (2 * DCA_STAGE_COUNT))(*[int(e) for e in stage_events])
-    c = cfg.to_c(**_ws(workspace), stream=_stream(stream),
+    c = cfg.to_c(**_ws(workspace), stream=st,
                  v_idx=_dev(v_idx, "v_idx", cfg.h_q * cfg.vs_k_vertical * 4, "int32"),
                  s_off=_dev(s_off, "s_off", cfg.h_q * cfg.vs_k_slash * 4, "int32"),
                  lse_out=_dev(lse_out, "lse_out", cfg.h_q * cfg.n_q * 4, "float32"),
                  cover_pairs=_dev(cover_pairs, "cover_pairs", 8, "int64"),
+                 attended_pairs=_dev(attended_pairs, "attended_pairs", 8, "int64"),
+                 status=_dev(status, "status", 4, "int32"),
                  stage_events=ctypes.cast(ev_arr, ctypes.c_void_p) if ev_arr is not None else None)
     qb, kb = cfg.n_q * cfg.h_q * cfg.head_dim * 2, cfg.n_k * cfg.h_kv * cfg.head_dim * 2
     rc = lib().dca_sparse_prefill(_dev(q, "q", qb, "bf16"), _dev(k, "k", kb, "bf16"), _dev(v, "v", kb, "bf16"),
@@ -435,17 +458,21 @@ def dca_decode(q, cache: KeyCache, v, cfg: Config, out, workspace, lse_out=None,
 
 def dca_sparse_prefill_cached(q, cache: KeyCache, v, positions, cfg: Config, out, workspace, v_idx=None, s_off=None,
                               lse_out=None, cover_pairs=None, stream=None,
-                              stage_events: Optional[Sequence[int]] = None) -> None:
+                              stage_events: Optional[Sequence[int]] = None, attended_pairs=None,
+                              status=None) -> None:
     """dca_sparse_prefill with keys 0 .. cfg.n_k - 1 from a rotated key cache."""
-    pos, pos_p = _positions(positions)
+    st = _stream(stream)
+    pos, pos_p = _positions(positions, cfg.n_q, st)
     ev_arr = None
     if stage_events is not None:
         ev_arr = (ctypes.c_void_p * (2 * DCA_STAGE_COUNT))(*[int(e) for e in stage_events])
-    c = cfg.to_c(**_ws(workspace), stream=_stream(stream),
+    c = cfg.to_c(**_ws(workspace), stream=st,
                  v_idx=_dev(v_idx, "v_idx", cfg.h_q * cfg.vs_k_vertical * 4, "int32"),
                  s_off=_dev(s_off, "s_off", cfg.h_q * cfg.vs_k_slash * 4, "int32"),
                  lse_out=_dev(lse_out, "lse_out", cfg.h_q * cfg.n_q * 4, "float32"),
                  cover_pairs=_dev(cover_pairs, "cover_pairs", 8, "int64"),
+                 attended_pairs=_dev(attended_pairs, "attended_pairs", 8, "int64"),
+                 status=_dev(status, "status", 4, "int32"),
                  stage_events=ctypes.cast(ev_arr, ctypes.c_void_p) if ev_arr is not None else None)
     _check_cache(cache, cfg)
     kc = cache.to_c()

@@ -5,6 +5,7 @@
 #include <cstring>
 
 #include "../../include/dcasparse.h"
+#include "entry.h"
 #include "args.h"
 #include "common.h"
 
@@ -19,7 +20,7 @@ hipError_t launch_rotate_queries(const uint16_t* q, uint16_t* qhi, uint16_t* qlo
                                  int n_q, int h_q, int p0, int S, int W, float qscale, hipStream_t stream);
 hipError_t launch_attn(const AttnArgs& A, hipStream_t stream);
 hipError_t launch_lse_merge(const uint16_t* part_o, const float* part_lse, uint16_t* out, float* lse_out,
-                            int P, int n_q, int h_q, hipStream_t stream);
+                            int P, int n_q, int h_q, const int32_t* bad, hipStream_t stream);
 hipError_t launch_vs_score(const VsArgs& A, const uint16_t* q, int n_q, hipStream_t stream);
 hipError_t launch_select(const SelArgs& A, hipStream_t stream);
 hipError_t launch_plan(const PlanArgs& A, hipStream_t stream);
@@ -37,7 +38,28 @@ namespace {
 using namespace dca;
 
 __global__ void write_freqs_kernel(Freqs f, double* dst) { dst[threadIdx.x] = f.v[threadIdx.x]; }
-__global__ void write_i64_kernel(long long* dst, long long v) { *dst = v; }
+
+// Dense calls: the cover and attended pair counts, known on the host.
+__global__ void write_pairs_kernel(long long* cover, long long cover_v, long long* att, long long att_v,
+                                   const int32_t* bad) {
+  if (bad && *bad) return;
+  if (cover) *cover = cover_v;
+  if (att) *att = att_v;
+}
+
+// The device check of a call's positions: every entry must be p0 + i.  One
+// workgroup; *bad (workspace) is rewritten by every checked call, and read by
+// each kernel that writes a caller-visible output.
+__global__ void __launch_bounds__(256) positions_check_kernel(const int32_t* pos, int n_q, int p0, int32_t* bad,
+                                                              int32_t* status) {
+  int wrong = 0;
+  for (int i = threadIdx.x; i < n_q; i += blockDim.x) wrong |= (pos[i] != p0 + i);
+  wrong = __syncthreads_or(wrong);
+  if (threadIdx.x == 0) {
+    *bad = wrong;
+    if (status) *status = wrong ? DCA_EINVAL : DCA_OK;
+  }
+}
 
 constexpr size_t ALIGN = 256;
 inline size_t up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
@@ -47,7 +69,7 @@ struct Region { size_t off = 0, bytes = 0; };
 // Workspace layouts of the two entry points (regions are 256-byte aligned).
 struct Layout {
   // shared
-  Region freqs;
+  Region freqs, flag;
   // prefill
   Region khi, klo, kbits, hn, qhi, qlo, iv, iv_pre, n_iv, cov, ext, n_ext, tiles, n_tiles, t_first, part_o, part_lse;
   Region dbits, vbits;
@@ -61,7 +83,9 @@ struct Layout {
 
 inline void place(Region& r, size_t& cur, size_t bytes) { r.off = cur; r.bytes = bytes; cur += up(bytes); }
 
-int validate(const dca_cfg* c, const int32_t* positions) {
+// Host checks of a call.  The positions array lives in device memory and is
+// checked by positions_check_kernel; the host checks p0 = n_k - n_q.
+int validate(const dca_cfg* c) {
   if (!c) return DCA_EINVAL;
   if (c->n_q < 1 || c->n_k < 1 || c->h_q < 1 || c->h_kv < 1) return DCA_EINVAL;
   if (c->h_q % c->h_kv != 0) return DCA_EINVAL;
@@ -83,10 +107,6 @@ int validate(const dca_cfg* c, const int32_t* positions) {
   if ((long long)c->n_k + 2LL * c->dca_chunk + 128 > (1LL << 30)) return DCA_EUNSUPPORTED;
   // K / V rows of one KV head are addressed by 32-bit byte offsets
   if ((long long)c->n_k * c->h_kv * c->head_dim * 2 >= (1LL << 32)) return DCA_EUNSUPPORTED;
-  if (positions) {
-    for (int i = 0; i < c->n_q; ++i)
-      if ((long long)positions[i] != p0 + i) return DCA_EINVAL;
-  }
   return DCA_OK;
 }
 
@@ -114,6 +134,7 @@ Layout make_layout(const dca_cfg* c) {
   }
   size_t cur = 0;
   place(L.freqs, cur, HALF * sizeof(double));
+  place(L.flag, cur, sizeof(int32_t));
   const size_t base = cur;
   // --- prefill
   place(L.khi, cur, (size_t)n_k * h_kv * D * 2);
@@ -258,7 +279,7 @@ extern "C" {
 
 int dca_workspace_size(const dca_cfg* cfg, size_t* bytes) {
   if (!bytes) return DCA_EINVAL;
-  const int rc = validate(cfg, nullptr);
+  const int rc = validate(cfg);
   if (rc != DCA_OK) return rc;
   const Layout L = make_layout(cfg);
   *bytes = L.prefill_bytes > L.index_bytes ? L.prefill_bytes : L.index_bytes;
@@ -267,9 +288,20 @@ int dca_workspace_size(const dca_cfg* cfg, size_t* bytes) {
 
 int vs_index_build(const dca_bf16* q, const dca_bf16* k, const int32_t* positions, const dca_cfg* cfg,
                    int32_t* v_idx, int32_t* s_off) {
-  int rc = validate(cfg, positions);
+  if (!positions) return DCA_EINVAL;
+  return dca::index_impl(q, k, positions, cfg, v_idx, s_off);
+}
+
+}  // extern "C"
+
+namespace dca {
+
+// The index build of one chunk; positions == nullptr: implied (p0 + i), not checked.
+int index_impl(const dca_bf16* q, const dca_bf16* k, const int32_t* positions, const dca_cfg* cfg,
+               int32_t* v_idx, int32_t* s_off) {
+  int rc = validate(cfg);
   if (rc != DCA_OK) return rc;
-  if (!q || !k || !positions) return DCA_EINVAL;
+  if (!q || !k) return DCA_EINVAL;
   if ((cfg->vs_k_vertical > 0 && !v_idx) || (cfg->vs_k_slash > 0 && !s_off)) return DCA_EINVAL;
   const Layout L = make_layout(cfg);
   rc = check_workspace(cfg, L.index_bytes);
@@ -278,6 +310,12 @@ int vs_index_build(const dca_bf16* q, const dca_bf16* k, const int32_t* position
   const int n_q = cfg->n_q, n_k = cfg->n_k, h_q = cfg->h_q;
   const int p_last = n_k - 1;
   const int n_s = cfg->vs_last_q < n_q ? cfg->vs_last_q : n_q;
+  int32_t* bad = nullptr;
+  if (positions) {
+    bad = at<int32_t>(cfg, L.flag);
+    hipLaunchKernelGGL(positions_check_kernel, dim3(1), dim3(256), 0, st, positions, n_q, n_k - n_q, bad,
+                       cfg->status);
+  }
 
   hipLaunchKernelGGL(write_freqs_kernel, dim3(1), dim3(HALF), 0, st, make_freqs(cfg->rope_base),
                      at<double>(cfg, L.freqs));
@@ -307,21 +345,23 @@ int vs_index_build(const dca_bf16* q, const dca_bf16* k, const int32_t* position
   S.bcount = at<uint32_t>(cfg, L.bcount);
   S.max_blocks = L.max_blocks;
   S.k_head = cfg->vs_k_per_head;
+  S.bad = bad;
   if (launch_select(S, st) != hipSuccess) return DCA_EHIP;
   return DCA_OK;
 }
 
-}  // extern "C"
+}  // namespace dca
 
-namespace {
+namespace dca {
 
 // The prefill of one chunk.  Keys come either raw (k: rotated here into the
 // workspace) or from a rotated key cache (cache: rotated when they entered it).
+// positions == nullptr: implied (p0 + i), not checked.
 int prefill_impl(const dca_bf16* q, const dca_bf16* k, const dca_key_cache* cache, const dca_bf16* v,
                  const int32_t* positions, const dca_cfg* cfg, dca_bf16* out) {
-  int rc = validate(cfg, positions);
+  int rc = validate(cfg);
   if (rc != DCA_OK) return rc;
-  if (!q || !(k || cache) || !v || !out || !positions) return DCA_EINVAL;
+  if (!q || !(k || cache) || !v || !out) return DCA_EINVAL;
   if (cache) {
     if (!cache->k_hi || !cache->k_lo || !cache->k_flags || cache->capacity < cfg->n_k) return DCA_EINVAL;
     if ((long long)cache->capacity * cfg->h_kv * cfg->head_dim * 2 >= (1LL << 32)) return DCA_EUNSUPPORTED;
@@ -337,6 +377,11 @@ int prefill_impl(const dca_bf16* q, const dca_bf16* k, const dca_key_cache* cach
   const int p0 = n_k - n_q;
   const int p_last = n_k - 1;
 
+  int32_t* bad = nullptr;
+  if (positions) {
+    bad = at<int32_t>(cfg, L.flag);
+    hipLaunchKernelGGL(positions_check_kernel, dim3(1), dim3(256), 0, st, positions, n_q, p0, bad, cfg->status);
+  }
   hipLaunchKernelGGL(write_freqs_kernel, dim3(1), dim3(HALF), 0, st, make_freqs(cfg->rope_base),
                      at<double>(cfg, L.freqs));
   // rotated keys and their high-norm bits: this call's own rotation, or the cache's
@@ -380,15 +425,19 @@ int prefill_impl(const dca_bf16* q, const dca_bf16* k, const dca_key_cache* cach
     P.dbits = cfg->slash_exact ? at<uint32_t>(cfg, L.dbits) : nullptr;
     P.vbits = cfg->slash_exact ? at<uint32_t>(cfg, L.vbits) : nullptr;
     P.dbits_words = L.dbits_words; P.vbits_words = L.vbits_words;
+    P.attended = (long long*)cfg->attended_pairs;
+    P.bad = bad;
     if (launch_plan(P, st) != hipSuccess) return DCA_EHIP;
-  } else if (cfg->cover_pairs) {
-    // dense: every block covers its whole causal extent [0, i0 + rows)
+  } else if (cfg->cover_pairs || cfg->attended_pairs) {
+    // dense: every block covers its whole causal extent [0, i0 + rows); row i attends p_i + 1 keys
     long long pairs = 0;
     for (int b = 0; b < L.nb; ++b) {
       const long long rows = std::min(64, n_q - 64 * b);
       pairs += rows * (long long)(p0 + 64 * b + rows);
     }
-    hipLaunchKernelGGL(write_i64_kernel, dim3(1), dim3(1), 0, st, (long long*)cfg->cover_pairs, pairs * h_q);
+    const long long att = ((long long)n_k * (n_k + 1) / 2 - (long long)p0 * (p0 + 1) / 2) * h_q;
+    hipLaunchKernelGGL(write_pairs_kernel, dim3(1), dim3(1), 0, st, (long long*)cfg->cover_pairs, pairs * h_q,
+                       (long long*)cfg->attended_pairs, att, bad);
   }
   record(cfg, 1, 1);
   // stage 2: attention
@@ -410,32 +459,33 @@ int prefill_impl(const dca_bf16* q, const dca_bf16* k, const dca_key_cache* cach
   A.dbits = A.exact ? at<uint32_t>(cfg, L.dbits) : nullptr;
   A.vbits = A.exact ? at<uint32_t>(cfg, L.vbits) : nullptr;
   A.dbits_words = L.dbits_words; A.vbits_words = L.vbits_words;
+  A.bad = bad;
   if (launch_attn(A, st) != hipSuccess) return DCA_EHIP;
   record(cfg, 2, 1);
   // stage 3: LSE merge of the split partials
   record(cfg, 3, 0);
   if (L.split > 1) {
-    if (launch_lse_merge(A.part_o, A.part_lse, out, cfg->lse_out, L.split, n_q, h_q, st) != hipSuccess)
+    if (launch_lse_merge(A.part_o, A.part_lse, out, cfg->lse_out, L.split, n_q, h_q, bad, st) != hipSuccess)
       return DCA_EHIP;
   }
   record(cfg, 3, 1);
   return DCA_OK;
 }
 
-}  // namespace
+}  // namespace dca
 
 extern "C" {
 
 int dca_sparse_prefill(const dca_bf16* q, const dca_bf16* k, const dca_bf16* v, const int32_t* positions,
                        const dca_cfg* cfg, dca_bf16* out) {
-  if (!k) return DCA_EINVAL;
-  return prefill_impl(q, k, nullptr, v, positions, cfg, out);
+  if (!k || !positions) return DCA_EINVAL;
+  return dca::prefill_impl(q, k, nullptr, v, positions, cfg, out);
 }
 
 int dca_sparse_prefill_cached(const dca_bf16* q, const dca_key_cache* cache, const dca_bf16* v,
                               const int32_t* positions, const dca_cfg* cfg, dca_bf16* out) {
-  if (!cache) return DCA_EINVAL;
-  return prefill_impl(q, nullptr, cache, v, positions, cfg, out);
+  if (!cache || !positions) return DCA_EINVAL;
+  return dca::prefill_impl(q, nullptr, cache, v, positions, cfg, out);
 }
 
 int dca_key_cache_append(const dca_bf16* k, int32_t j0, int32_t n, const dca_cfg* cfg, const dca_key_cache* cache) {

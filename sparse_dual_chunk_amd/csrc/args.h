@@ -26,6 +26,7 @@ struct AttnArgs {
   const uint32_t* vbits;    // exact diagonals: [h_q][vbits_words] bit j + 128 = selected vertical column
   int n_q, n_k, h_q, h_kv, p0, S, W, nb, tile_stride, ext_stride, split, dense, kbits_words, hn_pad;
   int exact, dbits_words, vbits_words;
+  const int32_t* bad;       // device flag set by the positions check: write no output when nonzero (or null)
 };
 
 struct DecArgs {
@@ -72,6 +73,7 @@ struct SelArgs {
   uint32_t* bcount;        // [2*h_q][max_blocks][2] (gt, eq)
   int max_blocks;
   const int32_t* k_head;   // optional [h_q][2] per-head (k_v, k_s), clamped to [0, k_v / k_s]
+  const int32_t* bad;      // device flag set by the positions check: write no output when nonzero (or null)
 };
 
 struct PlanArgs {
@@ -88,6 +90,8 @@ struct PlanArgs {
   int32_t* t_first;        // [h_q][nb]
   const uint32_t* kbits;   // [h_kv][kbits_words]
   long long* cover_pairs;  // optional: sum of rows * |cover| over all (head, block)
+  long long* attended;     // optional: sum over heads and rows of the attended (row, key) pairs
+  const int32_t* bad;      // device flag set by the positions check: write no output when nonzero (or null)
   uint32_t* dbits;         // exact diagonals (or null): [h_q][dbits_words], bit delta + 128
   uint32_t* vbits;         // exact diagonals (or null): [h_q][vbits_words], bit j + 128
   int h_q, h_kv, k_v, k_s, p_last, p0, n_q, nb, iv_stride, ext_stride, cov_words, tile_stride, kbits_words;

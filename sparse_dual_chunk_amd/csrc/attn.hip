@@ -71,6 +71,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A) {
   // first): the rows of one head share one cover pattern shifted by 64 keys a
   // row, so the workgroups in flight do near-equal work, start and end
   // together and walk the same keys at the same time through the die's L2.
+  if (A.bad && *A.bad) return;   // positions check failed: no output is written
   const int die = blockIdx.x % NXCD;
   const int local = blockIdx.x / NXCD;
   const int hpg = A.h_q / A.h_kv;
@@ -629,7 +630,8 @@ __global__ void __launch_bounds__(256, 2) dca_attn_dense4_kernel(AttnArgs A) { a
 __global__ void __launch_bounds__(256) lse_merge_kernel(const uint16_t* __restrict__ part_o,
                                                         const float* __restrict__ part_lse,
                                                         uint16_t* __restrict__ out, float* __restrict__ lse_out,
-                                                        int P, int n_q, int h_q) {
+                                                        int P, int n_q, int h_q, const int32_t* bad) {
+  if (bad && *bad) return;   // positions check failed: no output is written
   const long long item = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (item >= (long long)n_q * h_q) return;
@@ -702,11 +704,11 @@ hipError_t launch_attn(const AttnArgs& A, hipStream_t stream) {
 }
 
 hipError_t launch_lse_merge(const uint16_t* part_o, const float* part_lse, uint16_t* out, float* lse_out,
-                            int P, int n_q, int h_q, hipStream_t stream) {
+                            int P, int n_q, int h_q, const int32_t* bad, hipStream_t stream) {
   const long long items = (long long)n_q * h_q;
   const int blocks = (int)((items + 3) / 4);      // one wave per (row, head), four per workgroup
   hipLaunchKernelGGL(lse_merge_kernel, dim3(blocks), dim3(256), 0, stream, part_o, part_lse, out, lse_out,
-                     P, n_q, h_q);
+                     P, n_q, h_q, bad);
   return hipGetLastError();
 }
 

@@ -155,6 +155,7 @@ __global__ void __launch_bounds__(256) sel_write_kernel(SelArgs A) {
   const int list = blockIdx.y;
   const double* s; int32_t* out; int n, k, f, kcap;
   sel_list(A, list, s, out, n, k, f, kcap);
+  if (A.bad && *A.bad) return;   // positions check failed: v_idx / s_off keep their contents
   if (blockIdx.x == 0) {
     for (int i = min(k, n) + threadIdx.x; i < kcap; i += 256) out[i] = -1;
   }
@@ -314,7 +315,10 @@ __global__ void __launch_bounds__(1024) plan_intervals_kernel(PlanArgs A) {
   if (tid == 0) {
     if (carry_count > 0) ivh[2 * (carry_count - 1) + 1] = -carry_kept + 64;
     A.n_iv[h] = carry_count;
-    if (A.cover_pairs && h == 0) *A.cover_pairs = 0;
+    if (h == 0 && !(A.bad && *A.bad)) {
+      if (A.cover_pairs) *A.cover_pairs = 0;
+      if (A.attended) *A.attended = 0;
+    }
   }
   __syncthreads();   // the interval ends are written (global memory, same workgroup)
   __threadfence_block();
@@ -415,9 +419,15 @@ __global__ void __launch_bounds__(256) plan_ext_kernel(PlanArgs A) {
       below[t] = c;
     }
     A.t_first[unit] = (int)(below[0] / 32);
-    if (A.cover_pairs) {
-      const long long cover = (below[1] - below[0]) + cnt;
-      atomicAdd((unsigned long long*)A.cover_pairs, (unsigned long long)(cover * rows));
+    const long long cover = (below[1] - below[0]) + cnt;
+    if (!(A.bad && *A.bad)) {
+      if (A.cover_pairs) atomicAdd((unsigned long long*)A.cover_pairs, (unsigned long long)(cover * rows));
+      // block cover: the block's own keys [i0, i0 + rows) are always covered and
+      // nothing above them, so row r attends |cover| - rows + r + 1 keys
+      if (A.attended && !A.dbits) {
+        const long long att = (long long)rows * (cover - rows) + (long long)rows * (rows + 1) / 2;
+        atomicAdd((unsigned long long*)A.attended, (unsigned long long)att);
+      }
     }
   }
 }
@@ -479,6 +489,52 @@ __global__ void plan_bits_kernel(PlanArgs A) {
   }
 }
 
+// Exact diagonals: the (row, key) pairs of one head, sum over rows i of
+// |{delta selected (or 0) : delta <= p_i}| + |{j selected : j <= p_i}| minus the
+// keys that are both, i.e. the pairs (column j, offset delta) with
+// p0 <= j + delta <= p_last.  One workgroup per head over the two bitmaps.
+__global__ void __launch_bounds__(1024) plan_attended_exact_kernel(PlanArgs A) {
+  __shared__ unsigned long long red[16];
+  if (A.bad && *A.bad) return;
+  const int h = blockIdx.x;
+  const uint32_t* db = A.dbits + (long long)h * A.dbits_words;
+  const uint32_t* vb = A.vbits + (long long)h * A.vbits_words;
+  const int p_last = A.p_last;
+  const int p0 = A.p0;
+  // rows whose position is at least x
+  auto rows_from = [&](int x) -> long long { return x > p_last ? 0 : (long long)(p_last - max(x, p0) + 1); };
+  // set bits of db in offsets [lo, hi] (bit delta + 128)
+  auto dcount = [&](int lo, int hi) -> long long {
+    lo = max(lo, 0);
+    if (hi < lo) return 0;
+    const int b0 = lo + 128, b1 = hi + 128;   // inclusive
+    const int w0 = b0 >> 5, w1 = b1 >> 5;
+    long long c = 0;
+    for (int w = w0; w <= w1; ++w) {
+      uint32_t m = db[w];
+      if (w == w0) m &= ~0u << (b0 & 31);
+      if (w == w1 && (b1 & 31) != 31) m &= (1u << ((b1 & 31) + 1)) - 1u;
+      c += __popc(m);
+    }
+    return c;
+  };
+  long long acc = 0;
+  const int nbits = p_last + 1;
+  for (int x = threadIdx.x; x < nbits; x += blockDim.x) {
+    const int bit = x + 128;
+    if ((db[bit >> 5] >> (bit & 31)) & 1u) acc += rows_from(x);
+    if ((vb[bit >> 5] >> (bit & 31)) & 1u) acc += rows_from(x) - dcount(p0 - x, p_last - x);
+  }
+  for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = (unsigned long long)acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned long long t = 0;
+    for (int w = 0; w < (int)(blockDim.x >> 6); ++w) t += red[w];
+    atomicAdd((unsigned long long*)A.attended, t);
+  }
+}
+
 hipError_t launch_plan(const PlanArgs& A, hipStream_t stream) {
   if (A.dbits) {
     hipLaunchKernelGGL(plan_bits_clear_kernel, dim3(256), dim3(256), 0, stream, A);
@@ -492,6 +548,8 @@ hipError_t launch_plan(const PlanArgs& A, hipStream_t stream) {
   const int units = A.h_q * A.nb;
   hipLaunchKernelGGL(plan_ext_kernel, dim3((units + 3) / 4), dim3(256), 0, stream, A);
   hipLaunchKernelGGL(plan_tiles_kernel, dim3((A.tile_stride + 255) / 256, A.h_q), dim3(256), 0, stream, A);
+  if (A.dbits && A.attended)
+    hipLaunchKernelGGL(plan_attended_exact_kernel, dim3(A.h_q), dim3(1024), 0, stream, A);
   return hipGetLastError();
 }
 

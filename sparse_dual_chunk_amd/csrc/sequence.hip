@@ -12,6 +12,7 @@
 #include <vector>
 
 #include "../../include/dcasparse.h"
+#include "entry.h"
 
 namespace {
 
@@ -146,6 +147,8 @@ dca_cfg chunk_cfg(const dca_cfg* cfg, int b0, int b1) {
   c.s_off = nullptr;
   c.lse_out = nullptr;
   c.cover_pairs = nullptr;
+  c.attended_pairs = nullptr;
+  c.status = nullptr;
   c.stage_events = nullptr;
   c.workspace = nullptr;
   c.workspace_bytes = 0;
@@ -229,7 +232,7 @@ int dca_prefill_sequence_workspace_size(const dca_cfg* cfg, const dca_sequence_p
 int dca_prefill_sequence(const dca_bf16* q, const dca_bf16* k, const dca_bf16* v, const dca_sequence_plan* plan,
                          const dca_cfg* cfg, const dca_key_cache* cache, dca_bf16* out) {
   if (!q || !k || !v || !out || !cache || !cfg) return DCA_EINVAL;
-  if (cfg->v_idx || cfg->s_off || cfg->cover_pairs || cfg->stage_events) return DCA_EINVAL;
+  if (cfg->v_idx || cfg->s_off || cfg->cover_pairs || cfg->attended_pairs || cfg->stage_events) return DCA_EINVAL;
   SeqLayout L;
   int rc = seq_layout(cfg, plan, &L);
   if (rc != DCA_OK) return rc;
@@ -237,10 +240,6 @@ int dca_prefill_sequence(const dca_bf16* q, const dca_bf16* k, const dca_bf16* v
   if (!cache->k_hi || !cache->k_lo || !cache->k_flags || cache->capacity < cfg->n_k) return DCA_EINVAL;
   const int n_chunks = plan->n_chunks, h_q = cfg->h_q, D = cfg->head_dim;
   const int32_t* b = plan->bounds;
-  // host positions of the longest chunk, rewritten for every chunk call
-  int max_rows = 0;
-  for (int c = 0; c < n_chunks; ++c) max_rows = std::max(max_rows, b[c + 1] - b[c]);
-  std::vector<int32_t> pos(max_rows);
   // validate every chunk call before anything is enqueued
   for (int c = 0; c < n_chunks; ++c) {
     const dca_cfg cc = chunk_cfg(cfg, b[c], b[c + 1]);
@@ -280,9 +279,9 @@ int dca_prefill_sequence(const dca_bf16* q, const dca_bf16* k, const dca_bf16* v
       cc.workspace = slot(c);
       cc.workspace_bytes = L.ws_bytes;
       cc.stream = ist;
-      for (int i = 0; i < cc.n_q; ++i) pos[i] = b[c] + i;
-      const int r = vs_index_build(q + (size_t)b[c] * h_q * D, k, pos.data(), &cc, (int32_t*)(slot(c) + L.vidx_off),
-                                   (int32_t*)(slot(c) + L.soff_off));
+      // the chunk's positions are b_c .. b_{c+1}-1 by construction (implied, not checked)
+      const int r = dca::index_impl(q + (size_t)b[c] * h_q * D, k, nullptr, &cc, (int32_t*)(slot(c) + L.vidx_off),
+                                    (int32_t*)(slot(c) + L.soff_off));
       if (r != DCA_OK) return r;
     }
     record_opt(plan->index_events, 2 * c + 1, ist);
@@ -315,13 +314,12 @@ int dca_prefill_sequence(const dca_bf16* q, const dca_bf16* k, const dca_bf16* v
     }
     cc.lse_out = cfg->lse_out ? (float*)(slot(c) + L.lse_off) : nullptr;
     cc.cover_pairs = plan->cover_pairs ? plan->cover_pairs + c : nullptr;
-    for (int i = 0; i < n_q; ++i) pos[i] = b[c] + i;
     record_opt(plan->chunk_events, 2 * c, st);
     if (overlap && hipStreamWaitEvent(st, idx_done[c], 0) != hipSuccess) return DCA_EHIP;
     rc = dca_key_cache_append(k + (size_t)b[c] * cfg->h_kv * D, b[c], n_q, &cc, cache);
     if (rc != DCA_OK) return rc;
-    rc = dca_sparse_prefill_cached(q + (size_t)b[c] * h_q * D, cache, v, pos.data(), &cc,
-                                   out + (size_t)b[c] * h_q * D);
+    rc = dca::prefill_impl(q + (size_t)b[c] * h_q * D, nullptr, cache, v, nullptr, &cc,
+                           out + (size_t)b[c] * h_q * D);
     if (rc != DCA_OK) return rc;
     if (cfg->lse_out) {
       // the chunk's [h_q][n_q] block into columns b_c .. b_{c+1}-1 of [h_q][n]

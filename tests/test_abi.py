@@ -124,28 +124,35 @@ class _FakeTensor:
         return 1
 
 
-def _call_prefill(cfg, positions, ws=None):
+def _call_prefill(cfg, positions=None, ws=None):
     t = _FakeTensor()
-    S.dca_sparse_prefill(t, t, t, positions, cfg, t, ws or _FakeTensor(), stream=0)
+    S.dca_sparse_prefill(t, t, t, positions if positions is not None else _FakeTensor(), cfg, t,
+                         ws or _FakeTensor(), stream=0)
 
 
-def test_prefill_rejects_bad_positions_before_any_launch():
+def test_prefill_rejects_missing_positions_and_misaligned_chunks():
+    """positions is a device array checked by a kernel; the host rejects a missing array and
+    a chunk start p0 = n_k - n_q off a 64 boundary before anything is enqueued."""
     cfg = _cfg()
-    pos = np.arange(256, 512, dtype=np.int32)
-    pos[10] += 1
+    c = cfg.to_c(workspace=0x1000, workspace_bytes=1 << 30)
+    for fn in ("dca_sparse_prefill",):
+        rc = getattr(S.lib(), fn)(0x1000, 0x1000, 0x1000, None, ctypes.byref(c), 0x1000)
+        assert rc == S.DCA_EINVAL
+    rc = S.lib().vs_index_build(0x1000, 0x1000, None, ctypes.byref(c), 0x1000, 0x1000)
+    assert rc == S.DCA_EINVAL
+    kc = S.dca_key_cache(k_hi=0x1000, k_lo=0x1000, k_flags=0x1000, capacity=1 << 20)
+    rc = S.lib().dca_sparse_prefill_cached(0x1000, ctypes.byref(kc), 0x1000, None, ctypes.byref(c), 0x1000)
+    assert rc == S.DCA_EINVAL
     with pytest.raises(S.DcaError) as ei:
-        _call_prefill(cfg, pos)
-    assert ei.value.code == S.DCA_EINVAL
-    with pytest.raises(S.DcaError) as ei:
-        _call_prefill(cfg, np.arange(255, 511, dtype=np.int32))
-    assert ei.value.code == S.DCA_EINVAL
+        _call_prefill(_cfg(n_k=500))          # p0 = 244
+    assert ei.value.code == S.DCA_EUNSUPPORTED
 
 
 def test_prefill_rejects_small_or_missing_workspace():
     cfg = _cfg()
     need = S.dca_workspace_size(cfg)
     with pytest.raises(S.DcaError) as ei:
-        _call_prefill(cfg, np.arange(256, 512, dtype=np.int32), ws=_FakeTensor(need - 1))
+        _call_prefill(cfg, ws=_FakeTensor(need - 1))
     assert ei.value.code == S.DCA_EWORKSPACE
 
 
@@ -153,23 +160,30 @@ def test_prefill_rejects_one_sided_pattern_and_nulls():
     cfg = _cfg(vs_k_vertical=8, vs_k_slash=8)
     t = _FakeTensor(S.dca_workspace_size(cfg))
     with pytest.raises(S.DcaError) as ei:
-        S.dca_sparse_prefill(t, t, t, np.arange(256, 512, dtype=np.int32), cfg, t, t, v_idx=t, s_off=None, stream=0)
+        S.dca_sparse_prefill(t, t, t, _FakeTensor(), cfg, t, t, v_idx=t, s_off=None, stream=0)
     assert ei.value.code == S.DCA_EINVAL
     c = cfg.to_c(workspace=0x1000, workspace_bytes=1 << 30)
-    pos = np.arange(256, 512, dtype=np.int32)
-    rc = S.lib().dca_sparse_prefill(None, 0x1000, 0x1000, pos.ctypes.data_as(ctypes.c_void_p), ctypes.byref(c), 0x1000)
+    rc = S.lib().dca_sparse_prefill(None, 0x1000, 0x1000, 0x1000, ctypes.byref(c), 0x1000)
     assert rc == S.DCA_EINVAL
-    rc = S.lib().dca_sparse_prefill(0x1000, 0x1000, 0x1000, pos.ctypes.data_as(ctypes.c_void_p), None, 0x1000)
+    rc = S.lib().dca_sparse_prefill(0x1000, 0x1000, 0x1000, 0x1000, None, 0x1000)
     assert rc == S.DCA_EINVAL
 
 
 def test_index_rejects_missing_outputs():
     cfg = _cfg(vs_k_vertical=8, vs_k_slash=8)
-    t = _FakeTensor(S.dca_workspace_size(cfg))
     c = cfg.to_c(workspace=0x1000, workspace_bytes=1 << 40)
-    pos = np.arange(256, 512, dtype=np.int32)
-    rc = S.lib().vs_index_build(0x1000, 0x1000, pos.ctypes.data_as(ctypes.c_void_p), ctypes.byref(c), None, 0x1000)
+    rc = S.lib().vs_index_build(0x1000, 0x1000, 0x1000, ctypes.byref(c), None, 0x1000)
     assert rc == S.DCA_EINVAL
+
+
+def test_binding_checks_device_positions():
+    """A torch positions tensor must be int32 and hold n_q entries before its address crosses."""
+    torch = pytest.importorskip("torch")
+    cfg = _cfg()
+    with pytest.raises(ValueError):
+        S._dev(torch.zeros(cfg.n_q, dtype=torch.int64), "positions", cfg.n_q * 4, "int32")
+    with pytest.raises(ValueError):
+        S._dev(torch.zeros(cfg.n_q - 1, dtype=torch.int32), "positions", cfg.n_q * 4, "int32")
 
 
 def test_strerror_covers_codes():
@@ -251,12 +265,10 @@ def test_cached_prefill_rejects_small_cache_before_any_launch():
     cfg = _cfg()
     t = _FakeTensor(S.dca_workspace_size(cfg))
     with pytest.raises(S.DcaError) as ei:
-        S.dca_sparse_prefill_cached(t, _FakeCache(511), t, np.arange(256, 512, dtype=np.int32), cfg, t, t, stream=0)
+        S.dca_sparse_prefill_cached(t, _FakeCache(511), t, _FakeTensor(), cfg, t, t, stream=0)
     assert ei.value.code == S.DCA_EINVAL
     c = cfg.to_c(workspace=0x1000, workspace_bytes=1 << 30)
-    pos = np.arange(256, 512, dtype=np.int32)
-    assert S.lib().dca_sparse_prefill_cached(0x1000, None, 0x1000, pos.ctypes.data_as(ctypes.c_void_p),
-                                             ctypes.byref(c), 0x1000) == S.DCA_EINVAL
+    assert S.lib().dca_sparse_prefill_cached(0x1000, None, 0x1000, 0x1000, ctypes.byref(c), 0x1000) == S.DCA_EINVAL
 
 
 # ---- whole-prompt chunked prefill
@@ -393,7 +405,7 @@ def test_paged_append_validation():
 def test_binding_checks_tensors_before_the_call():
     torch = pytest.importorskip("torch")
     cfg = _cfg()                                   # n_q 256, n_k 512, h_q 4, h_kv 2
-    pos = np.arange(256, 512, dtype=np.int32)
+    pos = _FakeTensor()
     ws = _FakeTensor(S.dca_workspace_size(cfg))
     k = torch.zeros((512, 2, 128), dtype=torch.int16)
 

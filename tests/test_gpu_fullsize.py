@@ -3,11 +3,14 @@ bench.py times (default split, default high-norm threshold).
 
 The oracle cannot finish a whole call at these sizes, so each check uses outputs the
 oracle computes one by one:
-  * the vertical-slash index of sampled query heads, bit-exact;
-  * the exact F_blocks cover count of every head from the GPU's own index;
+  * the vertical-slash index of every query head, bit-exact (the 128K chunk, every
+    chunk of the 14B 256K prefill, the last chunk of 1M);
+  * the exact F_blocks cover count and the F_attended pair count of every head from
+    the GPU's own index;
   * the attention rows of sampled (head, query block) pairs (blocks 0, 1, middle,
-    last and two seeded random ones), within the bf16 output tolerance, plus lse
-    (for the 128K chunk also with the exact-diagonal semantics);
+    last and two seeded random ones) within the bf16 output tolerance, plus lse:
+    every head at 128K, one head per KV group (and the last head) elsewhere; the
+    exact-diagonal semantics at 128K and 1M;
   * properties that hold at any size on all rows (finite outputs, |o| <= max |v|).
 """
 from __future__ import annotations
@@ -26,13 +29,14 @@ from gpu_helpers import MAX_ABS, MEAN_ABS, bf16_f64, oracle_cfg
 pytestmark = pytest.mark.gpu
 
 LSE_TOL = 1e-2
-CASES = [
-    ("7b_dense_32k", 0, 0),
-    ("7b_chunk_at_98304_of_128k", 0, 0),
-    ("7b_chunk_at_98304_of_128k", 0, 1),
-    ("14b_256k_in_8_chunks", 7, 0),
-    ("7b_last_chunk_of_1m", 0, 0),
-]
+CASES = (
+    [("7b_dense_32k", 0, 0),
+     ("7b_chunk_at_98304_of_128k", 0, 0),
+     ("7b_chunk_at_98304_of_128k", 0, 1)]
+    + [("14b_256k_in_8_chunks", c, 0) for c in range(8)]
+    + [("7b_last_chunk_of_1m", 0, 0),
+       ("7b_last_chunk_of_1m", 0, 1)]
+)
 _cache: dict = {}
 
 
@@ -60,45 +64,68 @@ def gpu_call(name: str, chunk: int, exact: int = 0) -> dict:
     out = torch.empty(q.shape, dtype=torch.int16, device="cuda")
     lse = torch.empty((cfg.h_q, cfg.n_q), dtype=torch.float32, device="cuda")
     pairs = torch.zeros(1, dtype=torch.int64, device="cuda")
+    att = torch.zeros(1, dtype=torch.int64, device="cuda")
     vi = so = None
     if w.sparse:
         vi = torch.empty((w.h_q, w.k_vertical), dtype=torch.int32, device="cuda")
         so = torch.empty((w.h_q, w.k_slash), dtype=torch.int32, device="cuda")
         S.vs_index_build(q, k, inp["positions"], cfg, vi, so, ws)
     S.dca_sparse_prefill(q, k, v, inp["positions"], cfg, out, ws, v_idx=vi, s_off=so, lse_out=lse,
-                         cover_pairs=pairs)
+                         cover_pairs=pairs, attended_pairs=att)
     torch.cuda.synchronize()
     res = dict(w=w, inp=inp, cfg=cfg, exact=bool(exact), out=host_u16(out), lse=lse.cpu().numpy(), pairs=int(pairs.item()),
+               attended=int(att.item()),
                v_idx=None if vi is None else vi.cpu().numpy(), s_off=None if so is None else so.cpu().numpy())
-    del q, k, v, ws, out, lse, pairs, vi, so
+    del q, k, v, ws, out, lse, pairs, att, vi, so
     torch.cuda.empty_cache()
     _cache[key] = res
     return res
 
 
-def sampled_heads(h_q: int):
-    return [0, h_q - 1]
+def index_heads(r):
+    """Every head; the exact-diagonal reading reuses the same index build, so one head per
+    KV group there."""
+    return group_heads(r["w"]) if r["exact"] else list(range(r["w"].h_q))
+
+
+def block_heads(r):
+    """Heads whose sampled blocks meet the oracle: every head of the 128K chunk (block
+    cover), one per KV group plus the last head elsewhere."""
+    w = r["w"]
+    if w.name == "7b_chunk_at_98304_of_128k" and not r["exact"]:
+        return list(range(w.h_q))
+    return group_heads(w)
+
+
+def group_heads(w):
+    G = w.h_q // w.h_kv
+    return sorted(set(range(0, w.h_q, G)) | {w.h_q - 1})
 
 
 def check_index(r):
-    heads = sampled_heads(r["w"].h_q)
-    log(f"oracle index of heads {heads}")
-    v_ref, s_ref, _ = O.vs_index(r["inp"]["q"], r["inp"]["k"], r["inp"]["p0"], oracle_cfg(r["cfg"]), heads=heads)
+    heads = index_heads(r)
+    log(f"oracle index of {len(heads)} heads")
+    v_ref, s_ref, gaps = O.vs_index(r["inp"]["q"], r["inp"]["k"], r["inp"]["p0"], oracle_cfg(r["cfg"]), heads=heads)
     for h in heads:
         assert np.array_equal(r["v_idx"][h], v_ref[h]), f"vertical index of head {h} differs"
         assert np.array_equal(r["s_off"][h], s_ref[h]), f"slash index of head {h} differs"
+    # the selection is decided by gaps far above the scoring error (the cut rule)
+    for h, gv, gs in gaps:
+        for g in (gv, gs):
+            assert g is None or g >= 1e-9, f"head {h}: relative gap {g} at the cut"
 
 
-def check_cover_pairs(r):
+def check_pair_counts(r):
     cfg = r["cfg"]
-    log("oracle cover counts of every head")
-    fb, _ = O.flop_counts(cfg.n_q, cfg.h_q, 128, r["inp"]["p0"], cfg.n_k, r["v_idx"], r["s_off"])
+    log("oracle cover and attended counts of every head")
+    fb, fa = O.flop_counts(cfg.n_q, cfg.h_q, 128, r["inp"]["p0"], cfg.n_k, r["v_idx"], r["s_off"], exact=r["exact"])
     assert 4 * 128 * r["pairs"] == fb, f"F_blocks {4 * 128 * r['pairs']} != oracle {fb}"
+    assert 4 * 128 * r["attended"] == fa, f"F_attended {4 * 128 * r['attended']} != oracle {fa}"
 
 
 def check_sampled_blocks(r):
     w, inp, cfg = r["w"], r["inp"], r["cfg"]
-    heads = sampled_heads(w.h_q)
+    heads = block_heads(r)
     pairs = [(h, b) for (h, b) in W.sample_blocks(cfg.n_q, w.h_q, seed=0) if h in heads]
     log(f"oracle attention of {len(pairs)} (head, block) pairs")
     ocfg = oracle_cfg(cfg)
@@ -139,6 +166,6 @@ def test_fullsize(name, chunk, exact):
     r = gpu_call(name, chunk, exact)
     if r["w"].sparse:
         check_index(r)
-    check_cover_pairs(r)
+    check_pair_counts(r)
     check_sampled_blocks(r)
     check_all_rows_bounded(r)

@@ -395,6 +395,64 @@ def test_flop_counts_dense_closed_form():
     assert fa == 4 * 128 * 28 * (32768 * 32769 // 2)
 
 
+def _brute_attended(n_q, p0, n_k, v_idx, s_off, exact):
+    """sum over heads and rows of |A_h(i)|, from the brute-force module's own key sets."""
+    tot = 0
+    for h in range(len(v_idx)):
+        for i in range(n_q):
+            p = p0 + i
+            if exact:
+                keys = brute._exact_keys(p, v_idx[h].tolist(), s_off[h].tolist())
+            else:
+                i0 = p0 + (i // 64) * 64
+                keys = [j for j in brute._cover(i0, n_k, v_idx[h].tolist(), s_off[h].tolist()) if j <= p]
+            tot += len(keys)
+    return tot
+
+
+@pytest.mark.parametrize("exact", [False, True])
+def test_attended_pairs_match_brute_enumeration(exact):
+    """F_attended of a sparse call (block cover and exact diagonals) equals 4 d times the
+    number of (row, key) pairs the brute force attends, on random patterns with padding,
+    duplicates, out-of-range entries and partial last blocks."""
+    rng = np.random.default_rng(17 + exact)
+    for trial in range(8):
+        h_q = 2
+        p0 = int(rng.integers(0, 6)) * 64
+        n_q = int(rng.integers(1, 260))
+        n_k = p0 + n_q
+        v_idx = np.sort(rng.integers(-1, n_k + 3, size=(h_q, int(rng.integers(0, 25)))), axis=1).astype(np.int32)
+        s_off = np.sort(rng.integers(-1, n_k + 3, size=(h_q, int(rng.integers(0, 20)))), axis=1).astype(np.int32)
+        fb, fa = O.flop_counts(n_q, h_q, 8, p0, n_k, v_idx, s_off, exact=exact)
+        assert fa == 4 * 8 * _brute_attended(n_q, p0, n_k, v_idx, s_off, exact)
+        fb_block, _ = O.flop_counts(n_q, h_q, 8, p0, n_k, v_idx, s_off)
+        assert fb == fb_block     # the computed tiles are the same in both readings
+
+
+def test_attended_pairs_closed_forms():
+    n_q, p0, h_q, d = 200, 128, 3, 128
+    n_k = p0 + n_q
+    none = np.full((h_q, 4), -1, dtype=np.int32)
+    # offset 0 only, no columns: every row attends only itself (exact), its block's
+    # causal prefix (block cover)
+    _, fa = O.flop_counts(n_q, h_q, d, p0, n_k, none, none, exact=True)
+    assert fa == 4 * d * h_q * n_q
+    rows = [64, 64, 64, 8]
+    _, fa = O.flop_counts(n_q, h_q, d, p0, n_k, none, none)
+    assert fa == 4 * d * h_q * sum(r * (r + 1) // 2 for r in rows)
+    # every offset selected: both readings attend the dense causal set
+    all_off = np.tile(np.arange(n_k, dtype=np.int32), (h_q, 1))
+    _, fa_dense = O.flop_counts(n_q, h_q, d, p0, n_k)
+    assert fa_dense == 4 * d * h_q * sum(p + 1 for p in range(p0, n_k))
+    for exact in (False, True):
+        _, fa = O.flop_counts(n_q, h_q, d, p0, n_k, none, all_off, exact=exact)
+        assert fa == fa_dense
+    # every column selected, offset 0 only: exact attends all j <= p (columns) once
+    all_col = np.tile(np.arange(n_k, dtype=np.int32), (h_q, 1))
+    _, fa = O.flop_counts(n_q, h_q, d, p0, n_k, all_col, none, exact=True)
+    assert fa == fa_dense
+
+
 # ---------------------------------------------------------------- generator
 def test_bf16_rounding_matches_torch():
     x = np.random.default_rng(16).standard_normal(100000).astype(np.float32) * 7
