@@ -72,6 +72,7 @@ extern "C" {
 #define DCA_EUNSUPPORTED (-2)  /* head_dim != 128, dca_chunk % 64, p0 % 64, W > S, ... */
 #define DCA_EWORKSPACE   (-3)  /* workspace missing or smaller than dca_workspace_size */
 #define DCA_EHIP         (-4)  /* a HIP launch or runtime call failed */
+#define DCA_ESCRATCH     (-5)  /* dca_sparse_prefill_noalloc: the call needs more than its static scratch */
 
 typedef uint16_t dca_bf16;     /* raw bfloat16 bits */
 
@@ -161,6 +162,22 @@ DCA_API int vs_index_build(const dca_bf16 *q, const dca_bf16 *k, const int32_t *
  * natural-log LSE of every row.  bf16 inputs, fp32 accumulation. */
 DCA_API int dca_sparse_prefill(const dca_bf16 *q, const dca_bf16 *k, const dca_bf16 *v,
                        const int32_t *positions, const dca_cfg *cfg, dca_bf16 *out);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation):
+ * dca_sparse_prefill with the scratch taken from a static device array of
+ * DCA_STATIC_SCRATCH_BYTES per GPU that the library owns (each GPU the
+ * library runs on keeps its copy until the process ends) instead of
+ * cfg->workspace, which is ignored.  Same arguments, definition and outputs
+ * (bitwise equal to dca_sparse_prefill's).  Calls that need more scratch
+ * than the array holds (dca_workspace_size > DCA_STATIC_SCRATCH_BYTES) return
+ * DCA_ESCRATCH before anything is enqueued.  The call allocates nothing.
+ * Every call on one GPU shares that GPU's array and leaves its contents
+ * behind: calls that overlap in time on one GPU (different streams, threads
+ * or processes sharing the library) race, so the caller orders them. */
+#define DCA_STATIC_SCRATCH_BYTES (256u << 20)
+DCA_API int dca_sparse_prefill_noalloc(const dca_bf16 *q, const dca_bf16 *k, const dca_bf16 *v,
+                                       const int32_t *positions, const dca_cfg *cfg, dca_bf16 *out);
 
 /* ---- Generation step (decode) ------------------------------------------
  * After a prefill, each generated token attends the whole key cache with the

@@ -46,6 +46,8 @@ DCA_EINVAL = -1
 DCA_EUNSUPPORTED = -2
 DCA_EWORKSPACE = -3
 DCA_EHIP = -4
+DCA_ESCRATCH = -5
+DCA_STATIC_SCRATCH_BYTES = 256 << 20
 DCA_STAGE_COUNT = 4
 STAGES = ("rotate", "plan", "attention", "lse_merge")
 
@@ -174,6 +176,9 @@ def lib() -> ctypes.CDLL:
         L.dca_sparse_prefill.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                          ctypes.POINTER(dca_cfg), ctypes.c_void_p]
         L.dca_sparse_prefill.restype = ctypes.c_int
+        L.dca_sparse_prefill_noalloc.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                                 ctypes.POINTER(dca_cfg), ctypes.c_void_p]
+        L.dca_sparse_prefill_noalloc.restype = ctypes.c_int
         L.dca_key_cache_append.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(dca_cfg),
                                            ctypes.POINTER(dca_key_cache)]
         L.dca_key_cache_append.restype = ctypes.c_int
@@ -380,6 +385,27 @@ def dca_sparse_prefill(q, k, v, positions, cfg: Config, out, workspace, v_idx=No
                                   pos_p, ctypes.byref(c), _dev(out, "out", qb, "bf16"))
     if rc != DCA_OK:
         raise DcaError(rc, "dca_sparse_prefill")
+
+
+def dca_sparse_prefill_noalloc(q, k, v, positions, cfg: Config, out, v_idx=None, s_off=None, lse_out=None,
+                               cover_pairs=None, stream=None, attended_pairs=None, status=None) -> None:
+    """dca_sparse_prefill with the library's static per-GPU scratch instead of a workspace
+    (no allocation; calls that overlap in time on one GPU race)."""
+    st = _stream(stream)
+    pos, pos_p = _positions(positions, cfg.n_q, st)
+    c = cfg.to_c(workspace=None, workspace_bytes=0, stream=st,
+                 v_idx=_dev(v_idx, "v_idx", cfg.h_q * cfg.vs_k_vertical * 4, "int32"),
+                 s_off=_dev(s_off, "s_off", cfg.h_q * cfg.vs_k_slash * 4, "int32"),
+                 lse_out=_dev(lse_out, "lse_out", cfg.h_q * cfg.n_q * 4, "float32"),
+                 cover_pairs=_dev(cover_pairs, "cover_pairs", 8, "int64"),
+                 attended_pairs=_dev(attended_pairs, "attended_pairs", 8, "int64"),
+                 status=_dev(status, "status", 4, "int32"))
+    qb, kb = cfg.n_q * cfg.h_q * cfg.head_dim * 2, cfg.n_k * cfg.h_kv * cfg.head_dim * 2
+    rc = lib().dca_sparse_prefill_noalloc(_dev(q, "q", qb, "bf16"), _dev(k, "k", kb, "bf16"),
+                                          _dev(v, "v", kb, "bf16"), pos_p, ctypes.byref(c),
+                                          _dev(out, "out", qb, "bf16"))
+    if rc != DCA_OK:
+        raise DcaError(rc, "dca_sparse_prefill_noalloc")
 
 
 def config_for(w, chunk: int = 0, **overrides) -> Config:

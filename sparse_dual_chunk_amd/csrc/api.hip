@@ -3,6 +3,7 @@
 #include <cmath>
 #include <algorithm>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/dcasparse.h"
 #include "entry.h"
@@ -482,6 +483,54 @@ int dca_sparse_prefill(const dca_bf16* q, const dca_bf16* k, const dca_bf16* v, 
   return dca::prefill_impl(q, k, nullptr, v, positions, cfg, out);
 }
 
+}  // extern "C"
+
+// Scratch of the allocation-free prefill: one array per GPU (each device that
+// runs the library holds its own copy until the process ends).  Host code never
+// passes the array's name to a kernel: its device address is taken once per
+// device with hipGetSymbolAddress and kept below.
+static __device__ __align__(256) unsigned char scratch[DCA_STATIC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[MAX_DEVICES] = {};
+
+// device address of the current device's scratch array
+int static_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return DCA_EHIP;
+  if (dev < 0 || dev >= MAX_DEVICES) return DCA_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return DCA_EHIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return DCA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dca_sparse_prefill_noalloc(const dca_bf16* q, const dca_bf16* k, const dca_bf16* v, const int32_t* positions,
+                               const dca_cfg* cfg, dca_bf16* out) {
+  if (!cfg || !k || !positions) return DCA_EINVAL;
+  int rc = validate(cfg);
+  if (rc != DCA_OK) return rc;
+  if (make_layout(cfg).prefill_bytes > (size_t)DCA_STATIC_SCRATCH_BYTES) return DCA_ESCRATCH;
+  void* ws = nullptr;
+  rc = static_scratch(&ws);
+  if (rc != DCA_OK) return rc;
+  dca_cfg c = *cfg;
+  c.workspace = ws;
+  c.workspace_bytes = DCA_STATIC_SCRATCH_BYTES;
+  return dca::prefill_impl(q, k, nullptr, v, positions, &c, out);
+}
+
 int dca_sparse_prefill_cached(const dca_bf16* q, const dca_key_cache* cache, const dca_bf16* v,
                               const int32_t* positions, const dca_cfg* cfg, dca_bf16* out) {
   if (!cache || !positions) return DCA_EINVAL;
@@ -623,6 +672,7 @@ const char* dca_strerror(int code) {
     case DCA_EUNSUPPORTED: return "unsupported configuration (head_dim, chunk, window, alignment or size)";
     case DCA_EWORKSPACE: return "workspace missing, misaligned or smaller than dca_workspace_size";
     case DCA_EHIP: return "HIP launch or runtime error";
+    case DCA_ESCRATCH: return "the call needs more scratch than the allocation-free entry point holds";
     default: return "unknown error code";
   }
 }

@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
                           "dca_sparse_prefill_cached", "dca_decode_workspace_size", "dca_decode", "dca_strerror",
                           "dca_chunk_cost_default", "dca_chunk_schedule", "dca_prefill_sequence_workspace_size",
                           "dca_prefill_sequence", "moe_workspace_size", "moe_forward",
-                          "moe_pack_weights", "dca_paged_append", "dca_decode_paged"}
+                          "moe_pack_weights", "dca_paged_append", "dca_decode_paged", "dca_sparse_prefill_noalloc"}
     out = subprocess.run(["nm", "-D", "--defined-only", S.LIB_PATH], capture_output=True, text=True).stdout
     exported = {l.split()[-1] for l in out.splitlines() if l.strip()}
     for n in names:
@@ -146,6 +146,20 @@ def test_prefill_rejects_missing_positions_and_misaligned_chunks():
     with pytest.raises(S.DcaError) as ei:
         _call_prefill(_cfg(n_k=500))          # p0 = 244
     assert ei.value.code == S.DCA_EUNSUPPORTED
+
+
+def test_noalloc_prefill_rejects_calls_beyond_its_static_scratch():
+    """The allocation-free entry point checks the call's scratch need against its static
+    array on the host, before any HIP call: a call needing more returns DCA_ESCRATCH."""
+    big = _cfg(n_q=32768, n_k=32768 * 4, h_q=28, h_kv=4, dca_chunk=8192, dca_local=1024)
+    assert S.dca_workspace_size(big) > S.DCA_STATIC_SCRATCH_BYTES
+    c = big.to_c(workspace=None, workspace_bytes=0)
+    rc = S.lib().dca_sparse_prefill_noalloc(0x1000, 0x1000, 0x1000, 0x1000, ctypes.byref(c), 0x1000)
+    assert rc == S.DCA_ESCRATCH
+    # missing positions or keys: rejected like the workspace entry point
+    small = _cfg().to_c(workspace=None, workspace_bytes=0)
+    assert S.lib().dca_sparse_prefill_noalloc(0x1000, 0x1000, 0x1000, None, ctypes.byref(small), 0x1000) == S.DCA_EINVAL
+    assert S.lib().dca_sparse_prefill_noalloc(0x1000, None, 0x1000, 0x1000, ctypes.byref(small), 0x1000) == S.DCA_EINVAL
 
 
 def test_prefill_rejects_small_or_missing_workspace():
