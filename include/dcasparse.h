@@ -269,6 +269,23 @@ DCA_API int dca_paged_append(const dca_bf16 *k, const dca_bf16 *v, int32_t j0, i
  * keys and values the outputs equal dca_decode's bit for bit. */
 DCA_API int dca_decode_paged(const dca_bf16 *q, const dca_paged_kv *cache, const dca_cfg *cfg, dca_bf16 *out);
 
+/* Workspace bytes of dca_sparse_prefill_paged for this configuration:
+ * dca_workspace_size's plus room for the sequence's values gathered from
+ * the pool.  Pure host computation. */
+DCA_API int dca_paged_prefill_workspace_size(const dca_cfg *cfg, size_t *bytes);
+
+/* dca_sparse_prefill with keys and values 0 .. n_k-1 of a sequence taken
+ * from a paged pool through its page table (dca_paged_append put them
+ * there, the chunk's own keys included; n_k <= n_table * page_keys).  Same
+ * definition and outputs as dca_sparse_prefill_cached: with the same keys
+ * and values the outputs are bitwise equal.  The call first copies the
+ * sequence's rotated keys, values and flag words from their pages into the
+ * workspace (dca_paged_prefill_workspace_size); page entries outside
+ * [0, n_pages) are clamped (that key range then holds unspecified data,
+ * never an out-of-bounds access). */
+DCA_API int dca_sparse_prefill_paged(const dca_bf16 *q, const dca_paged_kv *cache, const int32_t *positions,
+                                     const dca_cfg *cfg, dca_bf16 *out);
+
 /* ---- Whole-sequence prefill ----------------------------------------------
  * The pages' chunked prefill runs a long prompt chunk by chunk: chunk c holds
  * query rows [b_c, b_{c+1}) and attends the prefix [0, b_{c+1}).  Dynamic
@@ -348,6 +365,23 @@ DCA_API int dca_prefill_sequence_workspace_size(const dca_cfg *cfg, const dca_se
 DCA_API int dca_prefill_sequence(const dca_bf16 *q, const dca_bf16 *k, const dca_bf16 *v,
                                  const dca_sequence_plan *plan, const dca_cfg *cfg, const dca_key_cache *cache,
                                  dca_bf16 *out);
+
+/* Workspace bytes of dca_prefill_sequence_paged (as
+ * dca_prefill_sequence_workspace_size, with the paged prefill's chunk
+ * workspace).  Pure host computation. */
+DCA_API int dca_prefill_sequence_paged_workspace_size(const dca_cfg *cfg, const dca_sequence_plan *plan,
+                                                      size_t *bytes);
+
+/* dca_prefill_sequence over a paged pool: each chunk's keys and values are
+ * appended into their pages (dca_paged_append) and its attention reads them
+ * back through the page table (dca_sparse_prefill_paged), so the pool a
+ * generation step reads (dca_decode_paged) is filled by the prefill itself.
+ * Requires n <= n_table * page_keys.  Same rules, schedule and streams as
+ * dca_prefill_sequence; the outputs are bitwise those of the contiguous
+ * driver. */
+DCA_API int dca_prefill_sequence_paged(const dca_bf16 *q, const dca_bf16 *k, const dca_bf16 *v,
+                                       const dca_sequence_plan *plan, const dca_cfg *cfg, const dca_paged_kv *cache,
+                                       dca_bf16 *out);
 
 /* Static message for an error code; never NULL. */
 DCA_API const char *dca_strerror(int code);

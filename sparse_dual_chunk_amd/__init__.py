@@ -209,6 +209,19 @@ def lib() -> ctypes.CDLL:
                                            ctypes.POINTER(dca_sequence_plan), ctypes.POINTER(dca_cfg),
                                            ctypes.POINTER(dca_key_cache), ctypes.c_void_p]
         L.dca_prefill_sequence.restype = ctypes.c_int
+        L.dca_paged_prefill_workspace_size.argtypes = [ctypes.POINTER(dca_cfg), ctypes.POINTER(ctypes.c_size_t)]
+        L.dca_paged_prefill_workspace_size.restype = ctypes.c_int
+        L.dca_sparse_prefill_paged.argtypes = [ctypes.c_void_p, ctypes.POINTER(dca_paged_kv), ctypes.c_void_p,
+                                               ctypes.POINTER(dca_cfg), ctypes.c_void_p]
+        L.dca_sparse_prefill_paged.restype = ctypes.c_int
+        L.dca_prefill_sequence_paged_workspace_size.argtypes = [ctypes.POINTER(dca_cfg),
+                                                                ctypes.POINTER(dca_sequence_plan),
+                                                                ctypes.POINTER(ctypes.c_size_t)]
+        L.dca_prefill_sequence_paged_workspace_size.restype = ctypes.c_int
+        L.dca_prefill_sequence_paged.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                                 ctypes.POINTER(dca_sequence_plan), ctypes.POINTER(dca_cfg),
+                                                 ctypes.POINTER(dca_paged_kv), ctypes.c_void_p]
+        L.dca_prefill_sequence_paged.restype = ctypes.c_int
         L.moe_workspace_size.argtypes = [ctypes.POINTER(moe_cfg), ctypes.POINTER(ctypes.c_size_t)]
         L.moe_workspace_size.restype = ctypes.c_int
         L.moe_pack_weights.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(moe_cfg), ctypes.c_void_p,
@@ -574,6 +587,36 @@ def dca_decode_paged(q, cache: PagedKV, cfg: Config, out, workspace, lse_out=Non
         raise DcaError(rc, "dca_decode_paged")
 
 
+def dca_paged_prefill_workspace_size(cfg: Config) -> int:
+    c = cfg.to_c()
+    n = ctypes.c_size_t(0)
+    rc = lib().dca_paged_prefill_workspace_size(ctypes.byref(c), ctypes.byref(n))
+    if rc != DCA_OK:
+        raise DcaError(rc, "dca_paged_prefill_workspace_size")
+    return int(n.value)
+
+
+def dca_sparse_prefill_paged(q, cache: PagedKV, positions, cfg: Config, out, workspace, v_idx=None, s_off=None,
+                             lse_out=None, cover_pairs=None, stream=None, attended_pairs=None, status=None) -> None:
+    """dca_sparse_prefill with keys and values 0 .. cfg.n_k - 1 of a sequence in a paged pool."""
+    st = _stream(stream)
+    pos, pos_p = _positions(positions, cfg.n_q, st)
+    c = cfg.to_c(**_ws(workspace), stream=st,
+                 v_idx=_dev(v_idx, "v_idx", cfg.h_q * cfg.vs_k_vertical * 4, "int32"),
+                 s_off=_dev(s_off, "s_off", cfg.h_q * cfg.vs_k_slash * 4, "int32"),
+                 lse_out=_dev(lse_out, "lse_out", cfg.h_q * cfg.n_q * 4, "float32"),
+                 cover_pairs=_dev(cover_pairs, "cover_pairs", 8, "int64"),
+                 attended_pairs=_dev(attended_pairs, "attended_pairs", 8, "int64"),
+                 status=_dev(status, "status", 4, "int32"))
+    _check_paged(cache, cfg)
+    kc = cache.to_c()
+    qb = cfg.n_q * cfg.h_q * cfg.head_dim * 2
+    rc = lib().dca_sparse_prefill_paged(_dev(q, "q", qb, "bf16"), ctypes.byref(kc), pos_p, ctypes.byref(c),
+                                        _dev(out, "out", qb, "bf16"))
+    if rc != DCA_OK:
+        raise DcaError(rc, "dca_sparse_prefill_paged")
+
+
 # ---------------------------------------------------------------- whole-prompt chunked prefill
 def dca_chunk_cost_default(cfg: Config, sparse: bool) -> dca_chunk_cost:
     """The library's MI355X cost coefficients (microseconds) for cfg's heads and budgets."""
@@ -648,6 +691,34 @@ def dca_prefill_sequence(q, k, v, bounds, cfg: Config, cache: KeyCache, out, wor
                                     ctypes.byref(p), ctypes.byref(c), ctypes.byref(kc), _dev(out, "out", qb, "bf16"))
     if rc != DCA_OK:
         raise DcaError(rc, "dca_prefill_sequence")
+
+
+def dca_prefill_sequence_paged_workspace_size(cfg: Config, bounds, sparse: bool, overlap: bool) -> int:
+    """Workspace bytes of dca_prefill_sequence_paged (overlap: an index stream will be passed)."""
+    p, _keep = _seq_plan(bounds, sparse, index_stream=1 if overlap else None)
+    c = cfg.to_c()
+    n = ctypes.c_size_t(0)
+    rc = lib().dca_prefill_sequence_paged_workspace_size(ctypes.byref(c), ctypes.byref(p), ctypes.byref(n))
+    if rc != DCA_OK:
+        raise DcaError(rc, "dca_prefill_sequence_paged_workspace_size")
+    return int(n.value)
+
+
+def dca_prefill_sequence_paged(q, k, v, bounds, cfg: Config, cache: PagedKV, out, workspace, sparse: bool = True,
+                               index_stream=None, lse_out=None, cover_pairs=None, chunk_events=None,
+                               index_events=None, stream=None) -> None:
+    """dca_prefill_sequence whose chunks append into and read from a paged pool."""
+    p, _keep = _seq_plan(bounds, sparse, index_stream, chunk_events, index_events, cover_pairs)
+    c = cfg.to_c(**_ws(workspace), stream=_stream(stream),
+                 lse_out=_dev(lse_out, "lse_out", cfg.h_q * cfg.n_q * 4, "float32"))
+    _check_paged(cache, cfg)
+    kc = cache.to_c()
+    qb, kb = cfg.n_q * cfg.h_q * cfg.head_dim * 2, cfg.n_k * cfg.h_kv * cfg.head_dim * 2
+    rc = lib().dca_prefill_sequence_paged(_dev(q, "q", qb, "bf16"), _dev(k, "k", kb, "bf16"),
+                                          _dev(v, "v", kb, "bf16"), ctypes.byref(p), ctypes.byref(c),
+                                          ctypes.byref(kc), _dev(out, "out", qb, "bf16"))
+    if rc != DCA_OK:
+        raise DcaError(rc, "dca_prefill_sequence_paged")
 
 
 # ---------------------------------------------------------------- fused MoE layer (include/moe.h)

@@ -11,7 +11,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libdcasparse.so")
-SOURCES = ["api.hip", "rope.hip", "attn.hip", "decode.hip", "vs_score.hip", "select.hip", "sequence.hip", "moe.hip"]
+SOURCES = ["api.hip", "rope.hip", "attn.hip", "attn_pipe.hip", "decode.hip", "vs_score.hip", "select.hip", "sequence.hip", "moe.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -22,18 +22,18 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC] + FLAGS + ["-o", tmp] + srcs
+    tmp = out + ".tmp"
+    cmd = [HIPCC] + FLAGS + [f"-D{d}" for d in defines] + ["-o", tmp] + srcs
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
         raise RuntimeError("hipcc failed building libdcasparse.so")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

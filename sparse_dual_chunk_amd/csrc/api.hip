@@ -17,6 +17,12 @@ hipError_t launch_rotate_keys(const uint16_t* k, uint16_t* khi, uint16_t* klo, u
                               bool clear_all, hipStream_t stream);
 hipError_t launch_hn_next(const uint32_t* kbits, uint8_t* hn, int n_pad, int h_kv, int kbits_words,
                           hipStream_t stream);
+hipError_t launch_paged_gather(const uint16_t* khi_p, const uint16_t* klo_p, const uint16_t* v_p,
+                               const uint32_t* flags_p, const int32_t* ptab, int page_keys, int n_pages, int n_table,
+                               int n_k, int h_kv, int kbits_words, uint16_t* khi, uint16_t* klo, uint16_t* vd,
+                               uint32_t* kbits, hipStream_t stream);
+hipError_t launch_hn_list(const uint32_t* kbits, int kbits_words, int n_k, int h_kv, int32_t* hnl, int32_t* hnl_n,
+                          hipStream_t stream);
 hipError_t launch_rotate_queries(const uint16_t* q, uint16_t* qhi, uint16_t* qlo, const double* inv_freq,
                                  int n_q, int h_q, int p0, int S, int W, float qscale, hipStream_t stream);
 hipError_t launch_attn(const AttnArgs& A, hipStream_t stream);
@@ -72,8 +78,10 @@ struct Layout {
   // shared
   Region freqs, flag;
   // prefill
+  Region hnl, hnl_n, ev, npe;
   Region khi, klo, kbits, hn, qhi, qlo, iv, iv_pre, n_iv, cov, ext, n_ext, tiles, n_tiles, t_first, part_o, part_lse;
   Region dbits, vbits;
+  Region vg;             // values gathered from a paged pool
   int dbits_words = 0, vbits_words = 0;
   // index
   Region qs, part_ms, lse, vert, slash, edge, logits, trig, hist, prefix, krem, bcount;
@@ -111,7 +119,7 @@ int validate(const dca_cfg* c) {
   return DCA_OK;
 }
 
-Layout make_layout(const dca_cfg* c) {
+Layout make_layout(const dca_cfg* c, bool paged = false) {
   Layout L;
   const int n_q = c->n_q, n_k = c->n_k, h_q = c->h_q, h_kv = c->h_kv;
   const int p_last = n_k - 1;
@@ -144,6 +152,8 @@ Layout make_layout(const dca_cfg* c) {
   place(L.kbits, cur, (size_t)h_kv * L.kbits_words * 4);
   L.hn_pad = (n_k + 128 + 3) / 4 * 4;   // runs may start up to 95 keys past n_k - 1
   place(L.hn, cur, (size_t)h_kv * L.hn_pad);
+  place(L.hnl, cur, (size_t)h_kv * HN_CAP * 4);
+  place(L.hnl_n, cur, (size_t)h_kv * 4);
   place(L.qhi, cur, (size_t)3 * n_q * h_q * D * 2);
   place(L.qlo, cur, (size_t)3 * n_q * h_q * D * 2);
   place(L.iv, cur, (size_t)h_q * (c->vs_k_slash + 1) * 2 * 4);
@@ -158,6 +168,8 @@ Layout make_layout(const dca_cfg* c) {
   place(L.tiles, cur, (size_t)h_q * L.tile_stride * 16);
   place(L.n_tiles, cur, (size_t)h_q * 4);
   place(L.t_first, cur, (size_t)h_q * L.nb * 4);
+  place(L.ev, cur, (size_t)h_q * L.nb * EV_REC * 4);
+  place(L.npe, cur, (size_t)h_q * 4);
   if (c->slash_exact) {
     // windows of up to 8 words start between bit 34 and bit p_last + 160
     L.dbits_words = (p_last + 160) / 32 + 9;
@@ -170,6 +182,7 @@ Layout make_layout(const dca_cfg* c) {
     place(L.part_o, cur, (size_t)L.split * n_q * h_q * D * 2);
     place(L.part_lse, cur, (size_t)L.split * h_q * n_q * 4);
   }
+  if (paged) place(L.vg, cur, (size_t)n_k * h_kv * D * 2);
   L.prefill_bytes = cur;
   // --- index (reuses the space after the frequencies)
   cur = base;
@@ -353,24 +366,46 @@ int index_impl(const dca_bf16* q, const dca_bf16* k, const int32_t* positions, c
 
 }  // namespace dca
 
+namespace {
+int paged_check(const dca_paged_kv* c, int h_kv, int head_dim);
+}  // namespace
+
 namespace dca {
 
-// The prefill of one chunk.  Keys come either raw (k: rotated here into the
-// workspace) or from a rotated key cache (cache: rotated when they entered it).
+int paged_valid(const dca_paged_kv* cache, int h_kv, int head_dim) { return paged_check(cache, h_kv, head_dim); }
+
+int paged_prefill_bytes(const dca_cfg* cfg, size_t* bytes) {
+  if (!bytes) return DCA_EINVAL;
+  const int rc = validate(cfg);
+  if (rc != DCA_OK) return rc;
+  const Layout L = make_layout(cfg, true);
+  *bytes = L.prefill_bytes > L.index_bytes ? L.prefill_bytes : L.index_bytes;
+  return DCA_OK;
+}
+
+// The prefill of one chunk.  Keys come raw (k: rotated here into the
+// workspace), from a rotated key cache (cache: rotated when they entered it)
+// or from a paged pool (paged: its keys, values and flags are gathered into
+// the workspace first, a coalesced copy of the sequence's pages).
 // positions == nullptr: implied (p0 + i), not checked.
-int prefill_impl(const dca_bf16* q, const dca_bf16* k, const dca_key_cache* cache, const dca_bf16* v,
-                 const int32_t* positions, const dca_cfg* cfg, dca_bf16* out) {
+int prefill_impl(const dca_bf16* q, const dca_bf16* k, const dca_key_cache* cache, const dca_paged_kv* paged,
+                 const dca_bf16* v, const int32_t* positions, const dca_cfg* cfg, dca_bf16* out) {
   int rc = validate(cfg);
   if (rc != DCA_OK) return rc;
-  if (!q || !(k || cache) || !v || !out) return DCA_EINVAL;
+  if (!q || !(k || cache || paged) || !(v || paged) || !out) return DCA_EINVAL;
   if (cache) {
     if (!cache->k_hi || !cache->k_lo || !cache->k_flags || cache->capacity < cfg->n_k) return DCA_EINVAL;
     if ((long long)cache->capacity * cfg->h_kv * cfg->head_dim * 2 >= (1LL << 32)) return DCA_EUNSUPPORTED;
   }
+  if (paged) {
+    rc = paged_check(paged, cfg->h_kv, cfg->head_dim);
+    if (rc != DCA_OK) return rc;
+    if ((long long)paged->n_table * paged->page_keys < cfg->n_k) return DCA_EINVAL;
+  }
   const bool sparse = cfg->v_idx || cfg->s_off;
   if (sparse && ((cfg->vs_k_vertical > 0 && !cfg->v_idx) || (cfg->vs_k_slash > 0 && !cfg->s_off)))
     return DCA_EINVAL;
-  const Layout L = make_layout(cfg);
+  const Layout L = make_layout(cfg, paged != nullptr);
   rc = check_workspace(cfg, L.prefill_bytes);
   if (rc != DCA_OK) return rc;
   hipStream_t st = (hipStream_t)cfg->stream;
@@ -390,9 +425,16 @@ int prefill_impl(const dca_bf16* q, const dca_bf16* k, const dca_key_cache* cach
   const uint16_t* klo = cache ? cache->k_lo : at<uint16_t>(cfg, L.klo);
   const uint32_t* kbits = cache ? cache->k_flags : at<uint32_t>(cfg, L.kbits);
   const int kbits_words = cache ? (cache->capacity + 31) / 32 : L.kbits_words;
-  // stage 0: chunk-local key rotation, query rotations of the three DCA modes
+  // stage 0: chunk-local key rotation (or the gather from the pages), query rotations of the three DCA modes
   record(cfg, 0, 0);
-  if (!cache) {
+  if (paged) {
+    if (launch_paged_gather(paged->k_hi, paged->k_lo, paged->v, paged->k_flags, paged->page_table,
+                            paged->page_keys, paged->n_pages, paged->n_table, n_k, h_kv, L.kbits_words,
+                            at<uint16_t>(cfg, L.khi), at<uint16_t>(cfg, L.klo), at<uint16_t>(cfg, L.vg),
+                            at<uint32_t>(cfg, L.kbits), st) != hipSuccess)
+      return DCA_EHIP;
+    v = at<uint16_t>(cfg, L.vg);
+  } else if (!cache) {
     float thr = cfg->precise_norm == 0.f ? 2.f * std::sqrt((float)D) : cfg->precise_norm;
     const float thr2 = thr < 0.f ? -1.f : thr * thr;
     if (launch_rotate_keys(k, at<uint16_t>(cfg, L.khi), at<uint16_t>(cfg, L.klo), at<uint32_t>(cfg, L.kbits),
@@ -401,6 +443,9 @@ int prefill_impl(const dca_bf16* q, const dca_bf16* k, const dca_key_cache* cach
       return DCA_EHIP;
   }
   if (launch_hn_next(kbits, at<uint8_t>(cfg, L.hn), L.hn_pad, h_kv, kbits_words, st) != hipSuccess)
+    return DCA_EHIP;
+  if (launch_hn_list(kbits, kbits_words, n_k, h_kv, at<int32_t>(cfg, L.hnl), at<int32_t>(cfg, L.hnl_n), st) !=
+      hipSuccess)
     return DCA_EHIP;
   // softmax scale sqrt(1/t)^2 / sqrt(d) and log2(e) (the kernel works in base 2)
   const float qscale = (float)(yarn_factor(cfg->yarn_s) / std::sqrt((double)D) * 1.4426950408889634);
@@ -428,6 +473,8 @@ int prefill_impl(const dca_bf16* q, const dca_bf16* k, const dca_key_cache* cach
     P.dbits_words = L.dbits_words; P.vbits_words = L.vbits_words;
     P.attended = (long long*)cfg->attended_pairs;
     P.bad = bad;
+    P.hnl = at<int32_t>(cfg, L.hnl); P.hnl_n = at<int32_t>(cfg, L.hnl_n);
+    P.ev = at<int32_t>(cfg, L.ev); P.npe = at<int32_t>(cfg, L.npe); P.S = cfg->dca_chunk;
     if (launch_plan(P, st) != hipSuccess) return DCA_EHIP;
   } else if (cfg->cover_pairs || cfg->attended_pairs) {
     // dense: every block covers its whole causal extent [0, i0 + rows); row i attends p_i + 1 keys
@@ -461,6 +508,8 @@ int prefill_impl(const dca_bf16* q, const dca_bf16* k, const dca_key_cache* cach
   A.vbits = A.exact ? at<uint32_t>(cfg, L.vbits) : nullptr;
   A.dbits_words = L.dbits_words; A.vbits_words = L.vbits_words;
   A.bad = bad;
+  A.hnl = at<int32_t>(cfg, L.hnl); A.hnl_n = at<int32_t>(cfg, L.hnl_n);
+  A.ev = sparse ? at<int32_t>(cfg, L.ev) : nullptr; A.npe = sparse ? at<int32_t>(cfg, L.npe) : nullptr;
   if (launch_attn(A, st) != hipSuccess) return DCA_EHIP;
   record(cfg, 2, 1);
   // stage 3: LSE merge of the split partials
@@ -480,7 +529,7 @@ extern "C" {
 int dca_sparse_prefill(const dca_bf16* q, const dca_bf16* k, const dca_bf16* v, const int32_t* positions,
                        const dca_cfg* cfg, dca_bf16* out) {
   if (!k || !positions) return DCA_EINVAL;
-  return dca::prefill_impl(q, k, nullptr, v, positions, cfg, out);
+  return dca::prefill_impl(q, k, nullptr, nullptr, v, positions, cfg, out);
 }
 
 }  // extern "C"
@@ -528,13 +577,21 @@ int dca_sparse_prefill_noalloc(const dca_bf16* q, const dca_bf16* k, const dca_b
   dca_cfg c = *cfg;
   c.workspace = ws;
   c.workspace_bytes = DCA_STATIC_SCRATCH_BYTES;
-  return dca::prefill_impl(q, k, nullptr, v, positions, &c, out);
+  return dca::prefill_impl(q, k, nullptr, nullptr, v, positions, &c, out);
 }
 
 int dca_sparse_prefill_cached(const dca_bf16* q, const dca_key_cache* cache, const dca_bf16* v,
                               const int32_t* positions, const dca_cfg* cfg, dca_bf16* out) {
   if (!cache || !positions) return DCA_EINVAL;
-  return dca::prefill_impl(q, nullptr, cache, v, positions, cfg, out);
+  return dca::prefill_impl(q, nullptr, cache, nullptr, v, positions, cfg, out);
+}
+
+int dca_paged_prefill_workspace_size(const dca_cfg* cfg, size_t* bytes) { return dca::paged_prefill_bytes(cfg, bytes); }
+
+int dca_sparse_prefill_paged(const dca_bf16* q, const dca_paged_kv* cache, const int32_t* positions, const dca_cfg* cfg,
+                             dca_bf16* out) {
+  if (!cache || !positions) return DCA_EINVAL;
+  return dca::prefill_impl(q, nullptr, nullptr, cache, nullptr, positions, cfg, out);
 }
 
 int dca_key_cache_append(const dca_bf16* k, int32_t j0, int32_t n, const dca_cfg* cfg, const dca_key_cache* cache) {

@@ -5,6 +5,17 @@
 
 namespace dca {
 
+// High-norm keys listed per KV head (the first HN_CAP, ascending) for the
+// attention walk's event lists; more than HN_CAP makes every tile an event.
+constexpr int HN_CAP = 64;
+// Per (head, query block) event record of the plan: [0], [1] the range tiles
+// (relative to the block's first) holding the first covered key of the
+// successive-chunk and intra-chunk DCA modes (-1: none), [2] the number n of
+// range tiles holding a high-norm key (-1: too many to list), [3, 3 + n)
+// those tiles, ascending.
+constexpr int EV_REC = 32;
+constexpr int EV_PREC = EV_REC - 3;
+
 struct AttnArgs {
   const uint16_t* qhi;      // [3 modes][n_q][h_q][128] rotated query * scale * log2(e), bf16 hi
   const uint16_t* qlo;      // same, lo residual
@@ -27,6 +38,10 @@ struct AttnArgs {
   int n_q, n_k, h_q, h_kv, p0, S, W, nb, tile_stride, ext_stride, split, dense, kbits_words, hn_pad;
   int exact, dbits_words, vbits_words;
   const int32_t* bad;       // device flag set by the positions check: write no output when nonzero (or null)
+  const int32_t* hnl;       // [h_kv][HN_CAP] the first high-norm keys of each KV head, ascending
+  const int32_t* hnl_n;     // [h_kv] how many high-norm keys the head has (may exceed HN_CAP)
+  const int32_t* ev;        // [h_q][nb][EV_REC] event records of the range walk (sparse calls)
+  const int32_t* npe;       // [h_q] first range tile holding an offset above 0 (sparse calls)
 };
 
 struct DecArgs {
@@ -92,6 +107,11 @@ struct PlanArgs {
   long long* cover_pairs;  // optional: sum of rows * |cover| over all (head, block)
   long long* attended;     // optional: sum over heads and rows of the attended (row, key) pairs
   const int32_t* bad;      // device flag set by the positions check: write no output when nonzero (or null)
+  const int32_t* hnl;      // [h_kv][HN_CAP] the first high-norm keys of each KV head, ascending
+  const int32_t* hnl_n;    // [h_kv] their number (may exceed HN_CAP)
+  int32_t* ev;             // [h_q][nb][EV_REC] event records of the attention walk
+  int32_t* npe;            // [h_q] first range tile holding an offset above 0
+  int S;                   // DCA chunk size
   uint32_t* dbits;         // exact diagonals (or null): [h_q][dbits_words], bit delta + 128
   uint32_t* vbits;         // exact diagonals (or null): [h_q][vbits_words], bit j + 128
   int h_q, h_kv, k_v, k_s, p_last, p0, n_q, nb, iv_stride, ext_stride, cov_words, tile_stride, kbits_words;

@@ -681,7 +681,14 @@ __global__ void __launch_bounds__(256) lse_merge_kernel(const uint16_t* __restri
   if (lse_out && dc == 0) lse_out[(long long)h * n_q + row] = (wsum > 0.f) ? m + __logf(wsum) : -INFINITY;
 }
 
+hipError_t launch_attn_pipe(const AttnArgs& A, hipStream_t stream);
+
+#ifndef DCA_ATTN_PIPE
+#define DCA_ATTN_PIPE 0
+#endif
+
 hipError_t launch_attn(const AttnArgs& A, hipStream_t stream) {
+  if (DCA_ATTN_PIPE && !A.exact) return launch_attn_pipe(A, stream);
   // every die runs split * (its block rows) * (heads per row) workgroups
   // dense calls: workgroups of two blocks (128 rows) when no pair can straddle
   // a DCA chunk boundary (the workgroup's rows must share one chunk), i.e. S

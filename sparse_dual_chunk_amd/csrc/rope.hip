@@ -8,7 +8,10 @@
 // the attention kernel adds the lo half only for tiles holding a key flagged as
 // high-norm (L2 norm above a threshold), whose logits would otherwise carry
 // bf16 rounding errors large enough to move the output (attention sinks).
+#include <algorithm>
+
 #include "common.h"
+#include "args.h"
 
 namespace dca {
 
@@ -201,6 +204,111 @@ hipError_t launch_hn_next(const uint32_t* kbits, uint8_t* hn, int n_pad, int h_k
   const long long n = (long long)h_kv * n_pad;
   hipLaunchKernelGGL(hn_next_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, kbits, hn, n_pad, h_kv,
                      kbits_words);
+  return hipGetLastError();
+}
+
+// Keys and values 0 .. n_k-1 of a sequence in a paged pool, gathered into the
+// contiguous rows the prefill attention reads ([n_k][h_kv][128] hi, lo and
+// value rows), and the sequence's high-norm flag words into a contiguous
+// [h_kv][kbits_words] bitmap (words past the page table read as zero).  Page
+// entries outside [0, n_pages) are clamped.  One 16-lane group per (key, KV
+// head) row, 16 bytes per lane of each tensor; the flag words follow in a
+// grid-stride loop.
+__global__ void __launch_bounds__(256) paged_gather_kernel(const uint16_t* __restrict__ khi_p,
+                                                           const uint16_t* __restrict__ klo_p,
+                                                           const uint16_t* __restrict__ v_p,
+                                                           const uint32_t* __restrict__ flags_p, PageMap pm,
+                                                           int n_table, int n_k, int h_kv, int kbits_words,
+                                                           uint16_t* __restrict__ khi, uint16_t* __restrict__ klo,
+                                                           uint16_t* __restrict__ vd, uint32_t* __restrict__ kbits) {
+  const long long row = (long long)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int lane16 = threadIdx.x & 15;
+  if (row < (long long)n_k * h_kv) {
+    const int j = (int)(row / h_kv), g = (int)(row % h_kv);
+    const int pg = min(max(pm.ptab[j / pm.page_keys], 0), pm.n_pages - 1);
+    const long long src = (((long long)pg * h_kv + g) * pm.page_keys + j % pm.page_keys) * D + 8 * lane16;
+    const long long dst = row * D + 8 * lane16;
+    *(uint4*)(khi + dst) = *(const uint4*)(khi_p + src);
+    *(uint4*)(klo + dst) = *(const uint4*)(klo_p + src);
+    *(uint4*)(vd + dst) = *(const uint4*)(v_p + src);
+  }
+  const int wpp = pm.page_keys / 32;   // flag words per page and head
+  const long long nwords = (long long)h_kv * kbits_words;
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < nwords;
+       i += (long long)gridDim.x * blockDim.x) {
+    const int g = (int)(i / kbits_words), w = (int)(i % kbits_words);
+    const int key0 = 32 * w;
+    const int lp = key0 / pm.page_keys;
+    uint32_t word = 0u;
+    if (lp < n_table) {
+      const int pg = min(max(pm.ptab[lp], 0), pm.n_pages - 1);
+      word = flags_p[((long long)pg * h_kv + g) * wpp + (key0 % pm.page_keys) / 32];
+    }
+    kbits[i] = word;
+  }
+}
+
+hipError_t launch_paged_gather(const uint16_t* khi_p, const uint16_t* klo_p, const uint16_t* v_p,
+                               const uint32_t* flags_p, const int32_t* ptab, int page_keys, int n_pages, int n_table,
+                               int n_k, int h_kv, int kbits_words, uint16_t* khi, uint16_t* klo, uint16_t* vd,
+                               uint32_t* kbits, hipStream_t stream) {
+  const long long rows = (long long)n_k * h_kv;
+  const int blocks = (int)std::max<long long>((rows + 15) / 16, 1);
+  const PageMap pm = {ptab, page_keys, n_pages};
+  hipLaunchKernelGGL(paged_gather_kernel, dim3(blocks), dim3(256), 0, stream, khi_p, klo_p, v_p, flags_p, pm,
+                     n_table, n_k, h_kv, kbits_words, khi, klo, vd, kbits);
+  return hipGetLastError();
+}
+
+// The first HN_CAP high-norm keys j < n_k of each KV head, ascending, and how
+// many there are in all (counting stops once it exceeds HN_CAP).  One
+// workgroup of 1024 threads per KV head: each round scans 1024 flag words,
+// places every word's keys after an exclusive prefix sum of the words' counts.
+__global__ void __launch_bounds__(1024) hn_list_kernel(const uint32_t* __restrict__ kbits, int kbits_words, int n_k,
+                                                       int32_t* __restrict__ hnl, int32_t* __restrict__ hnl_n) {
+  __shared__ int wave_tot[16];
+  __shared__ int base_s;
+  const int g = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const uint32_t* kb = kbits + (long long)g * kbits_words;
+  const int nw = (n_k + 31) / 32;
+  if (tid == 0) base_s = 0;
+  __syncthreads();
+  for (int w0 = 0; w0 < nw; w0 += 1024) {
+    const int w = w0 + tid;
+    uint32_t word = w < nw ? kb[w] : 0u;
+    if (w == nw - 1 && (n_k & 31)) word &= (1u << (n_k & 31)) - 1u;
+    const int c = __popc(word);
+    int incl = c;   // inclusive prefix within the wave
+    for (int d = 1; d < 64; d <<= 1) {
+      const int t = __shfl_up(incl, d);
+      if (lane >= d) incl += t;
+    }
+    if (lane == 63) wave_tot[wv] = incl;
+    __syncthreads();
+    int before = base_s;
+    for (int i = 0; i < wv; ++i) before += wave_tot[i];
+    int pos = before + incl - c;
+    while (word) {
+      if (pos < HN_CAP) hnl[g * HN_CAP + pos] = 32 * w + __builtin_ctz(word);
+      ++pos;
+      word &= word - 1u;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int t = base_s;
+      for (int i = 0; i < 16; ++i) t += wave_tot[i];
+      base_s = t;
+    }
+    __syncthreads();
+    if (base_s > HN_CAP) break;
+  }
+  if (tid == 0) hnl_n[g] = base_s;
+}
+
+hipError_t launch_hn_list(const uint32_t* kbits, int kbits_words, int n_k, int h_kv, int32_t* hnl, int32_t* hnl_n,
+                          hipStream_t stream) {
+  hipLaunchKernelGGL(hn_list_kernel, dim3(h_kv), dim3(1024), 0, stream, kbits, kbits_words, n_k, hnl, hnl_n);
   return hipGetLastError();
 }
 

@@ -363,6 +363,16 @@ __global__ void plan_cov_kernel(PlanArgs A) {
   }
 }
 
+// Covered offsets of head h below x: the whole intervals before the one that
+// holds x, plus the part of that one below x.
+__device__ inline long long covered_below(const int32_t* ivh, const int32_t* pre, int n_iv, int x) {
+  int a = 0, z = n_iv;
+  while (a < z) { const int mid = (a + z) >> 1; if (ivh[2 * mid + 1] > x) z = mid; else a = mid + 1; }
+  long long c = pre[a];
+  if (a < n_iv && x > ivh[2 * a]) c += x - ivh[2 * a];
+  return c;
+}
+
 // One wave per (head, query block): vertical columns inside the block's causal
 // extent that the block's ranges miss, ascending, duplicates dropped; bit 30
 // of an entry marks a high-norm key.  Also the block's first range tile (the
@@ -401,24 +411,63 @@ __global__ void __launch_bounds__(256) plan_ext_kernel(PlanArgs A) {
     }
     cnt += __popcll(bal);
   }
+  const int32_t* ivh = A.iv + (long long)h * A.iv_stride * 2;
+  const int32_t* pre = A.iv_pre + (long long)h * (A.iv_stride + 1);
+  const int n_iv = A.n_iv[h];
+  const int tf = (int)(covered_below(ivh, pre, n_iv, -i0) / 32);   // the block's first range tile
+  const int n_t = (pre[n_iv] + 31) / 32;
+  // Event record: range tiles (relative to the first) that hold a high-norm
+  // key, one lane per listed key of the KV head (ascending keys give
+  // ascending tiles), duplicates dropped; then the tiles where the DCA modes
+  // after the first begin.
+  int32_t* evr = A.ev + (long long)unit * EV_REC;
+  {
+    const int n_hn = A.hnl_n[g];
+    int rel = -1;
+    if (lane < min(n_hn, HN_CAP)) {
+      const int j = A.hnl[g * HN_CAP + lane];
+      const int o = j - i0;
+      if (j < hi_key) {
+        int a = 0, z = n_iv;   // last interval starting at or below o
+        while (z - a > 1) { const int mid = (a + z) >> 1; if (ivh[2 * mid] <= o) a = mid; else z = mid; }
+        if (n_iv > 0 && ivh[2 * a] <= o && o < ivh[2 * a + 1]) rel = (pre[a] + (o - ivh[2 * a])) / 32 - tf;
+      }
+    }
+    const unsigned long long have = __ballot(rel >= 0);
+    // compact through the wave's own LDS row (its accesses stay in order),
+    // then keep each tile once
+    __shared__ int comp[4][64];
+    const int pos = __popcll(have & ((1ull << lane) - 1ull));
+    if (rel >= 0) comp[threadIdx.x >> 6][pos] = rel;
+    __builtin_amdgcn_wave_barrier();
+    const int npk = __popcll(have);
+    const int packed = lane < npk ? comp[threadIdx.x >> 6][lane] : -1;
+    const int prev = __shfl_up(packed, 1);
+    const bool first = lane < npk && (lane == 0 || prev != packed);
+    const unsigned long long keep = __ballot(first);
+    const int kpos = __popcll(keep & ((1ull << lane) - 1ull));
+    const int nk = __popcll(keep);
+    const bool cut = n_hn > HN_CAP || nk > EV_PREC;
+    if (first && !cut) evr[3 + kpos] = packed;
+    if (lane == 2) evr[2] = cut ? -1 : nk;
+    if (lane < 2) {
+      const int m_blk = i0 / A.S;
+      const int seg = lane == 0 ? (m_blk - 1) * A.S : m_blk * A.S;
+      int r = -1;
+      if (seg > 0) {
+        const int t = (int)(covered_below(ivh, pre, n_iv, seg - i0) / 32);
+        if (t < n_t) r = t - tf;
+      }
+      evr[lane] = r;
+    }
+  }
   if (lane == 0) {
     A.n_ext[unit] = cnt;
-    // covered offsets below x: prefix of whole intervals plus the part of the one holding x
-    const int32_t* ivh = A.iv + (long long)h * A.iv_stride * 2;
-    const int32_t* pre = A.iv_pre + (long long)h * (A.iv_stride + 1);
-    const int n_iv = A.n_iv[h];
     const int rows = hi_key - i0;
     long long below[2];
-    const int xs[2] = {-i0, rows};
-    for (int t = 0; t < 2; ++t) {
-      const int x = xs[t];
-      int a = 0, z = n_iv;
-      while (a < z) { const int mid = (a + z) >> 1; if (ivh[2 * mid + 1] > x) z = mid; else a = mid + 1; }
-      long long c = pre[a];
-      if (a < n_iv && x > ivh[2 * a]) c += x - ivh[2 * a];
-      below[t] = c;
-    }
-    A.t_first[unit] = (int)(below[0] / 32);
+    below[0] = covered_below(ivh, pre, n_iv, -i0);
+    below[1] = covered_below(ivh, pre, n_iv, rows);
+    A.t_first[unit] = tf;
     const long long cover = (below[1] - below[0]) + cnt;
     if (!(A.bad && *A.bad)) {
       if (A.cover_pairs) atomicAdd((unsigned long long*)A.cover_pairs, (unsigned long long)(cover * rows));
@@ -443,7 +492,11 @@ __global__ void __launch_bounds__(256) plan_tiles_kernel(PlanArgs A) {
   const int32_t* pre = A.iv_pre + (long long)h * (A.iv_stride + 1);
   const int total = pre[n_iv];
   const int n_t = (total + 31) / 32;
-  if (t == 0) A.n_tiles[h] = n_t;
+  if (t == 0) {
+    A.n_tiles[h] = n_t;
+    // the first tile holding an offset above 0 (keys past a block's first row)
+    A.npe[h] = (int)(covered_below(ivh, pre, n_iv, 1) / 32);
+  }
   if (t >= n_t) return;
   const int r0 = 32 * t;
   int a = 0, z = n_iv;   // last interval with pre <= r0

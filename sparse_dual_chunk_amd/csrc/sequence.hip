@@ -169,7 +169,7 @@ struct SeqLayout {
 
 inline size_t up256(size_t x) { return (x + 255) / 256 * 256; }
 
-int seq_layout(const dca_cfg* cfg, const dca_sequence_plan* plan, SeqLayout* L) {
+int seq_layout(const dca_cfg* cfg, const dca_sequence_plan* plan, SeqLayout* L, bool paged = false) {
   if (!cfg || !plan || !plan->bounds) return DCA_EINVAL;
   if (plan->n_chunks < 1 || (plan->sparse != 0 && plan->sparse != 1)) return DCA_EINVAL;
   if (cfg->n_q != cfg->n_k) return DCA_EINVAL;
@@ -182,7 +182,7 @@ int seq_layout(const dca_cfg* cfg, const dca_sequence_plan* plan, SeqLayout* L) 
     if (b[c] % QB) return DCA_EUNSUPPORTED;
     const dca_cfg cc = chunk_cfg(cfg, b[c], b[c + 1]);
     size_t w = 0;
-    const int rc = dca_workspace_size(&cc, &w);
+    const int rc = paged ? dca::paged_prefill_bytes(&cc, &w) : dca_workspace_size(&cc, &w);
     if (rc != DCA_OK) return rc;
     ws = std::max(ws, w);
     max_rows = std::max(max_rows, b[c + 1] - b[c]);
@@ -229,22 +229,29 @@ int dca_prefill_sequence_workspace_size(const dca_cfg* cfg, const dca_sequence_p
   return DCA_OK;
 }
 
-int dca_prefill_sequence(const dca_bf16* q, const dca_bf16* k, const dca_bf16* v, const dca_sequence_plan* plan,
-                         const dca_cfg* cfg, const dca_key_cache* cache, dca_bf16* out) {
-  if (!q || !k || !v || !out || !cache || !cfg) return DCA_EINVAL;
+// The whole-prompt driver over a contiguous key cache (values in v) or a paged
+// pool (paged: keys and values appended into their pages).
+static int sequence_impl(const dca_bf16* q, const dca_bf16* k, const dca_bf16* v, const dca_sequence_plan* plan,
+                  const dca_cfg* cfg, const dca_key_cache* cache, const dca_paged_kv* paged, dca_bf16* out) {
+  if (!q || !k || !v || !out || !(cache || paged) || !cfg) return DCA_EINVAL;
   if (cfg->v_idx || cfg->s_off || cfg->cover_pairs || cfg->attended_pairs || cfg->stage_events) return DCA_EINVAL;
   SeqLayout L;
-  int rc = seq_layout(cfg, plan, &L);
+  int rc = seq_layout(cfg, plan, &L, paged != nullptr);
   if (rc != DCA_OK) return rc;
   if (!cfg->workspace || cfg->workspace_bytes < L.total || ((uintptr_t)cfg->workspace) % 256) return DCA_EWORKSPACE;
-  if (!cache->k_hi || !cache->k_lo || !cache->k_flags || cache->capacity < cfg->n_k) return DCA_EINVAL;
+  if (cache && (!cache->k_hi || !cache->k_lo || !cache->k_flags || cache->capacity < cfg->n_k)) return DCA_EINVAL;
+  if (paged) {
+    rc = dca::paged_valid(paged, cfg->h_kv, cfg->head_dim);
+    if (rc != DCA_OK) return rc;
+    if ((long long)paged->n_table * paged->page_keys < cfg->n_k) return DCA_EINVAL;
+  }
   const int n_chunks = plan->n_chunks, h_q = cfg->h_q, D = cfg->head_dim;
   const int32_t* b = plan->bounds;
   // validate every chunk call before anything is enqueued
   for (int c = 0; c < n_chunks; ++c) {
     const dca_cfg cc = chunk_cfg(cfg, b[c], b[c + 1]);
     size_t w = 0;
-    rc = dca_workspace_size(&cc, &w);
+    rc = paged ? dca::paged_prefill_bytes(&cc, &w) : dca_workspace_size(&cc, &w);
     if (rc != DCA_OK) return rc;
   }
   hipStream_t st = (hipStream_t)cfg->stream;
@@ -316,9 +323,11 @@ int dca_prefill_sequence(const dca_bf16* q, const dca_bf16* k, const dca_bf16* v
     cc.cover_pairs = plan->cover_pairs ? plan->cover_pairs + c : nullptr;
     record_opt(plan->chunk_events, 2 * c, st);
     if (overlap && hipStreamWaitEvent(st, idx_done[c], 0) != hipSuccess) return DCA_EHIP;
-    rc = dca_key_cache_append(k + (size_t)b[c] * cfg->h_kv * D, b[c], n_q, &cc, cache);
+    const size_t kv0 = (size_t)b[c] * cfg->h_kv * D;
+    rc = paged ? dca_paged_append(k + kv0, v + kv0, b[c], n_q, &cc, paged)
+               : dca_key_cache_append(k + kv0, b[c], n_q, &cc, cache);
     if (rc != DCA_OK) return rc;
-    rc = dca::prefill_impl(q + (size_t)b[c] * h_q * D, nullptr, cache, v, nullptr, &cc,
+    rc = dca::prefill_impl(q + (size_t)b[c] * h_q * D, nullptr, cache, paged, paged ? nullptr : v, nullptr, &cc,
                            out + (size_t)b[c] * h_q * D);
     if (rc != DCA_OK) return rc;
     if (cfg->lse_out) {
@@ -331,6 +340,27 @@ int dca_prefill_sequence(const dca_bf16* q, const dca_bf16* k, const dca_bf16* v
     if (overlap && hipEventRecord(chunk_done[c], st) != hipSuccess) return DCA_EHIP;
   }
   return DCA_OK;
+}
+
+int dca_prefill_sequence(const dca_bf16* q, const dca_bf16* k, const dca_bf16* v, const dca_sequence_plan* plan,
+                         const dca_cfg* cfg, const dca_key_cache* cache, dca_bf16* out) {
+  if (!cache) return DCA_EINVAL;
+  return sequence_impl(q, k, v, plan, cfg, cache, nullptr, out);
+}
+
+int dca_prefill_sequence_paged_workspace_size(const dca_cfg* cfg, const dca_sequence_plan* plan, size_t* bytes) {
+  if (!bytes) return DCA_EINVAL;
+  SeqLayout L;
+  const int rc = seq_layout(cfg, plan, &L, true);
+  if (rc != DCA_OK) return rc;
+  *bytes = L.total;
+  return DCA_OK;
+}
+
+int dca_prefill_sequence_paged(const dca_bf16* q, const dca_bf16* k, const dca_bf16* v, const dca_sequence_plan* plan,
+                               const dca_cfg* cfg, const dca_paged_kv* cache, dca_bf16* out) {
+  if (!cache) return DCA_EINVAL;
+  return sequence_impl(q, k, v, plan, cfg, nullptr, cache, out);
 }
 
 }  // extern "C"

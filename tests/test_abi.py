@@ -34,7 +34,9 @@ def test_library_exports_every_declared_symbol():
                           "dca_sparse_prefill_cached", "dca_decode_workspace_size", "dca_decode", "dca_strerror",
                           "dca_chunk_cost_default", "dca_chunk_schedule", "dca_prefill_sequence_workspace_size",
                           "dca_prefill_sequence", "moe_workspace_size", "moe_forward",
-                          "moe_pack_weights", "dca_paged_append", "dca_decode_paged", "dca_sparse_prefill_noalloc"}
+                          "moe_pack_weights", "dca_paged_append", "dca_decode_paged", "dca_sparse_prefill_noalloc",
+                          "dca_paged_prefill_workspace_size", "dca_sparse_prefill_paged",
+                          "dca_prefill_sequence_paged_workspace_size", "dca_prefill_sequence_paged"}
     out = subprocess.run(["nm", "-D", "--defined-only", S.LIB_PATH], capture_output=True, text=True).stdout
     exported = {l.split()[-1] for l in out.splitlines() if l.strip()}
     for n in names:
@@ -160,6 +162,23 @@ def test_noalloc_prefill_rejects_calls_beyond_its_static_scratch():
     small = _cfg().to_c(workspace=None, workspace_bytes=0)
     assert S.lib().dca_sparse_prefill_noalloc(0x1000, 0x1000, 0x1000, None, ctypes.byref(small), 0x1000) == S.DCA_EINVAL
     assert S.lib().dca_sparse_prefill_noalloc(0x1000, None, 0x1000, 0x1000, ctypes.byref(small), 0x1000) == S.DCA_EINVAL
+
+
+def test_paged_prefill_checks_the_pool_on_the_host():
+    """The paged prefill needs room for the gathered values, a page table that holds n_k keys
+    and pages of a multiple of 32 keys; each check fails before anything is enqueued."""
+    cfg = _cfg()
+    assert S.dca_paged_prefill_workspace_size(cfg) == S.dca_workspace_size(cfg) + cfg.n_k * cfg.h_kv * 128 * 2
+    c = cfg.to_c(workspace=0x1000, workspace_bytes=1 << 30)
+
+    def call(pages=64, page_keys=64, n_table=8, positions=0x1000):
+        pk = S.dca_paged_kv(k_hi=0x1000, k_lo=0x1000, v=0x1000, k_flags=0x1000, n_pages=pages, page_keys=page_keys,
+                            page_table=0x1000, n_table=n_table)
+        return S.lib().dca_sparse_prefill_paged(0x1000, ctypes.byref(pk), positions, ctypes.byref(c), 0x1000)
+    assert call(n_table=7) == S.DCA_EINVAL            # 7 * 64 < n_k = 512
+    assert call(page_keys=48) == S.DCA_EUNSUPPORTED
+    assert call(positions=None) == S.DCA_EINVAL
+    assert S.lib().dca_sparse_prefill_paged(0x1000, None, 0x1000, ctypes.byref(c), 0x1000) == S.DCA_EINVAL
 
 
 def test_prefill_rejects_small_or_missing_workspace():

@@ -135,3 +135,64 @@ def test_paged_decode_million_key_cache_equals_contiguous():
         c = S.Config(**{**cfg.__dict__, "n_q": n_t})
         (a, la), (b, lb) = _decode_both(q, paged, flat, vd, c)
         assert np.array_equal(a, b) and np.array_equal(la, lb), n_t
+
+
+# ------------------------------------------------------------------ prefill from the paged pool
+def _prefill_both(q, k, p0, paged, flat, vd, cfg, v_idx=None, s_off=None):
+    """(out, lse) of dca_sparse_prefill_cached over the contiguous cache and of
+    dca_sparse_prefill_paged over the pool, for the chunk [p0, n_k)."""
+    qd, pos = dev(q), dev(np.arange(p0, cfg.n_k, dtype=np.int32))
+    vi = dev(np.asarray(v_idx, dtype=np.int32)) if v_idx is not None else None
+    so = dev(np.asarray(s_off, dtype=np.int32)) if s_off is not None else None
+    res = []
+    for kind in ("flat", "paged"):
+        out = torch.full(qd.shape, -1, dtype=torch.int16, device="cuda")
+        lse = torch.empty((cfg.h_q, cfg.n_q), dtype=torch.float32, device="cuda")
+        if kind == "flat":
+            ws = torch.empty(S.dca_workspace_size(cfg), dtype=torch.uint8, device="cuda")
+            S.dca_sparse_prefill_cached(qd, flat, vd, pos, cfg, out, ws, v_idx=vi, s_off=so, lse_out=lse)
+        else:
+            ws = torch.empty(S.dca_paged_prefill_workspace_size(cfg), dtype=torch.uint8, device="cuda")
+            S.dca_sparse_prefill_paged(qd, paged, pos, cfg, out, ws, v_idx=vi, s_off=so, lse_out=lse)
+        torch.cuda.synchronize()
+        res.append((host_u16(out), lse.cpu().numpy()))
+    return res
+
+
+def _prefill_cfg(n_k, n_q, h_q, h_kv, sparse, split):
+    return S.Config(n_q=n_q, n_k=n_k, h_q=h_q, h_kv=h_kv, dca_chunk=256, dca_local=64, rope_base=1e6, yarn_s=4.0,
+                    vs_last_q=64, vs_k_vertical=24 if sparse else 0, vs_k_slash=40 if sparse else 0, split_k=split)
+
+
+def _index(q, k, p0, cfg):
+    from tests.gpu_helpers import run_index
+    inp = dict(q=q, k=k, positions=np.arange(p0, cfg.n_k, dtype=np.int32))
+    return run_index(inp, cfg)
+
+
+@pytest.mark.parametrize("P,sparse,split,h_q,h_kv", [(64, True, 0, 4, 2), (256, True, 2, 4, 2), (32, False, 0, 4, 2),
+                                                     (64, False, 3, 14, 2), (128, True, 0, 6, 3)])
+def test_paged_prefill_equals_cached(P, sparse, split, h_q, h_kv):
+    """The chunk [640, 960) of a prompt whose keys sit in scattered pages (appends that
+    cross page boundaries): output and LSE equal the contiguous-cache prefill bit for bit."""
+    p0, n_k = 640, 960
+    q, k, v = _inputs(P + h_q, n_k, n_k - p0, h_q, h_kv)
+    cfg = _prefill_cfg(n_k, n_k - p0, h_q, h_kv, sparse, split)
+    paged, flat, vd, _ = _build(k, v, cfg, P, P + 7, cuts=[P - 1, 333, 2 * P + 5, 700])
+    vi = so = None
+    if sparse:
+        vi, so = _index(q, k, p0, cfg)
+    (a, la), (b, lb) = _prefill_both(q, k, p0, paged, flat, vd, cfg, vi, so)
+    assert np.array_equal(a, b) and np.array_equal(la, lb)
+
+
+def test_paged_prefill_against_the_oracle():
+    p0, n_k, h_q, h_kv = 512, 896, 4, 2
+    q, k, v = _inputs(71, n_k, n_k - p0, h_q, h_kv)
+    cfg = _prefill_cfg(n_k, n_k - p0, h_q, h_kv, True, 0)
+    paged, flat, vd, _ = _build(k, v, cfg, 64, 13, cuts=[200, 640])
+    vi, so = _index(q, k, p0, cfg)
+    (a, la), _ = _prefill_both(q, k, p0, paged, flat, vd, cfg, vi, so)
+    ref, ref_lse = O.attention(q, k, v, p0, oracle_cfg(cfg), v_idx=vi, s_off=so)
+    check_close(a, ref, "paged prefill")
+    assert np.abs(la - ref_lse).max() <= 1e-2

@@ -88,6 +88,25 @@ def _sequence(qd, kd, vd, bounds, cfg, sparse, overlap):
     return out, lse, pairs
 
 
+def _sequence_paged(qd, kd, vd, bounds, cfg, sparse, overlap, page_keys=64, seed=0):
+    """The driver over a paged pool: pages of page_keys keys placed by a seeded permutation."""
+    n, h_q = cfg.n_k, cfg.h_q
+    n_table = (n + page_keys - 1) // page_keys
+    table = np.random.default_rng(seed).permutation(n_table + 2)[:n_table].astype(np.int32)
+    pool = S.PagedKV.allocate(n_table + 2, page_keys, cfg.h_kv, table)
+    out = torch.empty(qd.shape, dtype=torch.int16, device="cuda")
+    lse = torch.empty((h_q, n), dtype=torch.float32, device="cuda")
+    pairs = torch.zeros(len(bounds) - 1, dtype=torch.int64, device="cuda")
+    ws = torch.empty(S.dca_prefill_sequence_paged_workspace_size(cfg, bounds, sparse, overlap), dtype=torch.uint8,
+                     device="cuda")
+    side = torch.cuda.Stream() if overlap else None
+    S.dca_prefill_sequence_paged(qd, kd, vd, bounds, cfg, pool, out, ws, sparse=sparse,
+                                 index_stream=side.cuda_stream if side is not None else None, lse_out=lse,
+                                 cover_pairs=pairs)
+    torch.cuda.synchronize()
+    return out, lse, pairs
+
+
 CASES = [
     # (n, bounds, sparse, k_v, k_s)
     (960, [0, 320, 704, 960], True, 24, 40),
@@ -107,6 +126,18 @@ def test_sequence_equals_per_chunk_calls(n, bounds, sparse, kv, ks, overlap):
     cfg = _cfg(n, n, h_q, h_kv, vs_k_vertical=kv, vs_k_slash=ks)
     a, la, pa = _sequence(qd, kd, vd, bounds, cfg, sparse, overlap)
     b, lb, pb = _per_chunk(qd, kd, vd, bounds, cfg, sparse)
+    assert torch.equal(a, b) and torch.equal(la, lb) and torch.equal(pa, pb)
+
+
+@pytest.mark.parametrize("n,bounds,sparse,kv,ks", CASES)
+def test_paged_driver_equals_the_contiguous_driver(n, bounds, sparse, kv, ks):
+    """The driver over scattered pages of 64 keys equals the contiguous-cache driver bit for bit."""
+    h_q, h_kv = 4, 2
+    q, k, v = _prompt(n + ks + 1, n, h_q, h_kv)
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    cfg = _cfg(n, n, h_q, h_kv, vs_k_vertical=kv, vs_k_slash=ks)
+    a, la, pa = _sequence_paged(qd, kd, vd, bounds, cfg, sparse, overlap=True, seed=n)
+    b, lb, pb = _sequence(qd, kd, vd, bounds, cfg, sparse, overlap=True)
     assert torch.equal(a, b) and torch.equal(la, lb) and torch.equal(pa, pb)
 
 
@@ -171,3 +202,25 @@ def test_sequence_14b_256k_prompt_equals_per_chunk_calls():
         assert np.isfinite(o).all() and np.abs(o).max() <= vmax * (1 + 2 ** -7)
         del a, b, la, lb
         torch.cuda.empty_cache()
+
+
+@pytest.mark.timeout(900)
+def test_sequence_14b_256k_prompt_through_the_paged_driver():
+    """The 14B prompt of 262,144 tokens in the benchmark's eight 32K chunks, its keys and
+    values appended into scattered pages of 256 keys: the paged driver equals the
+    contiguous-cache driver bit for bit."""
+    import workloads as W
+    w = W.C4_14B_256K
+    n = w.n_k_total
+    log("generating the 256K prompt")
+    k, v = W.make_keys_values(w, n, seed=0)
+    fixed = list(range(0, n, 32768)) + [n]
+    q = np.concatenate([W.make_queries(w, a, b - a, seed=0) for a, b in zip(fixed[:-1], fixed[1:])])
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    cfg = S.Config(n_q=n, n_k=n, h_q=w.h_q, h_kv=w.h_kv, dca_chunk=w.dca_chunk, dca_local=w.dca_local,
+                   rope_base=w.rope_base, yarn_s=w.yarn_s, vs_k_vertical=w.k_vertical, vs_k_slash=w.k_slash)
+    log("paged driver")
+    a, la, pa = _sequence_paged(qd, kd, vd, fixed, cfg, True, overlap=True, page_keys=256, seed=5)
+    log("contiguous driver")
+    b, lb, pb = _sequence(qd, kd, vd, fixed, cfg, True, overlap=True)
+    assert torch.equal(a, b) and torch.equal(la, lb) and torch.equal(pa, pb)
