@@ -398,7 +398,19 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A) {
         if ((unsigned)(c - base) >= span) s[vv] = alt;
       }
     };
-    f32x16 s = qk(kt, T, skey, mode_first, precise);
+    // Exact diagonals: the rows' masks first.  A tile none of the wave's rows
+    // attends costs no MFMA, softmax or P V: the wave only keeps its place in
+    // the step's loads and barriers.
+    uint32_t xm = 0u;
+    bool skip = false;
+    if (EXACT && !T.cnt) {
+      xm = exact_run(T.a1, T.len1, 0) | exact_run(T.a2, T.len2, T.len1);
+      skip = !__any(xm != 0u);
+    }
+    f32x16 s = {};
+    bf16x8 pf[2] = {};
+    if (!skip) {
+    s = qk(kt, T, skey, mode_first, precise);
     // slots from the first key of mode m on take that mode's scores (the
     // modes after the first are spelled out: a loop here would make the
     // compiler wait for the staged loads in flight before every S^T)
@@ -421,17 +433,18 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A) {
       select_slots(s, t_lo, t_hi, -INFINITY);
     }
     if (EXACT && !T.cnt) {
-      const uint32_t m = exact_run(T.a1, T.len1, 0) | exact_run(T.a2, T.len2, T.len1);
 #pragma unroll
       for (int vv = 0; vv < 16; ++vv) {
         const int slot = 8 * (vv >> 2) + (vv & 3) + 4 * half;
-        s[vv] = ((m >> slot) & 1u) ? s[vv] - m_run : -INFINITY;
+        s[vv] = ((xm >> slot) & 1u) ? s[vv] - m_run : -INFINITY;
       }
     } else if (EXACT) {
 #pragma unroll
       for (int vv = 0; vv < 16; ++vv) s[vv] -= m_run;
     }
+    }
     after_qk();
+    if (!skip) {
     // ---- online softmax (log2 domain; s already holds score - m_run).  The
     // reference max moves only when a score exceeds it by more than 8 (so
     // p <= 2^8), or at the row's first keys.
@@ -457,7 +470,6 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A) {
       }
     }
     started = started || (mx != -INFINITY);
-    bf16x8 pf[2];
 #pragma unroll
     for (int vv = 0; vv < 16; ++vv) pf[vv >> 3][vv & 7] = (__bf16)fast_exp2(s[vv]);
     // row sum of the bf16 weights that enter P V (pairs summed by dot products)
@@ -469,10 +481,12 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A) {
       l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[G], pf[G], 4, 5), ones, l_run, false);
       l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[G], pf[G], 6, 7), ones, l_run, false);
     }
+    }
     // B3: this wave's loads of V(t) landed (issued after them: K(t+1), V(t+1)
     // and K(t+2)); barrier
     vm_wait(3 * LPW);
     wg_barrier();
+    if (skip) return;
     // ---- O^T += V^T P^T, V^T operand read transposed from the row-major V tile.
     // All 8 reads of a 16-key half are issued before its 4 MFMAs, so their
     // latency overlaps instead of stalling every MFMA.

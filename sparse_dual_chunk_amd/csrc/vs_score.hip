@@ -13,6 +13,8 @@
 // Grid: one workgroup per (key range, query head); wave w holds scoring rows
 // 16w..16w+15 as the A operand, the 32-key sub-tile of rotated keys sits in
 // LDS as fp64 and feeds the B operand.
+#include <type_traits>
+
 #include "common.h"
 #include "args.h"
 
@@ -69,13 +71,16 @@ __global__ void __launch_bounds__(256) vs_trig_kernel(const double* __restrict__
 
 struct __align__(16) VsSmem {
   double kt[SUB * KPD];          // rotated keys of the sub-tile, [key][dim]
-  double at[64 * APD];           // pass 2: probabilities [row][key]
+};
+// pass 2 holds no keys: a third of the LDS, so more workgroups share a CU
+struct __align__(16) VsSmem2 {
+  double at[64 * APD];           // probabilities [row][key]
   double ring_hi[RING], ring_lo[RING];
 };
 
 template <int PASS>
 __global__ void __launch_bounds__(256, 3) vs_pass_kernel(VsArgs A) {
-  __shared__ VsSmem sm;
+  __shared__ typename std::conditional<PASS == 1, VsSmem, VsSmem2>::type sm;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -140,7 +145,7 @@ __global__ void __launch_bounds__(256, 3) vs_pass_kernel(VsArgs A) {
     const int crow = 16 * wave + kd + 4 * v;
     lse_v[v] = (PASS == 2) ? A.lse[h * 64 + crow] : 0.0;
   }
-  if (PASS == 2) {
+  if constexpr (PASS == 2) {
     for (int i = tid; i < RING; i += 256) { sm.ring_hi[i] = 0.0; sm.ring_lo[i] = 0.0; }
   }
 
@@ -201,7 +206,7 @@ __global__ void __launch_bounds__(256, 3) vs_pass_kernel(VsArgs A) {
       if (t0 + SUB < kr1) load_lg(t0 + SUB);
     }
 
-    if (PASS == 1) {
+    if constexpr (PASS == 1) {
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
         const int j = t0 + 16 * nb + (lane & 15);
@@ -236,23 +241,39 @@ __global__ void __launch_bounds__(256, 3) vs_pass_kernel(VsArgs A) {
         }
       }
       __syncthreads();
-      if (tid < SUB) {
-        // vertical: column sum over rows 0..63 in order
-        const int j = t0 + tid;
-        if (j < kr1) {
-          double hi = 0.0, lo = 0.0;
-          for (int i = 0; i < 64; ++i) dd_add(hi, lo, sm.at[i * APD + tid]);
-          A.vert[(long long)h * A.n_k + j] = dd_round(hi, lo);
+      // vertical: column tid / 8 summed over rows 8 (tid % 8) .. +7 by each of
+      // eight consecutive lanes, the partial sums combined across the lanes
+      {
+        const int jj = tid >> 3, part = tid & 7;
+        double hi = 0.0, lo = 0.0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) dd_add(hi, lo, sm.at[(8 * part + i) * APD + jj]);
+#pragma unroll
+        for (int off = 1; off < 8; off <<= 1) {
+          const double oh = __shfl_xor(hi, off), ol = __shfl_xor(lo, off);
+          dd_add_dd(hi, lo, oh, ol);
         }
-      } else if (tid >= 64 && tid < 64 + 95) {
-        // slash: diagonal e = key of row 0 (delta = p_first - e); active e in [t0-63, t0+31]
-        const int e = t0 - 63 + (tid - 64);
-        if (e <= A.p_first) {
+        const int j = t0 + jj;
+        if (part == 0 && j < kr1) A.vert[(long long)h * A.n_k + j] = dd_round(hi, lo);
+      }
+      // slash: diagonal e = key of row 0 (delta = p_first - e), active e in
+      // [t0-63, t0+31]; two lanes take the two halves of its rows inside the
+      // sub-tile, the first adds both to the diagonal's running sum
+      if (tid < 2 * (SUB + 63)) {
+        const int d = tid >> 1, hf = tid & 1;
+        const int e = t0 - 63 + d;
+        // rows i of the diagonal inside the sub-tile: 0 <= e + i - t0 < SUB
+        const int i_lo = max(0, t0 - e), i_hi = min(64, t0 + SUB - e);
+        const int mid = (i_lo + i_hi) >> 1;
+        const int r0 = hf ? mid : i_lo, r1 = hf ? i_hi : mid;
+        double ph = 0.0, pl = 0.0;
+        for (int i = r0; i < r1; ++i) dd_add(ph, pl, sm.at[i * APD + (e + i - t0)]);
+        const double oh = __shfl_xor(ph, 1), ol = __shfl_xor(pl, 1);
+        if (hf == 0 && e <= A.p_first) {
+          dd_add_dd(ph, pl, oh, ol);
           const int slot = (e + (1 << 30)) & (RING - 1);
           double hi = sm.ring_hi[slot], lo = sm.ring_lo[slot];
-          // rows i of the diagonal inside the sub-tile: 0 <= e + i - t0 < SUB
-          const int i_lo = max(0, t0 - e), i_hi = min(64, t0 + SUB - e);
-          for (int i = i_lo; i < i_hi; ++i) dd_add(hi, lo, sm.at[i * APD + (e + i - t0)]);
+          dd_add_dd(hi, lo, ph, pl);
           const bool last_sub = (t0 + SUB >= kr1);
           const bool complete = (e + 63 < t0 + SUB) || (last_sub && kr1 == A.n_k);
           const bool started_here = (e >= kr0) || (kr0 == 0);
