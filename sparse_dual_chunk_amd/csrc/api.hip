@@ -80,7 +80,7 @@ struct Layout {
   // prefill
   Region hnl, hnl_n, ev, npe;
   Region khi, klo, kbits, hn, qhi, qlo, iv, iv_pre, n_iv, cov, ext, n_ext, tiles, n_tiles, t_first, part_o, part_lse;
-  Region dbits, vbits;
+  Region dbits, vbits, smask;
   Region vg;             // values gathered from a paged pool
   int dbits_words = 0, vbits_words = 0;
   // index
@@ -177,6 +177,7 @@ Layout make_layout(const dca_cfg* c, bool paged = false) {
     L.vbits_words = (n_k + 254) / 32 + 3;
     place(L.dbits, cur, (size_t)h_q * L.dbits_words * 4);
     place(L.vbits, cur, (size_t)h_q * L.vbits_words * 4);
+    place(L.smask, cur, (size_t)h_q * L.tile_stride * 64 * 4);
   }
   if (L.split > 1) {
     place(L.part_o, cur, (size_t)L.split * n_q * h_q * D * 2);
@@ -470,6 +471,7 @@ int prefill_impl(const dca_bf16* q, const dca_bf16* k, const dca_key_cache* cach
     P.kbits_words = kbits_words;
     P.dbits = cfg->slash_exact ? at<uint32_t>(cfg, L.dbits) : nullptr;
     P.vbits = cfg->slash_exact ? at<uint32_t>(cfg, L.vbits) : nullptr;
+    P.smask = cfg->slash_exact ? at<uint32_t>(cfg, L.smask) : nullptr;
     P.dbits_words = L.dbits_words; P.vbits_words = L.vbits_words;
     P.attended = (long long*)cfg->attended_pairs;
     P.bad = bad;
@@ -506,6 +508,7 @@ int prefill_impl(const dca_bf16* q, const dca_bf16* k, const dca_key_cache* cach
   A.exact = (sparse && cfg->slash_exact) ? 1 : 0;
   A.dbits = A.exact ? at<uint32_t>(cfg, L.dbits) : nullptr;
   A.vbits = A.exact ? at<uint32_t>(cfg, L.vbits) : nullptr;
+  A.smask = A.exact ? at<uint32_t>(cfg, L.smask) : nullptr;
   A.dbits_words = L.dbits_words; A.vbits_words = L.vbits_words;
   A.bad = bad;
   A.hnl = at<int32_t>(cfg, L.hnl); A.hnl_n = at<int32_t>(cfg, L.hnl_n);

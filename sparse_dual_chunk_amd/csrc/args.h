@@ -35,6 +35,8 @@ struct AttnArgs {
   const int32_t* n_ext;     // [h_q][nb]
   const uint32_t* dbits;    // exact diagonals: [h_q][dbits_words] bit delta + 128 = selected offset (and 0)
   const uint32_t* vbits;    // exact diagonals: [h_q][vbits_words] bit j + 128 = selected vertical column
+  const uint32_t* smask;    // exact diagonals: [h_q][tile_stride][64] slots of range tile t whose offset
+                            // from block row r is selected (or 0); the same for every block of the head
   int n_q, n_k, h_q, h_kv, p0, S, W, nb, tile_stride, ext_stride, split, dense, kbits_words, hn_pad;
   int exact, dbits_words, vbits_words;
   const int32_t* bad;       // device flag set by the positions check: write no output when nonzero (or null)
@@ -114,6 +116,7 @@ struct PlanArgs {
   int S;                   // DCA chunk size
   uint32_t* dbits;         // exact diagonals (or null): [h_q][dbits_words], bit delta + 128
   uint32_t* vbits;         // exact diagonals (or null): [h_q][vbits_words], bit j + 128
+  uint32_t* smask;         // exact diagonals (or null): [h_q][tile_stride][64] slash slots of (tile, block row)
   int h_q, h_kv, k_v, k_s, p_last, p0, n_q, nb, iv_stride, ext_stride, cov_words, tile_stride, kbits_words;
   int dbits_words, vbits_words;
 };

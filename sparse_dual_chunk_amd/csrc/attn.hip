@@ -37,6 +37,42 @@ __device__ __forceinline__ int range_key(Tile T, int t) {
   return t < T.len1 ? T.a1 + t : (t < T.len1 + T.len2 ? T.a2 + (t - T.len1) : -1);
 }
 
+#ifndef DCA_DMA_ASM
+#define DCA_DMA_ASM 1
+#endif
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer resource over [base, base + bytes): raw dwords, no stride.
+__device__ __forceinline__ i32x4 raw_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)base;
+  i32x4 r;
+  r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r.y = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xFFFFu));
+  r.z = (int)bytes;
+  r.w = 0x00020000;
+  return r;
+}
+
+// Direct loads into LDS: lane l's 16 (4) bytes at byte offset voff of the
+// buffer land at lds + 16 l (4 l).  They are issued where the compiler does
+// not see them, so it places no wait of its own for them (it cannot tell the
+// stages of consecutive loop iterations apart and would wait for the loads of
+// the next tile before reading the current one): every read of their data is
+// ordered by the walk's own vmcnt waits and barriers.  M0 takes the LDS
+// address one instruction before the load.
+__device__ __forceinline__ void dma_b128(i32x4 rs, uint32_t lds, int voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(lds), "v"(voff), "s"(rs) : "memory", "m0");
+}
+__device__ __forceinline__ void dma_b32(i32x4 rs, uint32_t lds, int voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :: "s"(lds), "v"(voff), "s"(rs) : "memory", "m0");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
+}
+
 // NW waves of 32 rows per workgroup: 2 (one 64-row block) for every call; 4
 // (two adjacent blocks, 128 rows, sharing every staged K / V tile) for dense
 // calls whose pairs of blocks lie inside one DCA chunk: their key ranges
@@ -48,6 +84,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A) {
   static_assert(NW == 2 || (NW == 4 && DENSE), "four-wave workgroups serve dense calls");
   constexpr int RB = 32 * NW;      // rows per workgroup
   constexpr int LPW = 8 / NW;      // direct loads per wave and tensor of a tile
+  constexpr int XL = EXACT ? 1 : 0;  // mask-word loads per lane and tile (exact diagonals)
   // K and V of the two stages are four LDS objects: the compiler then tells
   // the reads of one stage from the direct loads in flight into the other
   // and places no wait for those loads inside the tile's computation
@@ -210,41 +247,57 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A) {
   auto range_precise = [&](Tile T) __attribute__((always_inline)) -> bool {
     return run_flagged(T.a1, T.len1) || run_flagged(T.a2, T.len2);
   };
-  // Exact-diagonal semantics: the slots of run [a, a + len) (placed at slots
-  // so ..) that this lane's row attends: its offset prow - key is selected
-  // (or 0), or the key is a selected vertical column.  The offset bits of a
-  // row form a 32-bit window inside 6 words that the whole wave shares
-  // (scalar loads); the run's vertical bits are the same for every row.
+  // Exact-diagonal semantics: the slots of a range tile that this lane's row
+  // attends are the tile's slash slots for the row (its offset prow - key is
+  // selected, or 0) and the slots holding selected vertical columns.  The
+  // slash slots depend on the row's place in the block only (the tile's keys
+  // are offsets from the block's first row): the plan tabulates them per
+  // (tile, row) and each lane loads its word two tiles ahead.  The vertical
+  // bits of a run are the same for every row (scalar loads).
   typedef __attribute__((address_space(4))) const uint32_t cu32b;
-  cu32b* db4 = (cu32b*)(A.dbits + (long long)h * A.dbits_words);
   cu32b* vb4 = (cu32b*)(A.vbits + (long long)h * A.vbits_words);
-  auto exact_run = [&](int a, int len, int so) __attribute__((always_inline)) -> uint32_t {
-    if (len <= 0) return 0u;
-    const uint32_t runmask = (len >= 32 ? 0xFFFFFFFFu : ((1u << len) - 1u)) << so;
-    const int bw = (i0 - a - 31 + 128) >> 5;
-    uint32_t w[6];
-#pragma unroll
-    for (int k = 0; k < 6; ++k) w[k] = db4[bw + k];
-    const int sh = prow - a - (len - 1) + 128 - 32 * bw;   // 0 .. 125
-    const int kx = sh >> 5;
-    uint32_t lo = w[0], hi = w[1];
-#pragma unroll
-    for (int k = 1; k < 5; ++k)
-      if (kx == k) { lo = w[k]; hi = w[k + 1]; }
-    const uint32_t win = (uint32_t)((((uint64_t)hi << 32) | lo) >> (sh & 31));
-    // window bit x is offset prow - a - (len - 1) + x, i.e. slot so + len - 1 - x
-    const uint32_t md = __builtin_bitreverse32(win) >> (32 - len - so);
-    const int vbit = a + 128;
-    const uint32_t v0 = vb4[vbit >> 5], v1 = vb4[(vbit >> 5) + 1];
-    const uint32_t vw = (uint32_t)((((uint64_t)v1 << 32) | v0) >> (vbit & 31));
-    return (md | (vw << so)) & runmask;
+  // mask words: a ring of 4 tiles x 64 lanes per wave, filled by direct loads
+  // (lanes l and l + 32 load their row's word twice) two tiles ahead
+  __shared__ __align__(16) uint32_t msk_[EXACT ? NW * 4 * 64 : 1];
+  uint32_t* msk = msk_ + (EXACT ? wave * 4 * 64 : 0);
+  const i32x4 rs_m = EXACT ? raw_rsrc(A.smask + (long long)h * A.tile_stride * 64, (uint32_t)A.tile_stride * 256u)
+                           : i32x4{0, 0, 0, 0};
+  auto mask_issue = [&](int idx, int slot) __attribute__((always_inline)) {   // tile idx of the walk (phys)
+    if (!EXACT) return;
+    const int t = min(t_first + idx, A.tile_stride - 1);   // tiles past the walk: any word (unused)
+    dma_b32(rs_m, lds_addr(msk + 64 * (slot & 3)), (t * 64 + rloc) * 4);
+  };
+  auto mask_read = [&](int slot) __attribute__((always_inline)) -> uint32_t {
+    return EXACT ? msk[64 * (slot & 3) + lane] : 0u;
+  };
+  // the vertical bits of both runs of a range tile at their slots; the four
+  // words are loaded whatever the run lengths, so that one wait covers them.
+  // A run starts below n_k + 96; one far below key 0 (the tail of an interval
+  // in a block's first tile, all of its keys negative and masked) reads the
+  // bitmap's first words instead.
+  auto vert_bits = [&](Tile T) __attribute__((always_inline)) -> uint32_t {
+    const int b1 = max(T.a1 + 128, 0), b2 = max(T.a2 + 128, 0);
+    const uint32_t w10 = vb4[b1 >> 5], w11 = vb4[(b1 >> 5) + 1];
+    const uint32_t w20 = vb4[b2 >> 5], w21 = vb4[(b2 >> 5) + 1];
+    const uint32_t v1 = (uint32_t)((((uint64_t)w11 << 32) | w10) >> (b1 & 31));
+    const uint32_t v2 = (uint32_t)((((uint64_t)w21 << 32) | w20) >> (b2 & 31));
+    const uint32_t m1 = T.len1 >= 32 ? 0xFFFFFFFFu : ((1u << T.len1) - 1u);
+    const uint32_t m2 = T.len2 >= 32 ? 0xFFFFFFFFu : ((1u << T.len2) - 1u);
+    return (v1 & m1) | (T.len1 < 32 ? (v2 & m2) << T.len1 : 0u);
   };
   // slot key of an extra-vertical tile (bit 30 marks a high-norm key), -1 past the count
   auto ext_key = [&](Tile T) __attribute__((always_inline)) -> int { return (l32 < T.cnt) ? ext_h[T.eoff + l32] : -1; };
   // K and V rows of this KV head through buffer resources: one 32-bit byte
   // offset per row serves both tensors (the host bounds n_k * h_kv * 256 < 2^32)
-  const __amdgpu_buffer_rsrc_t rs_k = __builtin_amdgcn_make_buffer_rsrc((void*)kh_base, (short)0, -1, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rs_v = __builtin_amdgcn_make_buffer_rsrc((void*)v_base, (short)0, -1, 0x00020000);
+#if DCA_DMA_ASM
+  typedef i32x4 Rsrc;
+  const Rsrc rs_k = raw_rsrc(kh_base, 0xFFFFFFFFu);
+  const Rsrc rs_v = raw_rsrc(v_base, 0xFFFFFFFFu);
+#else
+  typedef __amdgpu_buffer_rsrc_t Rsrc;
+  const Rsrc rs_k = __builtin_amdgcn_make_buffer_rsrc((void*)kh_base, (short)0, -1, 0x00020000);
+  const Rsrc rs_v = __builtin_amdgcn_make_buffer_rsrc((void*)v_base, (short)0, -1, 0x00020000);
+#endif
   const int rowb = kstride * 2;
   const int lrow = lane >> 4;                       // row of a load's group this lane fills
   const int lchunk = 16 * ((lane & 15) ^ (5 * lrow));  // byte offset of the chunk it reads
@@ -288,11 +341,15 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A) {
     return f;
   };
   // the 4 direct loads of one tensor of a tile into a stage
-  auto issue = [&](__amdgpu_buffer_rsrc_t rs, uint8_t* stage, Offs f) __attribute__((always_inline)) {
+  auto issue = [&](Rsrc rs, uint8_t* stage, Offs f) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < LPW; ++j)
+#if DCA_DMA_ASM
+      dma_b128(rs, lds_addr(stage + (NW * j + wave) * GRPB), f.v[j]);
+#else
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(stage + (NW * j + wave) * GRPB),
                                                16, f.v[j], 0, 0, 0);
+#endif
   };
 
   // ---- pipeline.  The K and V stages are released separately: step t
@@ -310,7 +367,9 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A) {
   // of metadata in between only make a wait longer).  Barriers carry no memory
   // fence (a fence would wait for every load in flight).
   auto vm_wait = [&](int n) __attribute__((always_inline)) {   // at most n vector-memory ops outstanding
-    if (n >= 12) __builtin_amdgcn_s_waitcnt(0x0F7C);
+    if (n >= 14) __builtin_amdgcn_s_waitcnt(0x0F7E);
+    else if (n >= 12) __builtin_amdgcn_s_waitcnt(0x0F7C);
+    else if (n >= 9) __builtin_amdgcn_s_waitcnt(0x0F79);
     else if (n >= 8) __builtin_amdgcn_s_waitcnt(0x0F78);
     else if (n >= 6) __builtin_amdgcn_s_waitcnt(0x0F76);
     else if (n >= 4) __builtin_amdgcn_s_waitcnt(0x0F74);
@@ -367,8 +426,8 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A) {
   // [0, row] or past the count are masked (only tiles at the block's edges
   // have such slots).  Then one online softmax and one O += P V.  after_qk
   // runs once S^T is done (B2 and the K issue), B3 before the V reads.
-  auto compute_tile = [&](const uint8_t* kt, const uint8_t* vt, Tile T, int skey, bool precise, auto&& after_qk)
-      __attribute__((always_inline)) {
+  auto compute_tile = [&](const uint8_t* kt, const uint8_t* vt, Tile T, int skey, bool precise, uint32_t smk,
+                          auto&& after_qk) __attribute__((always_inline)) {
     const int count = tile_count(T);
     int key_first, key_last;
     if (T.cnt) {
@@ -404,7 +463,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A) {
     uint32_t xm = 0u;
     bool skip = false;
     if (EXACT && !T.cnt) {
-      xm = exact_run(T.a1, T.len1, 0) | exact_run(T.a2, T.len2, T.len1);
+      xm = smk | vert_bits(T);
       skip = !__any(xm != 0u);
     }
     f32x16 s = {};
@@ -433,10 +492,14 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A) {
       select_slots(s, t_lo, t_hi, -INFINITY);
     }
     if (EXACT && !T.cnt) {
+      // bit c of xh is slot c + 4 half; each score keeps s - m_run where its
+      // bit is set (a sign-extended 1-bit field selects it), else -inf
+      const uint32_t xh = xm >> (4 * half);
 #pragma unroll
       for (int vv = 0; vv < 16; ++vv) {
-        const int slot = 8 * (vv >> 2) + (vv & 3) + 4 * half;
-        s[vv] = ((xm >> slot) & 1u) ? s[vv] - m_run : -INFINITY;
+        const int c = 8 * (vv >> 2) + (vv & 3);
+        const uint32_t sel = (uint32_t)__builtin_amdgcn_sbfe((int)xh, c, 1);
+        s[vv] = __uint_as_float((__float_as_uint(s[vv] - m_run) & sel) | (0xFF800000u & ~sel));
       }
     } else if (EXACT) {
 #pragma unroll
@@ -483,8 +546,8 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A) {
     }
     }
     // B3: this wave's loads of V(t) landed (issued after them: K(t+1), V(t+1)
-    // and K(t+2)); barrier
-    vm_wait(3 * LPW);
+    // and K(t+2), and in the exact walk the mask words of t+1 and t+2); barrier
+    vm_wait(3 * LPW + 2 * XL);
     wg_barrier();
     if (skip) return;
     // ---- O^T += V^T P^T, V^T operand read transposed from the row-major V tile.
@@ -534,18 +597,22 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A) {
   };
   Tile T_c = range_tile(phys(t0), desc_load(phys(t0)));
   const Offs f_c = tile_offsets(t0 < r_end ? T_c : T_dummy, -1, true);
+  mask_issue(phys(t0), t0);
   issue(rs_k, kst0, f_c);
   issue(rs_v, vst0, f_c);
   bool p_c = t0 < r_end && range_precise(T_c);
   Tile T_n = range_tile(phys(t0 + 1), desc_load(phys(t0 + 1)));
   Offs f_n = tile_offsets(t0 + 1 < r_end ? T_n : T_dummy, -1, true);
+  mask_issue(phys(t0 + 1), t0 + 1);
   issue(rs_k, kst1, f_n);
   bool p_n = t0 + 1 < r_end && range_precise(T_n);
   int4 d_2 = desc_load(phys(t0 + 2));
 
   // One step on range tile ti: its stages kc / vc, and vn, the V stage of tile ti+1.
   auto step = [&](uint8_t* kc, const uint8_t* vc, uint8_t* vn, int ti) __attribute__((always_inline)) {
-    vm_wait(2 * LPW);      // K(ti) landed: V(ti) and K(ti+1) were issued after it
+    // K(ti) (and its mask words) landed: V(ti), K(ti+1) (and the mask words
+    // of ti+1) were issued after it
+    vm_wait(2 * LPW + XL);
     wg_barrier();          // B1: K(ti) visible; V(ti-1)'s stage is free
     issue(rs_v, vn, f_n);
     Tile T_2 = T_dummy;
@@ -557,11 +624,12 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A) {
       T_2 = range_tile(px, d_2);
       // the block's first range tile (negative keys) may now come after the prologue
       f_2 = tile_offsets(ti + 2 < r_end ? T_2 : T_dummy, -1, clamp_all || px == 0);
+      mask_issue(px, ti + 2);
       issue(rs_k, kc, f_2);
       p_2 = ti + 2 < r_end && range_precise(T_2);
       d_2 = desc_load(phys(ti + 3));
     };
-    compute_tile(kc, vc, T_c, -1, p_c, after_qk);
+    compute_tile(kc, vc, T_c, -1, p_c, mask_read(ti), after_qk);
     T_c = T_n; p_c = p_n;
     T_n = T_2; p_n = p_2; f_n = f_2;
   };
@@ -584,7 +652,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A) {
     issue(rs_v, vst0, f);
     vm_wait(0);
     wg_barrier();
-    compute_tile(kst0, vst0, T, sk, prec, [] {});
+    compute_tile(kst0, vst0, T, sk, prec, 0u, [] {});
     wg_barrier();          // the stage is read; the next tile may overwrite it
   }
 

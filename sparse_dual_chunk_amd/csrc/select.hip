@@ -542,6 +542,32 @@ __global__ void plan_bits_kernel(PlanArgs A) {
   }
 }
 
+// Exact diagonals: the slash part of every row's mask, per range tile of a
+// head and row r of a 64-row block.  Slot x of a run that starts d keys after
+// the block's first row holds offset r - d - x from row r, whatever the block
+// (the tiles are shared by the head's blocks), so one table serves them all:
+// bit s is set when the offset of slot s is selected (or 0).  Four tiles of
+// 64 rows per workgroup; slots past the tile's runs stay clear.
+__global__ void __launch_bounds__(256) plan_smask_kernel(PlanArgs A) {
+  const int h = blockIdx.y;
+  const int t = 4 * blockIdx.x + (threadIdx.x >> 6);
+  const int r = threadIdx.x & 63;
+  if (t >= A.tile_stride) return;
+  uint32_t m = 0u;
+  if (t < A.n_tiles[h]) {
+    const int4 d = A.tiles[(long long)h * A.tile_stride + t];
+    const uint32_t* db = A.dbits + (long long)h * A.dbits_words;
+    const int len1 = d.z & 0xFF, len2 = (d.z >> 8) & 0xFF;
+    auto bit = [&](int off) -> uint32_t {   // off > -128 always (r >= 0, d < 64, x < 32)
+      const int b = off + 128;
+      return (db[b >> 5] >> (b & 31)) & 1u;
+    };
+    for (int x = 0; x < len1; ++x) m |= bit(r - d.x - x) << x;
+    for (int x = 0; x < len2; ++x) m |= bit(r - d.y - x) << (len1 + x);
+  }
+  A.smask[((long long)h * A.tile_stride + t) * 64 + r] = m;
+}
+
 // Exact diagonals: the (row, key) pairs of one head, sum over rows i of
 // |{delta selected (or 0) : delta <= p_i}| + |{j selected : j <= p_i}| minus the
 // keys that are both, i.e. the pairs (column j, offset delta) with
@@ -601,6 +627,8 @@ hipError_t launch_plan(const PlanArgs& A, hipStream_t stream) {
   const int units = A.h_q * A.nb;
   hipLaunchKernelGGL(plan_ext_kernel, dim3((units + 3) / 4), dim3(256), 0, stream, A);
   hipLaunchKernelGGL(plan_tiles_kernel, dim3((A.tile_stride + 255) / 256, A.h_q), dim3(256), 0, stream, A);
+  if (A.smask)
+    hipLaunchKernelGGL(plan_smask_kernel, dim3((A.tile_stride + 3) / 4, A.h_q), dim3(256), 0, stream, A);
   if (A.dbits && A.attended)
     hipLaunchKernelGGL(plan_attended_exact_kernel, dim3(A.h_q), dim3(1024), 0, stream, A);
   return hipGetLastError();
