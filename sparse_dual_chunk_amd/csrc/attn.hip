@@ -37,10 +37,6 @@ __device__ __forceinline__ int range_key(Tile T, int t) {
   return t < T.len1 ? T.a1 + t : (t < T.len1 + T.len2 ? T.a2 + (t - T.len1) : -1);
 }
 
-#ifndef DCA_DMA_ASM
-#define DCA_DMA_ASM 1
-#endif
-
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 // Buffer resource over [base, base + bytes): raw dwords, no stride.
@@ -289,15 +285,8 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A) {
   auto ext_key = [&](Tile T) __attribute__((always_inline)) -> int { return (l32 < T.cnt) ? ext_h[T.eoff + l32] : -1; };
   // K and V rows of this KV head through buffer resources: one 32-bit byte
   // offset per row serves both tensors (the host bounds n_k * h_kv * 256 < 2^32)
-#if DCA_DMA_ASM
-  typedef i32x4 Rsrc;
-  const Rsrc rs_k = raw_rsrc(kh_base, 0xFFFFFFFFu);
-  const Rsrc rs_v = raw_rsrc(v_base, 0xFFFFFFFFu);
-#else
-  typedef __amdgpu_buffer_rsrc_t Rsrc;
-  const Rsrc rs_k = __builtin_amdgcn_make_buffer_rsrc((void*)kh_base, (short)0, -1, 0x00020000);
-  const Rsrc rs_v = __builtin_amdgcn_make_buffer_rsrc((void*)v_base, (short)0, -1, 0x00020000);
-#endif
+  const i32x4 rs_k = raw_rsrc(kh_base, 0xFFFFFFFFu);
+  const i32x4 rs_v = raw_rsrc(v_base, 0xFFFFFFFFu);
   const int rowb = kstride * 2;
   const int lrow = lane >> 4;                       // row of a load's group this lane fills
   const int lchunk = 16 * ((lane & 15) ^ (5 * lrow));  // byte offset of the chunk it reads
@@ -341,15 +330,9 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A) {
     return f;
   };
   // the 4 direct loads of one tensor of a tile into a stage
-  auto issue = [&](Rsrc rs, uint8_t* stage, Offs f) __attribute__((always_inline)) {
+  auto issue = [&](i32x4 rs, uint8_t* stage, Offs f) __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < LPW; ++j)
-#if DCA_DMA_ASM
-      dma_b128(rs, lds_addr(stage + (NW * j + wave) * GRPB), f.v[j]);
-#else
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(stage + (NW * j + wave) * GRPB),
-                                               16, f.v[j], 0, 0, 0);
-#endif
+    for (int j = 0; j < LPW; ++j) dma_b128(rs, lds_addr(stage + (NW * j + wave) * GRPB), f.v[j]);
   };
 
   // ---- pipeline.  The K and V stages are released separately: step t
