@@ -69,16 +69,24 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
 }
 
+
 // NW waves of 32 rows per workgroup: 2 (one 64-row block) for every call; 4
 // (two adjacent blocks, 128 rows, sharing every staged K / V tile) for dense
 // calls whose pairs of blocks lie inside one DCA chunk: their key ranges
 // differ only by the 64 keys of the second block, so the pair walks its
 // union at no extra work and loads half the bytes per MFMA.  The DCA mode
 // boundaries are per workgroup, hence the one-chunk condition.
-template <bool DENSE, bool EXACT, int NW = 2>
+//
+// HP (dense calls, NW = 4): the four waves serve one 64-row block of two query
+// heads of one KV group (waves 0-1 and 2-3), which walk the same keys; with an
+// odd number of heads per group the last pair has one head and its second pair
+// of waves only keeps its place in the loads and barriers.
+template <bool DENSE, bool EXACT, int NW = 2, bool HP = false>
 __device__ __forceinline__ void attn_body(const AttnArgs& A) {
   static_assert(NW == 2 || (NW == 4 && DENSE), "four-wave workgroups serve dense calls");
-  constexpr int RB = 32 * NW;      // rows per workgroup
+  static_assert(!HP || NW == 4, "head pairs take four waves");
+  constexpr int NR = HP ? 2 : NW;  // waves per row block
+  constexpr int RB = 32 * NR;      // rows per block
   constexpr int LPW = 8 / NW;      // direct loads per wave and tensor of a tile
   constexpr int XL = EXACT ? 1 : 0;  // mask-word loads per lane and tile (exact diagonals)
   // K and V of the two stages are four LDS objects: the compiler then tells
@@ -91,6 +99,8 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: LDS bases stay scalar
+  const int wrow = HP ? (wave & 1) : wave;   // the wave's rows in its block: 32 wrow ..
+  const int hsub = HP ? (wave >> 1) : 0;     // its head in the pair
   const int half = lane >> 5;
   const int l32 = lane & 31;
 
@@ -108,14 +118,16 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A) {
   const int die = blockIdx.x % NXCD;
   const int local = blockIdx.x / NXCD;
   const int hpg = A.h_q / A.h_kv;
-  const int NBW = (A.nb + NW / 2 - 1) / (NW / 2);   // row groups of RB rows
+  const int NBW = (A.nb + NR / 2 - 1) / (NR / 2);   // row groups of RB rows
+  const int hpw = HP ? (hpg + 1) / 2 : hpg;          // work items per KV group and row
   int b, h, part;
   int mpos = 0;              // the block's place in its die's row sequence (split calls)
+  bool idle = false;         // the absent second head of a pair (HP)
   if (NXCD % A.h_kv == 0) {
     const int dpg = NXCD / A.h_kv;                 // dies per KV group
     const int rows = (NBW + dpg - 1) / dpg;        // block rows of this die
-    part = local / (rows * hpg);
-    const int rem = local % (rows * hpg);
+    part = local / (rows * hpw);
+    const int rem = local % (rows * hpw);
     // split calls: each die takes a contiguous half of the block rows (the
     // halves swap with the part), so the rows in flight on a die are adjacent
     // and read nearly the same keys; one part: rows interleave (balance)
@@ -124,23 +136,27 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A) {
     if (cidx >= NBW) return;
     b = NBW - 1 - cidx;
     mpos = A.split > 1 ? rem % rows : 0;
-    h = ((die + part) % A.h_kv) * hpg + rem / rows;
+    h = ((die + part) % A.h_kv) * hpg + (HP ? 2 * (rem / rows) + hsub : rem / rows);
+    idle = HP && 2 * (rem / rows) + hsub >= hpg;
   } else {
     const int rows = (NBW + NXCD - 1) / NXCD;
-    part = local / (rows * A.h_q);
-    const int rem = local % (rows * A.h_q);
+    part = local / (rows * A.h_kv * hpw);
+    const int rem = local % (rows * A.h_kv * hpw);
     const int cidx = NXCD * (rem % rows) + die;
     if (cidx >= NBW) return;
     b = NBW - 1 - cidx;
-    h = rem / rows;
+    const int item = rem / rows;
+    h = HP ? (item / hpw) * hpg + 2 * (item % hpw) + hsub : item;
+    idle = HP && 2 * (item % hpw) + hsub >= hpg;
   }
+  if (idle) h -= 1;   // a valid head for the addresses; nothing is computed or written
   const int g = h / (A.h_q / A.h_kv);
 
   const int i0 = A.p0 + RB * b;                  // absolute position of the block's first row
   const int rows = min(RB, A.n_q - RB * b);
   const int hi_key = i0 + rows;                  // keys [0, hi_key): the block's causal extent
   const int m_blk = i0 / A.S;
-  const int rloc = 32 * wave + l32;              // row inside the block owned by this lane
+  const int rloc = 32 * wrow + l32;              // row inside the block owned by this lane
   const bool row_ok = rloc < rows;
   const int qrow = RB * b + (row_ok ? rloc : 0);
   const int prow = i0 + rloc;                    // absolute position of this lane's row
@@ -444,7 +460,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A) {
     // attends costs no MFMA, softmax or P V: the wave only keeps its place in
     // the step's loads and barriers.
     uint32_t xm = 0u;
-    bool skip = false;
+    bool skip = HP && idle;
     if (EXACT && !T.cnt) {
       xm = smk | vert_bits(T);
       skip = !__any(xm != 0u);
@@ -598,9 +614,9 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A) {
     vm_wait(2 * LPW + XL);
     wg_barrier();          // B1: K(ti) visible; V(ti-1)'s stage is free
     issue(rs_v, vn, f_n);
-    Tile T_2 = T_dummy;
     bool p_2 = false;
     Offs f_2;
+    Tile T_2 = T_dummy;
     auto after_qk = [&]() __attribute__((always_inline)) {
       wg_barrier();        // B2: both waves are done with K(ti)
       const int px = phys(ti + 2);
@@ -644,7 +660,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A) {
   const float inv_l = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const float lse2 = l_tot > 0.f ? m_run + __log2f(l_tot) : -INFINITY;
   const float lse = lse2 * 0.69314718055994531f;
-  if (!row_ok) return;
+  if (!row_ok || idle) return;
   if (A.split == 1) {
     uint16_t* dst = A.out + ((long long)qrow * A.h_q + h) * D;
 #pragma unroll
@@ -686,6 +702,7 @@ __global__ void __launch_bounds__(128, 2) dca_attn_kernel(AttnArgs A) { attn_bod
 __global__ void __launch_bounds__(128, 2) dca_attn_exact_kernel(AttnArgs A) { attn_body<false, true>(A); }
 __global__ void __launch_bounds__(128, 2) dca_attn_dense_kernel(AttnArgs A) { attn_body<true, false>(A); }
 __global__ void __launch_bounds__(256, 2) dca_attn_dense4_kernel(AttnArgs A) { attn_body<true, false, 4>(A); }
+__global__ void __launch_bounds__(256, 2) dca_attn_dense_hp_kernel(AttnArgs A) { attn_body<true, false, 4, true>(A); }
 
 // LSE merge of the key parts of one (row, head): m = max_p lse_p,
 // O = sum_p e^{lse_p - m} O_p / sum_p e^{lse_p - m}.  One wave per (row, head):
@@ -752,13 +769,26 @@ hipError_t launch_attn_pipe(const AttnArgs& A, hipStream_t stream);
 #define DCA_ATTN_PIPE 0
 #endif
 
+
 hipError_t launch_attn(const AttnArgs& A, hipStream_t stream) {
   if (DCA_ATTN_PIPE && !A.exact) return launch_attn_pipe(A, stream);
   // every die runs split * (its block rows) * (heads per row) workgroups
   // dense calls: workgroups of two blocks (128 rows) when no pair can straddle
   // a DCA chunk boundary (the workgroup's rows must share one chunk), i.e. S
   // and p0 multiples of 128; else one block per workgroup
+  // dense calls whose block pairs may straddle a chunk, with an even number of
+  // query heads per KV group: workgroups of two heads of one block instead
+  // (the same sharing of each staged tile; with an odd number per group the
+  // idle half of the last pair costs more than the sharing gains)
+  const int hpg = A.h_q / A.h_kv;
   const bool pairs = A.dense && A.S % 128 == 0 && A.p0 % 128 == 0;
+  if (A.dense && !pairs && hpg % 2 == 0) {
+    const int hpw = hpg / 2;
+    const int blocks = NXCD % A.h_kv == 0 ? NXCD * A.split * ((A.nb + NXCD / A.h_kv - 1) / (NXCD / A.h_kv)) * hpw
+                                          : NXCD * A.split * ((A.nb + NXCD - 1) / NXCD) * A.h_kv * hpw;
+    hipLaunchKernelGGL(dca_attn_dense_hp_kernel, dim3(blocks), dim3(256), 0, stream, A);
+    return hipGetLastError();
+  }
   const int nbw = pairs ? (A.nb + 1) / 2 : A.nb;
   const int blocks = NXCD % A.h_kv == 0
       ? NXCD * A.split * ((nbw + NXCD / A.h_kv - 1) / (NXCD / A.h_kv)) * (A.h_q / A.h_kv)
