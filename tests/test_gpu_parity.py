@@ -145,11 +145,16 @@ def test_determinism_bitwise():
 # ------------------------------------------------------------------ head counts
 # Workgroups map to the 8 dies per KV group when the KV-head count divides 8
 # (1, 2, 4, 8); other counts (3, 5, 16 here) take the all-heads mapping.  Also
-# one query head per KV head (no grouping).
+# one query head per KV head (no grouping).  Dense workgroups: two blocks when
+# p0 and S are multiples of 128, else two heads of one block when a group has
+# an even number of heads, else one block of one head.
 @pytest.mark.parametrize("h_q,h_kv,p0,n_q,split", [(6, 3, 0, 200, 0),      # two-block workgroups
-                                                   (6, 3, 192, 150, 2),    # one block per workgroup, split
+                                                   (6, 3, 192, 150, 2),    # head pairs, split
+                                                   (8, 4, 320, 190, 0),    # head pairs, die-per-group mapping
+                                                   (8, 2, 64, 130, 3),     # head pairs, four heads per group
                                                    (10, 5, 256, 64, 1),
-                                                   (16, 16, 128, 130, 0)])
+                                                   (16, 16, 128, 130, 0),
+                                                   (4, 4, 64, 100, 0)])    # one block of one head
 def test_dense_head_counts(h_q, h_kv, p0, n_q, split):
     inp = _inputs(60 + h_kv + p0, p0, n_q, h_q, h_kv, sinks=True)
     cfg = _cfg(inp, h_q, h_kv, 256, 64, split_k=split)
