@@ -21,7 +21,7 @@ hipError_t launch_paged_gather(const uint16_t* khi_p, const uint16_t* klo_p, con
                                const uint32_t* flags_p, const int32_t* ptab, int page_keys, int n_pages, int n_table,
                                int n_k, int h_kv, int kbits_words, uint16_t* khi, uint16_t* klo, uint16_t* vd,
                                uint32_t* kbits, hipStream_t stream);
-hipError_t launch_hn_list(const uint32_t* kbits, int kbits_words, int n_k, int h_kv, int32_t* hnl, int32_t* hnl_n,
+hipError_t launch_hn_list(const uint32_t* kbits, int kbits_words, int n_k, int h_kv, int32_t* hnl_n, int32_t* hnall,
                           hipStream_t stream);
 hipError_t launch_rotate_queries(const uint16_t* q, uint16_t* qhi, uint16_t* qlo, const double* inv_freq,
                                  int n_q, int h_q, int p0, int S, int W, float qscale, hipStream_t stream);
@@ -73,12 +73,16 @@ inline size_t up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 
 struct Region { size_t off = 0, bytes = 0; };
 
+// entries per (head, block) of the extra-vertical lists: the vertical columns
+// the ranges miss, and up to HN_MOVE_CAP covered high-norm keys
+int ext_stride(const dca_cfg* c) { return (c->vs_k_vertical > 0 ? c->vs_k_vertical : 1) + HN_MOVE_CAP; }
+
 // Workspace layouts of the two entry points (regions are 256-byte aligned).
 struct Layout {
   // shared
   Region freqs, flag;
   // prefill
-  Region hnl, hnl_n, ev, npe;
+  Region hnl_n, hnall;
   Region khi, klo, kbits, hn, qhi, qlo, iv, iv_pre, n_iv, cov, ext, n_ext, tiles, n_tiles, t_first, part_o, part_lse;
   Region dbits, vbits, smask;
   Region vg;             // values gathered from a paged pool
@@ -152,8 +156,8 @@ Layout make_layout(const dca_cfg* c, bool paged = false) {
   place(L.kbits, cur, (size_t)h_kv * L.kbits_words * 4);
   L.hn_pad = (n_k + 128 + 3) / 4 * 4;   // runs may start up to 95 keys past n_k - 1
   place(L.hn, cur, (size_t)h_kv * L.hn_pad);
-  place(L.hnl, cur, (size_t)h_kv * HN_CAP * 4);
   place(L.hnl_n, cur, (size_t)h_kv * 4);
+  place(L.hnall, cur, (size_t)h_kv * HN_MOVE_CAP * 4);
   place(L.qhi, cur, (size_t)3 * n_q * h_q * D * 2);
   place(L.qlo, cur, (size_t)3 * n_q * h_q * D * 2);
   place(L.iv, cur, (size_t)h_q * (c->vs_k_slash + 1) * 2 * 4);
@@ -161,15 +165,13 @@ Layout make_layout(const dca_cfg* c, bool paged = false) {
   place(L.n_iv, cur, (size_t)h_q * 4);
   L.cov_words = (p_last + 64 + 31) / 32;
   place(L.cov, cur, (size_t)h_q * L.cov_words * 4);
-  place(L.ext, cur, (size_t)h_q * L.nb * (size_t)(c->vs_k_vertical > 0 ? c->vs_k_vertical : 1) * 4);
+  place(L.ext, cur, (size_t)h_q * L.nb * (size_t)ext_stride(c) * 4);
   place(L.n_ext, cur, (size_t)h_q * L.nb * 4);
   // range tiles of 32 covered offsets: every merged interval is at least 64 long
   L.tile_stride = 2 * (c->vs_k_slash + 1) + 1;
   place(L.tiles, cur, (size_t)h_q * L.tile_stride * 16);
   place(L.n_tiles, cur, (size_t)h_q * 4);
   place(L.t_first, cur, (size_t)h_q * L.nb * 4);
-  place(L.ev, cur, (size_t)h_q * L.nb * EV_REC * 4);
-  place(L.npe, cur, (size_t)h_q * 4);
   if (c->slash_exact) {
     // windows of up to 8 words start between bit 34 and bit p_last + 160
     L.dbits_words = (p_last + 160) / 32 + 9;
@@ -445,7 +447,7 @@ int prefill_impl(const dca_bf16* q, const dca_bf16* k, const dca_key_cache* cach
   }
   if (launch_hn_next(kbits, at<uint8_t>(cfg, L.hn), L.hn_pad, h_kv, kbits_words, st) != hipSuccess)
     return DCA_EHIP;
-  if (launch_hn_list(kbits, kbits_words, n_k, h_kv, at<int32_t>(cfg, L.hnl), at<int32_t>(cfg, L.hnl_n), st) !=
+  if (launch_hn_list(kbits, kbits_words, n_k, h_kv, at<int32_t>(cfg, L.hnl_n), at<int32_t>(cfg, L.hnall), st) !=
       hipSuccess)
     return DCA_EHIP;
   // softmax scale sqrt(1/t)^2 / sqrt(d) and log2(e) (the kernel works in base 2)
@@ -465,7 +467,7 @@ int prefill_impl(const dca_bf16* q, const dca_bf16* k, const dca_key_cache* cach
     P.ext = at<int32_t>(cfg, L.ext); P.n_ext = at<int32_t>(cfg, L.n_ext);
     P.h_q = h_q; P.k_v = cfg->vs_k_vertical; P.k_s = cfg->vs_k_slash; P.p_last = p_last; P.p0 = p0;
     P.n_q = n_q; P.nb = L.nb; P.iv_stride = cfg->vs_k_slash + 1;
-    P.ext_stride = cfg->vs_k_vertical > 0 ? cfg->vs_k_vertical : 1; P.cov_words = L.cov_words;
+    P.ext_stride = ext_stride(cfg); P.cov_words = L.cov_words;
     P.tiles = at<int4>(cfg, L.tiles); P.n_tiles = at<int32_t>(cfg, L.n_tiles); P.t_first = at<int32_t>(cfg, L.t_first);
     P.kbits = kbits; P.h_kv = h_kv; P.tile_stride = L.tile_stride;
     P.kbits_words = kbits_words;
@@ -475,8 +477,8 @@ int prefill_impl(const dca_bf16* q, const dca_bf16* k, const dca_key_cache* cach
     P.dbits_words = L.dbits_words; P.vbits_words = L.vbits_words;
     P.attended = (long long*)cfg->attended_pairs;
     P.bad = bad;
-    P.hnl = at<int32_t>(cfg, L.hnl); P.hnl_n = at<int32_t>(cfg, L.hnl_n);
-    P.ev = at<int32_t>(cfg, L.ev); P.npe = at<int32_t>(cfg, L.npe); P.S = cfg->dca_chunk;
+    P.hnl_n = at<int32_t>(cfg, L.hnl_n); P.hnall = at<int32_t>(cfg, L.hnall);
+    P.S = cfg->dca_chunk;
     if (launch_plan(P, st) != hipSuccess) return DCA_EHIP;
   } else if (cfg->cover_pairs || cfg->attended_pairs) {
     // dense: every block covers its whole causal extent [0, i0 + rows); row i attends p_i + 1 keys
@@ -503,7 +505,7 @@ int prefill_impl(const dca_bf16* q, const dca_bf16* k, const dca_key_cache* cach
   A.ext = at<int32_t>(cfg, L.ext); A.n_ext = at<int32_t>(cfg, L.n_ext);
   A.n_q = n_q; A.n_k = n_k; A.h_q = h_q; A.h_kv = h_kv; A.p0 = p0; A.S = cfg->dca_chunk; A.W = cfg->dca_local;
   A.nb = L.nb; A.tile_stride = L.tile_stride; A.kbits_words = kbits_words;
-  A.ext_stride = cfg->vs_k_vertical > 0 ? cfg->vs_k_vertical : 1;
+  A.ext_stride = ext_stride(cfg);
   A.split = L.split; A.dense = sparse ? 0 : 1;
   A.exact = (sparse && cfg->slash_exact) ? 1 : 0;
   A.dbits = A.exact ? at<uint32_t>(cfg, L.dbits) : nullptr;
@@ -511,8 +513,7 @@ int prefill_impl(const dca_bf16* q, const dca_bf16* k, const dca_key_cache* cach
   A.smask = A.exact ? at<uint32_t>(cfg, L.smask) : nullptr;
   A.dbits_words = L.dbits_words; A.vbits_words = L.vbits_words;
   A.bad = bad;
-  A.hnl = at<int32_t>(cfg, L.hnl); A.hnl_n = at<int32_t>(cfg, L.hnl_n);
-  A.ev = sparse ? at<int32_t>(cfg, L.ev) : nullptr; A.npe = sparse ? at<int32_t>(cfg, L.npe) : nullptr;
+  A.hnl_n = at<int32_t>(cfg, L.hnl_n);
   if (launch_attn(A, st) != hipSuccess) return DCA_EHIP;
   record(cfg, 2, 1);
   // stage 3: LSE merge of the split partials

@@ -5,16 +5,11 @@
 
 namespace dca {
 
-// High-norm keys listed per KV head (the first HN_CAP, ascending) for the
-// attention walk's event lists; more than HN_CAP makes every tile an event.
-constexpr int HN_CAP = 64;
-// Per (head, query block) event record of the plan: [0], [1] the range tiles
-// (relative to the block's first) holding the first covered key of the
-// successive-chunk and intra-chunk DCA modes (-1: none), [2] the number n of
-// range tiles holding a high-norm key (-1: too many to list), [3, 3 + n)
-// those tiles, ascending.
-constexpr int EV_REC = 32;
-constexpr int EV_PREC = EV_REC - 3;
+// A sparse block-cover call whose KV head has at most HN_MOVE_CAP high-norm
+// keys takes the covered ones below a block's first row out of the block's
+// range tiles (there they are masked, so those tiles need one MFMA pass) and
+// lists them with the block's extra-vertical keys (split-precision logits).
+constexpr int HN_MOVE_CAP = 1024;
 
 struct AttnArgs {
   const uint16_t* qhi;      // [3 modes][n_q][h_q][128] rotated query * scale * log2(e), bf16 hi
@@ -31,7 +26,9 @@ struct AttnArgs {
   const int4* tiles;        // [h_q][tile_stride] range tiles in offset space: {o1, o2, len1 | len2 << 8, 0}
   const int32_t* n_tiles;   // [h_q]
   const int32_t* t_first;   // [h_q][nb] first range tile of each query block
-  const int32_t* ext;       // [h_q][nb][ext_stride] vertical keys outside the ranges (bit 30: high-norm)
+  const int32_t* ext;       // [h_q][nb][ext_stride] vertical keys outside the ranges and, with few high-norm
+                            // keys, the covered high-norm keys below the block (bit 30: high-norm), ordered
+                            // by DCA mode
   const int32_t* n_ext;     // [h_q][nb]
   const uint32_t* dbits;    // exact diagonals: [h_q][dbits_words] bit delta + 128 = selected offset (and 0)
   const uint32_t* vbits;    // exact diagonals: [h_q][vbits_words] bit j + 128 = selected vertical column
@@ -40,10 +37,7 @@ struct AttnArgs {
   int n_q, n_k, h_q, h_kv, p0, S, W, nb, tile_stride, ext_stride, split, dense, kbits_words, hn_pad;
   int exact, dbits_words, vbits_words;
   const int32_t* bad;       // device flag set by the positions check: write no output when nonzero (or null)
-  const int32_t* hnl;       // [h_kv][HN_CAP] the first high-norm keys of each KV head, ascending
-  const int32_t* hnl_n;     // [h_kv] how many high-norm keys the head has (may exceed HN_CAP)
-  const int32_t* ev;        // [h_q][nb][EV_REC] event records of the range walk (sparse calls)
-  const int32_t* npe;       // [h_q] first range tile holding an offset above 0 (sparse calls)
+  const int32_t* hnl_n;     // [h_kv] how many high-norm keys the head has (counting stops past HN_MOVE_CAP)
 };
 
 struct DecArgs {
@@ -109,10 +103,8 @@ struct PlanArgs {
   long long* cover_pairs;  // optional: sum of rows * |cover| over all (head, block)
   long long* attended;     // optional: sum over heads and rows of the attended (row, key) pairs
   const int32_t* bad;      // device flag set by the positions check: write no output when nonzero (or null)
-  const int32_t* hnl;      // [h_kv][HN_CAP] the first high-norm keys of each KV head, ascending
-  const int32_t* hnl_n;    // [h_kv] their number (may exceed HN_CAP)
-  int32_t* ev;             // [h_q][nb][EV_REC] event records of the attention walk
-  int32_t* npe;            // [h_q] first range tile holding an offset above 0
+  const int32_t* hnl_n;    // [h_kv] how many high-norm keys the head has (counting stops past HN_MOVE_CAP)
+  const int32_t* hnall;    // [h_kv][HN_MOVE_CAP] the first high-norm keys of each KV head, ascending
   int S;                   // DCA chunk size
   uint32_t* dbits;         // exact diagonals (or null): [h_q][dbits_words], bit delta + 128
   uint32_t* vbits;         // exact diagonals (or null): [h_q][vbits_words], bit j + 128

@@ -81,7 +81,12 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // heads of one KV group (waves 0-1 and 2-3), which walk the same keys; with an
 // odd number of heads per group the last pair has one head and its second pair
 // of waves only keeps its place in the loads and barriers.
-template <bool DENSE, bool EXACT, int NW = 2, bool HP = false>
+//
+// HNM (sparse block-cover calls): the work items of KV heads with at most
+// HN_MOVE_CAP high-norm keys, whose covered high-norm keys the plan lists with
+// the extra keys: a range tile masks its high-norm slots and needs no
+// split-precision pass.  The instance without HNM takes the other heads.
+template <bool DENSE, bool EXACT, int NW = 2, bool HP = false, bool HNM = false>
 __device__ __forceinline__ void attn_body(const AttnArgs& A) {
   static_assert(NW == 2 || (NW == 4 && DENSE), "four-wave workgroups serve dense calls");
   static_assert(!HP || NW == 4, "head pairs take four waves");
@@ -151,6 +156,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A) {
   }
   if (idle) h -= 1;   // a valid head for the addresses; nothing is computed or written
   const int g = h / (A.h_q / A.h_kv);
+  if (!DENSE && !EXACT && HNM != (A.hnl_n[g] <= HN_MOVE_CAP)) return;   // the other instance's item
 
   const int i0 = A.p0 + RB * b;                  // absolute position of the block's first row
   const int rows = min(RB, A.n_q - RB * b);
@@ -258,6 +264,30 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A) {
   };
   auto range_precise = [&](Tile T) __attribute__((always_inline)) -> bool {
     return run_flagged(T.a1, T.len1) || run_flagged(T.a2, T.len2);
+  };
+  // HNM: the plan lists the covered high-norm keys with the block's extra
+  // keys, so a range tile masks its high-norm slots, found in the flag bitmap
+  // (two words per run; indexes clamped into it: the slots of keys past n_k
+  // are masked anyway).
+  cu32* kb4 = (cu32*)(A.kbits + (long long)g * A.kbits_words);
+  auto run_hn = [&](int a, int len) __attribute__((always_inline)) -> uint32_t {   // bit t: key a + t high-norm
+    const int ac = max(a, 0);
+    const int sh = ac - a;
+    if (sh >= len) return 0u;
+    const int w = ac >> 5;
+    const uint32_t w0 = kb4[min(w, A.kbits_words - 1)], w1 = kb4[min(w + 1, A.kbits_words - 1)];
+    uint32_t v = (uint32_t)((((uint64_t)w1 << 32) | w0) >> (ac & 31));
+    const int n = len - sh;
+    if (n < 32) v &= (1u << n) - 1u;
+    return v << sh;
+  };
+  // the slots to mask (HNM) and whether the split-precision passes are needed
+  auto hn_split = [&](Tile T, uint32_t& mv) __attribute__((always_inline)) -> bool {
+    mv = 0u;
+    if (!range_precise(T)) return false;
+    if (!HNM) return true;
+    mv = run_hn(T.a1, T.len1) | (T.len1 < 32 ? run_hn(T.a2, T.len2) << T.len1 : 0u);
+    return false;
   };
   // Exact-diagonal semantics: the slots of a range tile that this lane's row
   // attends are the tile's slash slots for the row (its offset prow - key is
@@ -426,7 +456,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A) {
   // have such slots).  Then one online softmax and one O += P V.  after_qk
   // runs once S^T is done (B2 and the K issue), B3 before the V reads.
   auto compute_tile = [&](const uint8_t* kt, const uint8_t* vt, Tile T, int skey, bool precise, uint32_t smk,
-                          auto&& after_qk) __attribute__((always_inline)) {
+                          uint32_t mv, auto&& after_qk) __attribute__((always_inline)) {
     const int count = tile_count(T);
     int key_first, key_last;
     if (T.cnt) {
@@ -485,10 +515,28 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A) {
     if (mode_first + 1 <= mode_last) merge_mode(mode_first + 1);
     if (mode_first + 2 <= mode_last) merge_mode(mode_first + 2);
     if (count < BN || key_first < 0 || key_last > i0) {
-      // extra-vertical keys all lie below the block (its own keys are range-covered)
+      // the keys of an extra tile at or above the block's first row (listed
+      // high-norm keys) are its ascending last slots: the row keeps the slots
+      // of the tile's keys up to its own position, counted slot by slot
+      // (below() counts for wave-uniform bounds only)
       const int t_lo = T.cnt ? 0 : below(0);
-      const int t_hi = T.cnt ? count : below(prow + 1);
+      int t_hi;
+      if (T.cnt) {
+        t_hi = 0;
+        for (int t = 0; t < count; ++t) t_hi += (__builtin_amdgcn_readlane(skey, t) & 0x3FFFFFFF) <= prow;
+      } else {
+        t_hi = below(prow + 1);
+      }
       select_slots(s, t_lo, t_hi, -INFINITY);
+    }
+    if (HNM && mv) {
+      // high-norm keys taken by the extra list: slot c + 4 half is bit c of xh
+      const uint32_t xh = mv >> (4 * half);
+#pragma unroll
+      for (int vv = 0; vv < 16; ++vv) {
+        const int c = 8 * (vv >> 2) + (vv & 3);
+        if ((xh >> c) & 1u) s[vv] = -INFINITY;
+      }
     }
     if (EXACT && !T.cnt) {
       // bit c of xh is slot c + 4 half; each score keeps s - m_run where its
@@ -599,12 +647,14 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A) {
   mask_issue(phys(t0), t0);
   issue(rs_k, kst0, f_c);
   issue(rs_v, vst0, f_c);
-  bool p_c = t0 < r_end && range_precise(T_c);
+  uint32_t mv_c = 0u;
+  bool p_c = t0 < r_end && hn_split(T_c, mv_c);
   Tile T_n = range_tile(phys(t0 + 1), desc_load(phys(t0 + 1)));
   Offs f_n = tile_offsets(t0 + 1 < r_end ? T_n : T_dummy, -1, true);
   mask_issue(phys(t0 + 1), t0 + 1);
   issue(rs_k, kst1, f_n);
-  bool p_n = t0 + 1 < r_end && range_precise(T_n);
+  uint32_t mv_n = 0u;
+  bool p_n = t0 + 1 < r_end && hn_split(T_n, mv_n);
   int4 d_2 = desc_load(phys(t0 + 2));
 
   // One step on range tile ti: its stages kc / vc, and vn, the V stage of tile ti+1.
@@ -615,6 +665,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A) {
     wg_barrier();          // B1: K(ti) visible; V(ti-1)'s stage is free
     issue(rs_v, vn, f_n);
     bool p_2 = false;
+    uint32_t mv_2 = 0u;
     Offs f_2;
     Tile T_2 = T_dummy;
     auto after_qk = [&]() __attribute__((always_inline)) {
@@ -625,12 +676,12 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A) {
       f_2 = tile_offsets(ti + 2 < r_end ? T_2 : T_dummy, -1, clamp_all || px == 0);
       mask_issue(px, ti + 2);
       issue(rs_k, kc, f_2);
-      p_2 = ti + 2 < r_end && range_precise(T_2);
+      p_2 = ti + 2 < r_end && hn_split(T_2, mv_2);
       d_2 = desc_load(phys(ti + 3));
     };
-    compute_tile(kc, vc, T_c, -1, p_c, mask_read(ti), after_qk);
-    T_c = T_n; p_c = p_n;
-    T_n = T_2; p_n = p_2; f_n = f_2;
+    compute_tile(kc, vc, T_c, -1, p_c, mask_read(ti), mv_c, after_qk);
+    T_c = T_n; p_c = p_n; mv_c = mv_n;
+    T_n = T_2; p_n = p_2; mv_n = mv_2; f_n = f_2;
   };
   for (int ti = t_beg; ti < r_end; ti += 2) {
     step(kst0, vst0, vst1, ti);
@@ -651,7 +702,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A) {
     issue(rs_v, vst0, f);
     vm_wait(0);
     wg_barrier();
-    compute_tile(kst0, vst0, T, sk, prec, 0u, [] {});
+    compute_tile(kst0, vst0, T, sk, prec, 0u, 0u, [] {});
     wg_barrier();          // the stage is read; the next tile may overwrite it
   }
 
@@ -698,7 +749,8 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A) {
 // sparse (vertical-slash) calls, sparse calls with exact diagonals, and dense
 // calls: one body, the variant known at compile time (the exact masks cost
 // registers the other two do not pay for)
-__global__ void __launch_bounds__(128, 2) dca_attn_kernel(AttnArgs A) { attn_body<false, false>(A); }
+__global__ void __launch_bounds__(128, 2) dca_attn_kernel(AttnArgs A) { attn_body<false, false, 2, false, true>(A); }
+__global__ void __launch_bounds__(128, 2) dca_attn_hn_kernel(AttnArgs A) { attn_body<false, false>(A); }
 __global__ void __launch_bounds__(128, 2) dca_attn_exact_kernel(AttnArgs A) { attn_body<false, true>(A); }
 __global__ void __launch_bounds__(128, 2) dca_attn_dense_kernel(AttnArgs A) { attn_body<true, false>(A); }
 __global__ void __launch_bounds__(256, 2) dca_attn_dense4_kernel(AttnArgs A) { attn_body<true, false, 4>(A); }
@@ -763,15 +815,7 @@ __global__ void __launch_bounds__(256) lse_merge_kernel(const uint16_t* __restri
   if (lse_out && dc == 0) lse_out[(long long)h * n_q + row] = (wsum > 0.f) ? m + __logf(wsum) : -INFINITY;
 }
 
-hipError_t launch_attn_pipe(const AttnArgs& A, hipStream_t stream);
-
-#ifndef DCA_ATTN_PIPE
-#define DCA_ATTN_PIPE 0
-#endif
-
-
 hipError_t launch_attn(const AttnArgs& A, hipStream_t stream) {
-  if (DCA_ATTN_PIPE && !A.exact) return launch_attn_pipe(A, stream);
   // every die runs split * (its block rows) * (heads per row) workgroups
   // dense calls: workgroups of two blocks (128 rows) when no pair can straddle
   // a DCA chunk boundary (the workgroup's rows must share one chunk), i.e. S
@@ -800,7 +844,11 @@ hipError_t launch_attn(const AttnArgs& A, hipStream_t stream) {
   } else if (A.exact) {
     hipLaunchKernelGGL(dca_attn_exact_kernel, dim3(blocks), dim3(128), 0, stream, A);
   } else {
+    // block cover: KV heads with few high-norm keys, then the others (each
+    // launch leaves the other's work items alone)
     hipLaunchKernelGGL(dca_attn_kernel, dim3(blocks), dim3(128), 0, stream, A);
+    if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+    hipLaunchKernelGGL(dca_attn_hn_kernel, dim3(blocks), dim3(128), 0, stream, A);
   }
   return hipGetLastError();
 }

@@ -260,12 +260,12 @@ hipError_t launch_paged_gather(const uint16_t* khi_p, const uint16_t* klo_p, con
   return hipGetLastError();
 }
 
-// The first HN_CAP high-norm keys j < n_k of each KV head, ascending, and how
-// many there are in all (counting stops once it exceeds HN_CAP).  One
+// The first HN_MOVE_CAP high-norm keys j < n_k of each KV head, ascending, and
+// how many there are in all (counting stops once it exceeds HN_MOVE_CAP).  One
 // workgroup of 1024 threads per KV head: each round scans 1024 flag words,
 // places every word's keys after an exclusive prefix sum of the words' counts.
 __global__ void __launch_bounds__(1024) hn_list_kernel(const uint32_t* __restrict__ kbits, int kbits_words, int n_k,
-                                                       int32_t* __restrict__ hnl, int32_t* __restrict__ hnl_n) {
+                                                       int32_t* __restrict__ hnl_n, int32_t* __restrict__ hnall) {
   __shared__ int wave_tot[16];
   __shared__ int base_s;
   const int g = blockIdx.x;
@@ -290,7 +290,7 @@ __global__ void __launch_bounds__(1024) hn_list_kernel(const uint32_t* __restric
     for (int i = 0; i < wv; ++i) before += wave_tot[i];
     int pos = before + incl - c;
     while (word) {
-      if (pos < HN_CAP) hnl[g * HN_CAP + pos] = 32 * w + __builtin_ctz(word);
+      if (pos < HN_MOVE_CAP) hnall[g * HN_MOVE_CAP + pos] = 32 * w + __builtin_ctz(word);
       ++pos;
       word &= word - 1u;
     }
@@ -301,14 +301,14 @@ __global__ void __launch_bounds__(1024) hn_list_kernel(const uint32_t* __restric
       base_s = t;
     }
     __syncthreads();
-    if (base_s > HN_CAP) break;
+    if (base_s > HN_MOVE_CAP) break;
   }
   if (tid == 0) hnl_n[g] = base_s;
 }
 
-hipError_t launch_hn_list(const uint32_t* kbits, int kbits_words, int n_k, int h_kv, int32_t* hnl, int32_t* hnl_n,
-                          hipStream_t stream) {
-  hipLaunchKernelGGL(hn_list_kernel, dim3(h_kv), dim3(1024), 0, stream, kbits, kbits_words, n_k, hnl, hnl_n);
+hipError_t launch_hn_list(const uint32_t* kbits, int kbits_words, int n_k, int h_kv, int32_t* hnl_n,
+                          int32_t* hnall, hipStream_t stream) {
+  hipLaunchKernelGGL(hn_list_kernel, dim3(h_kv), dim3(1024), 0, stream, kbits, kbits_words, n_k, hnl_n, hnall);
   return hipGetLastError();
 }
 

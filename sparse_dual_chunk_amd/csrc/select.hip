@@ -375,8 +375,16 @@ __device__ inline long long covered_below(const int32_t* ivh, const int32_t* pre
 
 // One wave per (head, query block): vertical columns inside the block's causal
 // extent that the block's ranges miss, ascending, duplicates dropped; bit 30
-// of an entry marks a high-norm key.  Also the block's first range tile (the
-// one holding its lowest in-range offset) and its cover size.
+// of an entry marks a high-norm key.  For a block-cover call whose KV head has
+// at most HN_MOVE_CAP high-norm keys, the list also takes the high-norm keys
+// of the block's causal extent that the ranges cover (the attention walk masks
+// them in the range tiles): the list is then ordered by DCA mode (inter-chunk,
+// successive, intra-chunk), each mode's columns first, then its high-norm
+// keys, so every 32 entries still hold each mode's keys in one run of slots,
+// and the keys at or above the block's first row, all intra-chunk, are the
+// list's ascending tail.
+// Also the block's first range tile (the one holding its lowest in-range
+// offset) and its cover size.
 __global__ void __launch_bounds__(256) plan_ext_kernel(PlanArgs A) {
   const int unit = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -390,7 +398,28 @@ __global__ void __launch_bounds__(256) plan_ext_kernel(PlanArgs A) {
   const uint32_t* cv = A.cov + (long long)h * A.cov_words;
   const uint32_t* kb = A.kbits + (long long)g * A.kbits_words;
   int32_t* dst = A.ext + ((long long)h * A.nb + b) * A.ext_stride;
-  int cnt = 0;
+  const int m_blk = i0 / A.S;
+  const int segA = max(0, (m_blk - 1) * A.S);    // DCA modes: [0, segA), [segA, segB), [segB, ..)
+  const int segB = max(0, m_blk * A.S);
+  // covered high-norm keys of the block's causal extent, per mode (ascending in the list)
+  const int n_mv = (!A.dbits && A.hnl_n[g] <= HN_MOVE_CAP) ? A.hnl_n[g] : 0;
+  const int32_t* hall = A.hnall + (long long)g * HN_MOVE_CAP;
+  auto moved = [&](int t, int& j) -> bool {
+    if (t >= n_mv) return false;
+    j = hall[t];
+    if (j >= hi_key) return false;
+    const int bit = j - i0 + A.p_last;
+    return (cv[bit >> 5] >> (bit & 31)) & 1u;
+  };
+  int mb0 = 0, mb1 = 0, mbn = 0;   // moved keys below segA, below segB, in all
+  for (int base = 0; base < n_mv; base += 64) {
+    int j = 0;
+    const bool mk = moved(base + lane, j);
+    mb0 += __popcll(__ballot(mk && j < segA));
+    mb1 += __popcll(__ballot(mk && j < segB));
+    mbn += __popcll(__ballot(mk));
+  }
+  int cnt = 0, ca0 = 0, ca1 = 0;   // columns in all, below segA, below segB
   for (int base = 0; base < A.k_v; base += 64) {
     const int t = base + lane;
     bool keep = false;
@@ -407,62 +436,30 @@ __global__ void __launch_bounds__(256) plan_ext_kernel(PlanArgs A) {
     if (keep) {
       const int pos = __popcll(bal & ((1ull << lane) - 1ull));
       const int flagged = (kb[j >> 5] >> (j & 31)) & 1u;
-      dst[cnt + pos] = j | (flagged << 30);
+      // after the moved keys of the earlier modes
+      dst[cnt + pos + (j < segA ? 0 : (j < segB ? mb0 : mb1))] = j | (flagged << 30);
     }
     cnt += __popcll(bal);
+    ca0 += __popcll(__ballot(keep && j < segA));
+    ca1 += __popcll(__ballot(keep && j < segB));
+  }
+  // the moved keys, each after the columns of its mode and the earlier modes
+  for (int base = 0, k0 = 0; base < n_mv; base += 64) {
+    int j = 0;
+    const bool mk = moved(base + lane, j);
+    const unsigned long long bal = __ballot(mk);
+    if (mk) {
+      const int pos = k0 + __popcll(bal & ((1ull << lane) - 1ull));
+      dst[pos + (j < segA ? ca0 : (j < segB ? ca1 : cnt))] = j | (1 << 30);
+    }
+    k0 += __popcll(bal);
   }
   const int32_t* ivh = A.iv + (long long)h * A.iv_stride * 2;
   const int32_t* pre = A.iv_pre + (long long)h * (A.iv_stride + 1);
   const int n_iv = A.n_iv[h];
   const int tf = (int)(covered_below(ivh, pre, n_iv, -i0) / 32);   // the block's first range tile
-  const int n_t = (pre[n_iv] + 31) / 32;
-  // Event record: range tiles (relative to the first) that hold a high-norm
-  // key, one lane per listed key of the KV head (ascending keys give
-  // ascending tiles), duplicates dropped; then the tiles where the DCA modes
-  // after the first begin.
-  int32_t* evr = A.ev + (long long)unit * EV_REC;
-  {
-    const int n_hn = A.hnl_n[g];
-    int rel = -1;
-    if (lane < min(n_hn, HN_CAP)) {
-      const int j = A.hnl[g * HN_CAP + lane];
-      const int o = j - i0;
-      if (j < hi_key) {
-        int a = 0, z = n_iv;   // last interval starting at or below o
-        while (z - a > 1) { const int mid = (a + z) >> 1; if (ivh[2 * mid] <= o) a = mid; else z = mid; }
-        if (n_iv > 0 && ivh[2 * a] <= o && o < ivh[2 * a + 1]) rel = (pre[a] + (o - ivh[2 * a])) / 32 - tf;
-      }
-    }
-    const unsigned long long have = __ballot(rel >= 0);
-    // compact through the wave's own LDS row (its accesses stay in order),
-    // then keep each tile once
-    __shared__ int comp[4][64];
-    const int pos = __popcll(have & ((1ull << lane) - 1ull));
-    if (rel >= 0) comp[threadIdx.x >> 6][pos] = rel;
-    __builtin_amdgcn_wave_barrier();
-    const int npk = __popcll(have);
-    const int packed = lane < npk ? comp[threadIdx.x >> 6][lane] : -1;
-    const int prev = __shfl_up(packed, 1);
-    const bool first = lane < npk && (lane == 0 || prev != packed);
-    const unsigned long long keep = __ballot(first);
-    const int kpos = __popcll(keep & ((1ull << lane) - 1ull));
-    const int nk = __popcll(keep);
-    const bool cut = n_hn > HN_CAP || nk > EV_PREC;
-    if (first && !cut) evr[3 + kpos] = packed;
-    if (lane == 2) evr[2] = cut ? -1 : nk;
-    if (lane < 2) {
-      const int m_blk = i0 / A.S;
-      const int seg = lane == 0 ? (m_blk - 1) * A.S : m_blk * A.S;
-      int r = -1;
-      if (seg > 0) {
-        const int t = (int)(covered_below(ivh, pre, n_iv, seg - i0) / 32);
-        if (t < n_t) r = t - tf;
-      }
-      evr[lane] = r;
-    }
-  }
   if (lane == 0) {
-    A.n_ext[unit] = cnt;
+    A.n_ext[unit] = cnt + mbn;
     const int rows = hi_key - i0;
     long long below[2];
     below[0] = covered_below(ivh, pre, n_iv, -i0);
@@ -494,8 +491,6 @@ __global__ void __launch_bounds__(256) plan_tiles_kernel(PlanArgs A) {
   const int n_t = (total + 31) / 32;
   if (t == 0) {
     A.n_tiles[h] = n_t;
-    // the first tile holding an offset above 0 (keys past a block's first row)
-    A.npe[h] = (int)(covered_below(ivh, pre, n_iv, 1) / 32);
   }
   if (t >= n_t) return;
   const int r0 = 32 * t;

@@ -105,6 +105,23 @@ def test_sparse_random_pattern(p0, n_q, kv, ks, split):
     assert np.abs(lse - ref_lse).max() <= LSE_TOL
 
 
+@pytest.mark.parametrize("p0,n_q,split", [(512, 300, 0), (512, 300, 3), (1024, 130, 0), (1024, 130, 2)])
+def test_sparse_every_key_high_norm(p0, n_q, split):
+    """Every key takes split-precision logits (a norm threshold of 1e-3).  With at
+    most 1024 such keys per KV head (n_k 812) the plan lists every covered key with
+    the block's extra keys and the range tiles mask them all, including the
+    block's own rows (causal masks inside the extra tiles); with more (n_k 1154)
+    the range tiles take the split-precision passes."""
+    inp = _inputs(30 + p0, p0, n_q, 4, 1, sinks=True)
+    rng = np.random.default_rng(p0 + 7)
+    v_idx, s_off = _random_pattern(rng, 4, inp["n_k"], 40, 25)
+    cfg = _cfg(inp, 4, 1, 256, 32, vs_k_vertical=40, vs_k_slash=25, split_k=split, precise_norm=1e-3)
+    out, lse = run_prefill(inp, cfg, v_idx=v_idx, s_off=s_off, with_lse=True)
+    ref, ref_lse = _oracle(inp, cfg, v_idx, s_off)
+    check_close(out, ref, "every key high-norm")
+    assert np.abs(lse - ref_lse).max() <= LSE_TOL
+
+
 def test_sparse_all_offsets_equals_dense():
     inp = _inputs(20, 192, 200, 2, 1, sinks=True)
     n_k = inp["n_k"]
