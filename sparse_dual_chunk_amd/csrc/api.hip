@@ -82,7 +82,7 @@ struct Layout {
   // shared
   Region freqs, flag;
   // prefill
-  Region hnl_n, hnall;
+  Region hnl_n, hnall, hnt;
   Region khi, klo, kbits, hn, qhi, qlo, iv, iv_pre, n_iv, cov, ext, n_ext, tiles, n_tiles, t_first, part_o, part_lse;
   Region dbits, vbits, smask;
   Region vg;             // values gathered from a paged pool
@@ -90,6 +90,7 @@ struct Layout {
   // index
   Region qs, part_ms, lse, vert, slash, edge, logits, trig, hist, prefix, krem, bcount;
   size_t prefill_bytes = 0, index_bytes = 0;
+  int hnt_words = 0;
   int split = 1, nb = 0, n_ranges = 0, range_keys = 0, cov_words = 0, max_blocks = 0, kbits_words = 0, hn_pad = 0,
       tile_stride = 0;
 };
@@ -170,6 +171,9 @@ Layout make_layout(const dca_cfg* c, bool paged = false) {
   // range tiles of 32 covered offsets: every merged interval is at least 64 long
   L.tile_stride = 2 * (c->vs_k_slash + 1) + 1;
   place(L.tiles, cur, (size_t)h_q * L.tile_stride * 16);
+  // bitmaps over a block's range tiles (one word past the last: the walk reads a tile ahead)
+  L.hnt_words = (L.tile_stride + 31) / 32 + 1;
+  place(L.hnt, cur, (size_t)h_q * L.nb * L.hnt_words * 4);
   place(L.n_tiles, cur, (size_t)h_q * 4);
   place(L.t_first, cur, (size_t)h_q * L.nb * 4);
   if (c->slash_exact) {
@@ -478,6 +482,7 @@ int prefill_impl(const dca_bf16* q, const dca_bf16* k, const dca_key_cache* cach
     P.attended = (long long*)cfg->attended_pairs;
     P.bad = bad;
     P.hnl_n = at<int32_t>(cfg, L.hnl_n); P.hnall = at<int32_t>(cfg, L.hnall);
+    P.hnt = at<uint32_t>(cfg, L.hnt); P.hnt_words = L.hnt_words;
     P.S = cfg->dca_chunk;
     if (launch_plan(P, st) != hipSuccess) return DCA_EHIP;
   } else if (cfg->cover_pairs || cfg->attended_pairs) {
@@ -514,6 +519,7 @@ int prefill_impl(const dca_bf16* q, const dca_bf16* k, const dca_key_cache* cach
   A.dbits_words = L.dbits_words; A.vbits_words = L.vbits_words;
   A.bad = bad;
   A.hnl_n = at<int32_t>(cfg, L.hnl_n);
+  A.hnt = sparse ? at<uint32_t>(cfg, L.hnt) : nullptr; A.hnt_words = L.hnt_words;
   if (launch_attn(A, st) != hipSuccess) return DCA_EHIP;
   record(cfg, 2, 1);
   // stage 3: LSE merge of the split partials

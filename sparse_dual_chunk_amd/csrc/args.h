@@ -38,6 +38,9 @@ struct AttnArgs {
   int exact, dbits_words, vbits_words;
   const int32_t* bad;       // device flag set by the positions check: write no output when nonzero (or null)
   const int32_t* hnl_n;     // [h_kv] how many high-norm keys the head has (counting stops past HN_MOVE_CAP)
+  const uint32_t* hnt;      // [h_q][nb][hnt_words] bit i: range tile i of the block (from its first) holds a
+                            // listed high-norm key (KV heads with at most HN_MOVE_CAP of them)
+  int hnt_words;
 };
 
 struct DecArgs {
@@ -105,6 +108,8 @@ struct PlanArgs {
   const int32_t* bad;      // device flag set by the positions check: write no output when nonzero (or null)
   const int32_t* hnl_n;    // [h_kv] how many high-norm keys the head has (counting stops past HN_MOVE_CAP)
   const int32_t* hnall;    // [h_kv][HN_MOVE_CAP] the first high-norm keys of each KV head, ascending
+  uint32_t* hnt;           // [h_q][nb][hnt_words] range tiles holding a listed high-norm key
+  int hnt_words;
   int S;                   // DCA chunk size
   uint32_t* dbits;         // exact diagonals (or null): [h_q][dbits_words], bit delta + 128
   uint32_t* vbits;         // exact diagonals (or null): [h_q][vbits_words], bit j + 128

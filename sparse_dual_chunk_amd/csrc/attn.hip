@@ -281,10 +281,18 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A) {
     if (n < 32) v &= (1u << n) - 1u;
     return v << sh;
   };
+  // HNM: which range tiles hold a listed high-norm key, one bitmap word per 32
+  // tiles of the walk, read a step ahead of its use (its address depends on
+  // the walk position only); without HNM, a test of the tile's runs
+  cu32* hbm4 = (cu32*)(HNM ? A.hnt + (long long)unit * A.hnt_words : A.hnt);
+  auto flag_word = [&](int px) __attribute__((always_inline)) -> uint32_t { return HNM ? hbm4[px >> 5] : 0u; };
+  auto tile_flagged = [&](Tile T, int px, uint32_t fw) __attribute__((always_inline)) -> bool {
+    return HNM ? ((fw >> (px & 31)) & 1u) != 0u : range_precise(T);
+  };
   // the slots to mask (HNM) and whether the split-precision passes are needed
-  auto hn_split = [&](Tile T, uint32_t& mv) __attribute__((always_inline)) -> bool {
+  auto hn_split = [&](Tile T, bool flagged, uint32_t& mv) __attribute__((always_inline)) -> bool {
     mv = 0u;
-    if (!range_precise(T)) return false;
+    if (!flagged) return false;
     if (!HNM) return true;
     mv = run_hn(T.a1, T.len1) | (T.len1 < 32 ? run_hn(T.a2, T.len2) << T.len1 : 0u);
     return false;
@@ -648,13 +656,14 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A) {
   issue(rs_k, kst0, f_c);
   issue(rs_v, vst0, f_c);
   uint32_t mv_c = 0u;
-  bool p_c = t0 < r_end && hn_split(T_c, mv_c);
+  bool p_c = t0 < r_end && hn_split(T_c, tile_flagged(T_c, phys(t0), flag_word(phys(t0))), mv_c);
   Tile T_n = range_tile(phys(t0 + 1), desc_load(phys(t0 + 1)));
   Offs f_n = tile_offsets(t0 + 1 < r_end ? T_n : T_dummy, -1, true);
   mask_issue(phys(t0 + 1), t0 + 1);
   issue(rs_k, kst1, f_n);
   uint32_t mv_n = 0u;
-  bool p_n = t0 + 1 < r_end && hn_split(T_n, mv_n);
+  bool p_n = t0 + 1 < r_end && hn_split(T_n, tile_flagged(T_n, phys(t0 + 1), flag_word(phys(t0 + 1))), mv_n);
+  uint32_t fw_2 = flag_word(phys(t0 + 2));   // the flag word of the next step's third tile
   int4 d_2 = desc_load(phys(t0 + 2));
 
   // One step on range tile ti: its stages kc / vc, and vn, the V stage of tile ti+1.
@@ -676,7 +685,8 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A) {
       f_2 = tile_offsets(ti + 2 < r_end ? T_2 : T_dummy, -1, clamp_all || px == 0);
       mask_issue(px, ti + 2);
       issue(rs_k, kc, f_2);
-      p_2 = ti + 2 < r_end && hn_split(T_2, mv_2);
+      p_2 = ti + 2 < r_end && hn_split(T_2, tile_flagged(T_2, px, fw_2), mv_2);
+      fw_2 = flag_word(phys(ti + 3));
       d_2 = desc_load(phys(ti + 3));
     };
     compute_tile(kc, vc, T_c, -1, p_c, mask_read(ti), mv_c, after_qk);

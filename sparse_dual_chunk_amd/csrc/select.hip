@@ -458,6 +458,20 @@ __global__ void __launch_bounds__(256) plan_ext_kernel(PlanArgs A) {
   const int32_t* pre = A.iv_pre + (long long)h * (A.iv_stride + 1);
   const int n_iv = A.n_iv[h];
   const int tf = (int)(covered_below(ivh, pre, n_iv, -i0) / 32);   // the block's first range tile
+  // the range tiles (from the block's first) holding a listed high-norm key,
+  // as a bitmap the attention walk reads a word per tile
+  if (!A.dbits && A.hnl_n[g] <= HN_MOVE_CAP) {
+    uint32_t* bm = A.hnt + (long long)unit * A.hnt_words;
+    for (int w = lane; w < A.hnt_words; w += 64) bm[w] = 0u;
+    __threadfence();
+    for (int base = 0; base < n_mv; base += 64) {
+      int j = 0;
+      if (moved(base + lane, j)) {
+        const int rel = (int)(covered_below(ivh, pre, n_iv, j - i0) / 32) - tf;
+        atomicOr(&bm[rel >> 5], 1u << (rel & 31));
+      }
+    }
+  }
   if (lane == 0) {
     A.n_ext[unit] = cnt + mbn;
     const int rows = hi_key - i0;
