@@ -584,7 +584,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A) {
 #pragma unroll
       for (int vv = 0; vv < 16; ++vv) {
         s[vv] -= shift;
-        if (!EXACT) negm[vv] = -m_run;
+        if (!EXACT) negm[vv] -= shift;   // = -m_run exactly, updated in place
       }
     }
     started = started || (mx != -INFINITY);
