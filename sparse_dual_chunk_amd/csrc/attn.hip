@@ -82,11 +82,13 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // odd number of heads per group the last pair has one head and its second pair
 // of waves only keeps its place in the loads and barriers.
 //
-// HNM (sparse block-cover calls): the work items of KV heads with at most
-// HN_MOVE_CAP high-norm keys, whose covered high-norm keys the plan lists with
-// the extra keys: a range tile masks its high-norm slots and needs no
-// split-precision pass.  The instance without HNM takes the other heads.
-template <bool DENSE, bool EXACT, int NW = 2, bool HP = false, bool HNM = false>
+// HNF (sparse calls): the work items of KV heads with at most HN_MOVE_CAP
+// high-norm keys, for which the plan marks the range tiles holding one.  For
+// block-cover calls it also lists those keys with the extra keys, so a range
+// tile masks its high-norm slots and needs no split-precision pass; with
+// exact diagonals the marked tiles take the passes.  The instance without
+// HNF takes the other heads and tests each tile's runs.
+template <bool DENSE, bool EXACT, int NW = 2, bool HP = false, bool HNF = false>
 __device__ __forceinline__ void attn_body(const AttnArgs& A) {
   static_assert(NW == 2 || (NW == 4 && DENSE), "four-wave workgroups serve dense calls");
   static_assert(!HP || NW == 4, "head pairs take four waves");
@@ -156,7 +158,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A) {
   }
   if (idle) h -= 1;   // a valid head for the addresses; nothing is computed or written
   const int g = h / (A.h_q / A.h_kv);
-  if (!DENSE && !EXACT && HNM != (A.hnl_n[g] <= HN_MOVE_CAP)) return;   // the other instance's item
+  if (!DENSE && HNF != (A.hnl_n[g] <= HN_MOVE_CAP)) return;   // the other instance's item
 
   const int i0 = A.p0 + RB * b;                  // absolute position of the block's first row
   const int rows = min(RB, A.n_q - RB * b);
@@ -265,10 +267,10 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A) {
   auto range_precise = [&](Tile T) __attribute__((always_inline)) -> bool {
     return run_flagged(T.a1, T.len1) || run_flagged(T.a2, T.len2);
   };
-  // HNM: the plan lists the covered high-norm keys with the block's extra
-  // keys, so a range tile masks its high-norm slots, found in the flag bitmap
-  // (two words per run; indexes clamped into it: the slots of keys past n_k
-  // are masked anyway).
+  // HNF, block cover: the plan lists the covered high-norm keys with the
+  // block's extra keys, so a range tile masks its high-norm slots, found in the
+  // flag bitmap (two words per run; indexes clamped into it: the slots of keys
+  // past n_k are masked anyway).
   cu32* kb4 = (cu32*)(A.kbits + (long long)g * A.kbits_words);
   auto run_hn = [&](int a, int len) __attribute__((always_inline)) -> uint32_t {   // bit t: key a + t high-norm
     const int ac = max(a, 0);
@@ -281,19 +283,19 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A) {
     if (n < 32) v &= (1u << n) - 1u;
     return v << sh;
   };
-  // HNM: which range tiles hold a listed high-norm key, one bitmap word per 32
-  // tiles of the walk, read a step ahead of its use (its address depends on
-  // the walk position only); without HNM, a test of the tile's runs
-  cu32* hbm4 = (cu32*)(HNM ? A.hnt + (long long)unit * A.hnt_words : A.hnt);
-  auto flag_word = [&](int px) __attribute__((always_inline)) -> uint32_t { return HNM ? hbm4[px >> 5] : 0u; };
+  // HNF: which range tiles hold a covered high-norm key, one bitmap word per
+  // 32 tiles of the walk, read a step ahead of its use (its address depends on
+  // the walk position only); without HNF, a test of the tile's runs
+  cu32* hbm4 = (cu32*)(HNF ? A.hnt + (long long)unit * A.hnt_words : A.hnt);
+  auto flag_word = [&](int px) __attribute__((always_inline)) -> uint32_t { return HNF ? hbm4[px >> 5] : 0u; };
   auto tile_flagged = [&](Tile T, int px, uint32_t fw) __attribute__((always_inline)) -> bool {
-    return HNM ? ((fw >> (px & 31)) & 1u) != 0u : range_precise(T);
+    return HNF ? ((fw >> (px & 31)) & 1u) != 0u : range_precise(T);
   };
-  // the slots to mask (HNM) and whether the split-precision passes are needed
+  // the slots to mask (HNF, block cover) and whether the split-precision passes are needed
   auto hn_split = [&](Tile T, bool flagged, uint32_t& mv) __attribute__((always_inline)) -> bool {
     mv = 0u;
     if (!flagged) return false;
-    if (!HNM) return true;
+    if (!HNF || EXACT) return true;
     mv = run_hn(T.a1, T.len1) | (T.len1 < 32 ? run_hn(T.a2, T.len2) << T.len1 : 0u);
     return false;
   };
@@ -325,12 +327,21 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A) {
   // A run starts below n_k + 96; one far below key 0 (the tail of an interval
   // in a block's first tile, all of its keys negative and masked) reads the
   // bitmap's first words instead.
-  auto vert_bits = [&](Tile T) __attribute__((always_inline)) -> uint32_t {
+  // The words are requested a step before the tile is computed (vert_words),
+  // so no wait for them falls on the walk.
+  struct VW { uint32_t w10, w11, w20, w21; };
+  auto vert_words = [&](Tile T) __attribute__((always_inline)) -> VW {
+    VW w = {0u, 0u, 0u, 0u};
+    if (!EXACT) return w;
     const int b1 = max(T.a1 + 128, 0), b2 = max(T.a2 + 128, 0);
-    const uint32_t w10 = vb4[b1 >> 5], w11 = vb4[(b1 >> 5) + 1];
-    const uint32_t w20 = vb4[b2 >> 5], w21 = vb4[(b2 >> 5) + 1];
-    const uint32_t v1 = (uint32_t)((((uint64_t)w11 << 32) | w10) >> (b1 & 31));
-    const uint32_t v2 = (uint32_t)((((uint64_t)w21 << 32) | w20) >> (b2 & 31));
+    w.w10 = vb4[b1 >> 5]; w.w11 = vb4[(b1 >> 5) + 1];
+    w.w20 = vb4[b2 >> 5]; w.w21 = vb4[(b2 >> 5) + 1];
+    return w;
+  };
+  auto vert_bits = [&](Tile T, VW w) __attribute__((always_inline)) -> uint32_t {
+    const int b1 = max(T.a1 + 128, 0), b2 = max(T.a2 + 128, 0);
+    const uint32_t v1 = (uint32_t)((((uint64_t)w.w11 << 32) | w.w10) >> (b1 & 31));
+    const uint32_t v2 = (uint32_t)((((uint64_t)w.w21 << 32) | w.w20) >> (b2 & 31));
     const uint32_t m1 = T.len1 >= 32 ? 0xFFFFFFFFu : ((1u << T.len1) - 1u);
     const uint32_t m2 = T.len2 >= 32 ? 0xFFFFFFFFu : ((1u << T.len2) - 1u);
     return (v1 & m1) | (T.len1 < 32 ? (v2 & m2) << T.len1 : 0u);
@@ -464,7 +475,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A) {
   // have such slots).  Then one online softmax and one O += P V.  after_qk
   // runs once S^T is done (B2 and the K issue), B3 before the V reads.
   auto compute_tile = [&](const uint8_t* kt, const uint8_t* vt, Tile T, int skey, bool precise, uint32_t smk,
-                          uint32_t mv, auto&& after_qk) __attribute__((always_inline)) {
+                          uint32_t mv, VW vw, auto&& after_qk) __attribute__((always_inline)) {
     const int count = tile_count(T);
     int key_first, key_last;
     if (T.cnt) {
@@ -500,7 +511,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A) {
     uint32_t xm = 0u;
     bool skip = HP && idle;
     if (EXACT && !T.cnt) {
-      xm = smk | vert_bits(T);
+      xm = smk | vert_bits(T, vw);
       skip = !__any(xm != 0u);
     }
     f32x16 s = {};
@@ -537,7 +548,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A) {
       }
       select_slots(s, t_lo, t_hi, -INFINITY);
     }
-    if (HNM && mv) {
+    if (HNF && !EXACT && mv) {
       // high-norm keys taken by the extra list: slot c + 4 half is bit c of xh
       const uint32_t xh = mv >> (4 * half);
 #pragma unroll
@@ -664,6 +675,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A) {
   uint32_t mv_n = 0u;
   bool p_n = t0 + 1 < r_end && hn_split(T_n, tile_flagged(T_n, phys(t0 + 1), flag_word(phys(t0 + 1))), mv_n);
   uint32_t fw_2 = flag_word(phys(t0 + 2));   // the flag word of the next step's third tile
+  VW vw_c = vert_words(T_c), vw_n = {0u, 0u, 0u, 0u};
   int4 d_2 = desc_load(phys(t0 + 2));
 
   // One step on range tile ti: its stages kc / vc, and vn, the V stage of tile ti+1.
@@ -687,10 +699,11 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A) {
       issue(rs_k, kc, f_2);
       p_2 = ti + 2 < r_end && hn_split(T_2, tile_flagged(T_2, px, fw_2), mv_2);
       fw_2 = flag_word(phys(ti + 3));
+      vw_n = vert_words(T_n);
       d_2 = desc_load(phys(ti + 3));
     };
-    compute_tile(kc, vc, T_c, -1, p_c, mask_read(ti), mv_c, after_qk);
-    T_c = T_n; p_c = p_n; mv_c = mv_n;
+    compute_tile(kc, vc, T_c, -1, p_c, mask_read(ti), mv_c, vw_c, after_qk);
+    T_c = T_n; p_c = p_n; mv_c = mv_n; vw_c = vw_n;
     T_n = T_2; p_n = p_2; mv_n = mv_2; f_n = f_2;
   };
   for (int ti = t_beg; ti < r_end; ti += 2) {
@@ -712,7 +725,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A) {
     issue(rs_v, vst0, f);
     vm_wait(0);
     wg_barrier();
-    compute_tile(kst0, vst0, T, sk, prec, 0u, 0u, [] {});
+    compute_tile(kst0, vst0, T, sk, prec, 0u, 0u, VW{0u, 0u, 0u, 0u}, [] {});
     wg_barrier();          // the stage is read; the next tile may overwrite it
   }
 
@@ -761,7 +774,8 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A) {
 // registers the other two do not pay for)
 __global__ void __launch_bounds__(128, 2) dca_attn_kernel(AttnArgs A) { attn_body<false, false, 2, false, true>(A); }
 __global__ void __launch_bounds__(128, 2) dca_attn_hn_kernel(AttnArgs A) { attn_body<false, false>(A); }
-__global__ void __launch_bounds__(128, 2) dca_attn_exact_kernel(AttnArgs A) { attn_body<false, true>(A); }
+__global__ void __launch_bounds__(128, 2) dca_attn_exact_kernel(AttnArgs A) { attn_body<false, true, 2, false, true>(A); }
+__global__ void __launch_bounds__(128, 2) dca_attn_exact_hn_kernel(AttnArgs A) { attn_body<false, true>(A); }
 __global__ void __launch_bounds__(128, 2) dca_attn_dense_kernel(AttnArgs A) { attn_body<true, false>(A); }
 __global__ void __launch_bounds__(256, 2) dca_attn_dense4_kernel(AttnArgs A) { attn_body<true, false, 4>(A); }
 __global__ void __launch_bounds__(256, 2) dca_attn_dense_hp_kernel(AttnArgs A) { attn_body<true, false, 4, true>(A); }
@@ -852,7 +866,10 @@ hipError_t launch_attn(const AttnArgs& A, hipStream_t stream) {
   } else if (A.dense) {
     hipLaunchKernelGGL(dca_attn_dense_kernel, dim3(blocks), dim3(128), 0, stream, A);
   } else if (A.exact) {
+    // KV heads with few high-norm keys, then the others
     hipLaunchKernelGGL(dca_attn_exact_kernel, dim3(blocks), dim3(128), 0, stream, A);
+    if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+    hipLaunchKernelGGL(dca_attn_exact_hn_kernel, dim3(blocks), dim3(128), 0, stream, A);
   } else {
     // block cover: KV heads with few high-norm keys, then the others (each
     // launch leaves the other's work items alone)

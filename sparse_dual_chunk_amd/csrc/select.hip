@@ -404,13 +404,15 @@ __global__ void __launch_bounds__(256) plan_ext_kernel(PlanArgs A) {
   // covered high-norm keys of the block's causal extent, per mode (ascending in the list)
   const int n_mv = (!A.dbits && A.hnl_n[g] <= HN_MOVE_CAP) ? A.hnl_n[g] : 0;
   const int32_t* hall = A.hnall + (long long)g * HN_MOVE_CAP;
-  auto moved = [&](int t, int& j) -> bool {
-    if (t >= n_mv) return false;
+  // listed high-norm key t of the KV head, if covered inside the block's causal extent
+  auto covered_hn = [&](int t, int& j) -> bool {
+    if (t >= min(A.hnl_n[g], HN_MOVE_CAP)) return false;
     j = hall[t];
     if (j >= hi_key) return false;
     const int bit = j - i0 + A.p_last;
     return (cv[bit >> 5] >> (bit & 31)) & 1u;
   };
+  auto moved = [&](int t, int& j) -> bool { return t < n_mv && covered_hn(t, j); };
   int mb0 = 0, mb1 = 0, mbn = 0;   // moved keys below segA, below segB, in all
   for (int base = 0; base < n_mv; base += 64) {
     int j = 0;
@@ -460,13 +462,14 @@ __global__ void __launch_bounds__(256) plan_ext_kernel(PlanArgs A) {
   const int tf = (int)(covered_below(ivh, pre, n_iv, -i0) / 32);   // the block's first range tile
   // the range tiles (from the block's first) holding a listed high-norm key,
   // as a bitmap the attention walk reads a word per tile
-  if (!A.dbits && A.hnl_n[g] <= HN_MOVE_CAP) {
+  if (A.hnl_n[g] <= HN_MOVE_CAP) {
     uint32_t* bm = A.hnt + (long long)unit * A.hnt_words;
     for (int w = lane; w < A.hnt_words; w += 64) bm[w] = 0u;
     __threadfence();
-    for (int base = 0; base < n_mv; base += 64) {
+    const int n_hn = A.hnl_n[g];
+    for (int base = 0; base < n_hn; base += 64) {
       int j = 0;
-      if (moved(base + lane, j)) {
+      if (covered_hn(base + lane, j)) {
         const int rel = (int)(covered_below(ivh, pre, n_iv, j - i0) / 32) - tf;
         atomicOr(&bm[rel >> 5], 1u << (rel & 31));
       }
