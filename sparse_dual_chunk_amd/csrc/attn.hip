@@ -285,11 +285,15 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A) {
   };
   // HNF: which range tiles hold a covered high-norm key, one bitmap word per
   // 32 tiles of the walk, read a step ahead of its use (its address depends on
-  // the walk position only); without HNF, a test of the tile's runs
+  // the walk position only).  Dense tiles hold keys 32 t .. 32 t + 31: the
+  // word of the flag bitmap with those keys, read a step ahead the same way.
+  // Otherwise a test of the tile's runs.
   cu32* hbm4 = (cu32*)(HNF ? A.hnt + (long long)unit * A.hnt_words : A.hnt);
-  auto flag_word = [&](int px) __attribute__((always_inline)) -> uint32_t { return HNF ? hbm4[px >> 5] : 0u; };
+  auto flag_word = [&](int px) __attribute__((always_inline)) -> uint32_t {
+    return HNF ? hbm4[px >> 5] : (DENSE ? kb4[min(px, A.kbits_words - 1)] : 0u);
+  };
   auto tile_flagged = [&](Tile T, int px, uint32_t fw) __attribute__((always_inline)) -> bool {
-    return HNF ? ((fw >> (px & 31)) & 1u) != 0u : range_precise(T);
+    return HNF ? ((fw >> (px & 31)) & 1u) != 0u : (DENSE ? fw != 0u : range_precise(T));
   };
   // the slots to mask (HNF, block cover) and whether the split-precision passes are needed
   auto hn_split = [&](Tile T, bool flagged, uint32_t& mv) __attribute__((always_inline)) -> bool {
