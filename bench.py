@@ -742,9 +742,12 @@ def main() -> int:
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
-            "kernel": ("dca_attn_exact_kernel" if args.slash_exact else "dca_attn_kernel") if w.sparse
-                      else ("dca_attn_dense4_kernel" if w.dca_chunk % 128 == 0 and all(p0 % 128 == 0 for p0, _ in w.chunks)
-                            else "dca_attn_dense_kernel"),
+            # sparse calls: the stage is two launches, the second serving KV heads with more
+            # than 1024 high-norm keys (none in these workloads: its workgroups return at once)
+            "kernel": (("dca_attn_exact_kernel + dca_attn_exact_hn_kernel" if args.slash_exact
+                        else "dca_attn_kernel + dca_attn_hn_kernel") if w.sparse
+                       else ("dca_attn_dense4_kernel" if w.dca_chunk % 128 == 0 and all(p0 % 128 == 0 for p0, _ in w.chunks)
+                             else "dca_attn_dense_kernel")),
             "avg_launch_ms": round(attn_avg_ms, 4),
             "algorithmic_flops_per_launch": f_per_launch,
         },
