@@ -19,6 +19,8 @@
 #include "args.h"
 #include "attn_tile.h"
 
+#include <algorithm>
+
 namespace dca {
 
 
@@ -88,8 +90,11 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // tile masks its high-norm slots and needs no split-precision pass; with
 // exact diagonals the marked tiles take the passes.  The instance without
 // HNF takes the other heads and tests each tile's runs.
+//
+// wg: the work item's index in the launch order (the workgroup index, or the
+// grid-stride position of the instance that serves few work items).
 template <bool DENSE, bool EXACT, int NW = 2, bool HP = false, bool HNF = false>
-__device__ __forceinline__ void attn_body(const AttnArgs& A) {
+__device__ __forceinline__ void attn_body(const AttnArgs& A, int wg) {
   static_assert(NW == 2 || (NW == 4 && DENSE), "four-wave workgroups serve dense calls");
   static_assert(!HP || NW == 4, "head pairs take four waves");
   constexpr int NR = HP ? 2 : NW;  // waves per row block
@@ -122,8 +127,8 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A) {
   // row, so the workgroups in flight do near-equal work, start and end
   // together and walk the same keys at the same time through the die's L2.
   if (A.bad && *A.bad) return;   // positions check failed: no output is written
-  const int die = blockIdx.x % NXCD;
-  const int local = blockIdx.x / NXCD;
+  const int die = wg % NXCD;   // wg and the workgroup index agree modulo 8: same die
+  const int local = wg / NXCD;
   const int hpg = A.h_q / A.h_kv;
   const int NBW = (A.nb + NR / 2 - 1) / (NR / 2);   // row groups of RB rows
   const int hpw = HP ? (hpg + 1) / 2 : hpg;          // work items per KV group and row
@@ -776,13 +781,20 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A) {
 // sparse (vertical-slash) calls, sparse calls with exact diagonals, and dense
 // calls: one body, the variant known at compile time (the exact masks cost
 // registers the other two do not pay for)
-__global__ void __launch_bounds__(128, 2) dca_attn_kernel(AttnArgs A) { attn_body<false, false, 2, false, true>(A); }
-__global__ void __launch_bounds__(128, 2) dca_attn_hn_kernel(AttnArgs A) { attn_body<false, false>(A); }
-__global__ void __launch_bounds__(128, 2) dca_attn_exact_kernel(AttnArgs A) { attn_body<false, true, 2, false, true>(A); }
-__global__ void __launch_bounds__(128, 2) dca_attn_exact_hn_kernel(AttnArgs A) { attn_body<false, true>(A); }
-__global__ void __launch_bounds__(128, 2) dca_attn_dense_kernel(AttnArgs A) { attn_body<true, false>(A); }
-__global__ void __launch_bounds__(256, 2) dca_attn_dense4_kernel(AttnArgs A) { attn_body<true, false, 4>(A); }
-__global__ void __launch_bounds__(256, 2) dca_attn_dense_hp_kernel(AttnArgs A) { attn_body<true, false, 4, true>(A); }
+__global__ void __launch_bounds__(128, 2) dca_attn_kernel(AttnArgs A) { attn_body<false, false, 2, false, true>(A, blockIdx.x); }
+__global__ void __launch_bounds__(128, 2) dca_attn_exact_kernel(AttnArgs A) { attn_body<false, true, 2, false, true>(A, blockIdx.x); }
+// KV heads with many high-norm keys are rare: these instances walk the work
+// items grid-stride over a bounded grid (a multiple of 8 workgroups, so an
+// item stays on its die), which costs little when none of the items is theirs
+__global__ void __launch_bounds__(128, 2) dca_attn_hn_kernel(AttnArgs A, int items) {
+  for (int w = blockIdx.x; w < items; w += gridDim.x) attn_body<false, false>(A, w);
+}
+__global__ void __launch_bounds__(128, 2) dca_attn_exact_hn_kernel(AttnArgs A, int items) {
+  for (int w = blockIdx.x; w < items; w += gridDim.x) attn_body<false, true>(A, w);
+}
+__global__ void __launch_bounds__(128, 2) dca_attn_dense_kernel(AttnArgs A) { attn_body<true, false>(A, blockIdx.x); }
+__global__ void __launch_bounds__(256, 2) dca_attn_dense4_kernel(AttnArgs A) { attn_body<true, false, 4>(A, blockIdx.x); }
+__global__ void __launch_bounds__(256, 2) dca_attn_dense_hp_kernel(AttnArgs A) { attn_body<true, false, 4, true>(A, blockIdx.x); }
 
 // LSE merge of the key parts of one (row, head): m = max_p lse_p,
 // O = sum_p e^{lse_p - m} O_p / sum_p e^{lse_p - m}.  One wave per (row, head):
@@ -869,17 +881,19 @@ hipError_t launch_attn(const AttnArgs& A, hipStream_t stream) {
     hipLaunchKernelGGL(dca_attn_dense4_kernel, dim3(blocks), dim3(256), 0, stream, A);
   } else if (A.dense) {
     hipLaunchKernelGGL(dca_attn_dense_kernel, dim3(blocks), dim3(128), 0, stream, A);
-  } else if (A.exact) {
-    // KV heads with few high-norm keys, then the others
-    hipLaunchKernelGGL(dca_attn_exact_kernel, dim3(blocks), dim3(128), 0, stream, A);
-    if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
-    hipLaunchKernelGGL(dca_attn_exact_hn_kernel, dim3(blocks), dim3(128), 0, stream, A);
   } else {
-    // block cover: KV heads with few high-norm keys, then the others (each
-    // launch leaves the other's work items alone)
-    hipLaunchKernelGGL(dca_attn_kernel, dim3(blocks), dim3(128), 0, stream, A);
-    if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
-    hipLaunchKernelGGL(dca_attn_hn_kernel, dim3(blocks), dim3(128), 0, stream, A);
+    // KV heads with few high-norm keys, then the others (each launch leaves the
+    // other's work items alone; blocks is a multiple of 8)
+    const int hn_grid = std::min(blocks, 2048);
+    if (A.exact) {
+      hipLaunchKernelGGL(dca_attn_exact_kernel, dim3(blocks), dim3(128), 0, stream, A);
+      if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+      hipLaunchKernelGGL(dca_attn_exact_hn_kernel, dim3(hn_grid), dim3(128), 0, stream, A, blocks);
+    } else {
+      hipLaunchKernelGGL(dca_attn_kernel, dim3(blocks), dim3(128), 0, stream, A);
+      if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+      hipLaunchKernelGGL(dca_attn_hn_kernel, dim3(hn_grid), dim3(128), 0, stream, A, blocks);
+    }
   }
   return hipGetLastError();
 }

@@ -106,18 +106,22 @@ def test_sparse_random_pattern(p0, n_q, kv, ks, split):
 
 
 @pytest.mark.parametrize("p0,n_q,split", [(512, 300, 0), (512, 300, 3), (1024, 130, 0), (1024, 130, 2)])
-def test_sparse_every_key_high_norm(p0, n_q, split):
+@pytest.mark.parametrize("exact", [0, 1])
+def test_sparse_every_key_high_norm(p0, n_q, split, exact):
     """Every key takes split-precision logits (a norm threshold of 1e-3).  With at
-    most 1024 such keys per KV head (n_k 812) the plan lists every covered key with
-    the block's extra keys and the range tiles mask them all, including the
-    block's own rows (causal masks inside the extra tiles); with more (n_k 1154)
-    the range tiles take the split-precision passes."""
+    most 1024 such keys per KV head (n_k 812) the plan marks the range tiles
+    holding them; for the block cover it lists every covered key with the
+    block's extra keys and the range tiles mask them all, including the block's
+    own rows (causal masks inside the extra tiles).  With more (n_k 1154) the
+    second kernel instance serves every work item, walking them grid-stride and
+    testing each tile's runs."""
     inp = _inputs(30 + p0, p0, n_q, 4, 1, sinks=True)
     rng = np.random.default_rng(p0 + 7)
     v_idx, s_off = _random_pattern(rng, 4, inp["n_k"], 40, 25)
-    cfg = _cfg(inp, 4, 1, 256, 32, vs_k_vertical=40, vs_k_slash=25, split_k=split, precise_norm=1e-3)
+    cfg = _cfg(inp, 4, 1, 256, 32, vs_k_vertical=40, vs_k_slash=25, split_k=split, precise_norm=1e-3,
+               slash_exact=exact)
     out, lse = run_prefill(inp, cfg, v_idx=v_idx, s_off=s_off, with_lse=True)
-    ref, ref_lse = _oracle(inp, cfg, v_idx, s_off)
+    ref, ref_lse = (_oracle_exact if exact else _oracle)(inp, cfg, v_idx, s_off)
     check_close(out, ref, "every key high-norm")
     assert np.abs(lse - ref_lse).max() <= LSE_TOL
 
