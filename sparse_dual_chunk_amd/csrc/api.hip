@@ -82,7 +82,7 @@ struct Layout {
   // shared
   Region freqs, flag;
   // prefill
-  Region hnl_n, hnall, hnt;
+  Region hnl_n, hnall, hnt, cov_pre;
   Region khi, klo, kbits, hn, qhi, qlo, iv, iv_pre, n_iv, cov, ext, n_ext, tiles, n_tiles, t_first, part_o, part_lse;
   Region dbits, vbits, smask;
   Region vg;             // values gathered from a paged pool
@@ -166,6 +166,7 @@ Layout make_layout(const dca_cfg* c, bool paged = false) {
   place(L.n_iv, cur, (size_t)h_q * 4);
   L.cov_words = (p_last + 64 + 31) / 32;
   place(L.cov, cur, (size_t)h_q * L.cov_words * 4);
+  place(L.cov_pre, cur, (size_t)h_q * L.cov_words * 4);
   place(L.ext, cur, (size_t)h_q * L.nb * (size_t)ext_stride(c) * 4);
   place(L.n_ext, cur, (size_t)h_q * L.nb * 4);
   // range tiles of 32 covered offsets: every merged interval is at least 64 long
@@ -467,7 +468,7 @@ int prefill_impl(const dca_bf16* q, const dca_bf16* k, const dca_key_cache* cach
     P.v_idx = cfg->v_idx; P.s_off = cfg->s_off;
     P.iv = at<int32_t>(cfg, L.iv); P.iv_pre = at<int32_t>(cfg, L.iv_pre); P.n_iv = at<int32_t>(cfg, L.n_iv);
     P.cover_pairs = (long long*)cfg->cover_pairs;
-    P.cov = at<uint32_t>(cfg, L.cov);
+    P.cov = at<uint32_t>(cfg, L.cov); P.cov_pre = at<int32_t>(cfg, L.cov_pre);
     P.ext = at<int32_t>(cfg, L.ext); P.n_ext = at<int32_t>(cfg, L.n_ext);
     P.h_q = h_q; P.k_v = cfg->vs_k_vertical; P.k_s = cfg->vs_k_slash; P.p_last = p_last; P.p0 = p0;
     P.n_q = n_q; P.nb = L.nb; P.iv_stride = cfg->vs_k_slash + 1;

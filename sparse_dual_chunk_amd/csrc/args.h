@@ -97,6 +97,7 @@ struct PlanArgs {
   int32_t* iv_pre;         // [h_q][iv_stride + 1] covered offsets before interval k
   int32_t* n_iv;           // [h_q]
   uint32_t* cov;           // [h_q][cov_words] bitmap over offsets o in [-p_last, 64)
+  int32_t* cov_pre;        // [h_q][cov_words] set bits of cov before each word
   int32_t* ext;            // [h_q][nb][ext_stride]
   int32_t* n_ext;          // [h_q][nb]
   int4* tiles;             // [h_q][tile_stride]

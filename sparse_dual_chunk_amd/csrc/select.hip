@@ -363,6 +363,26 @@ __global__ void plan_cov_kernel(PlanArgs A) {
   }
 }
 
+// Exclusive prefix counts of the coverage bitmap's words, one workgroup per head.
+__global__ void __launch_bounds__(1024) plan_cov_scan_kernel(PlanArgs A) {
+  __shared__ int32_t wred[16];
+  __shared__ int32_t tot;
+  const int h = blockIdx.x, tid = threadIdx.x;
+  const uint32_t* cv = A.cov + (long long)h * A.cov_words;
+  int32_t* pc = A.cov_pre + (long long)h * A.cov_words;
+  int acc = 0;
+  for (int base = 0; base < A.cov_words; base += 1024) {
+    const int w = base + tid;
+    const int c = w < A.cov_words ? __popc(cv[w]) : 0;
+    const int inc = scan1024_sum(c, wred);
+    if (w < A.cov_words) pc[w] = acc + inc - c;
+    if (tid == 1023) tot = inc;
+    __syncthreads();
+    acc += tot;
+    __syncthreads();
+  }
+}
+
 // Covered offsets of head h below x: the whole intervals before the one that
 // holds x, plus the part of that one below x.
 __device__ inline long long covered_below(const int32_t* ivh, const int32_t* pre, int n_iv, int x) {
@@ -463,14 +483,21 @@ __global__ void __launch_bounds__(256) plan_ext_kernel(PlanArgs A) {
   // the range tiles (from the block's first) holding a listed high-norm key,
   // as a bitmap the attention walk reads a word per tile
   if (A.hnl_n[g] <= HN_MOVE_CAP) {
+    // the walk reads the words of its tiles and of up to two tiles past them
     uint32_t* bm = A.hnt + (long long)unit * A.hnt_words;
-    for (int w = lane; w < A.hnt_words; w += 64) bm[w] = 0u;
+    const int n_range = (pre[n_iv] + 31) / 32 - tf;
+    const int nw = min(A.hnt_words, (n_range + 2) / 32 + 1);
+    for (int w = lane; w < nw; w += 64) bm[w] = 0u;
     __threadfence();
+    const int32_t* pc = A.cov_pre + (long long)h * A.cov_words;
     const int n_hn = A.hnl_n[g];
     for (int base = 0; base < n_hn; base += 64) {
       int j = 0;
       if (covered_hn(base + lane, j)) {
-        const int rel = (int)(covered_below(ivh, pre, n_iv, j - i0) / 32) - tf;
+        // covered offsets below j - i0: set bits of the coverage bitmap below its bit
+        const int bit = j - i0 + A.p_last;
+        const int below = pc[bit >> 5] + __popc(cv[bit >> 5] & ((1u << (bit & 31)) - 1u));
+        const int rel = below / 32 - tf;
         atomicOr(&bm[rel >> 5], 1u << (rel & 31));
       }
     }
@@ -636,6 +663,7 @@ hipError_t launch_plan(const PlanArgs& A, hipStream_t stream) {
   hipLaunchKernelGGL(plan_cov_clear_kernel, dim3(256), dim3(256), 0, stream, A);
   const int ivb = (A.iv_stride + 255) / 256;
   hipLaunchKernelGGL(plan_cov_kernel, dim3(ivb, A.h_q), dim3(256), 0, stream, A);
+  hipLaunchKernelGGL(plan_cov_scan_kernel, dim3(A.h_q), dim3(1024), 0, stream, A);
   const int units = A.h_q * A.nb;
   hipLaunchKernelGGL(plan_ext_kernel, dim3((units + 3) / 4), dim3(256), 0, stream, A);
   hipLaunchKernelGGL(plan_tiles_kernel, dim3((A.tile_stride + 255) / 256, A.h_q), dim3(256), 0, stream, A);
