@@ -780,10 +780,17 @@ __global__ void __launch_bounds__(128, 2) dca_attn_exact_kernel(AttnArgs A) { at
 // KV heads with many high-norm keys are rare: these instances walk the work
 // items grid-stride over a bounded grid (a multiple of 8 workgroups, so an
 // item stays on its die), which costs little when none of the items is theirs
+__device__ __forceinline__ bool some_head_has_many_high_norm_keys(const AttnArgs& A) {
+  bool many = false;
+  for (int g = 0; g < A.h_kv; ++g) many = many || A.hnl_n[g] > HN_MOVE_CAP;
+  return many;
+}
 __global__ void __launch_bounds__(128, 2) dca_attn_hn_kernel(AttnArgs A, int items) {
+  if (!some_head_has_many_high_norm_keys(A)) return;
   for (int w = blockIdx.x; w < items; w += gridDim.x) attn_body<false, false>(A, w);
 }
 __global__ void __launch_bounds__(128, 2) dca_attn_exact_hn_kernel(AttnArgs A, int items) {
+  if (!some_head_has_many_high_norm_keys(A)) return;
   for (int w = blockIdx.x; w < items; w += gridDim.x) attn_body<false, true>(A, w);
 }
 __global__ void __launch_bounds__(128, 2) dca_attn_dense_kernel(AttnArgs A) { attn_body<true, false>(A, blockIdx.x); }
