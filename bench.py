@@ -74,17 +74,18 @@ def kernel_source_hash() -> str:
     return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
 
 
-def traffic_from_profile(units_per_launch: float):
+def traffic_from_profile(workload: str, exact: bool):
     """HBM bytes per attention launch from the committed counter summary, if it was taken
-    on the current attention kernel source; else None."""
+    on the current attention kernel source, for this workload and the block-cover
+    semantics; else None."""
     path = os.path.join(ROOT, "profiles", "attn_traffic.json")
-    if not os.path.exists(path):
+    if exact or not os.path.exists(path):
         return None
     try:
         d = json.load(open(path))
     except Exception:
         return None
-    if d.get("attn_source_sha256_16") != kernel_source_hash():
+    if d.get("attn_source_sha256_16") != kernel_source_hash() or d.get("workload") != workload:
         return None
     return d.get("hbm_bytes_per_launch")
 
@@ -144,9 +145,11 @@ def cpu_baseline(w, inputs, p0s, f_blocks_total: float, n_blocks_total: int):
     }
 
 
-def decode_traffic_from_profile():
+def decode_traffic_from_profile(n_tokens: int, page_keys: int):
     """HBM bytes per decode launch from the committed counter summary, if it was taken on
-    the current decode kernel source; else None."""
+    the current decode kernel source and the same step (one token, contiguous cache); else None."""
+    if n_tokens != 1 or page_keys:
+        return None
     path = os.path.join(ROOT, "profiles", "decode_traffic.json")
     src = os.path.join(ROOT, "sparse_dual_chunk_amd", "csrc", "decode.hip")
     if not os.path.exists(path):
@@ -254,7 +257,7 @@ def bench_decode(args) -> int:
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
-            "traffic": decode_traffic_from_profile(),
+            "traffic": decode_traffic_from_profile(n_t, args.page_keys),
             "kernel": "dca_decode_kernel",
             "avg_launch_ms": round(attn_ms, 5),
             "algorithmic_bytes_per_launch": algo_bytes,
@@ -498,7 +501,7 @@ def bench_moe(args) -> int:
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
-            "traffic": moe_traffic_from_profile(gate_up_bytes),
+            "traffic": moe_traffic_from_profile(args.moe_tokens),
             "kernel": "moe_mma_kernel<true> (gate/up + SwiGLU)",
             "avg_launch_ms": round(stage_ms["gate_up"], 5),
             "algorithmic_bytes_per_launch": gate_up_bytes,
@@ -529,9 +532,11 @@ def bench_moe(args) -> int:
     return 0
 
 
-def moe_traffic_from_profile(algo_bytes: float):
+def moe_traffic_from_profile(n_tokens: int):
     """HBM bytes per gate/up launch from the committed FETCH_SIZE / WRITE_SIZE summary, if it
-    was taken on the current kernel source."""
+    was taken on the current kernel source for the same token count (64)."""
+    if n_tokens != 64:
+        return None
     path = os.path.join(ROOT, "profiles", "moe_traffic.json")
     if not os.path.exists(path):
         return None
@@ -709,7 +714,7 @@ def main() -> int:
     attn_avg_ms = float(np.mean(attn_launch_ms))
     f_per_launch = f_blocks / len(gpu_calls)
     achieved = f_per_launch / (attn_avg_ms / 1e3) / 1e12
-    traffic = traffic_from_profile(f_per_launch)
+    traffic = traffic_from_profile(w.name, args.slash_exact)
     dense_pairs = sum(
         sum(min(64, inp["n_q"] - 64 * b) * (inp["p0"] + 64 * b + min(64, inp["n_q"] - 64 * b))
             for b in range((inp["n_q"] + 63) // 64)) * w.h_q for inp, _ in calls)
