@@ -73,9 +73,13 @@ inline size_t up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 
 struct Region { size_t off = 0, bytes = 0; };
 
-// entries per (head, block) of the extra-vertical lists: the vertical columns
-// the ranges miss, and up to HN_MOVE_CAP covered high-norm keys
-int ext_stride(const dca_cfg* c) { return (c->vs_k_vertical > 0 ? c->vs_k_vertical : 1) + HN_MOVE_CAP; }
+// words per (head, block) of the extra-vertical lists: E entries (the vertical
+// columns the ranges miss, and up to HN_MOVE_CAP covered high-norm keys); with
+// exact diagonals also a two-word row mask per entry after them (3E words)
+int ext_stride(const dca_cfg* c) {
+  const int e = (c->vs_k_vertical > 0 ? c->vs_k_vertical : 1) + HN_MOVE_CAP;
+  return c->slash_exact ? 3 * e : e;
+}
 
 // Workspace layouts of the two entry points (regions are 256-byte aligned).
 struct Layout {

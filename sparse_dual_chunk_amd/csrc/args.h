@@ -5,10 +5,11 @@
 
 namespace dca {
 
-// A sparse block-cover call whose KV head has at most HN_MOVE_CAP high-norm
-// keys takes the covered ones below a block's first row out of the block's
-// range tiles (there they are masked, so those tiles need one MFMA pass) and
-// lists them with the block's extra-vertical keys (split-precision logits).
+// A sparse call whose KV head has at most HN_MOVE_CAP high-norm keys takes the
+// covered ones out of a block's range tiles (there they are masked, so those
+// tiles need one MFMA pass) and lists them with the block's extra-vertical keys
+// (split-precision logits; with exact diagonals each with a mask of the block
+// rows that attend it).
 constexpr int HN_MOVE_CAP = 1024;
 
 struct AttnArgs {
@@ -27,8 +28,9 @@ struct AttnArgs {
   const int32_t* n_tiles;   // [h_q]
   const int32_t* t_first;   // [h_q][nb] first range tile of each query block
   const int32_t* ext;       // [h_q][nb][ext_stride] vertical keys outside the ranges and, with few high-norm
-                            // keys, the covered high-norm keys below the block (bit 30: high-norm), ordered
-                            // by DCA mode
+                            // keys, the covered high-norm keys of the block's extent (bit 30: high-norm,
+                            // bit 29: a covered key taken from the range tiles), ordered by DCA mode; with
+                            // exact diagonals ext_stride = 3E: E entries, then a row mask (2 words) per entry
   const int32_t* n_ext;     // [h_q][nb]
   const uint32_t* dbits;    // exact diagonals: [h_q][dbits_words] bit delta + 128 = selected offset (and 0)
   const uint32_t* vbits;    // exact diagonals: [h_q][vbits_words] bit j + 128 = selected vertical column

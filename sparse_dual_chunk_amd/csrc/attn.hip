@@ -297,11 +297,11 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A, int wg) {
   auto tile_flagged = [&](Tile T, int px, uint32_t fw) __attribute__((always_inline)) -> bool {
     return HNF ? ((fw >> (px & 31)) & 1u) != 0u : (DENSE ? fw != 0u : range_precise(T));
   };
-  // the slots to mask (HNF, block cover) and whether the split-precision passes are needed
+  // the slots to mask (HNF) and whether the split-precision passes are needed
   auto hn_split = [&](Tile T, bool flagged, uint32_t& mv) __attribute__((always_inline)) -> bool {
     mv = 0u;
     if (!flagged) return false;
-    if (!HNF || EXACT) return true;
+    if (!HNF) return true;
     mv = run_hn(T.a1, T.len1) | (T.len1 < 32 ? run_hn(T.a2, T.len2) << T.len1 : 0u);
     return false;
   };
@@ -381,7 +381,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A, int wg) {
       for (int j = 0; j < LPW; ++j) {
         const int r = 4 * (NW * j + wave) + lrow;
         int key;
-        if (T.cnt) key = __shfl(skey, r) & 0x3FFFFFFF;
+        if (T.cnt) key = __shfl(skey, r) & 0x1FFFFFFF;
         else key = (r < T.len1 ? T.a1 : T.a2 - T.len1) + r;   // slots past the count are masked later
         key = min(max(key, 0), A.n_k - 1);
         f.v[j] = __umul24((unsigned)key, (unsigned)rowb) + lchunk;
@@ -459,7 +459,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A, int wg) {
     }
     if (precise) {
       // + K_lo Q_hi + K_hi Q_lo; K_lo rows come straight from global memory
-      int kr = T.cnt ? (skey & 0x3FFFFFFF) : range_key(T, l32);
+      int kr = T.cnt ? (skey & 0x1FFFFFFF) : range_key(T, l32);
       kr = min(max(kr, 0), A.n_k - 1);
       const uint16_t* klrow = kl_base + kr * kstride;
 #pragma unroll
@@ -485,8 +485,8 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A, int wg) {
     const int count = tile_count(T);
     int key_first, key_last;
     if (T.cnt) {
-      key_first = __builtin_amdgcn_readlane(skey, 0) & 0x3FFFFFFF;
-      key_last = __builtin_amdgcn_readlane(skey, count - 1) & 0x3FFFFFFF;
+      key_first = __builtin_amdgcn_readlane(skey, 0) & 0x1FFFFFFF;
+      key_last = __builtin_amdgcn_readlane(skey, count - 1) & 0x1FFFFFFF;
     } else {
       key_first = T.a1;
       key_last = T.len2 ? T.a2 + T.len2 - 1 : T.a1 + T.len1 - 1;
@@ -496,7 +496,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A, int wg) {
     // number of the tile's keys below x
     auto below = [&](int x) __attribute__((always_inline)) -> int {
       if (T.cnt) {
-        const int kj = skey & 0x3FFFFFFF;
+        const int kj = skey & 0x1FFFFFFF;
         return __builtin_popcountll(__ballot(l32 < T.cnt && half == 0 && kj < x));
       }
       return min(max(x - T.a1, 0), T.len1) + min(max(x - T.a2, 0), T.len2);
@@ -517,7 +517,8 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A, int wg) {
     uint32_t xm = 0u;
     bool skip = HP && idle;
     if (EXACT && !T.cnt) {
-      xm = smk | vert_bits(T, vw);
+      // the listed high-norm keys are attended in the extra tiles
+      xm = (smk | vert_bits(T, vw)) & ~mv;
       skip = !__any(xm != 0u);
     }
     f32x16 s = {};
@@ -548,7 +549,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A, int wg) {
       int t_hi;
       if (T.cnt) {
         t_hi = 0;
-        for (int t = 0; t < count; ++t) t_hi += (__builtin_amdgcn_readlane(skey, t) & 0x3FFFFFFF) <= prow;
+        for (int t = 0; t < count; ++t) t_hi += (__builtin_amdgcn_readlane(skey, t) & 0x1FFFFFFF) <= prow;
       } else {
         t_hi = below(prow + 1);
       }
@@ -561,6 +562,29 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A, int wg) {
       for (int vv = 0; vv < 16; ++vv) {
         const int c = 8 * (vv >> 2) + (vv & 3);
         if ((xh >> c) & 1u) s[vv] = -INFINITY;
+      }
+    }
+    if (EXACT && T.cnt && HNF) {
+      // extra tiles: a listed high-norm key (bit 29; the ranges cover it) is
+      // attended by the rows of its row mask, which the plan stores after the
+      // block's list (two words per entry: rows 0-31, 32-63); the other
+      // entries are vertical columns, attended by every row they do not
+      // follow (causal mask above)
+      const int E = A.ext_stride / 3;
+      uint32_t xh = 0u;
+#pragma unroll
+      for (int vv = 0; vv < 16; ++vv) {
+        const int c = 8 * (vv >> 2) + (vv & 3);
+        const int e = __shfl(skey, c + 4 * half);
+        const int idx = min(T.eoff + c + 4 * half, E - 1);
+        const uint32_t w = (uint32_t)ext_h[E + 2 * idx + wrow];
+        const bool keep = !((e >> 29) & 1) || ((w >> l32) & 1u);
+        xh |= (uint32_t)keep << c;
+      }
+#pragma unroll
+      for (int vv = 0; vv < 16; ++vv) {
+        const int c = 8 * (vv >> 2) + (vv & 3);
+        if (!((xh >> c) & 1u)) s[vv] = -INFINITY;
       }
     }
     if (EXACT && !T.cnt) {

@@ -395,10 +395,11 @@ __device__ inline long long covered_below(const int32_t* ivh, const int32_t* pre
 
 // One wave per (head, query block): vertical columns inside the block's causal
 // extent that the block's ranges miss, ascending, duplicates dropped; bit 30
-// of an entry marks a high-norm key.  For a block-cover call whose KV head has
-// at most HN_MOVE_CAP high-norm keys, the list also takes the high-norm keys
-// of the block's causal extent that the ranges cover (the attention walk masks
-// them in the range tiles): the list is then ordered by DCA mode (inter-chunk,
+// of an entry marks a high-norm key.  When the KV head has at most
+// HN_MOVE_CAP high-norm keys, the list also takes the high-norm keys of the
+// block's causal extent that the ranges cover, marked by bit 29 (the attention
+// walk masks them in the range tiles; with exact diagonals it tests each
+// row's offset to them): the list is then ordered by DCA mode (inter-chunk,
 // successive, intra-chunk), each mode's columns first, then its high-norm
 // keys, so every 32 entries still hold each mode's keys in one run of slots,
 // and the keys at or above the block's first row, all intra-chunk, are the
@@ -422,7 +423,7 @@ __global__ void __launch_bounds__(256) plan_ext_kernel(PlanArgs A) {
   const int segA = max(0, (m_blk - 1) * A.S);    // DCA modes: [0, segA), [segA, segB), [segB, ..)
   const int segB = max(0, m_blk * A.S);
   // covered high-norm keys of the block's causal extent, per mode (ascending in the list)
-  const int n_mv = (!A.dbits && A.hnl_n[g] <= HN_MOVE_CAP) ? A.hnl_n[g] : 0;
+  const int n_mv = (A.hnl_n[g] <= HN_MOVE_CAP) ? A.hnl_n[g] : 0;
   const int32_t* hall = A.hnall + (long long)g * HN_MOVE_CAP;
   // listed high-norm key t of the KV head, if covered inside the block's causal extent
   auto covered_hn = [&](int t, int& j) -> bool {
@@ -472,7 +473,26 @@ __global__ void __launch_bounds__(256) plan_ext_kernel(PlanArgs A) {
     const unsigned long long bal = __ballot(mk);
     if (mk) {
       const int pos = k0 + __popcll(bal & ((1ull << lane) - 1ull));
-      dst[pos + (j < segA ? ca0 : (j < segB ? ca1 : cnt))] = j | (1 << 30);
+      const int at = pos + (j < segA ? ca0 : (j < segB ? ca1 : cnt));
+      dst[at] = j | (3 << 29);
+      if (A.dbits) {
+        // exact diagonals: the block rows r that attend key j, whose offset
+        // i0 + r - j is selected (bits i0 - j + 128 .. + 63 of the offset
+        // bitmap; negative offsets read its leading zero bits) or for which j
+        // is a selected vertical column not above the row
+        const uint32_t* db = A.dbits + (long long)h * A.dbits_words;
+        const int b0 = i0 - j + 128;   // >= 65: j < i0 + 64
+        const int w = b0 >> 5, sh = b0 & 31;
+        const uint64_t x01 = (uint64_t)db[w] | ((uint64_t)db[w + 1] << 32);
+        const uint64_t x12 = (uint64_t)db[w + 1] | ((uint64_t)db[w + 2] << 32);
+        uint64_t rm = (uint64_t)(uint32_t)(x01 >> sh) | ((uint64_t)(uint32_t)(x12 >> sh) << 32);
+        const int vb = j + 128;
+        if ((A.vbits[(long long)h * A.vbits_words + (vb >> 5)] >> (vb & 31)) & 1u)
+          rm |= j <= i0 ? ~0ull : (~0ull << (j - i0));
+        const int E = A.ext_stride / 3;
+        dst[E + 2 * at] = (int32_t)(uint32_t)rm;
+        dst[E + 2 * at + 1] = (int32_t)(uint32_t)(rm >> 32);
+      }
     }
     k0 += __popcll(bal);
   }
