@@ -630,7 +630,7 @@ __global__ void __launch_bounds__(256) plan_smask_kernel(PlanArgs A) {
 // Exact diagonals: the (row, key) pairs of one head, sum over rows i of
 // |{delta selected (or 0) : delta <= p_i}| + |{j selected : j <= p_i}| minus the
 // keys that are both, i.e. the pairs (column j, offset delta) with
-// p0 <= j + delta <= p_last.  One workgroup per head over the two bitmaps.
+// p0 <= j + delta <= p_last.  Workgroups (head, slice) over the two bitmaps.
 __global__ void __launch_bounds__(1024) plan_attended_exact_kernel(PlanArgs A) {
   __shared__ unsigned long long red[16];
   if (A.bad && *A.bad) return;
@@ -658,7 +658,7 @@ __global__ void __launch_bounds__(1024) plan_attended_exact_kernel(PlanArgs A) {
   };
   long long acc = 0;
   const int nbits = p_last + 1;
-  for (int x = threadIdx.x; x < nbits; x += blockDim.x) {
+  for (int x = blockIdx.y * blockDim.x + threadIdx.x; x < nbits; x += gridDim.y * blockDim.x) {
     const int bit = x + 128;
     if ((db[bit >> 5] >> (bit & 31)) & 1u) acc += rows_from(x);
     if ((vb[bit >> 5] >> (bit & 31)) & 1u) acc += rows_from(x) - dcount(p0 - x, p_last - x);
@@ -690,7 +690,8 @@ hipError_t launch_plan(const PlanArgs& A, hipStream_t stream) {
   if (A.smask)
     hipLaunchKernelGGL(plan_smask_kernel, dim3((A.tile_stride + 3) / 4, A.h_q), dim3(256), 0, stream, A);
   if (A.dbits && A.attended)
-    hipLaunchKernelGGL(plan_attended_exact_kernel, dim3(A.h_q), dim3(1024), 0, stream, A);
+    hipLaunchKernelGGL(plan_attended_exact_kernel, dim3(A.h_q, min(64, (A.p_last + 1024) / 1024)), dim3(1024), 0,
+                       stream, A);
   return hipGetLastError();
 }
 
