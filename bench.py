@@ -768,12 +768,65 @@ def main() -> int:
                   "Infinity Cache, timed alone with HIP events; warm: mean of back-to-back steps",
         "warm": {"ms_per_step": round(ms_per_step, 3), "value": round(value_warm, 2)},
     }
+    if w.sparse and not args.slash_exact:
+        result["exact_diagonals"] = exact_reading(args, w, calls, gpu_calls, hev, f_blocks)
     if not args.no_cpu_baseline:
         log("cpu baseline: timing the oracle on a sample")
         result["cpu_baseline"] = cpu_baseline(w, [c[0] for c in calls], [p0 for p0, _ in w.chunks],
                                               f_blocks, 0)
     print(json.dumps(result), flush=True)
     return 0
+
+
+def exact_reading(args, w, calls, gpu_calls, hev, f_blocks):
+    """The same calls with exact-diagonal slashes, on the index the timed steps built:
+    the prefill's stages timed with HIP events over back-to-back calls, and the pairs
+    the rows attend (F_attended) next to the computed blocks (F_blocks, unchanged)."""
+    import torch
+    import sparse_dual_chunk_amd as S
+    cfgs = [S.config_for(w, c, **({"split_k": args.split_k} if args.split_k else {}), slash_exact=1)
+            for c in range(len(calls))]
+    ws = torch.empty(max(S.dca_workspace_size(c) for c in cfgs), dtype=torch.uint8, device="cuda")
+    n_stage_ev = 2 * S.DCA_STAGE_COUNT
+
+    def run(stage_events=None, attended=None):
+        for ci, g in enumerate(gpu_calls):
+            S.dca_sparse_prefill(g["q"], g["k"], g["v"], g["pos"], cfgs[ci], g["out"], ws, v_idx=g["vi"],
+                                 s_off=g["so"], stage_events=None if stage_events is None else stage_events[ci],
+                                 attended_pairs=None if attended is None else attended[ci])
+
+    log("exact-diagonal slashes on the same index")
+    run()
+    torch.cuda.synchronize()
+    n = max(1, min(args.steps, 3))
+    evs = [[hev.create(n_stage_ev) for _ in gpu_calls] for _ in range(n)]
+    for s in range(n):
+        run(evs[s])
+    torch.cuda.synchronize()
+    stage_ms = {name: 0.0 for name in S.STAGES}
+    attn = []
+    for s in range(n):
+        for ci in range(len(gpu_calls)):
+            ev = evs[s][ci]
+            for si, name in enumerate(S.STAGES):
+                stage_ms[name] += hev.elapsed_ms(ev[2 * si], ev[2 * si + 1]) / n
+            attn.append(hev.elapsed_ms(ev[4], ev[5]))
+    attended = [torch.zeros(1, dtype=torch.int64, device="cuda") for _ in gpu_calls]
+    run(attended=attended)
+    torch.cuda.synchronize()
+    f_att = 4 * 128 * sum(int(a.item()) for a in attended)
+    t_attn = float(np.mean(attn)) * len(gpu_calls) / 1e3   # seconds of attention per step
+    del ws
+    torch.cuda.empty_cache()
+    return {
+        "kernel": "dca_attn_exact_kernel + dca_attn_exact_hn_kernel",
+        "steps": n,
+        "stage_ms": {k: round(v, 3) for k, v in stage_ms.items()},
+        "attention_tflops": round(f_blocks / t_attn / 1e12, 2),
+        "f_attended": f_att,
+        "attended_fraction_of_blocks": round(f_att / f_blocks, 4),
+        "attention_tflops_attended": round(f_att / t_attn / 1e12, 2),
+    }
 
 
 if __name__ == "__main__":
