@@ -17,9 +17,11 @@ from __future__ import annotations
 
 import gc
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import pytest
+from threadpoolctl import threadpool_limits
 
 import workloads as W
 from oracle import dca_oracle as O
@@ -42,6 +44,15 @@ _cache: dict = {}
 
 def log(msg: str) -> None:
     print(f"[fullsize] {msg}", file=sys.stderr, flush=True)
+
+
+def in_parallel(fn, items, workers):
+    """fn over items in a thread pool: the oracle's numpy array loops and BLAS calls
+    release the GIL; one BLAS thread per task keeps the host's cores from being
+    oversubscribed."""
+    with threadpool_limits(limits=1, user_api="blas"):
+        with ThreadPoolExecutor(max_workers=max(1, min(workers, len(items)))) as ex:
+            return list(ex.map(fn, items))
 
 
 def gpu_call(name: str, chunk: int, exact: int = 0) -> dict:
@@ -105,14 +116,21 @@ def group_heads(w):
 def check_index(r):
     heads = index_heads(r)
     log(f"oracle index of {len(heads)} heads")
-    v_ref, s_ref, gaps = O.vs_index(r["inp"]["q"], r["inp"]["k"], r["inp"]["p0"], oracle_cfg(r["cfg"]), heads=heads)
-    for h in heads:
-        assert np.array_equal(r["v_idx"][h], v_ref[h]), f"vertical index of head {h} differs"
-        assert np.array_equal(r["s_off"][h], s_ref[h]), f"slash index of head {h} differs"
-    # the selection is decided by gaps far above the scoring error (the cut rule)
-    for h, gv, gs in gaps:
-        for g in (gv, gs):
-            assert g is None or g >= 1e-9, f"head {h}: relative gap {g} at the cut"
+    G = r["w"].h_q // r["w"].h_kv
+    groups = sorted({h // G for h in heads})
+    # one task per KV group (its heads share the rotated keys)
+    parts = in_parallel(lambda g: ([h for h in heads if h // G == g],
+                                   O.vs_index(r["inp"]["q"], r["inp"]["k"], r["inp"]["p0"], oracle_cfg(r["cfg"]),
+                                              heads=[h for h in heads if h // G == g])),
+                        groups, workers=8)
+    for hs, (v_ref, s_ref, gaps) in parts:
+        for h in hs:
+            assert np.array_equal(r["v_idx"][h], v_ref[h]), f"vertical index of head {h} differs"
+            assert np.array_equal(r["s_off"][h], s_ref[h]), f"slash index of head {h} differs"
+        # the selection is decided by gaps far above the scoring error (the cut rule)
+        for h, gv, gs in gaps:
+            for g in (gv, gs):
+                assert g is None or g >= 1e-9, f"head {h}: relative gap {g} at the cut"
 
 
 def check_pair_counts(r):
@@ -130,9 +148,10 @@ def check_sampled_blocks(r):
     log(f"oracle attention of {len(pairs)} (head, block) pairs")
     ocfg = oracle_cfg(cfg)
     worst, tot, cnt = 0.0, 0.0, 0
-    for h, b in pairs:
-        ref, lse_ref, _ = O.attention_block(inp["q"], inp["k"], inp["v"], inp["p0"], h, b, ocfg,
-                                            r["v_idx"], r["s_off"], exact=r["exact"])
+    refs = in_parallel(lambda hb: O.attention_block(inp["q"], inp["k"], inp["v"], inp["p0"], hb[0], hb[1], ocfg,
+                                                    r["v_idx"], r["s_off"], exact=r["exact"])[:2],
+                       pairs, workers=8)
+    for (h, b), (ref, lse_ref) in zip(pairs, refs):
         r0 = 64 * b
         got = bf16_f64(r["out"][r0:r0 + ref.shape[0], h])
         err = np.abs(got - ref)
