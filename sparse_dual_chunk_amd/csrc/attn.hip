@@ -338,7 +338,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A, int wg) {
   struct VW { uint32_t w10, w11, w20, w21; };
   auto vert_words = [&](Tile T) __attribute__((always_inline)) -> VW {
     VW w = {0u, 0u, 0u, 0u};
-    if (!EXACT) return w;
+    if (!EXACT || HNF) return w;   // HNF: the plan lists the covered columns with the extra keys
     const int b1 = max(T.a1 + 128, 0), b2 = max(T.a2 + 128, 0);
     w.w10 = vb4[b1 >> 5]; w.w11 = vb4[(b1 >> 5) + 1];
     w.w20 = vb4[b2 >> 5]; w.w21 = vb4[(b2 >> 5) + 1];
@@ -518,7 +518,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A, int wg) {
     bool skip = HP && idle;
     if (EXACT && !T.cnt) {
       // the listed high-norm keys are attended in the extra tiles
-      xm = (smk | vert_bits(T, vw)) & ~mv;
+      xm = (smk | (HNF ? 0u : vert_bits(T, vw))) & ~mv;
       skip = !__any(xm != 0u);
     }
     f32x16 s = {};
@@ -540,7 +540,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A, int wg) {
     };
     if (mode_first + 1 <= mode_last) merge_mode(mode_first + 1);
     if (mode_first + 2 <= mode_last) merge_mode(mode_first + 2);
-    if (count < BN || key_first < 0 || key_last > i0) {
+    if (!(EXACT && HNF && T.cnt) && (count < BN || key_first < 0 || key_last > i0)) {
       // the keys of an extra tile at or above the block's first row (listed
       // high-norm keys) are its ascending last slots: the row keeps the slots
       // of the tile's keys up to its own position, counted slot by slot
@@ -565,20 +565,22 @@ __device__ __forceinline__ void attn_body(const AttnArgs& A, int wg) {
       }
     }
     if (EXACT && T.cnt && HNF) {
-      // extra tiles: a listed high-norm key (bit 29; the ranges cover it) is
-      // attended by the rows of its row mask, which the plan stores after the
-      // block's list (two words per entry: rows 0-31, 32-63); the other
-      // entries are vertical columns, attended by every row they do not
-      // follow (causal mask above)
+      // extra tiles: an entry with bit 29 (a covered high-norm key or a
+      // covered vertical column) is attended by the rows of its row mask,
+      // which the plan stores after the block's list (two words per entry:
+      // rows 0-31, 32-63; causal included); the other entries are vertical
+      // columns the ranges miss, attended by every row they do not follow.
+      // The entries of a mode are not in key order, so each slot is tested.
       const int E = A.ext_stride / 3;
       uint32_t xh = 0u;
 #pragma unroll
       for (int vv = 0; vv < 16; ++vv) {
         const int c = 8 * (vv >> 2) + (vv & 3);
-        const int e = __shfl(skey, c + 4 * half);
-        const int idx = min(T.eoff + c + 4 * half, E - 1);
+        const int slot = c + 4 * half;
+        const int e = __shfl(skey, slot);
+        const int idx = min(T.eoff + slot, E - 1);
         const uint32_t w = (uint32_t)ext_h[E + 2 * idx + wrow];
-        const bool keep = !((e >> 29) & 1) || ((w >> l32) & 1u);
+        const bool keep = slot < count && (((e >> 29) & 1) ? ((w >> l32) & 1u) != 0u : (e & 0x1FFFFFFF) <= prow);
         xh |= (uint32_t)keep << c;
       }
 #pragma unroll

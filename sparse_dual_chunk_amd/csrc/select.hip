@@ -442,6 +442,31 @@ __global__ void __launch_bounds__(256) plan_ext_kernel(PlanArgs A) {
     mb1 += __popcll(__ballot(mk && j < segB));
     mbn += __popcll(__ballot(mk));
   }
+  // Exact diagonals, KV heads with at most HN_MOVE_CAP high-norm keys: the
+  // vertical columns the ranges cover (other than the listed high-norm keys)
+  // are listed too, after each mode's high-norm keys (bit 29, with a row mask
+  // of the rows whose diagonal does not already reach them in the range
+  // tiles), so the range tiles need no vertical-column test.
+  const bool list_cv = A.dbits && A.hnl_n[g] <= HN_MOVE_CAP;
+  auto covered_col = [&](int t, int& j) -> bool {
+    j = -1;
+    if (!list_cv || t >= A.k_v) return false;
+    j = vi[t];
+    const int prev = (t > 0) ? vi[t - 1] : -1;
+    if (j < 0 || j >= hi_key || j == prev) return false;
+    const int bit = j - i0 + A.p_last;
+    return ((cv[bit >> 5] >> (bit & 31)) & 1u) && !((kb[j >> 5] >> (j & 31)) & 1u);
+  };
+  int vb0 = 0, vb1 = 0, vbn = 0;   // listed covered columns below segA, below segB, in all
+  if (list_cv) {
+    for (int base = 0; base < A.k_v; base += 64) {
+      int j;
+      const bool ck = covered_col(base + lane, j);
+      vb0 += __popcll(__ballot(ck && j < segA));
+      vb1 += __popcll(__ballot(ck && j < segB));
+      vbn += __popcll(__ballot(ck));
+    }
+  }
   int cnt = 0, ca0 = 0, ca1 = 0;   // columns in all, below segA, below segB
   for (int base = 0; base < A.k_v; base += 64) {
     const int t = base + lane;
@@ -459,8 +484,8 @@ __global__ void __launch_bounds__(256) plan_ext_kernel(PlanArgs A) {
     if (keep) {
       const int pos = __popcll(bal & ((1ull << lane) - 1ull));
       const int flagged = (kb[j >> 5] >> (j & 31)) & 1u;
-      // after the moved keys of the earlier modes
-      dst[cnt + pos + (j < segA ? 0 : (j < segB ? mb0 : mb1))] = j | (flagged << 30);
+      // after the moved keys and listed covered columns of the earlier modes
+      dst[cnt + pos + (j < segA ? 0 : (j < segB ? mb0 + vb0 : mb1 + vb1))] = j | (flagged << 30);
     }
     cnt += __popcll(bal);
     ca0 += __popcll(__ballot(keep && j < segA));
@@ -473,7 +498,7 @@ __global__ void __launch_bounds__(256) plan_ext_kernel(PlanArgs A) {
     const unsigned long long bal = __ballot(mk);
     if (mk) {
       const int pos = k0 + __popcll(bal & ((1ull << lane) - 1ull));
-      const int at = pos + (j < segA ? ca0 : (j < segB ? ca1 : cnt));
+      const int at = pos + (j < segA ? ca0 : (j < segB ? ca1 + vb0 : cnt + vb1));
       dst[at] = j | (3 << 29);
       if (A.dbits) {
         // exact diagonals: the block rows r that attend key j, whose offset
@@ -495,6 +520,31 @@ __global__ void __launch_bounds__(256) plan_ext_kernel(PlanArgs A) {
       }
     }
     k0 += __popcll(bal);
+  }
+  // the listed covered columns, each after its mode's columns and moved keys:
+  // row mask = the rows not above the column whose offset to it is not selected
+  if (list_cv) {
+    const uint32_t* db = A.dbits + (long long)h * A.dbits_words;
+    const int E = A.ext_stride / 3;
+    for (int base = 0, k0 = 0; base < A.k_v; base += 64) {
+      int j;
+      const bool ck = covered_col(base + lane, j);
+      const unsigned long long bal = __ballot(ck);
+      if (ck) {
+        const int pos = k0 + __popcll(bal & ((1ull << lane) - 1ull));
+        const int at = pos + (j < segA ? ca0 + mb0 : (j < segB ? ca1 + mb1 : cnt + mbn));
+        dst[at] = j | (1 << 29);
+        const int b0 = i0 - j + 128;   // >= 65: j < i0 + 64
+        const int w = b0 >> 5, sh = b0 & 31;
+        const uint64_t x01 = (uint64_t)db[w] | ((uint64_t)db[w + 1] << 32);
+        const uint64_t x12 = (uint64_t)db[w + 1] | ((uint64_t)db[w + 2] << 32);
+        const uint64_t slash = (uint64_t)(uint32_t)(x01 >> sh) | ((uint64_t)(uint32_t)(x12 >> sh) << 32);
+        const uint64_t rm = (j <= i0 ? ~0ull : (~0ull << (j - i0))) & ~slash;
+        dst[E + 2 * at] = (int32_t)(uint32_t)rm;
+        dst[E + 2 * at + 1] = (int32_t)(uint32_t)(rm >> 32);
+      }
+      k0 += __popcll(bal);
+    }
   }
   const int32_t* ivh = A.iv + (long long)h * A.iv_stride * 2;
   const int32_t* pre = A.iv_pre + (long long)h * (A.iv_stride + 1);
@@ -523,7 +573,7 @@ __global__ void __launch_bounds__(256) plan_ext_kernel(PlanArgs A) {
     }
   }
   if (lane == 0) {
-    A.n_ext[unit] = cnt + mbn;
+    A.n_ext[unit] = cnt + mbn + vbn;
     const int rows = hi_key - i0;
     long long below[2];
     below[0] = covered_below(ivh, pre, n_iv, -i0);
